@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Decode-step throughput of the top-k sparse attention path on one MI355X.
+
+Workload: the batched grouped-query exact variant at L = 128K, k = 4096
+(B = 16 sequences, 64 query heads over 8 KV heads, d = 128, bf16 caches with
+0.5% planted aligned keys), one fused topk_decode call per step: score every
+cached key, exact top-k per (sequence, query head), softmax attention over
+the kept K/V rows. Inputs are seeded synthetic caches resident in HBM before
+timing starts (8 GiB of K and V, far above the 256 MB last-level cache).
+
+Prints one JSON line: queries/s (value), the HBM GB/s over the counted bytes
+(full K scan + k gathered K and V rows per query head) and its fraction of
+8 TB/s, the roofline of the dominant kernel (the scoring scan, timed alone
+with HIP events on the launch stream), and the fp64 CPU oracle's throughput
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
+METRIC = "decode queries/sec and HBM GB/s (% of roofline) at L=128K, k=4096, 1 MI355X"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def esize(w):
+    import fixtures as fx
+    return 4 if w.dtype == fx.F32 else 2
+
+
+def counted_bytes(w) -> int:
+    """Bytes a decode step must move: the full scan of the scored keys plus the
+    kept K and V rows of every query head (shared kept sets: per KV head)."""
+    import fixtures as fx
+    es = esize(w)
+    row = w.d * es
+    if w.mode == fx.MODE_EXACT:
+        kk = min(w.k, w.L)
+        return w.B * w.Hkv * w.L * row + 2 * w.B * w.Hq * kk * row
+    if w.mode == fx.MODE_BLOCK:
+        m = w.m
+        kk = min(w.k, m - 1)
+        cur = w.L - (m - 1) * w.block
+        return w.B * w.Hkv * m * w.d * 4 + 2 * w.B * w.Hq * (kk * w.block + cur) * row
+    kk = min(w.k, w.L)
+    return w.B * w.L * w.dI + 2 * w.B * w.Hkv * kk * row
+
+
+def score_kernel_bytes(w) -> int:
+    """Algorithmic bytes of one scoring launch: keys read once, q read, fp32 scores written."""
+    import fixtures as fx
+    es = esize(w)
+    if w.mode == fx.MODE_EXACT:
+        return w.B * w.Hkv * w.L * w.d * es + w.B * w.Hq * w.d * es + 4 * w.B * w.Hq * w.L
+    if w.mode == fx.MODE_BLOCK:
+        return w.B * w.Hkv * w.m * w.d * 4 + w.B * w.Hq * w.d * es + 4 * w.B * w.Hq * (w.m - 1)
+    return w.B * w.L * w.dI + w.B * w.HI * (w.dI + 4) + 4 * w.B * w.L
+
+
+def traffic_from_profiles(kernel: str, source: str):
+    """Measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated),
+    if profiles/counters.json holds them for the current kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)[kernel]
+        with open(source, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def time_loop(fn, steps: int) -> float:
+    """Average ms per call from HIP events on the current stream (the launch stream)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(w, q, K, V, budget_s: float):
+    """The fp64 oracle, as it stands, on whole queries (all heads of one
+    sequence) of the same workload until about budget_s seconds have passed."""
+    import oracle as orc
+    p = orc.problem_for(w)
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.B:
+        rows = list(range(done * w.Hq, (done + 1) * w.Hq))
+        orc.decode(p, q, K, V, rows=rows)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "queries/s", "cores": orc.threads(), "kind": "oracle",
+            "sample": f"{done} whole queries ({done * w.Hq} query-head rows of L={w.L}) of the timed workload: "
+                      f"fp64 scores, full sort, fp64 attention; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C3", help="fixtures.WORKLOADS key (C3 is the headline)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    import top_sparse_attention_topk_amd as tka
+
+    w = fx.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name}")
+    q, K, V = fx.make_attn(w)
+    to = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()) if w.dtype == fx.BF16 else \
+        (lambda a: torch.from_numpy(a).cuda())
+    qt, Kt, Vt = to(q), to(K), to(V)
+    dt = tka.TKA_BF16 if w.dtype == fx.BF16 else tka.TKA_F32
+    p = tka.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, 0.0, w.block, w.HI, w.dI)
+    kw = {}
+    if w.mode == fx.MODE_BLOCK:
+        kw["proxy_keys"] = tka.topk_block_mean_build(p, Kt)
+    elif w.mode == fx.MODE_INDEXER:
+        qI, kI, wt = fx.make_indexer(w)
+        kw = dict(proxy_keys=torch.from_numpy(kI).cuda(), q_idx=torch.from_numpy(qI).cuda(),
+                  idx_w=torch.from_numpy(wt).cuda())
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.B, w.k) if w.mode == fx.MODE_INDEXER else (w.B, w.Hq, w.k), dtype=torch.int32,
+                      device="cuda")
+    ws = torch.empty(tka.topk_decode_workspace_size(p), dtype=torch.uint8, device="cuda")
+    step = lambda: tka.topk_decode(p, qt, Kt, Vt, out=out, idx_out=idx, ws=ws, **kw)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    qps = w.B / (ms / 1e3)
+    cb = counted_bytes(w)
+    gbps = cb / (ms / 1e3) / 1e9
+
+    # per-kernel split: each step of the path launched alone on the same stream
+    log("[bench] per-kernel timing")
+    if w.mode == fx.MODE_INDEXER:
+        score_call = lambda: tka.topk_attn_score(p, kw["q_idx"], kw["proxy_keys"], idx_w=kw["idx_w"], scores=sc)
+    elif w.mode == fx.MODE_BLOCK:
+        score_call = lambda: tka.topk_attn_score(p, qt, kw["proxy_keys"], scores=sc)
+    else:
+        score_call = lambda: tka.topk_attn_score(p, qt, Kt, scores=sc)
+    sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
+    t_score = time_loop(score_call, args.steps)
+    rows = sc.numel() // sc.shape[-1]
+    sel_idx = torch.empty((rows, w.k), dtype=torch.int32, device="cuda")
+    sel_val = torch.empty((rows, w.k), dtype=torch.float32, device="cuda")
+    nws = tka.topk_select_workspace_size(rows, sc.shape[-1], w.k)
+    sws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    exact = w.mode == fx.MODE_EXACT
+    t_select = time_loop(lambda: tka.topk_select(sc.reshape(rows, -1), w.k, idx_out=sel_idx,
+                                                 sel_out=sel_val if exact else None, want_sel=exact, ws=sws),
+                         args.steps)
+    unit = w.block if w.mode == fx.MODE_BLOCK else 0
+    shared = w.mode == fx.MODE_INDEXER
+    gout = torch.empty_like(out)
+    t_gather = time_loop(lambda: tka.sparse_attn_gather(p, qt, Kt, Vt, sel_idx, idx_unit=unit, shared=shared,
+                                                        sel_scores=sel_val if exact else None, out=gout),
+                         args.steps)
+    kname = {fx.MODE_EXACT: "score_exact_mfma_kernel" if tka.TKA_BF16 == dt and 2 <= w.G <= 16
+             else "score_vec_kernel", fx.MODE_BLOCK: "score_vec_kernel",
+             fx.MODE_INDEXER: "score_indexer_kernel"}[w.mode]
+    sbytes = score_kernel_bytes(w)
+    achieved = sbytes / (t_score / 1e3) / 1e9
+    traffic = traffic_from_profiles(kname, os.path.join(ROOT, "top_sparse_attention_topk_amd", "csrc",
+                                                        "score.hip"))
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": kname, "algorithmic_bytes": sbytes, "avg_launch_ms": round(t_score, 4)}
+
+    result = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == fx.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "seq_len": w.L, "top_k": w.k, "path": "fused topk_decode",
+                   "gather_logits": "selected scores" if exact else "K rows"},
+        "hbm_gbps_counted": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "counted_bytes_per_step": cb, "event_ms_per_step": round(ev_ms, 4),
+        "kernel_ms": {"score": round(t_score, 4), "select": round(t_select, 4), "gather": round(t_gather, 4)},
+        "roofline": roofline,
+    }
+    del Kt, Vt, sc, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, q, K, V, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

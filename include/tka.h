@@ -1,0 +1,182 @@
+/*
+ * tka.h - C ABI of the MI355X (gfx950) top-k sparse decode-attention library
+ * (libtka.so).
+ *
+ * One decode step of top-k sparse attention, as the pages state it: for the
+ * current query, score every cached position (or block of positions), keep
+ * the k highest scores, then run exact softmax attention over the kept keys
+ * and values only ("Sparse Attention in LLM Inference: Practical
+ * Trade-Offs", "The Role of the Indexer" workflow; "Evolution of Sparse
+ * Attention in Long-Context LLMs", section 2; the scoring variants are those
+ * of "Sparse Attention Landscape", "Block Sparse Attention" and "Token Sparse
+ * Attention").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is caller-owned DEVICE memory. The library allocates
+ *   and frees nothing; scratch comes from a caller workspace whose size the
+ *   *_workspace_size calls report. Inputs are never written; outputs are
+ *   overwritten in full. Outputs must not overlap inputs.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *   only enqueue work; the library never synchronises. A device fault shows
+ *   up at the caller's next synchronisation.
+ * - All argument checks run on the host before any launch and need no GPU.
+ *   A failed check returns its status and launches nothing;
+ *   tka_last_error() then names the argument (per calling thread).
+ * - Base pointers and row strides must be 16-byte aligned (128-bit loads);
+ *   otherwise TKA_ERR_ALIGNMENT.
+ * - Same inputs, shapes and device give bitwise-identical outputs; the fused
+ *   topk_decode equals the three-call composition bitwise.
+ * - Calls are stateless and reentrant; concurrent calls on different streams
+ *   need distinct workspaces.
+ *
+ * Shapes (all contiguous unless a stride is given; element counts):
+ *   q          [B, Hq, d]       in qkv_dtype
+ *   K, V cache [B, Hkv, L, d]   in qkv_dtype, element strides kv_stride_b/h/l,
+ *                               the d elements of a row contiguous
+ *   out        [B, Hq, d]       fp32
+ *   Query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ */
+#ifndef TKA_H
+#define TKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TKA_ABI_VERSION 1
+
+typedef enum {
+  TKA_OK = 0,
+  TKA_ERR_INVALID_ARG = 1, /* bad shape, count, null pointer or overlap */
+  TKA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, dtype, head grouping */
+  TKA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required */
+  TKA_ERR_ALIGNMENT = 4,   /* pointer or stride not 16-byte aligned */
+  TKA_ERR_HIP = 5          /* a HIP launch reported an error */
+} tka_status;
+
+typedef enum { TKA_F32 = 0, TKA_BF16 = 1, TKA_FP8_E4M3 = 2 /* OCP E4M3FN */ } tka_dtype;
+
+typedef enum {
+  /* s[b,h,i] = scale * <q[b,h], K[b,g(h),i]>, i < L; one kept set per (b, h).
+     ("Sparse Attention Landscape", "Token Sparse Attention", s_i = f(q_t, k_i).) */
+  TKA_SCORE_EXACT = 0,
+  /* r[b,h,j] = <q[b,h], mean of K[b,g(h)] over block j>, j < m-1, m = ceil(L/b),
+     no scale; keep the top-k blocks, then also attend the current block m-1.
+     ("Sparse Attention Landscape", "Block Sparse Attention", MoBA mean-pooling.) */
+  TKA_SCORE_BLOCK_MEAN = 1,
+  /* I[b,i] = sum_j w[b,j] * max(0, <qI[b,j], kI[b,i]>), no scale; one kept set per
+     sequence, shared by every head. ("Sparse Attention Landscape", "Token Sparse
+     Attention", lightning indexer with query-dependent head weights.) */
+  TKA_SCORE_INDEXER = 2
+} tka_score_mode;
+
+typedef struct {
+  int32_t batch;      /* B >= 1 */
+  int32_t n_q_heads;  /* Hq >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;   /* d: 32, 64, 128 or 256 */
+  int32_t seq_len;    /* L >= 1 cached keys; the query sits at position L-1 (no causal mask) */
+  int32_t top_k;      /* k >= 1 tokens (EXACT, INDEXER) or blocks (BLOCK_MEAN); k' = min(k, candidates) */
+  int64_t kv_stride_b, kv_stride_h, kv_stride_l; /* element strides of the K and V caches */
+  tka_dtype qkv_dtype; /* TKA_F32 or TKA_BF16 (q, K, V) */
+  float scale;         /* softmax logit scale; <= 0 selects 1/sqrt(d) */
+  tka_score_mode mode;
+  int32_t block_size;  /* BLOCK_MEAN: b >= 1 */
+  int32_t n_idx_heads; /* INDEXER: H_I in [1, 128] */
+  int32_t idx_dim;     /* INDEXER: d_I, a multiple of 64 up to 256 */
+  tka_dtype idx_dtype; /* INDEXER: TKA_FP8_E4M3 */
+} tka_problem;
+
+/*
+ * Scoring pass (one of the three variants above), writes fp32 scores.
+ *   EXACT:      q [B,Hq,d]; keys = K cache; scores [B,Hq,L].
+ *   BLOCK_MEAN: q [B,Hq,d]; keys = block means [B,Hkv,m,d] fp32 contiguous (from
+ *               topk_block_mean_build); scores [B,Hq,m-1] (the current block does
+ *               not compete). Nothing is written when m == 1.
+ *   INDEXER:    q = qI [B,H_I,d_I] E4M3FN; keys = kI [B,L,d_I] E4M3FN;
+ *               idx_w [B,H_I] fp32; scores [B,L].
+ * idx_w must be NULL unless mode is INDEXER.
+ */
+tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys, const float* idx_w,
+                           float* scores, void* stream);
+
+/*
+ * Exact top-k of each score row ("Sparse Attention Landscape", "Block Sparse
+ * Attention", the TopK_j s_j operator). Order: i before j when s_i > s_j, or
+ * s_i == s_j and i < j; -0 equals +0; NaN ranks below every number. Row r
+ * holds row_len fp32 values at scores + r*row_stride.
+ *   idx_out       [n_rows, k] int32: the k' = min(k, row_len) kept positions in
+ *                 ascending order, then -1 up to k.
+ *   sel_scores_out [n_rows, k] fp32 or NULL: the kept scores aligned with idx_out
+ *                 (bit patterns copied), -inf in padded slots.
+ * ws/ws_bytes: scratch of at least topk_select_workspace_size bytes.
+ */
+tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, int32_t k,
+                       int32_t* idx_out, float* sel_scores_out, void* ws, size_t ws_bytes, void* stream);
+
+tka_status topk_select_workspace_size(int64_t n_rows, int32_t row_len, int32_t k, size_t* bytes);
+
+/*
+ * Exact softmax attention over kept positions only ("Sparse Attention in LLM
+ * Inference", "Changes in Caching Strategy": batch reads of the KV cache
+ * through a position index built from the Top-K result; "Computational and
+ * Memory Access Benefits": O(K d) work per query).
+ *   idx: [B,Hq,n_idx] lists (one per query head) or, with
+ *        shared_across_heads != 0, [B,n_idx] lists used by every head of b.
+ *   idx_unit: 0 -> entries are token positions; b >= 1 -> entries are block ids
+ *        covering [j b, min((j+1) b, L)) and the current block ceil(L/b)-1 is
+ *        attended as well (ids outside [0, ceil(L/b)-1) are skipped).
+ *        Entries < 0 or >= L (tokens) are skipped.
+ *   sel_scores: NULL, or (idx_unit 0, per-head lists only) the logits of the
+ *        listed tokens aligned with idx, i.e. scale*<q,K_i> as written by
+ *        topk_attn_score (EXACT) and topk_select; K rows are then not re-read.
+ *   out: [B,Hq,d] fp32, o = sum_i e^(z_i - M) V_i / sum_i e^(z_i - M) with
+ *        z_i = scale*<q, K_i>; a row with no valid entry is written as zeros.
+ */
+tka_status sparse_attn_gather(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* idx, int32_t n_idx, int32_t idx_unit, int32_t shared_across_heads,
+                              const float* sel_scores, float* out, void* ws, size_t ws_bytes, void* stream);
+
+tka_status sparse_attn_gather_workspace_size(const tka_problem* p, int32_t n_idx, int32_t idx_unit,
+                                             int32_t shared_across_heads, size_t* bytes);
+
+/*
+ * The whole step in one call, on one stream: score -> select -> gather, with
+ * the same kernels and launch shapes as the three calls above (bitwise equal
+ * results).
+ *   EXACT:      proxy_keys, q_idx, idx_w NULL; the gather uses the selected scores.
+ *   BLOCK_MEAN: proxy_keys = block means [B,Hkv,m,d] fp32; idx_out (if given)
+ *               [B,Hq,k] block ids without the current block.
+ *   INDEXER:    proxy_keys = kI [B,L,d_I], q_idx = qI [B,H_I,d_I], idx_w [B,H_I];
+ *               idx_out (if given) [B,k].
+ * idx_out may be NULL (the indices then live in the workspace).
+ */
+tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                       const void* proxy_keys, const void* q_idx, const float* idx_w, float* out,
+                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+tka_status topk_decode_workspace_size(const tka_problem* p, size_t* bytes);
+
+/*
+ * Block-mean key cache for BLOCK_MEAN ("Sparse Attention Landscape", "Block
+ * Sparse Attention": MoBA mean-pools the keys of each block): means[b,g,j,:] =
+ * (1/n_j) sum over the n_j keys of block j of K[b,g,i,:], fp32, [B,Hkv,m,d]
+ * contiguous, m = ceil(L/b) (the last block may be partial). Built once, off
+ * the decode step.
+ */
+tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, float* means, void* stream);
+
+const char* tka_status_str(tka_status s);
+/* detail of the last failed argument check in the calling thread ("" if none) */
+const char* tka_last_error(void);
+int32_t tka_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TKA_H */

@@ -56,6 +56,7 @@ def lib():
         L.orc_decode.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp]
         L.orc_diag_exact.argtypes = [P, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp]
         L.orc_decode_buf.argtypes = [ctypes.c_int, _vp, _i64, _vp]
+        L.orc_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -162,3 +163,8 @@ def decode_values(dt: int, raw):
     out = np.empty(raw.size, np.float64)
     lib().orc_decode_buf(dt, _ptr(raw), raw.size, _ptr(out))
     return out.reshape(raw.shape)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())

@@ -35,6 +35,7 @@
  * KL(P-hat||P), the head/tail means of V and the entropy of P.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -398,3 +399,6 @@ int orc_diag_exact(const orc_problem* p, const void* q, const void* K, const voi
   free(srt);
   return 0;
 }
+
+/* threads an OpenMP region of the oracle uses */
+int orc_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,71 @@
+"""Helpers shared by the GPU parity tests (the oracle side and the library
+side see the same fixture bytes; nothing here computes the method)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import fixtures as fx
+import oracle as orc
+
+BF16_TOL = 2e-3   # max abs error of outputs for bf16 inputs
+F32_TOL = 1e-5    # max abs error of outputs for fp32 inputs
+
+
+def tka():
+    import top_sparse_attention_topk_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def problem(w: fx.Workload, scale: float = 0.0):
+    m = tka()
+    dt = m.TKA_BF16 if w.dtype == fx.BF16 else m.TKA_F32
+    return m.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, scale, w.block, w.HI, w.dI)
+
+
+def tol(w: fx.Workload) -> float:
+    return BF16_TOL if w.dtype == fx.BF16 else F32_TOL
+
+
+def as_f64(a: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == fx.BF16:
+        return fx.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def exact_score_bound(w, q, K, rows):
+    """Forward-error bound of an fp32 dot product of length d, scaled:
+    d * 2^-23 * scale * sum_c |q_c k_c| (recursive summation bound with slack)."""
+    qf, Kf = np.abs(as_f64(q, w.dtype)), np.abs(as_f64(K, w.dtype))
+    G = w.Hq // w.Hkv
+    out = []
+    for r in rows:
+        b, h = divmod(int(r), w.Hq)
+        out.append(Kf[b, h // G] @ qf[b, h])
+    scale = 1.0 / np.sqrt(w.d)
+    return np.stack(out) * scale * w.d * 2.0 ** -23 + 1e-30
+
+
+def indexer_score_bound(w, qI, kI, wt, b):
+    qd = np.abs(orc.decode_values(orc.E4M3, qI[b]))
+    kd = np.abs(orc.decode_values(orc.E4M3, kI[b]))
+    s = (kd @ qd.T) @ wt[b].astype(np.float64)
+    return s * (w.dI + w.HI + 2) * 2.0 ** -23 + 1e-30
+
+
+def gpu_scores_np(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy()

@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/tka.h declares, and every argument check fails with its own status
+before any launch (so these calls are safe on a machine without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tka.h")
+
+tka = pytest.importorskip("top_sparse_attention_topk_amd")
+LIB = tka.LIB
+
+FAKE = 1 << 40  # aligned, never dereferenced: every call below fails its checks first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"topk_attn_score", "topk_select", "sparse_attn_gather", "topk_decode"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", tka.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert LIB.tka_abi_version() == 1
+
+
+def _status(code):
+    return LIB.tka_status_str(code).decode()
+
+
+def _p(**kw):
+    base = dict(mode=tka.EXACT, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=1000, top_k=64,
+                dtype=tka.TKA_BF16)
+    base.update(kw)
+    return tka.problem(**base)
+
+
+def _score(p, q=FAKE, keys=FAKE * 2, w=None, scores=FAKE * 3):
+    return LIB.topk_attn_score(ctypes.byref(p), q, keys, w, scores, None)
+
+
+def test_status_strings():
+    assert [_status(i) for i in range(6)] == ["TKA_OK", "TKA_ERR_INVALID_ARG", "TKA_ERR_UNSUPPORTED",
+                                               "TKA_ERR_WORKSPACE", "TKA_ERR_ALIGNMENT", "TKA_ERR_HIP"]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), tka.TKA_ERR_INVALID_ARG),
+    (dict(seq_len=0), tka.TKA_ERR_INVALID_ARG),
+    (dict(batch=0), tka.TKA_ERR_INVALID_ARG),
+    (dict(n_q_heads=6, n_kv_heads=4), tka.TKA_ERR_INVALID_ARG),
+    (dict(head_dim=96), tka.TKA_ERR_UNSUPPORTED),
+    (dict(dtype=tka.TKA_FP8_E4M3), tka.TKA_ERR_UNSUPPORTED),
+    (dict(mode=tka.BLOCK_MEAN, block_size=0), tka.TKA_ERR_INVALID_ARG),
+    (dict(mode=tka.INDEXER, n_idx_heads=32, idx_dim=96), tka.TKA_ERR_UNSUPPORTED),
+    (dict(mode=tka.INDEXER, n_idx_heads=0, idx_dim=64), tka.TKA_ERR_INVALID_ARG),
+    (dict(strides=(1000 * 2 * 128, 1000 * 128, 100)), tka.TKA_ERR_INVALID_ARG),
+    (dict(strides=(1000 * 2 * 136, 1000 * 136, 132)), tka.TKA_ERR_ALIGNMENT),
+])
+def test_problem_checks(kw, status):
+    p = _p(**kw)
+    assert _score(p, w=FAKE * 4 if p.mode == tka.INDEXER else None) == status
+    assert LIB.tka_last_error().decode() != ""
+
+
+def test_score_pointer_checks():
+    p = _p()
+    assert _score(p, q=None) == tka.TKA_ERR_INVALID_ARG
+    assert _score(p, q=FAKE + 8) == tka.TKA_ERR_ALIGNMENT
+    assert _score(p, scores=None) == tka.TKA_ERR_INVALID_ARG
+    assert _score(p, w=FAKE * 4) == tka.TKA_ERR_INVALID_ARG  # idx_w only for the indexer
+    assert _score(p, scores=FAKE * 2 + 64) == tka.TKA_ERR_INVALID_ARG  # scores inside the K cache
+    pi = _p(mode=tka.INDEXER, n_idx_heads=32, idx_dim=64)
+    assert _score(pi, w=None) == tka.TKA_ERR_INVALID_ARG
+
+
+def _select(scores=FAKE, n_rows=4, row_len=100, stride=100, k=10, idx=FAKE * 2, sel=None, ws=None, ws_bytes=0):
+    return LIB.topk_select(scores, n_rows, row_len, stride, k, idx, sel, ws, ws_bytes, None)
+
+
+def test_select_checks():
+    assert _select(k=0) == tka.TKA_ERR_INVALID_ARG
+    assert _select(stride=50) == tka.TKA_ERR_INVALID_ARG
+    assert _select(idx=None) == tka.TKA_ERR_INVALID_ARG
+    assert _select(scores=FAKE + 2) == tka.TKA_ERR_ALIGNMENT
+    assert _select(idx=FAKE + 8) == tka.TKA_ERR_INVALID_ARG  # idx_out inside the scores
+    assert _select(n_rows=-1) == tka.TKA_ERR_INVALID_ARG
+    # few long rows need scratch
+    need = tka.topk_select_workspace_size(2, 1 << 20, 2048)
+    assert need > 0
+    assert _select(n_rows=2, row_len=1 << 20, stride=1 << 20, k=2048, idx=FAKE * 4) == tka.TKA_ERR_WORKSPACE
+    assert _select(n_rows=2, row_len=1 << 20, stride=1 << 20, k=2048, idx=FAKE * 4, ws=FAKE * 8,
+                   ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
+    # many rows: one workgroup per row, no scratch
+    assert tka.topk_select_workspace_size(1024, 131072, 4096) == 0
+
+
+def _gather(p, q=FAKE, K=FAKE * 2, V=FAKE * 3, idx=FAKE * 4, n_idx=64, unit=0, shared=0, sel=None, out=FAKE * 5,
+            ws=None, ws_bytes=0):
+    return LIB.sparse_attn_gather(ctypes.byref(p), q, K, V, idx, n_idx, unit, shared, sel, out, ws, ws_bytes, None)
+
+
+def test_gather_checks():
+    p = _p()
+    assert _gather(p, n_idx=0) == tka.TKA_ERR_INVALID_ARG
+    assert _gather(p, unit=-1) == tka.TKA_ERR_INVALID_ARG
+    assert _gather(p, V=None) == tka.TKA_ERR_INVALID_ARG
+    assert _gather(p, out=FAKE * 2 + 256) == tka.TKA_ERR_INVALID_ARG  # out inside K
+    assert _gather(p, shared=1, sel=FAKE * 6) == tka.TKA_ERR_INVALID_ARG
+    assert _gather(p, unit=64, sel=FAKE * 6) == tka.TKA_ERR_INVALID_ARG
+    assert _gather(_p(n_q_heads=6, n_kv_heads=2), shared=1) == tka.TKA_ERR_UNSUPPORTED
+    # split work needs partials
+    small = _p(batch=1, n_q_heads=4, n_kv_heads=1, seq_len=100000, top_k=4096)
+    need = tka.sparse_attn_gather_workspace_size(small, 4096)
+    assert need > 0 and _gather(small, n_idx=4096) == tka.TKA_ERR_WORKSPACE
+
+
+def test_decode_checks_and_workspace():
+    p = _p()
+    need = tka.topk_decode_workspace_size(p)
+    assert need >= 2 * 8 * 1000 * 4  # at least the score array
+    call = lambda **kw: LIB.topk_decode(ctypes.byref(p), kw.get("q", FAKE), kw.get("K", FAKE * 2),
+                                        kw.get("V", FAKE * 3), kw.get("proxy"), kw.get("qi"), kw.get("w"),
+                                        kw.get("out", FAKE * 5), kw.get("idx"), kw.get("ws", FAKE * 8),
+                                        kw.get("ws_bytes", need), None)
+    assert call(ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
+    assert call(ws=None) == tka.TKA_ERR_WORKSPACE
+    assert call(proxy=FAKE * 6) == tka.TKA_ERR_INVALID_ARG  # no proxy keys in the exact variant
+    assert call(out=None) == tka.TKA_ERR_INVALID_ARG
+    assert call(idx=FAKE * 5) == tka.TKA_ERR_INVALID_ARG  # idx_out overlapping out
+    pb = _p(mode=tka.BLOCK_MEAN, block_size=64)
+    assert LIB.topk_decode(ctypes.byref(pb), FAKE, FAKE * 2, FAKE * 3, None, None, None, FAKE * 5, None, FAKE * 8,
+                           1 << 30, None) == tka.TKA_ERR_INVALID_ARG  # block means missing
+    assert LIB.topk_block_mean_build(ctypes.byref(p), FAKE, FAKE * 2, None) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_scale_with_problem():
+    c3 = tka.problem(tka.EXACT, 16, 64, 8, 128, 131072, 4096)
+    n = tka.topk_decode_workspace_size(c3)
+    assert 16 * 64 * 131072 * 4 <= n < 16 * 64 * 131072 * 4 + (64 << 20)

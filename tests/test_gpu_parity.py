@@ -1,0 +1,196 @@
+"""GPU parity of each step and of the whole step against the fp64 oracle, on
+seeded inputs of every workload recipe at sizes the oracle finishes in
+seconds (several tiles, ragged tails, both select launch shapes, split and
+unsplit gathers).
+
+Bars: scores within the fp32 forward-error bound; selected indices bit-exact
+against the oracle's select run on the GPU's own fp32 score array (and the
+returned scores equal to those array entries); outputs within 2e-3 (bf16
+inputs) / 1e-5 (fp32) of the oracle's attention over the GPU's index set;
+fused == three calls, bitwise; a second run is bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fixtures as fx
+import oracle as orc
+from tests.gpu_common import (as_f64, dev, exact_score_bound, gpu_scores_np, indexer_score_bound, problem, say,
+                              tka, tol)
+
+pytestmark = pytest.mark.gpu
+
+W = fx.WORKLOADS
+CASES = {
+    "C1": W["C1"],
+    "C1-ragged": fx.shrink(W["C1"], 1001, k=64),
+    "C2-rows": fx.shrink(W["C2"], 5003, k=300),
+    "C2-split": fx.shrink(W["C2"], 40000),
+    "C3-small": fx.shrink(W["C3"], 6000, B=2, k=512),
+    "C4-small": fx.shrink(W["C4"], 64 * 150 + 17, B=2),
+    "C5-small": fx.shrink(W["C5"], 50001),
+}
+
+
+class Data:
+    pass
+
+
+_cache = {}
+
+
+def data(name):
+    if name in _cache:
+        return _cache[name]
+    w = CASES[name]
+    say(f"[gpu parity] generating {name}: {w}")
+    d = Data()
+    d.w = w
+    d.q, d.K, d.V = fx.make_attn(w)
+    d.qt, d.Kt, d.Vt = dev(d.q), dev(d.K), dev(d.V)
+    d.p = problem(w)
+    d.op = orc.problem_for(w)
+    if w.mode == fx.MODE_INDEXER:
+        d.qI, d.kI, d.wt = fx.make_indexer(w)
+        d.qIt, d.kIt, d.wtt = dev(d.qI), dev(d.kI), dev(d.wt)
+    _cache[name] = d
+    return d
+
+
+def gpu_scores(d):
+    m = tka()
+    if d.w.mode == fx.MODE_EXACT:
+        return m.topk_attn_score(d.p, d.qt, d.Kt)
+    if d.w.mode == fx.MODE_BLOCK:
+        d.means = m.topk_block_mean_build(d.p, d.Kt)
+        return m.topk_attn_score(d.p, d.qt, d.means)
+    return m.topk_attn_score(d.p, d.qIt, d.kIt, idx_w=d.wtt)
+
+
+def unit_of(w):
+    return w.block if w.mode == fx.MODE_BLOCK else 0
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_scores_within_forward_error_bound(name):
+    d = data(name)
+    w = d.w
+    s = gpu_scores_np(gpu_scores(d)).reshape(-1, orc.score_len(d.op))
+    ref = orc.score(d.op, d.q, d.K, getattr(d, "qI", None), getattr(d, "kI", None), getattr(d, "wt", None))
+    if w.mode == fx.MODE_EXACT:
+        bound = exact_score_bound(w, d.q, d.K, range(w.B * w.Hq))
+    elif w.mode == fx.MODE_INDEXER:
+        bound = np.stack([indexer_score_bound(w, d.qI, d.kI, d.wt, b) for b in range(w.B)])
+    else:  # block means (b + d terms) then a d-term dot
+        qa = np.abs(as_f64(d.q, w.dtype))
+        Ka = np.abs(as_f64(d.K, w.dtype))
+        m = w.m
+        pad = m * w.block - w.L
+        Kp = np.concatenate([Ka, np.zeros(Ka.shape[:2] + (pad, w.d))], 2) if pad else Ka
+        sizes = np.minimum(w.block, w.L - np.arange(m) * w.block)
+        mabs = Kp.reshape(w.B, w.Hkv, m, w.block, w.d).sum(3) / sizes[None, None, :, None]
+        G = w.G
+        bound = np.stack([mabs[b, h // G, : m - 1] @ qa[b, h] for b in range(w.B) for h in range(w.Hq)])
+        bound = bound * (w.d + w.block + 2) * 2.0 ** -23 + 1e-30
+    err = np.abs(s - ref)
+    assert np.all(err <= bound), (name, float((err / bound).max()))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_select_bit_exact_on_gpu_scores(name):
+    d = data(name)
+    w, m = d.w, tka()
+    st = gpu_scores(d)
+    s = gpu_scores_np(st).reshape(-1, orc.score_len(d.op))
+    idx, sel = m.topk_select(st.reshape(s.shape[0], s.shape[1]) if s.shape[1] else st.reshape(s.shape[0], 0), w.k)
+    idx2, sel2 = m.topk_select(st.reshape(s.shape[0], s.shape[1]), w.k)
+    gi, gs = idx.cpu().numpy(), sel.cpu().numpy()
+    want = orc.select(s.astype(np.float32), w.k)
+    assert np.array_equal(gi, want)
+    kk = min(w.k, s.shape[1])
+    rows = np.arange(s.shape[0])[:, None]
+    assert np.array_equal(gs[:, :kk].view(np.uint32), s[rows, gi[:, :kk]].astype(np.float32).view(np.uint32))
+    assert np.array_equal(gi, idx2.cpu().numpy()) and torch.equal(sel, sel2)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_gather_on_gpu_indices(name):
+    d = data(name)
+    w, m = d.w, tka()
+    st = gpu_scores(d)
+    rows = st.numel() // max(orc.score_len(d.op), 1)
+    idx, sel = m.topk_select(st.reshape(rows, -1), w.k)
+    shared = w.mode == fx.MODE_INDEXER
+    out = m.sparse_attn_gather(d.p, d.qt, d.Kt, d.Vt, idx, idx_unit=unit_of(w), shared=shared)
+    gi = idx.cpu().numpy()
+    ref = orc.attend(d.op, d.q, d.K, d.V, gi, unit=unit_of(w), list_mode=1 if shared else 0)
+    got = out.cpu().numpy().reshape(-1, w.d).astype(np.float64)
+    assert np.abs(got - ref).max() <= tol(w), float(np.abs(got - ref).max())
+    if w.mode == fx.MODE_EXACT:  # logits from the selected scores instead of the K rows
+        out2 = m.sparse_attn_gather(d.p, d.qt, d.Kt, d.Vt, idx, sel_scores=sel)
+        got2 = out2.cpu().numpy().reshape(-1, w.d).astype(np.float64)
+        assert np.abs(got2 - ref).max() <= tol(w), float(np.abs(got2 - ref).max())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_equals_three_calls_and_repeats(name):
+    d = data(name)
+    w, m = d.w, tka()
+    shared = w.mode == fx.MODE_INDEXER
+    if w.mode == fx.MODE_BLOCK:
+        means = m.topk_block_mean_build(d.p, d.Kt)
+        fused = lambda: m.topk_decode(d.p, d.qt, d.Kt, d.Vt, proxy_keys=means)
+    elif shared:
+        fused = lambda: m.topk_decode(d.p, d.qt, d.Kt, d.Vt, proxy_keys=d.kIt, q_idx=d.qIt, idx_w=d.wtt)
+    else:
+        fused = lambda: m.topk_decode(d.p, d.qt, d.Kt, d.Vt)
+    out_f, idx_f = fused()
+    out_f2, idx_f2 = fused()
+    st = gpu_scores(d)
+    rows = st.numel() // max(orc.score_len(d.op), 1)
+    idx, sel = m.topk_select(st.reshape(rows, -1), w.k, want_sel=w.mode == fx.MODE_EXACT)
+    out = m.sparse_attn_gather(d.p, d.qt, d.Kt, d.Vt, idx, idx_unit=unit_of(w), shared=shared,
+                               sel_scores=sel if w.mode == fx.MODE_EXACT else None)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f.reshape(idx.shape), idx)
+    assert torch.equal(out_f.view(torch.int32), out.view(torch.int32))
+    assert torch.equal(out_f2.view(torch.int32), out_f.view(torch.int32)) and torch.equal(idx_f2, idx_f)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_end_to_end_against_oracle(name):
+    """Oracle decode in fp64 vs the GPU step. Kept sets agree except where the
+    oracle's own scores put an element within the score error bound of the
+    k-th score; rows with the same set agree within the output tolerance."""
+    d = data(name)
+    w, m = d.w, tka()
+    if w.mode == fx.MODE_BLOCK:
+        means = m.topk_block_mean_build(d.p, d.Kt)
+        out, idx = m.topk_decode(d.p, d.qt, d.Kt, d.Vt, proxy_keys=means)
+    elif w.mode == fx.MODE_INDEXER:
+        out, idx = m.topk_decode(d.p, d.qt, d.Kt, d.Vt, proxy_keys=d.kIt, q_idx=d.qIt, idx_w=d.wtt)
+    else:
+        out, idx = m.topk_decode(d.p, d.qt, d.Kt, d.Vt)
+    gi = idx.cpu().numpy().reshape(-1, w.k)
+    got = out.cpu().numpy().reshape(-1, w.d).astype(np.float64)
+    ref_out, ref_idx = orc.decode(d.op, d.q, d.K, d.V, getattr(d, "qI", None), getattr(d, "kI", None),
+                                  getattr(d, "wt", None))
+    ref_out = ref_out.reshape(-1, w.d)
+    s_ref = orc.score(d.op, d.q, d.K, getattr(d, "qI", None), getattr(d, "kI", None), getattr(d, "wt", None))
+    same = np.all(gi == ref_idx, axis=1)
+    if w.mode == fx.MODE_EXACT:
+        bound = exact_score_bound(w, d.q, d.K, range(w.B * w.Hq)).max(1)
+    else:
+        bound = np.abs(s_ref).max(1) * 1e-5 + 1e-6
+    for r in np.nonzero(~same)[0]:
+        kk = min(w.k, s_ref.shape[1])
+        T = np.sort(s_ref[r])[::-1][kk - 1]
+        diff = set(gi[r][gi[r] >= 0].tolist()) ^ set(ref_idx[r][ref_idx[r] >= 0].tolist())
+        assert all(abs(s_ref[r][i] - T) <= 2 * bound[r] for i in diff), (name, r, sorted(diff)[:8])
+    say(f"[gpu parity] {name}: {int(same.sum())}/{len(same)} rows with identical kept sets")
+    if w.mode == fx.MODE_INDEXER:
+        same_rows = np.repeat(same, w.Hq)
+    else:
+        same_rows = same
+    if same_rows.any():
+        assert np.abs(got[same_rows] - ref_out[same_rows]).max() <= tol(w)

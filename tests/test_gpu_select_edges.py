@@ -1,0 +1,91 @@
+"""GPU top-k select on adversarial rows, bit-exact against the oracle's select
+on the same fp32 array: ties across the threshold (lower index wins), +-0,
++-inf, NaN (below -inf), all-equal rows, values sharing their top 20 bits
+(forces every radix level), sorted rows (candidates all in one wave), huge
+tie runs (streaming emit), k = 1, k = n - 1, k = n, k > n, empty rows, rows
+with a stride, and both launch shapes (one workgroup per row; chunked rows)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from tests.gpu_common import say, tka
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(kind, n_rows, n, rng):
+    if kind == "normal":
+        return rng.standard_normal((n_rows, n)).astype(np.float32)
+    if kind == "dups":
+        return np.round(rng.standard_normal((n_rows, n)), 1).astype(np.float32)
+    if kind == "equal":
+        return np.full((n_rows, n), 0.75, np.float32)
+    if kind == "zeros":
+        return rng.choice(np.array([0.0, -0.0, -1.0, 1.0], np.float32), size=(n_rows, n))
+    if kind == "special":
+        x = rng.standard_normal((n_rows, n)).astype(np.float32)
+        m = rng.random((n_rows, n))
+        x[m < 0.02] = np.inf
+        x[(m >= 0.02) & (m < 0.05)] = -np.inf
+        x[(m >= 0.05) & (m < 0.09)] = np.nan
+        x[(m >= 0.09) & (m < 0.12)] = -0.0
+        return x
+    if kind == "lowbits":
+        bits = np.uint32(0x3FC00000) + rng.integers(0, 1 << 12, size=(n_rows, n)).astype(np.uint32)
+        return bits.view(np.float32)
+    if kind == "ascending":
+        return np.tile(np.arange(n, dtype=np.float32), (n_rows, 1))
+    if kind == "descending":
+        return np.tile(-np.arange(n, dtype=np.float32), (n_rows, 1))
+    if kind == "tierun":  # a long run of one value straddles the threshold
+        x = rng.standard_normal((n_rows, n)).astype(np.float32)
+        x[:, rng.random(n) < 0.6] = 0.5
+        return x
+    if kind == "staircase":
+        return np.tile(np.repeat(np.arange(n // 7 + 1, dtype=np.float32)[::-1], 7)[:n], (n_rows, 1))
+    raise ValueError(kind)
+
+
+KINDS = ["normal", "dups", "equal", "zeros", "special", "lowbits", "ascending", "descending", "tierun", "staircase"]
+SHAPES = [(200, 3000), (130, 20000), (3, 70001), (1, 300000)]  # row mode x2, chunked mode x2
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_select_adversarial(kind, shape):
+    n_rows, n = shape
+    rng = np.random.default_rng(hash((kind, n)) % (1 << 32))
+    x = _rows(kind, n_rows, n, rng)
+    xt = torch.from_numpy(x).cuda()
+    m = tka()
+    for k in sorted({1, 37, n // 33 + 1, 2048, n - 1, n, n + 5}):
+        say(f"[select edges] {kind} {shape} k={k}")
+        idx, sel = m.topk_select(xt, k)
+        idx2, sel2 = m.topk_select(xt, k)
+        gi = idx.cpu().numpy()
+        want = orc.select(x, k)
+        assert np.array_equal(gi, want), (kind, shape, k)
+        kk = min(k, n)
+        rows = np.arange(n_rows)[:, None]
+        gs = sel.cpu().numpy()
+        assert np.array_equal(gs[:, :kk].view(np.uint32), x[rows, gi[:, :kk]].view(np.uint32))
+        assert np.all(np.isneginf(gs[:, kk:]))
+        assert torch.equal(idx, idx2) and torch.equal(sel.view(torch.int32), sel2.view(torch.int32))
+
+
+def test_select_strided_and_unaligned_rows():
+    rng = np.random.default_rng(5)
+    base = torch.from_numpy(rng.standard_normal((64, 5003)).astype(np.float32)).cuda()
+    view = base[:, 1:4001]  # rows start 4 bytes off 16-byte alignment, stride 5003
+    m = tka()
+    idx, _ = m.topk_select(view, 100, row_len=4000, row_stride=5003)
+    want = orc.select(base.cpu().numpy()[:, 1:4001].copy(), 100)
+    assert np.array_equal(idx.cpu().numpy(), want)
+
+
+def test_select_empty_rows_pad():
+    m = tka()
+    x = torch.empty((4, 0), dtype=torch.float32, device="cuda")
+    idx, sel = m.topk_select(x, 8, row_len=0, row_stride=0)
+    assert (idx.cpu() == -1).all() and torch.isneginf(sel.cpu()).all()

@@ -1,0 +1,215 @@
+"""Python binding of libtka, the gfx950 top-k sparse decode-attention library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+(include/tka.h). Tensors are torch device tensors; pointers and the current
+HIP stream are handed to the library as integers. Importing this package
+raises ImportError when libtka.so has not been built - there is no fallback.
+
+The names match the C entry points: topk_attn_score, topk_select,
+sparse_attn_gather, topk_decode, topk_block_mean_build and the workspace-size
+queries.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtka.so")
+
+TKA_OK, TKA_ERR_INVALID_ARG, TKA_ERR_UNSUPPORTED, TKA_ERR_WORKSPACE, TKA_ERR_ALIGNMENT, TKA_ERR_HIP = range(6)
+TKA_F32, TKA_BF16, TKA_FP8_E4M3 = 0, 1, 2
+EXACT, BLOCK_MEAN, INDEXER = 0, 1, 2
+
+
+class TkaError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: status {status} ({detail})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
+                ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("mode", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("idx_dtype", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m top_sparse_attention_topk_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER(Problem)
+    sig = {
+        "topk_attn_score": [P, vp, vp, vp, vp, vp],
+        "topk_select": [vp, i64, i32, i64, i32, vp, vp, vp, sz, vp],
+        "topk_select_workspace_size": [i64, i32, i32, ctypes.POINTER(sz)],
+        "sparse_attn_gather": [P, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
+        "sparse_attn_gather_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
+        "topk_decode": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "topk_decode_workspace_size": [P, ctypes.POINTER(sz)],
+        "topk_block_mean_build": [P, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.tka_status_str.argtypes = [ctypes.c_int]
+    lib.tka_status_str.restype = ctypes.c_char_p
+    lib.tka_last_error.argtypes = []
+    lib.tka_last_error.restype = ctypes.c_char_p
+    lib.tka_abi_version.argtypes = []
+    lib.tka_abi_version.restype = ctypes.c_int32
+    return lib
+
+
+LIB = _load()
+EXPORTS = ["topk_attn_score", "topk_select", "topk_select_workspace_size", "sparse_attn_gather",
+           "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
+           "topk_block_mean_build", "tka_status_str", "tka_last_error", "tka_abi_version"]
+
+
+def _check(status: int, fn: str):
+    if status != TKA_OK:
+        raise TkaError(status, fn, LIB.tka_status_str(status).decode() + ": " + LIB.tka_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def problem(mode: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int, top_k: int,
+            dtype: int = TKA_BF16, scale: float = 0.0, block_size: int = 0, n_idx_heads: int = 0, idx_dim: int = 0,
+            strides=None) -> Problem:
+    """tka_problem; strides default to a contiguous [B, Hkv, L, d] cache."""
+    sb, sh, sl = strides if strides is not None else (n_kv_heads * seq_len * head_dim, seq_len * head_dim, head_dim)
+    return Problem(batch, n_q_heads, n_kv_heads, head_dim, seq_len, top_k, sb, sh, sl, dtype, scale, mode,
+                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3)
+
+
+def score_shape(p: Problem):
+    if p.mode == INDEXER:
+        return (p.batch, p.seq_len)
+    if p.mode == BLOCK_MEAN:
+        m = (p.seq_len + p.block_size - 1) // p.block_size
+        return (p.batch, p.n_q_heads, m - 1)
+    return (p.batch, p.n_q_heads, p.seq_len)
+
+
+def _empty(shape, dtype, like):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def _ws(nbytes: int, like):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
+def topk_attn_score(p: Problem, q, keys, idx_w=None, scores=None, stream=None):
+    import torch
+    if scores is None:
+        scores = _empty(score_shape(p), torch.float32, keys)
+    _check(LIB.topk_attn_score(ctypes.byref(p), _ptr(q), _ptr(keys), _ptr(idx_w), _ptr(scores), _stream(stream)),
+           "topk_attn_score")
+    return scores
+
+
+def topk_select_workspace_size(n_rows: int, row_len: int, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.topk_select_workspace_size(n_rows, row_len, k, ctypes.byref(n)), "topk_select_workspace_size")
+    return n.value
+
+
+def topk_select(scores, k: int, row_len: int | None = None, row_stride: int | None = None, idx_out=None,
+                sel_out=None, want_sel: bool = True, ws=None, stream=None):
+    """scores [..., row_len] fp32 -> (idx [n_rows, k] int32, sel [n_rows, k] fp32 or None)."""
+    import torch
+    row_len = scores.shape[-1] if row_len is None else row_len
+    row_stride = (scores.stride(-2) if scores.dim() > 1 else row_len) if row_stride is None else row_stride
+    n_rows = 1
+    for dim in scores.shape[:-1]:
+        n_rows *= int(dim)
+    if idx_out is None:
+        idx_out = _empty((n_rows, k), torch.int32, scores)
+    if sel_out is None and want_sel:
+        sel_out = _empty((n_rows, k), torch.float32, scores)
+    nbytes = topk_select_workspace_size(n_rows, row_len, k)
+    if ws is None and nbytes:
+        ws = _ws(nbytes, scores)
+    _check(LIB.topk_select(_ptr(scores), n_rows, row_len, row_stride, k, _ptr(idx_out), _ptr(sel_out), _ptr(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)), "topk_select")
+    return idx_out, sel_out
+
+
+def sparse_attn_gather_workspace_size(p: Problem, n_idx: int, idx_unit: int = 0, shared: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.sparse_attn_gather_workspace_size(ctypes.byref(p), n_idx, idx_unit, int(shared), ctypes.byref(n)),
+           "sparse_attn_gather_workspace_size")
+    return n.value
+
+
+def sparse_attn_gather(p: Problem, q, k_cache, v_cache, idx, idx_unit: int = 0, shared: bool = False,
+                       sel_scores=None, out=None, ws=None, stream=None):
+    import torch
+    n_idx = idx.shape[-1]
+    if out is None:
+        out = _empty((p.batch, p.n_q_heads, p.head_dim), torch.float32, q)
+    nbytes = sparse_attn_gather_workspace_size(p, n_idx, idx_unit, shared)
+    if ws is None and nbytes:
+        ws = _ws(nbytes, q)
+    _check(LIB.sparse_attn_gather(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), n_idx,
+                                  idx_unit, int(shared), _ptr(sel_scores), _ptr(out), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)), "sparse_attn_gather")
+    return out
+
+
+def topk_decode_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.topk_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)), "topk_decode_workspace_size")
+    return n.value
+
+
+def topk_decode(p: Problem, q, k_cache, v_cache, proxy_keys=None, q_idx=None, idx_w=None, out=None, idx_out=None,
+                ws=None, want_idx: bool = True, stream=None):
+    """One fused decode step. Returns (out [B,Hq,d] fp32, idx or None)."""
+    import torch
+    if out is None:
+        out = _empty((p.batch, p.n_q_heads, p.head_dim), torch.float32, q)
+    if idx_out is None and want_idx:
+        shape = (p.batch, p.top_k) if p.mode == INDEXER else (p.batch, p.n_q_heads, p.top_k)
+        idx_out = _empty(shape, torch.int32, q)
+    if ws is None:
+        ws = _ws(topk_decode_workspace_size(p), q)
+    _check(LIB.topk_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(proxy_keys), _ptr(q_idx),
+                           _ptr(idx_w), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "topk_decode")
+    return out, idx_out
+
+
+def topk_block_mean_build(p: Problem, k_cache, means=None, stream=None):
+    import torch
+    if means is None:
+        m = (p.seq_len + p.block_size - 1) // p.block_size
+        means = _empty((p.batch, p.n_kv_heads, m, p.head_dim), torch.float32, k_cache)
+    _check(LIB.topk_block_mean_build(ctypes.byref(p), _ptr(k_cache), _ptr(means), _stream(stream)),
+           "topk_block_mean_build")
+    return means
+
+
+def abi_version() -> int:
+    return LIB.tka_abi_version()

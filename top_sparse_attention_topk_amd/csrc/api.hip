@@ -1,0 +1,497 @@
+// C ABI of libtka (include/tka.h): argument checks on the host (no GPU call
+// before they pass), workspace planning and the launch sequence of one
+// decode step on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "internal.h"
+#include "tka.h"
+
+using namespace tka;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+tka_status fail(tka_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tka_status ok() {
+  g_err[0] = 0;
+  return TKA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(tka_dtype t) { return t == TKA_F32 ? 4 : (t == TKA_BF16 ? 2 : 1); }
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+int64_t n_blocks(const tka_problem* p) { return ((int64_t)p->seq_len + p->block_size - 1) / p->block_size; }
+
+// extent in bytes of a KV cache with the problem's strides
+size_t kv_bytes(const tka_problem* p) {
+  const int64_t last = (int64_t)(p->batch - 1) * p->kv_stride_b + (int64_t)(p->n_kv_heads - 1) * p->kv_stride_h +
+                       (int64_t)(p->seq_len - 1) * p->kv_stride_l + p->head_dim;
+  return (size_t)last * esize(p->qkv_dtype);
+}
+
+float eff_scale(const tka_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim); }
+
+// Shapes and dtypes of the attention part (q, K, V, grouping).
+tka_status check_attn_shape(const tka_problem* p) {
+  if (!p) return fail(TKA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1) return fail(TKA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", p->batch);
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(TKA_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", p->n_q_heads, p->n_kv_heads);
+  if (p->n_q_heads % p->n_kv_heads)
+    return fail(TKA_ERR_INVALID_ARG, "n_q_heads %d is not a multiple of n_kv_heads %d", p->n_q_heads,
+                p->n_kv_heads);
+  if (p->seq_len < 1) return fail(TKA_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", p->seq_len);
+  if (p->top_k < 1) return fail(TKA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", p->top_k);
+  if (p->mode != TKA_SCORE_EXACT && p->mode != TKA_SCORE_BLOCK_MEAN && p->mode != TKA_SCORE_INDEXER)
+    return fail(TKA_ERR_INVALID_ARG, "unknown score mode %d", (int)p->mode);
+  if (p->qkv_dtype != TKA_F32 && p->qkv_dtype != TKA_BF16)
+    return fail(TKA_ERR_UNSUPPORTED, "qkv_dtype must be TKA_F32 or TKA_BF16 (got %d)", (int)p->qkv_dtype);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(TKA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", p->head_dim);
+  if (p->kv_stride_l < p->head_dim || p->kv_stride_h < 0 || p->kv_stride_b < 0)
+    return fail(TKA_ERR_INVALID_ARG, "bad KV strides (b=%lld h=%lld l=%lld)", (long long)p->kv_stride_b,
+                (long long)p->kv_stride_h, (long long)p->kv_stride_l);
+  const int64_t es = (int64_t)esize(p->qkv_dtype);
+  if ((p->kv_stride_l * es) % 16 || (p->kv_stride_h * es) % 16 || (p->kv_stride_b * es) % 16)
+    return fail(TKA_ERR_ALIGNMENT, "KV strides must be multiples of 16 bytes");
+  if (p->mode == TKA_SCORE_BLOCK_MEAN && p->block_size < 1)
+    return fail(TKA_ERR_INVALID_ARG, "block_size must be >= 1 (got %d)", p->block_size);
+  if (p->mode == TKA_SCORE_INDEXER) {
+    if (p->n_idx_heads < 1 || p->n_idx_heads > 128)
+      return fail(p->n_idx_heads < 1 ? TKA_ERR_INVALID_ARG : TKA_ERR_UNSUPPORTED, "n_idx_heads %d not in [1, 128]",
+                  p->n_idx_heads);
+    if (p->idx_dim != 64 && p->idx_dim != 128)
+      return fail(TKA_ERR_UNSUPPORTED, "idx_dim %d not built (64, 128)", p->idx_dim);
+    if (p->idx_dtype != TKA_FP8_E4M3) return fail(TKA_ERR_UNSUPPORTED, "idx_dtype must be TKA_FP8_E4M3");
+  }
+  return TKA_OK;
+}
+
+tka_status need_ptr(const void* ptr, const char* name, bool align = true) {
+  if (!ptr) return fail(TKA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (align && !aligned16(ptr)) return fail(TKA_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return TKA_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+tka_status launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TKA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys, float* scores) {
+  ScoreArgs a;
+  a.q = q;
+  a.keys = keys;
+  a.scores = scores;
+  a.B = p->batch;
+  a.Hq = p->n_q_heads;
+  a.Hkv = p->n_kv_heads;
+  a.G = p->n_q_heads / p->n_kv_heads;
+  a.d = p->head_dim;
+  if (p->mode == TKA_SCORE_BLOCK_MEAN) {
+    const int64_t m = n_blocks(p);
+    a.nrows = (int)(m - 1);
+    a.sb = (int64_t)p->n_kv_heads * m * p->head_dim;
+    a.sh = m * p->head_dim;
+    a.sl = p->head_dim;
+    a.scale = 1.0f;
+    a.bf16 = 0;
+  } else {
+    a.nrows = p->seq_len;
+    a.sb = p->kv_stride_b;
+    a.sh = p->kv_stride_h;
+    a.sl = p->kv_stride_l;
+    a.scale = eff_scale(p);
+    a.bf16 = p->qkv_dtype == TKA_BF16;
+  }
+  return a;
+}
+
+int64_t score_rows(const tka_problem* p) {
+  return p->mode == TKA_SCORE_INDEXER ? p->batch : (int64_t)p->batch * p->n_q_heads;
+}
+
+int32_t score_len(const tka_problem* p) {
+  return p->mode == TKA_SCORE_BLOCK_MEAN ? (int32_t)(n_blocks(p) - 1) : p->seq_len;
+}
+
+size_t q_bytes(const tka_problem* p) {
+  if (p->mode == TKA_SCORE_INDEXER) return (size_t)p->batch * p->n_idx_heads * p->idx_dim;
+  return (size_t)p->batch * p->n_q_heads * p->head_dim * esize(p->qkv_dtype);
+}
+
+size_t proxy_bytes(const tka_problem* p) {
+  if (p->mode == TKA_SCORE_BLOCK_MEAN)
+    return sizeof(float) * (size_t)p->batch * p->n_kv_heads * n_blocks(p) * p->head_dim;
+  if (p->mode == TKA_SCORE_INDEXER) return (size_t)p->batch * p->seq_len * p->idx_dim;
+  return kv_bytes(p);
+}
+
+tka_status check_score_call(const tka_problem* p, const void* q, const void* keys, const float* w,
+                            const float* scores) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  if ((s = need_ptr(q, "q")) || (s = need_ptr(keys, "keys")) || (s = need_ptr(scores, "scores", false))) return s;
+  if (reinterpret_cast<uintptr_t>(scores) & 3) return fail(TKA_ERR_ALIGNMENT, "scores is not 4-byte aligned");
+  if (p->mode == TKA_SCORE_INDEXER) {
+    if ((s = need_ptr(w, "idx_w", false))) return s;
+    if (reinterpret_cast<uintptr_t>(w) & 3) return fail(TKA_ERR_ALIGNMENT, "idx_w is not 4-byte aligned");
+  } else if (w) {
+    return fail(TKA_ERR_INVALID_ARG, "idx_w must be NULL unless mode is TKA_SCORE_INDEXER");
+  }
+  const Range so = span_of(scores, sizeof(float) * (size_t)score_rows(p) * score_len(p));
+  if (overlap(so, span_of(q, q_bytes(p))) || overlap(so, span_of(keys, proxy_bytes(p))) ||
+      (w && overlap(so, span_of(w, sizeof(float) * (size_t)p->batch * p->n_idx_heads))))
+    return fail(TKA_ERR_INVALID_ARG, "scores overlaps an input");
+  return TKA_OK;
+}
+
+void run_score(const tka_problem* p, const void* q, const void* keys, const float* w, float* scores,
+               hipStream_t st) {
+  if (p->mode == TKA_SCORE_INDEXER) {
+    IndexerArgs a;
+    a.qI = static_cast<const uint8_t*>(q);
+    a.kI = static_cast<const uint8_t*>(keys);
+    a.w = w;
+    a.scores = scores;
+    a.B = p->batch;
+    a.HI = p->n_idx_heads;
+    a.dI = p->idx_dim;
+    a.L = p->seq_len;
+    launch_score_indexer(a, st);
+  } else {
+    launch_score_dense(dense_score_args(p, q, keys, scores), st);
+  }
+}
+
+tka_status check_select_args(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, int32_t k,
+                             const int32_t* idx_out, const float* sel) {
+  if (n_rows < 0) return fail(TKA_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (row_len < 0) return fail(TKA_ERR_INVALID_ARG, "row_len must be >= 0");
+  if (k < 1) return fail(TKA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (n_rows > 0x7fffffff) return fail(TKA_ERR_UNSUPPORTED, "n_rows above 2^31-1");
+  if (row_stride < row_len) return fail(TKA_ERR_INVALID_ARG, "row_stride %lld < row_len %d", (long long)row_stride,
+                                        row_len);
+  if (n_rows == 0) return TKA_OK;
+  if (!scores && row_len > 0) return fail(TKA_ERR_INVALID_ARG, "scores is NULL");
+  if (!idx_out) return fail(TKA_ERR_INVALID_ARG, "idx_out is NULL");
+  if ((reinterpret_cast<uintptr_t>(scores) & 3) || (reinterpret_cast<uintptr_t>(idx_out) & 3) ||
+      (reinterpret_cast<uintptr_t>(sel) & 3))
+    return fail(TKA_ERR_ALIGNMENT, "scores, idx_out and sel_scores_out must be 4-byte aligned");
+  const Range in = span_of(scores, sizeof(float) * (size_t)((n_rows - 1) * row_stride + row_len));
+  const Range io = span_of(idx_out, sizeof(int32_t) * (size_t)n_rows * k);
+  if (overlap(in, io)) return fail(TKA_ERR_INVALID_ARG, "idx_out overlaps scores");
+  if (sel) {
+    const Range so = span_of(sel, sizeof(float) * (size_t)n_rows * k);
+    if (overlap(in, so) || overlap(io, so)) return fail(TKA_ERR_INVALID_ARG, "sel_scores_out overlaps");
+  }
+  return TKA_OK;
+}
+
+GatherArgs gather_args(const tka_problem* p, const void* q, const void* K, const void* V, const int32_t* idx,
+                       int32_t n_idx, int32_t unit, int32_t shared, const float* sel, float* out) {
+  GatherArgs a;
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.idx = idx;
+  a.sel = sel;
+  a.out = out;
+  a.B = p->batch;
+  a.Hq = p->n_q_heads;
+  a.Hkv = p->n_kv_heads;
+  a.G = p->n_q_heads / p->n_kv_heads;
+  a.d = p->head_dim;
+  a.L = p->seq_len;
+  a.sb = p->kv_stride_b;
+  a.sh = p->kv_stride_h;
+  a.sl = p->kv_stride_l;
+  a.scale = eff_scale(p);
+  a.bf16 = p->qkv_dtype == TKA_BF16;
+  a.n_idx = n_idx;
+  a.unit = unit;
+  a.shared = shared ? 1 : 0;
+  return a;
+}
+
+tka_status check_gather_shape(const tka_problem* p, int32_t n_idx, int32_t unit, int32_t shared,
+                              const float* sel) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  if (n_idx < 1) return fail(TKA_ERR_INVALID_ARG, "n_idx must be >= 1 (got %d)", n_idx);
+  if (unit < 0) return fail(TKA_ERR_INVALID_ARG, "idx_unit must be >= 0 (got %d)", unit);
+  if ((int64_t)n_idx * (unit > 0 ? unit : 1) + unit > 0x7fffffffLL)
+    return fail(TKA_ERR_UNSUPPORTED, "expanded index list too long");
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (shared && G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(TKA_ERR_UNSUPPORTED, "shared index lists need Hq/Hkv in {1,2,4,8,16} (got %d)", G);
+  if (sel && (shared || unit != 0))
+    return fail(TKA_ERR_INVALID_ARG, "sel_scores needs per-head token lists (shared 0, idx_unit 0)");
+  return TKA_OK;
+}
+
+size_t attn_q_bytes(const tka_problem* p) {
+  return (size_t)p->batch * p->n_q_heads * p->head_dim * esize(p->qkv_dtype);
+}
+
+size_t out_bytes(const tka_problem* p) { return sizeof(float) * (size_t)p->batch * p->n_q_heads * p->head_dim; }
+
+// q, K, V, out pointers of the attention part and out's overlap with them
+tka_status check_attn_ptrs(const tka_problem* p, const void* q, const void* K, const void* V, const float* out) {
+  tka_status s;
+  if ((s = need_ptr(q, "q")) || (s = need_ptr(K, "k_cache")) || (s = need_ptr(V, "v_cache")) ||
+      (s = need_ptr(out, "out")))
+    return s;
+  const Range o = span_of(out, out_bytes(p));
+  if (overlap(o, span_of(q, attn_q_bytes(p))) || overlap(o, span_of(K, kv_bytes(p))) ||
+      overlap(o, span_of(V, kv_bytes(p))))
+    return fail(TKA_ERR_INVALID_ARG, "out overlaps an input");
+  return TKA_OK;
+}
+
+tka_status check_gather_ptrs(const tka_problem* p, const void* q, const void* K, const void* V, const int32_t* idx,
+                             int32_t n_idx, int32_t shared, const float* sel, const float* out) {
+  tka_status s;
+  if ((s = check_attn_ptrs(p, q, K, V, out)) || (s = need_ptr(idx, "idx", false))) return s;
+  if ((reinterpret_cast<uintptr_t>(idx) & 3) || (reinterpret_cast<uintptr_t>(sel) & 3))
+    return fail(TKA_ERR_ALIGNMENT, "idx and sel_scores must be 4-byte aligned");
+  const Range o = span_of(out, out_bytes(p));
+  const size_t lists = shared ? (size_t)p->batch : (size_t)p->batch * p->n_q_heads;
+  if (overlap(o, span_of(idx, sizeof(int32_t) * lists * n_idx)) ||
+      (sel && overlap(o, span_of(sel, sizeof(float) * lists * n_idx))))
+    return fail(TKA_ERR_INVALID_ARG, "out overlaps an input");
+  return TKA_OK;
+}
+
+// ---- fused step: workspace layout ----
+struct DecodeLayout {
+  size_t scores, sel_ws, idx, selv, gather_ws, total;
+  int64_t rows;
+  int32_t len;
+  int32_t k;
+  GatherPlan gp;
+  int unit, shared;
+};
+
+DecodeLayout decode_layout(const tka_problem* p) {
+  DecodeLayout d;
+  d.rows = score_rows(p);
+  d.len = score_len(p);
+  d.k = p->top_k;
+  d.unit = p->mode == TKA_SCORE_BLOCK_MEAN ? p->block_size : 0;
+  d.shared = p->mode == TKA_SCORE_INDEXER;
+  size_t o = 0;
+  d.scores = o;
+  o += al256(sizeof(float) * (size_t)d.rows * (d.len > 0 ? d.len : 1));
+  d.sel_ws = o;
+  o += al256(select_workspace_bytes(d.rows, d.len, d.k));
+  d.idx = o;
+  o += al256(sizeof(int32_t) * (size_t)d.rows * d.k);
+  d.selv = o;
+  o += al256(sizeof(float) * (size_t)d.rows * d.k);
+  GatherArgs ga = gather_args(p, nullptr, nullptr, nullptr, nullptr, d.k, d.unit, d.shared, nullptr, nullptr);
+  d.gp = plan_gather(ga);
+  d.gather_ws = o;
+  o += al256(d.gp.ws_bytes);
+  d.total = o;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tka_abi_version(void) { return TKA_ABI_VERSION; }
+
+const char* tka_last_error(void) { return g_err; }
+
+const char* tka_status_str(tka_status s) {
+  switch (s) {
+    case TKA_OK: return "TKA_OK";
+    case TKA_ERR_INVALID_ARG: return "TKA_ERR_INVALID_ARG";
+    case TKA_ERR_UNSUPPORTED: return "TKA_ERR_UNSUPPORTED";
+    case TKA_ERR_WORKSPACE: return "TKA_ERR_WORKSPACE";
+    case TKA_ERR_ALIGNMENT: return "TKA_ERR_ALIGNMENT";
+    case TKA_ERR_HIP: return "TKA_ERR_HIP";
+  }
+  return "TKA_UNKNOWN_STATUS";
+}
+
+tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys, const float* idx_w, float* scores,
+                           void* stream) {
+  tka_status s = check_score_call(p, q, keys, idx_w, scores);
+  if (s) return s;
+  if (score_len(p) <= 0) return ok();
+  run_score(p, q, keys, idx_w, scores, as_stream(stream));
+  return launched("topk_attn_score");
+}
+
+tka_status topk_select_workspace_size(int64_t n_rows, int32_t row_len, int32_t k, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  if (n_rows < 0 || row_len < 0 || k < 1) return fail(TKA_ERR_INVALID_ARG, "bad select shape");
+  *bytes = select_workspace_bytes(n_rows, row_len, k);
+  return ok();
+}
+
+tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, int32_t k,
+                       int32_t* idx_out, float* sel_scores_out, void* ws, size_t ws_bytes, void* stream) {
+  tka_status s = check_select_args(scores, n_rows, row_len, row_stride, k, idx_out, sel_scores_out);
+  if (s) return s;
+  const size_t need = select_workspace_bytes(n_rows, row_len, k);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TKA_ERR_WORKSPACE, "select needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  if (need > 0 && !aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (n_rows == 0) return ok();
+  SelectArgs a{scores, n_rows, row_len, row_stride, k, idx_out, sel_scores_out};
+  launch_select(a, ws, as_stream(stream));
+  return launched("topk_select");
+}
+
+tka_status sparse_attn_gather_workspace_size(const tka_problem* p, int32_t n_idx, int32_t idx_unit,
+                                             int32_t shared_across_heads, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  tka_status s = check_gather_shape(p, n_idx, idx_unit, shared_across_heads, nullptr);
+  if (s) return s;
+  GatherArgs ga = gather_args(p, nullptr, nullptr, nullptr, nullptr, n_idx, idx_unit, shared_across_heads, nullptr,
+                              nullptr);
+  *bytes = plan_gather(ga).ws_bytes;
+  return ok();
+}
+
+tka_status sparse_attn_gather(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* idx, int32_t n_idx, int32_t idx_unit, int32_t shared_across_heads,
+                              const float* sel_scores, float* out, void* ws, size_t ws_bytes, void* stream) {
+  tka_status s = check_gather_shape(p, n_idx, idx_unit, shared_across_heads, sel_scores);
+  if (s) return s;
+  if ((s = check_gather_ptrs(p, q, k_cache, v_cache, idx, n_idx, shared_across_heads, sel_scores, out))) return s;
+  GatherArgs ga =
+      gather_args(p, q, k_cache, v_cache, idx, n_idx, idx_unit, shared_across_heads, sel_scores, out);
+  const GatherPlan pl = plan_gather(ga);
+  if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes))
+    return fail(TKA_ERR_WORKSPACE, "gather needs %zu workspace bytes (got %zu)", pl.ws_bytes, ws_bytes);
+  if (pl.ws_bytes > 0 && !aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  launch_gather(ga, pl, ws, as_stream(stream));
+  return launched("sparse_attn_gather");
+}
+
+tka_status topk_decode_workspace_size(const tka_problem* p, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  *bytes = decode_layout(p).total;
+  return ok();
+}
+
+tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                       const void* proxy_keys, const void* q_idx, const float* idx_w, float* out, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  const int shared = p->mode == TKA_SCORE_INDEXER ? 1 : 0;
+  if ((s = check_gather_shape(p, p->top_k, p->mode == TKA_SCORE_BLOCK_MEAN ? p->block_size : 0, shared, nullptr)))
+    return s;
+  if (p->mode == TKA_SCORE_EXACT) {
+    if (proxy_keys || q_idx || idx_w)
+      return fail(TKA_ERR_INVALID_ARG, "proxy_keys, q_idx and idx_w must be NULL for TKA_SCORE_EXACT");
+  } else if (p->mode == TKA_SCORE_BLOCK_MEAN) {
+    if ((s = need_ptr(proxy_keys, "proxy_keys (block means)"))) return s;
+    if (q_idx || idx_w) return fail(TKA_ERR_INVALID_ARG, "q_idx and idx_w must be NULL for TKA_SCORE_BLOCK_MEAN");
+  } else {
+    if ((s = need_ptr(proxy_keys, "proxy_keys (indexer keys)")) || (s = need_ptr(q_idx, "q_idx")) ||
+        (s = need_ptr(idx_w, "idx_w", false)))
+      return s;
+    if (reinterpret_cast<uintptr_t>(idx_w) & 3) return fail(TKA_ERR_ALIGNMENT, "idx_w is not 4-byte aligned");
+  }
+  const DecodeLayout d = decode_layout(p);
+  if ((s = check_attn_ptrs(p, q, k_cache, v_cache, out))) return s;
+  const Range o = span_of(out, out_bytes(p));
+  if (proxy_keys && overlap(o, span_of(proxy_keys, proxy_bytes(p))))
+    return fail(TKA_ERR_INVALID_ARG, "out overlaps proxy_keys");
+  if (q_idx && overlap(o, span_of(q_idx, q_bytes(p)))) return fail(TKA_ERR_INVALID_ARG, "out overlaps q_idx");
+  if (idx_w && overlap(o, span_of(idx_w, sizeof(float) * (size_t)p->batch * p->n_idx_heads)))
+    return fail(TKA_ERR_INVALID_ARG, "out overlaps idx_w");
+  if (idx_out) {
+    if (reinterpret_cast<uintptr_t>(idx_out) & 3) return fail(TKA_ERR_ALIGNMENT, "idx_out is not 4-byte aligned");
+    const Range io = span_of(idx_out, sizeof(int32_t) * (size_t)d.rows * d.k);
+    if (overlap(io, o) || overlap(io, span_of(k_cache, kv_bytes(p))) || overlap(io, span_of(v_cache, kv_bytes(p))) ||
+        overlap(io, span_of(q, attn_q_bytes(p))) ||
+        (proxy_keys && overlap(io, span_of(proxy_keys, proxy_bytes(p)))))
+      return fail(TKA_ERR_INVALID_ARG, "idx_out overlaps another buffer");
+  }
+  if (!ws || ws_bytes < d.total)
+    return fail(TKA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", d.total, ws_bytes);
+  if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + d.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx);
+  float* selv = reinterpret_cast<float*>(base + d.selv);
+  const bool exact = p->mode == TKA_SCORE_EXACT;
+
+  // 1. score
+  if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);
+  else if (d.len > 0) run_score(p, q, exact ? k_cache : proxy_keys, nullptr, scores, st);
+  // 2. select
+  SelectArgs sa{scores, d.rows, d.len, (int64_t)d.len, d.k, idx, exact ? selv : nullptr};
+  launch_select(sa, base + d.sel_ws, st);
+  // 3. gather
+  GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, d.k, d.unit, d.shared, exact ? selv : nullptr, out);
+  launch_gather(ga, d.gp, base + d.gather_ws, st);
+  return launched("topk_decode");
+}
+
+tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, float* means, void* stream) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  if (p->mode != TKA_SCORE_BLOCK_MEAN) return fail(TKA_ERR_INVALID_ARG, "mode must be TKA_SCORE_BLOCK_MEAN");
+  if ((s = need_ptr(k_cache, "k_cache")) || (s = need_ptr(means, "means"))) return s;
+  const Range mo = span_of(means, proxy_bytes(p));
+  if (overlap(mo, span_of(k_cache, kv_bytes(p)))) return fail(TKA_ERR_INVALID_ARG, "means overlaps k_cache");
+  BlockMeanArgs a;
+  a.K = k_cache;
+  a.means = means;
+  a.B = p->batch;
+  a.Hkv = p->n_kv_heads;
+  a.d = p->head_dim;
+  a.L = p->seq_len;
+  a.bsz = p->block_size;
+  a.m = (int)n_blocks(p);
+  a.sb = p->kv_stride_b;
+  a.sh = p->kv_stride_h;
+  a.sl = p->kv_stride_l;
+  a.bf16 = p->qkv_dtype == TKA_BF16;
+  launch_block_mean(a, as_stream(stream));
+  return launched("topk_block_mean_build");
+}
+
+}  // extern "C"

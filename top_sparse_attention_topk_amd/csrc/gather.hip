@@ -1,0 +1,352 @@
+// Gather - softmax - PV over the kept positions only, for gfx950.
+//
+// "Sparse Attention in LLM Inference", "Changes in Caching Strategy": the
+// sparse layer reads only the KV entries at the positions the Top-K step
+// kept, through a position index; "Computational and Memory Access
+// Benefits": the attention work is O(K d) per query instead of O(L d).
+//
+// A task is one (b, query head) with its own kept list, or one (b, KV head)
+// with the G query heads that share a kept list (indexer variant: one set per
+// sequence). A task's expanded token list (block ids expand to their keys,
+// plus the current block) is cut into splits; each workgroup:
+//   1. resolves its tokens into LDS,
+//   2. computes the logits z = scale <q, K_t> (16-byte row gathers, lane
+//      groups reduce with xor shuffles) - or takes them from the selected
+//      scores when the caller passes them, skipping the K rows,
+//   3. max / exp / sum per head in fp32 (fixed-order wave reductions),
+//   4. gathers the V rows and accumulates w * V in fp32,
+//   5. writes o (one split) or (M, l, acc) partials merged in split order.
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace tka {
+
+struct GatherK {
+  const void* q;
+  const void* K;
+  const void* V;
+  const int32_t* idx;
+  const float* sel;
+  float* out;
+  float* part;
+  int Hq, Hkv, G, L, m;
+  int64_t sb, sh, sl;
+  float scale;
+  int n_idx, unit, shared, nsplit, span;
+  int64_t E;
+};
+
+template <bool BF16, int D, int NH, bool SEL>
+__global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
+  using U = Unpack<BF16>;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPL = U::N;
+  constexpr int LPR = D * ES / 16;
+  constexpr int RPW = 64 / LPR;
+  constexpr int UNR = 8;
+  extern __shared__ uint4 smem_raw[];
+  float* red = reinterpret_cast<float*>(smem_raw);  // [NH][D]
+  float* stat = red + NH * D;                      // M[NH], l[NH]
+  int32_t* tok = reinterpret_cast<int32_t*>(stat + 2 * NH);
+  float* lg = reinterpret_cast<float*>(tok + a.span);  // [NH][span]
+
+  const int task = blockIdx.y, split = blockIdx.x;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int sub = lane % LPR, grp = lane / LPR;
+  int b, h0, g;
+  const int32_t* list;
+  const float* sl_list = nullptr;
+  if (a.shared) {
+    b = task / a.Hkv;
+    g = task % a.Hkv;
+    h0 = g * a.G;
+    list = a.idx + (int64_t)b * a.n_idx;
+  } else {
+    b = task / a.Hq;
+    h0 = task % a.Hq;
+    g = h0 / a.G;
+    list = a.idx + (int64_t)task * a.n_idx;
+    if (SEL) sl_list = a.sel + (int64_t)task * a.n_idx;
+  }
+  const int64_t e0 = (int64_t)split * a.span;
+  const int ne = (int)max((int64_t)0, min(a.E, e0 + a.span) - e0);
+
+  // 1. tokens (and the given logits)
+  const int64_t nb = (int64_t)a.n_idx * (a.unit > 0 ? a.unit : 1);
+  for (int i = t; i < ne; i += 256) {
+    const int64_t e = e0 + i;
+    int tk = -1;
+    if (a.unit == 0) {
+      const int v = list[e];
+      tk = (v >= 0 && v < a.L) ? v : -1;
+    } else if (e < nb) {
+      const int j = list[e / a.unit];
+      if (j >= 0 && j < a.m - 1) {
+        const int64_t x = (int64_t)j * a.unit + e % a.unit;
+        tk = x < a.L ? (int)x : -1;
+      }
+    } else {
+      const int64_t x = (int64_t)(a.m - 1) * a.unit + (e - nb);
+      tk = x < a.L ? (int)x : -1;
+    }
+    tok[i] = tk;
+    if (SEL) lg[i] = tk >= 0 ? sl_list[e] : -INFINITY;
+  }
+  __syncthreads();
+
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.K) + ((int64_t)b * a.sb + (int64_t)g * a.sh) * ES;
+  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.V) + ((int64_t)b * a.sb + (int64_t)g * a.sh) * ES;
+
+  // 2. logits from the K rows
+  if (!SEL) {
+    float qf[NH][EPL];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const uint8_t* qp =
+          reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(b * a.Hq + h0 + h) * D + sub * EPL) * ES;
+      U::run(ld16(qp), qf[h]);
+    }
+    for (int ib = w * RPW * UNR; ib < ne; ib += 4 * RPW * UNR) {
+      uint4 raw[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int i = ib + u * RPW + grp;
+        const int tk = i < ne ? tok[i] : -1;
+        raw[u] = tk >= 0 ? ld16(Kb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        float kf[EPL];
+        U::run(raw[u], kf);
+        float part[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          float x = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) x = fmaf(qf[h][e], kf[e], x);
+          part[h] = x;
+        }
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) part[h] += __shfl_xor(part[h], o, kWave);
+        const int i = ib + u * RPW + grp;
+        if (i < ne) {
+          const bool ok = tok[i] >= 0;
+#pragma unroll
+          for (int h = 0; h < NH; ++h)
+            if (h % LPR == sub) lg[h * a.span + i] = ok ? part[h] * a.scale : -INFINITY;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. softmax statistics per head (one wave per head, fixed order)
+  for (int h = w; h < NH; h += 4) {
+    float* lh = lg + h * a.span;
+    float mx = -INFINITY;
+    for (int i = lane; i < ne; i += 64) mx = fmaxf(mx, lh[i]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int i = lane; i < ne; i += 64) {
+      const float p = (mx == -INFINITY) ? 0.f : expf(lh[i] - mx);
+      lh[i] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      stat[h] = mx;
+      stat[NH + h] = sum;
+    }
+  }
+  __syncthreads();
+
+  // 4. V gather and weighted accumulation
+  float acc[NH][EPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  for (int ib = w * RPW * UNR; ib < ne; ib += 4 * RPW * UNR) {
+    uint4 raw[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = ib + u * RPW + grp;
+      const int tk = i < ne ? tok[i] : -1;
+      raw[u] = tk >= 0 ? ld16(Vb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = ib + u * RPW + grp;
+      if (i < ne) {
+        float vf[EPL];
+        U::run(raw[u], vf);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const float p = lg[h * a.span + i];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, kWave);
+  // waves add their sums in a fixed order
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww && grp == 0) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float* r = red + h * D + sub * EPL + e;
+          *r = (ww == 0) ? acc[h][e] : *r + acc[h][e];
+        }
+    }
+    __syncthreads();
+  }
+
+  // 5. output or partials
+  if (a.nsplit == 1) {
+    for (int i = t; i < NH * D; i += 256) {
+      const int h = i / D, c = i % D;
+      const float l = stat[NH + h];
+      a.out[((int64_t)b * a.Hq + h0 + h) * D + c] = l > 0.f ? red[i] / l : 0.f;
+    }
+  } else {
+    float* p = a.part + ((int64_t)task * a.nsplit + split) * (NH * (D + 2));
+    for (int i = t; i < NH * D; i += 256) p[i] = red[i];
+    if (t < 2 * NH) p[NH * D + t] = stat[t];
+  }
+}
+
+// o = sum_s e^(M_s - M) acc_s / sum_s e^(M_s - M) l_s, splits in order.
+template <int D, int NH>
+__global__ __launch_bounds__(256) void gather_merge_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                           int nsplit, int Hq, int Hkv, int G, int shared) {
+  const int task = blockIdx.x;
+  int b, h0;
+  if (shared) {
+    b = task / Hkv;
+    h0 = (task % Hkv) * G;
+  } else {
+    b = task / Hq;
+    h0 = task % Hq;
+  }
+  const float* p = part + (int64_t)task * nsplit * (NH * (D + 2));
+  for (int i = threadIdx.x; i < NH * D; i += 256) {
+    const int h = i / D;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (NH * (D + 2)) + NH * D + h]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < nsplit; ++s) {
+        const float* ps = p + s * (NH * (D + 2));
+        const float ms = ps[NH * D + h];
+        if (ms == -INFINITY) continue;
+        const float f = expf(ms - M);
+        num = fmaf(f, ps[i], num);
+        den = fmaf(f, ps[NH * D + NH + h], den);
+      }
+    }
+    out[((int64_t)b * Hq + h0 + h) * D + (i % D)] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+GatherPlan plan_gather(const GatherArgs& a) {
+  GatherPlan pl;
+  pl.heads_per_task = a.shared ? a.G : 1;
+  pl.tasks = a.shared ? a.B * a.Hkv : a.B * a.Hq;
+  pl.expanded = a.unit == 0 ? (int64_t)a.n_idx : (int64_t)a.n_idx * a.unit + a.unit;
+  const int NH = pl.heads_per_task;
+  const int span_max = NH == 1 ? 4096 : 8192 / NH;
+  int64_t ns = (pl.expanded + span_max - 1) / span_max;
+  const int64_t want = (512 + pl.tasks - 1) / pl.tasks;
+  const int64_t cap64 = (pl.expanded + 63) / 64;
+  int64_t ns2 = want < cap64 ? want : cap64;
+  if (ns2 > ns) ns = ns2;
+  if (ns < 1) ns = 1;
+  int64_t span = (pl.expanded + ns - 1) / ns;
+  span = ((span + 15) / 16) * 16;
+  if (span < 16) span = 16;
+  ns = (pl.expanded + span - 1) / span;
+  if (ns < 1) ns = 1;
+  pl.nsplit = (int)ns;
+  pl.span = (int)span;
+  pl.ws_bytes = pl.nsplit > 1 ? sizeof(float) * (size_t)pl.tasks * pl.nsplit * NH * (a.d + 2) : 0;
+  return pl;
+}
+
+template <bool BF16, int D, int NH, bool SEL>
+static void launch_g(const GatherK& k, const GatherPlan& pl, hipStream_t st) {
+  const size_t lds = sizeof(float) * (NH * D + 2 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
+  hipLaunchKernelGGL((gather_kernel<BF16, D, NH, SEL>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
+  if (pl.nsplit > 1)
+    hipLaunchKernelGGL((gather_merge_kernel<D, NH>), dim3(pl.tasks), dim3(256), 0, st, k.part, k.out, pl.nsplit,
+                       k.Hq, k.Hkv, k.G, k.shared);
+}
+
+template <bool BF16, int D>
+static void launch_gd(const GatherK& k, const GatherPlan& pl, bool sel, hipStream_t st) {
+  switch (pl.heads_per_task) {
+    case 1:
+      if (sel) launch_g<BF16, D, 1, true>(k, pl, st);
+      else launch_g<BF16, D, 1, false>(k, pl, st);
+      break;
+    case 2: launch_g<BF16, D, 2, false>(k, pl, st); break;
+    case 4: launch_g<BF16, D, 4, false>(k, pl, st); break;
+    case 8: launch_g<BF16, D, 8, false>(k, pl, st); break;
+    default: launch_g<BF16, D, 16, false>(k, pl, st); break;
+  }
+}
+
+template <bool BF16>
+static void launch_gb(const GatherK& k, const GatherPlan& pl, int d, bool sel, hipStream_t st) {
+  switch (d) {
+    case 64: launch_gd<BF16, 64>(k, pl, sel, st); break;
+    case 128: launch_gd<BF16, 128>(k, pl, sel, st); break;
+    default: launch_gd<BF16, 256>(k, pl, sel, st); break;
+  }
+}
+
+void launch_gather(const GatherArgs& a, const GatherPlan& pl, void* ws, hipStream_t st) {
+  if (pl.tasks <= 0) return;
+  GatherK k;
+  k.q = a.q;
+  k.K = a.K;
+  k.V = a.V;
+  k.idx = a.idx;
+  k.sel = a.sel;
+  k.out = a.out;
+  k.part = static_cast<float*>(ws);
+  k.Hq = a.Hq;
+  k.Hkv = a.Hkv;
+  k.G = a.G;
+  k.L = a.L;
+  k.m = a.unit > 0 ? (a.L + a.unit - 1) / a.unit : 0;
+  k.sb = a.sb;
+  k.sh = a.sh;
+  k.sl = a.sl;
+  k.scale = a.scale;
+  k.n_idx = a.n_idx;
+  k.unit = a.unit;
+  k.shared = a.shared;
+  k.nsplit = pl.nsplit;
+  k.span = pl.span;
+  k.E = pl.expanded;
+  const bool sel = a.sel != nullptr;
+  if (a.bf16) launch_gb<true>(k, pl, a.d, sel, st);
+  else launch_gb<false>(k, pl, a.d, sel, st);
+}
+
+}  // namespace tka

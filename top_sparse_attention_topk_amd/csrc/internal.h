@@ -1,0 +1,76 @@
+// Host-side interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tka {
+
+struct ScoreArgs {
+  const void* q;     // [B,Hq,d]
+  const void* keys;  // rows of d elements at b*sb + g*sh + i*sl
+  float* scores;     // [B,Hq,nrows]
+  int B, Hq, Hkv, G, d, nrows;
+  int64_t sb, sh, sl;
+  float scale;
+  int bf16;  // 1: bf16 rows and q, 0: fp32
+};
+
+struct IndexerArgs {
+  const uint8_t* qI;  // [B,HI,dI]
+  const uint8_t* kI;  // [B,L,dI]
+  const float* w;     // [B,HI]
+  float* scores;      // [B,L]
+  int B, HI, dI, L;
+};
+
+struct BlockMeanArgs {
+  const void* K;
+  float* means;  // [B,Hkv,m,d]
+  int B, Hkv, d, L, bsz, m;
+  int64_t sb, sh, sl;
+  int bf16;
+};
+
+struct SelectArgs {
+  const float* scores;
+  int64_t n_rows;
+  int n;  // row length
+  int64_t stride;
+  int k;
+  int32_t* idx;
+  float* sel;  // nullable
+};
+
+struct GatherArgs {
+  const void* q;
+  const void* K;
+  const void* V;
+  const int32_t* idx;
+  const float* sel;  // nullable
+  float* out;
+  int B, Hq, Hkv, G, d, L;
+  int64_t sb, sh, sl;
+  float scale;
+  int bf16;
+  int n_idx, unit, shared;
+};
+
+bool score_uses_mfma(int dtype_bf16, int G);
+void launch_score_dense(const ScoreArgs& a, hipStream_t st);
+void launch_score_indexer(const IndexerArgs& a, hipStream_t st);
+void launch_block_mean(const BlockMeanArgs& a, hipStream_t st);
+
+size_t select_workspace_bytes(int64_t n_rows, int n, int k);
+void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
+
+// gather planning is shared by the workspace query and the launch
+struct GatherPlan {
+  int tasks, heads_per_task, span, nsplit;
+  int64_t expanded;  // tokens per task after block expansion
+  size_t ws_bytes;
+};
+GatherPlan plan_gather(const GatherArgs& a);
+void launch_gather(const GatherArgs& a, const GatherPlan& pl, void* ws, hipStream_t st);
+
+}  // namespace tka

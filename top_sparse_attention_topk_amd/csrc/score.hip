@@ -1,0 +1,413 @@
+// Scoring kernels for gfx950.
+//
+// Exact token scores ("Sparse Attention Landscape", "Token Sparse Attention":
+// s_i = f(q_t, k_i), here scale * <q, k_i>), block-mean scores (same page,
+// "Block Sparse Attention": dot product of q with the mean-pooled keys of a
+// block) and lightning-indexer scores (same page, "Token Sparse Attention":
+// sum over indexer heads of w_j * ReLU(<q^I_j, k^I_i>)).
+//
+// All three stream their key rows once from HBM with 128-bit loads. The scan
+// is bandwidth-bound (about G flop per byte for grouped heads), so MFMA is
+// used only where several query heads share a key row (a real small-M
+// contraction) and for the fp8 indexer; the rest uses wave dot-reductions.
+#include "device_common.h"
+#include "internal.h"
+
+namespace tka {
+
+// ---------------------------------------------------------------------------
+// Exact scores, bf16, 2 <= G <= 16 query heads per KV head: one
+// v_mfma_f32_16x16x32_bf16 tile = 16 positions x 16 heads (G used) x 32 dims.
+// A = 16 key rows (lane l: row l%16, dims 8*(l/16)+[0,8) of each 32-dim step),
+// B = q^T of the group (lane l: head l%16, same dims), C[pos][head]: lane l
+// holds head l%16 for positions 4*(l/16)+[0,4).
+// Grid (chunks, B*Hkv), 256 threads; each wave takes 64 positions per round.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ K,
+                                                               float* __restrict__ S, int Hq, int Hkv, int G, int L,
+                                                               int64_t sb, int64_t sh, int64_t sl, float scale,
+                                                               int chunk) {
+  constexpr int KS = D / 32;
+  const int task = blockIdx.y;
+  const int b = task / Hkv, g = task % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+
+  bf16x8_t bq[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n < G) v = ld16(q + ((int64_t)(b * Hq + g * G + n)) * D + 32 * s + 8 * kg);
+    bq[s] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  const uint16_t* Kb = K + (int64_t)b * sb + (int64_t)g * sh;
+  const int p0 = blockIdx.x * chunk;
+  const int p1 = min(p0 + chunk, L);
+  float* Srow = S + ((int64_t)(b * Hq + g * G + (n < G ? n : 0))) * L;
+  const bool vec_store = (L & 3) == 0;
+
+  auto load = [&](uint4 (&a)[4][KS], int base) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int pos = min(base + 16 * t + n, L - 1);
+      const uint16_t* row = Kb + (int64_t)pos * sl + 8 * kg;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[t][s] = ld16_stream(row + 32 * s);
+    }
+  };
+
+  int base = p0 + wave * 64;
+  if (base >= p1) return;
+  uint4 cur[4][KS];
+  load(cur, base);
+  for (; base < p1; base += 256) {
+    uint4 nxt[4][KS];
+    const bool more = base + 256 < p1;
+    if (more) load(nxt, base + 256);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[t][s]), bq[s], acc, 0, 0,
+                                                      0);
+      const int pos = base + 16 * t + 4 * kg;
+      if (n < G) {
+        if (vec_store && pos + 3 < p1) {
+          *reinterpret_cast<float4*>(Srow + pos) =
+              make_float4(acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (pos + i < p1) Srow[pos + i] = acc[i] * scale;
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cur[t][s] = nxt[t][s];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave dot-reduction scores for fp32 or bf16 rows, NH query heads per task.
+// A row of D elements is 16*LPR bytes: LPR lanes load 16 B each, RPW = 64/LPR
+// rows per wave load. Each lane keeps its 16-byte slice of q for every head,
+// the partial dots are reduced across the LPR lanes with xor shuffles.
+// Used for G = 1 heads, fp32 caches and the fp32 block-mean cache.
+// Grid (chunks, B*Hkv*htiles), 256 threads.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, int NH>
+__global__ __launch_bounds__(256) void score_vec_kernel(const void* __restrict__ qv, const void* __restrict__ Kv,
+                                                        float* __restrict__ S, int Hq, int Hkv, int G, int nrows,
+                                                        int64_t sb, int64_t sh, int64_t sl, float scale, int chunk,
+                                                        int htiles) {
+  using U = Unpack<BF16>;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPL = U::N;
+  constexpr int LPR = D * ES / 16;
+  constexpr int RPW = 64 / LPR;
+  constexpr int UNR = 4;
+  const int task = blockIdx.y;
+  const int ht = task % htiles;
+  const int bg = task / htiles;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR, grp = lane / LPR;
+  const int h0 = g * G + ht * NH;
+  const int nh = min(NH, g * G + G - h0);
+
+  float qf[NH][EPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    if (h < nh) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(qv) + ((int64_t)(b * Hq + h0 + h) * D + sub * EPL) * ES;
+      U::run(ld16(qp), qf[h]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] = 0.f;
+    }
+  }
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(Kv) + ((int64_t)b * sb + (int64_t)g * sh) * ES;
+  const int p0 = blockIdx.x * chunk;
+  const int p1 = min(p0 + chunk, nrows);
+  for (int base = p0 + wave * RPW * UNR; base < p1; base += 4 * RPW * UNR) {
+    uint4 raw[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int pos = min(base + u * RPW + grp, nrows - 1);
+      raw[u] = ld16_stream(Kb + ((int64_t)pos * sl + sub * EPL) * ES);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float kf[EPL];
+      U::run(raw[u], kf);
+      float part[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(qf[h][e], kf[e], a);
+        part[h] = a;
+      }
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) part[h] += __shfl_xor(part[h], o, kWave);
+      const int pos = base + u * RPW + grp;
+      if (pos < p1) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          if (h % LPR == sub && h < nh) S[((int64_t)(b * Hq + h0 + h)) * nrows + pos] = part[h] * scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Lightning-indexer scores, E4M3FN inputs, fp32 out:
+//   I[b,i] = sum_j w[b,j] * max(0, <qI[b,j], kI[b,i]>).
+// v_mfma_scale_f32_32x32x64_f8f6f4 (both formats E4M3, unit scales):
+// A = 32 indexer heads x 64 dims (lane l: head l%32, dims 32*(l/32)+[0,32)),
+// B = 64 dims x 32 positions (lane l: position l%32, same dims),
+// C[head][pos]: lane l holds position l%32 for heads 8a + 4*(l/32) + c.
+// ReLU and the weighted head sum stay in registers; lanes l and l^32 hold
+// the two halves of the head sum. Grid (chunks, B), 256 threads.
+// ---------------------------------------------------------------------------
+template <int DI, int NT>
+__global__ __launch_bounds__(256) void score_indexer_kernel(const uint8_t* __restrict__ qI,
+                                                            const uint8_t* __restrict__ kI,
+                                                            const float* __restrict__ w, float* __restrict__ S,
+                                                            int HI, int L, int chunk) {
+  constexpr int KS = DI / 64;
+  constexpr int UNR = 4;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 31, half = lane >> 5;
+
+  i32x8_t aq[NT][KS];
+  float wt[NT][16];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int head = t * 32 + j;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+      if (head < HI) {
+        const uint8_t* p = qI + ((int64_t)b * HI + head) * DI + 64 * s + 32 * half;
+        lo = ld16(p);
+        hi = ld16(p + 16);
+      }
+      i32x8_t v;
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      aq[t][s] = v;
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int hh = t * 32 + 8 * a + 4 * half + c;
+        wt[t][4 * a + c] = hh < HI ? w[(int64_t)b * HI + hh] : 0.f;
+      }
+  }
+  const uint8_t* kb = kI + (int64_t)b * L * DI;
+  float* Sb = S + (int64_t)b * L;
+  const int p0 = blockIdx.x * chunk;
+  const int p1 = min(p0 + chunk, L);
+  for (int base = p0 + wave * 32 * UNR; base < p1; base += 4 * 32 * UNR) {
+    uint4 raw[UNR][KS][2];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int pos = min(base + 32 * u + j, L - 1);
+      const uint8_t* row = kb + (int64_t)pos * DI + 32 * half;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        raw[u][s][0] = ld16_stream(row + 64 * s);
+        raw[u][s][1] = ld16_stream(row + 64 * s + 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float tot = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          i32x8_t bk;
+          bk[0] = raw[u][s][0].x; bk[1] = raw[u][s][0].y; bk[2] = raw[u][s][0].z; bk[3] = raw[u][s][0].w;
+          bk[4] = raw[u][s][1].x; bk[5] = raw[u][s][1].y; bk[6] = raw[u][s][1].z; bk[7] = raw[u][s][1].w;
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq[t][s], bk, acc, 0, 0, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tot = fmaf(wt[t][i], fmaxf(acc[i], 0.f), tot);
+      }
+      tot += __shfl_xor(tot, 32, kWave);
+      const int pos = base + 32 * u + j;
+      if (half == 0 && pos < p1) Sb[pos] = tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block means, fp32 out [B,Hkv,m,D]: one wave per block, lanes split a row
+// into 16-byte slices, RPW rows per load; partial sums are combined across
+// lane groups with xor shuffles. Grid (ceil(m/4), B*Hkv), 256 threads.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void block_mean_kernel(const void* __restrict__ Kv, float* __restrict__ means,
+                                                         int Hkv, int L, int bsz, int m, int64_t sb, int64_t sh,
+                                                         int64_t sl) {
+  using U = Unpack<BF16>;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPL = U::N;
+  constexpr int LPR = D * ES / 16;
+  constexpr int RPW = 64 / LPR;
+  const int task = blockIdx.y;
+  const int b = task / Hkv, g = task % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR, grp = lane / LPR;
+  const int j = blockIdx.x * 4 + wave;
+  if (j >= m) return;
+  const int i0 = j * bsz, i1 = min(i0 + bsz, L);
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(Kv) + ((int64_t)b * sb + (int64_t)g * sh) * ES;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int i = i0 + grp; i < i1; i += RPW) {
+    float kf[EPL];
+    U::run(ld16(Kb + ((int64_t)i * sl + sub * EPL) * ES), kf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += kf[e];
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  if (grp == 0) {
+    const float inv = 1.0f / (float)(i1 - i0);
+    float* dst = means + (((int64_t)b * Hkv + g) * m + j) * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv,
+                                                         acc[e + 3] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static int pick_chunk(int64_t rows_per_task, int64_t tasks, int granule, int lo, int hi) {
+  // Enough workgroups to fill 256 CUs several times over, each streaming a
+  // contiguous run of rows.
+  int64_t c = hi;
+  while (c > lo && tasks * ((rows_per_task + c - 1) / c) < 2048) c >>= 1;
+  c = (c / granule) * granule;
+  return (int)(c < granule ? granule : c);
+}
+
+template <int D>
+static void launch_mfma_d(const ScoreArgs& a, hipStream_t st) {
+  const int chunk = pick_chunk(a.nrows, (int64_t)a.B * a.Hkv, 256, 256, 4096);
+  dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv);
+  hipLaunchKernelGGL(score_exact_mfma_kernel<D>, grid, dim3(256), 0, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.keys, a.scores, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk);
+}
+
+template <bool BF16, int D, int NH>
+static void launch_vec_nh(const ScoreArgs& a, hipStream_t st) {
+  const int htiles = (a.G + NH - 1) / NH;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int RPW = 64 / (D * ES / 16);
+  const int gran = 4 * RPW * 4;
+  const int chunk = pick_chunk(a.nrows, (int64_t)a.B * a.Hkv * htiles, gran, gran, 4096);
+  dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv * htiles);
+  hipLaunchKernelGGL((score_vec_kernel<BF16, D, NH>), grid, dim3(256), 0, st, a.q, a.keys, a.scores, a.Hq, a.Hkv,
+                     a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, htiles);
+}
+
+template <bool BF16, int D>
+static void launch_vec_d(const ScoreArgs& a, hipStream_t st) {
+  if (a.G >= 8) launch_vec_nh<BF16, D, 8>(a, st);
+  else if (a.G >= 4) launch_vec_nh<BF16, D, 4>(a, st);
+  else if (a.G >= 2) launch_vec_nh<BF16, D, 2>(a, st);
+  else launch_vec_nh<BF16, D, 1>(a, st);
+}
+
+template <bool BF16>
+static void launch_vec(const ScoreArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 64: launch_vec_d<BF16, 64>(a, st); break;
+    case 128: launch_vec_d<BF16, 128>(a, st); break;
+    default: launch_vec_d<BF16, 256>(a, st); break;
+  }
+}
+
+bool score_uses_mfma(int dtype_bf16, int G) { return dtype_bf16 && G >= 2 && G <= 16; }
+
+void launch_score_dense(const ScoreArgs& a, hipStream_t st) {
+  if (a.nrows <= 0) return;
+  if (score_uses_mfma(a.bf16, a.G)) {
+    switch (a.d) {
+      case 64: launch_mfma_d<64>(a, st); break;
+      case 128: launch_mfma_d<128>(a, st); break;
+      default: launch_mfma_d<256>(a, st); break;
+    }
+  } else if (a.bf16) {
+    launch_vec<true>(a, st);
+  } else {
+    launch_vec<false>(a, st);
+  }
+}
+
+template <int DI, int NT>
+static void launch_idx_t(const IndexerArgs& a, hipStream_t st) {
+  const int chunk = pick_chunk(a.L, a.B, 512, 512, 8192);
+  dim3 grid((a.L + chunk - 1) / chunk, a.B);
+  hipLaunchKernelGGL((score_indexer_kernel<DI, NT>), grid, dim3(256), 0, st, a.qI, a.kI, a.w, a.scores, a.HI, a.L,
+                     chunk);
+}
+
+template <int DI>
+static void launch_idx_d(const IndexerArgs& a, hipStream_t st) {
+  if (a.HI <= 32) launch_idx_t<DI, 1>(a, st);
+  else if (a.HI <= 64) launch_idx_t<DI, 2>(a, st);
+  else launch_idx_t<DI, 4>(a, st);
+}
+
+void launch_score_indexer(const IndexerArgs& a, hipStream_t st) {
+  if (a.dI == 64) launch_idx_d<64>(a, st);
+  else launch_idx_d<128>(a, st);
+}
+
+template <bool BF16>
+static void launch_bm(const BlockMeanArgs& a, hipStream_t st) {
+  dim3 grid((a.m + 3) / 4, a.B * a.Hkv);
+  switch (a.d) {
+    case 64:
+      hipLaunchKernelGGL((block_mean_kernel<BF16, 64>), grid, dim3(256), 0, st, a.K, a.means, a.Hkv, a.L, a.bsz, a.m,
+                         a.sb, a.sh, a.sl);
+      break;
+    case 128:
+      hipLaunchKernelGGL((block_mean_kernel<BF16, 128>), grid, dim3(256), 0, st, a.K, a.means, a.Hkv, a.L, a.bsz,
+                         a.m, a.sb, a.sh, a.sl);
+      break;
+    default:
+      hipLaunchKernelGGL((block_mean_kernel<BF16, 256>), grid, dim3(256), 0, st, a.K, a.means, a.Hkv, a.L, a.bsz,
+                         a.m, a.sb, a.sh, a.sl);
+      break;
+  }
+}
+
+void launch_block_mean(const BlockMeanArgs& a, hipStream_t st) {
+  if (a.bf16) launch_bm<true>(a, st);
+  else launch_bm<false>(a, st);
+}
+
+}  // namespace tka

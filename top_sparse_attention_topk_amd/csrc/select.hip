@@ -1,0 +1,543 @@
+// Exact top-k selection for gfx950 (TopK_j s_j of "Sparse Attention
+// Landscape", "Block Sparse Attention"; the fixed budget of "Sparse Attention
+// in LLM Inference", "The Significance of Top-K").
+//
+// Order: i before j when s_i > s_j, or s_i == s_j and i < j; -0 == +0; NaN
+// below every number. Scores become order-preserving 32-bit keys and the
+// k-th key T is found digit by digit (bits 31..20, 19..10, 9..0) with LDS
+// histograms. Elements whose key is at least the lower edge of T's current
+// digit range are compacted in position order (wave ballots + mbcnt), so the
+// answer is emitted in ascending position with no sort: every key > T, and
+// the first (k - #(key > T)) keys == T in position order.
+//
+// Two launch shapes:
+//  - row mode: one workgroup per row (many rows). Pass 1 builds the level-0
+//    histogram, pass 2 compacts the candidates into LDS; the rest runs on
+//    LDS. Extra histogram passes (and a streaming emit) only when the
+//    candidates do not fit (heavy ties).
+//  - split mode: few long rows. Chunks of 4096 elements per workgroup build a
+//    global histogram, then compact their candidates into per-chunk regions;
+//    one workgroup per row finishes on the (small) candidate list.
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace tka {
+
+constexpr int ST = 256;  // threads per workgroup
+constexpr int SW = 4;    // waves per workgroup
+constexpr int NB0 = 4096;
+constexpr int NB1 = 1024;
+constexpr int UNR = 4;          // float4 loads per lane per round
+constexpr int CHUNK = 4096;     // split mode: elements per workgroup
+constexpr int SUBCH = CHUNK / SW;
+
+__device__ __forceinline__ int lv_shift(int lv) { return lv == 0 ? 20 : (lv == 1 ? 10 : 0); }
+__device__ __forceinline__ int lv_bits(int lv) { return lv == 0 ? 12 : 10; }
+__device__ __forceinline__ int lv_bins(int lv) { return lv == 0 ? NB0 : NB1; }
+__device__ __forceinline__ uint32_t lv_digit(uint32_t key, int lv) {
+  return (key >> lv_shift(lv)) & (lv == 0 ? 0xFFFu : 0x3FFu);
+}
+// the digits above level lv equal `prefix`
+__device__ __forceinline__ bool lv_in_range(uint32_t key, int lv, uint32_t prefix) {
+  return lv == 0 || (key >> lv_shift(lv - 1)) == prefix;
+}
+
+struct SelSmem {
+  uint32_t hist[NB0];
+  uint32_t scan[SW];
+  uint32_t res[2];
+  uint32_t cnt[SW];
+  uint32_t gt[SW], eq[SW];
+  uint32_t obase[SW], eqbase[SW];
+};
+
+__device__ uint32_t block_incl_scan(uint32_t v, SelSmem& sm, uint32_t* total) {
+  const int w = threadIdx.x >> 6, l = lane_id();
+  uint32_t x = wave_incl_scan(v);
+  if (l == 63) sm.scan[w] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < SW; ++i) {
+    off += (i < w) ? sm.scan[i] : 0u;
+    tot += sm.scan[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return x + off;
+}
+
+// Bin b with above(b) < need <= above(b) + hist[b], above(b) = sum of the
+// bins over b. Result in sm.res (bin, above). need must not exceed the total.
+__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, SelSmem& sm) {
+  const int t = threadIdx.x;
+  const int per = nb / ST;
+  uint32_t s = 0;
+  for (int i = 0; i < per; ++i) s += hist[t * per + i];
+  uint32_t tot;
+  const uint32_t incl = block_incl_scan(s, sm, &tot);
+  const uint32_t above = tot - incl;
+  if (above < need && need <= above + s) {
+    uint32_t acc = above;
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t h = hist[t * per + i];
+      if (acc + h >= need) {
+        sm.res[0] = (uint32_t)(t * per + i);
+        sm.res[1] = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void load4(const float* s, int p, int end, bool aligned, float (&v)[4]) {
+  if (aligned && p + 3 < end) {
+    const float4 x = *reinterpret_cast<const float4*>(s + p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (p + j < end) ? s[p + j] : 0.f;
+  }
+}
+
+// LDS histogram of digit lv over the elements of [r0, r1) inside the range.
+__device__ void hist_pass(const float* s, int r0, int r1, bool aligned, int lv, uint32_t prefix, uint32_t* hist) {
+  const int lane = lane_id();
+  for (int base = r0; base < r1; base += 256 * UNR) {
+    float v[UNR][4];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = base + u * 256 + 4 * lane + j;
+        const uint32_t key = score_key(v[u][j]);
+        if (p < r1 && lv_in_range(key, lv, prefix)) atomicAdd(&hist[lv_digit(key, lv)], 1u);
+      }
+  }
+}
+
+// Keys >= lo of [r0, r1), in position order, to cb/cp (first `cap` of them).
+// Returns the number found (the same value in every lane).
+__device__ uint32_t collect_pass(const float* s, int r0, int r1, bool aligned, uint32_t lo, uint32_t* cb,
+                                 int32_t* cp, uint32_t cap) {
+  const int lane = lane_id();
+  uint32_t cnt = 0;
+  for (int base = r0; base < r1; base += 256 * UNR) {
+    float v[UNR][4];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      bool f[4];
+      uint32_t before = 0, tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = base + u * 256 + 4 * lane + j;
+        f[j] = p < r1 && score_key(v[u][j]) >= lo;
+        const uint64_t bl = ballot(f[j]);
+        before += count_below(bl);
+        tot += __popcll(bl);
+      }
+      uint32_t slot = cnt + before;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (f[j]) {
+          if (slot < cap) {
+            cb[slot] = __float_as_uint(v[u][j]);
+            cp[slot] = base + u * 256 + 4 * lane + j;
+          }
+          ++slot;
+        }
+      }
+      cnt += tot;
+    }
+  }
+  return cnt;
+}
+
+// Continue the radix search inside the candidates (each wave owns
+// [off, off+cnt) of cb) through levels lv+1..2. Returns T in sm.res[0] and
+// the number of keys == T to keep in sm.res[1].
+__device__ void refine_candidates(const uint32_t* cb, uint32_t off, uint32_t cnt, int lv, uint32_t prefix,
+                                  uint32_t need, SelSmem& sm) {
+  const int lane = lane_id();
+  for (int l = lv + 1; l <= 2; ++l) {
+    for (int i = threadIdx.x; i < NB1; i += ST) sm.hist[i] = 0;
+    __syncthreads();
+    for (uint32_t e = lane; e < cnt; e += 64) {
+      const uint32_t key = score_key(__uint_as_float(cb[off + e]));
+      if (lv_in_range(key, l, prefix)) atomicAdd(&sm.hist[lv_digit(key, l)], 1u);
+    }
+    __syncthreads();
+    find_bin(sm.hist, NB1, need, sm);
+    const uint32_t bin = sm.res[0], above = sm.res[1];
+    __syncthreads();
+    need -= above;
+    prefix = (prefix << 10) | bin;
+  }
+  if (threadIdx.x == 0) {
+    sm.res[0] = prefix;
+    sm.res[1] = need;
+  }
+  __syncthreads();
+}
+
+// Emit, in position order, every element with key > T and the first need_eq
+// elements with key == T. Wave w walks its own segment [0, cnt) through
+// get(e) -> (bits, position); segments are in position order by wave.
+template <typename Get>
+__device__ void emit_segments(Get get, uint32_t cnt, uint32_t T, uint32_t need_eq, SelSmem& sm, int32_t* oidx,
+                              float* osel, uint32_t kk) {
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  uint32_t ngt = 0, neq = 0;
+  for (uint32_t e = lane; e < cnt; e += 64) {
+    uint32_t bits;
+    int32_t pos;
+    get(e, bits, pos);
+    const uint32_t key = score_key(__uint_as_float(bits));
+    ngt += key > T;
+    neq += key == T;
+  }
+  ngt = wave_sum(ngt);
+  neq = wave_sum(neq);
+  if (lane == 0) {
+    sm.gt[w] = ngt;
+    sm.eq[w] = neq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t eb = 0, ob = 0;
+    for (int i = 0; i < SW; ++i) {
+      sm.eqbase[i] = eb;
+      sm.obase[i] = ob;
+      const uint32_t take = need_eq > eb ? min(need_eq - eb, sm.eq[i]) : 0u;
+      ob += sm.gt[i] + take;
+      eb += sm.eq[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t eqb = sm.eqbase[w];
+  uint32_t run = sm.obase[w], eqrun = 0;
+  for (uint32_t e0 = 0; e0 < cnt; e0 += 64) {
+    const uint32_t e = e0 + lane;
+    uint32_t bits = 0;
+    int32_t pos = 0;
+    const bool valid = e < cnt;
+    if (valid) get(e, bits, pos);
+    const uint32_t key = score_key(__uint_as_float(bits));
+    const bool gt = valid && key > T;
+    const bool eq = valid && key == T;
+    const uint64_t be = ballot(eq);
+    const uint32_t er = eqb + eqrun + count_below(be);
+    const bool take = gt || (eq && er < need_eq);
+    const uint64_t bs = ballot(take);
+    const uint32_t slot = run + count_below(bs);
+    if (take && slot < kk) {  // slot < kk always holds: exactly kk elements qualify
+      oidx[slot] = pos;
+      if (osel) osel[slot] = __uint_as_float(bits);
+    }
+    run += __popcll(bs);
+    eqrun += __popcll(be);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row mode: one workgroup per row. Dynamic LDS: SelSmem, then 4*capw
+// candidate bits and 4*capw candidate positions.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void select_rows_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
+                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
+                                                          int capw) {
+  extern __shared__ uint4 smem_raw[];
+  SelSmem& sm = *reinterpret_cast<SelSmem*>(smem_raw);
+  uint32_t* cb = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(smem_raw) + ((sizeof(SelSmem) + 15) & ~15));
+  int32_t* cp = reinterpret_cast<int32_t*>(cb + 4 * capw);
+
+  const int64_t row = blockIdx.x;
+  const float* s = S + row * stride;
+  int32_t* oidx = idx + row * k;
+  float* osel = sel ? sel + row * k : nullptr;
+  const int kk = min(k, n);
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  for (int j = kk + t; j < k; j += ST) {
+    oidx[j] = -1;
+    if (osel) osel[j] = -INFINITY;
+  }
+  if (kk <= 0) return;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  const int seg = ((n + 4 * SW - 1) / (4 * SW)) * 4;
+  const int r0 = min(n, w * seg), r1 = min(n, r0 + seg);
+  if (kk == n) {
+    for (int p = r0 + lane; p < r1; p += 64) {
+      oidx[p] = p;
+      if (osel) osel[p] = s[p];
+    }
+    return;
+  }
+  int lv = 0;
+  uint32_t prefix = 0, need = (uint32_t)kk, cnt_above = 0;
+  while (true) {
+    const int nb = lv_bins(lv);
+    for (int i = t; i < nb; i += ST) sm.hist[i] = 0;
+    __syncthreads();
+    hist_pass(s, r0, r1, aligned, lv, prefix, sm.hist);
+    __syncthreads();
+    find_bin(sm.hist, nb, need, sm);
+    const uint32_t bin = sm.res[0], above = sm.res[1];
+    const uint32_t inbin = sm.hist[bin];
+    __syncthreads();
+    need -= above;
+    cnt_above += above;
+    prefix = (prefix << lv_bits(lv)) | bin;
+    const uint32_t lo = prefix << lv_shift(lv);
+    if (cnt_above + inbin <= (uint32_t)(SW * capw)) {
+      uint32_t c = collect_pass(s, r0, r1, aligned, lo, cb + w * capw, cp + w * capw, (uint32_t)capw);
+      if (lane == 0) sm.cnt[w] = c;
+      __syncthreads();
+      bool over = false;
+      uint32_t base = 0;
+      for (int i = 0; i < SW; ++i) {
+        over |= sm.cnt[i] > (uint32_t)capw;
+        base += (i < w) ? sm.cnt[i] : 0u;
+      }
+      uint32_t off = (uint32_t)(w * capw);
+      if (over) {  // uneven spread across waves: pack the waves' candidates back to back
+        collect_pass(s, r0, r1, aligned, lo, cb + base, cp + base, 0xffffffffu);
+        off = base;
+        __syncthreads();
+      }
+      refine_candidates(cb, off, c, lv, prefix, need, sm);
+      const uint32_t T = sm.res[0], need_eq = sm.res[1];
+      __syncthreads();
+      emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = cb[off + e]; pos = cp[off + e]; }, c, T,
+                    need_eq, sm, oidx, osel, (uint32_t)kk);
+      return;
+    }
+    if (lv == 2) {  // T fully known and still too many ties for LDS: stream the row
+      emit_segments(
+          [&](uint32_t e, uint32_t& bits, int32_t& pos) {
+            pos = r0 + (int)e;
+            bits = __float_as_uint(s[pos]);
+          },
+          (uint32_t)(r1 - r0), prefix, need, sm, oidx, osel, (uint32_t)kk);
+      return;
+    }
+    ++lv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split mode (few long rows)
+// ---------------------------------------------------------------------------
+__global__ void select_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void select_chunk_hist_kernel(const float* __restrict__ S, int n, int64_t stride,
+                                                                int k, uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t hist[NB0];
+  const int64_t row = blockIdx.y;
+  if (min(k, n) == n) return;
+  const float* s = S + row * stride;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  const int w = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * CHUNK;
+  const int r0 = min(n, c0 + w * SUBCH), r1 = min(n, r0 + SUBCH);
+  for (int i = threadIdx.x; i < NB0; i += ST) hist[i] = 0;
+  __syncthreads();
+  hist_pass(s, r0, r1, aligned, 0, 0, hist);
+  __syncthreads();
+  uint32_t* gh = ghist + row * NB0;
+  for (int i = threadIdx.x; i < NB0; i += ST)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+__global__ __launch_bounds__(256) void select_chunk_collect_kernel(const float* __restrict__ S, int n,
+                                                                   int64_t stride, int k,
+                                                                   const uint32_t* __restrict__ ghist,
+                                                                   uint32_t* __restrict__ cbits,
+                                                                   int32_t* __restrict__ cpos,
+                                                                   uint32_t* __restrict__ ccount, int nch) {
+  __shared__ SelSmem sm;
+  const int64_t row = blockIdx.y;
+  const int kk = min(k, n);
+  if (kk == n) return;
+  const float* s = S + row * stride;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  const uint32_t* gh = ghist + row * NB0;
+  for (int i = threadIdx.x; i < NB0; i += ST) sm.hist[i] = gh[i];
+  __syncthreads();
+  find_bin(sm.hist, NB0, (uint32_t)kk, sm);
+  const uint32_t lo = sm.res[0] << 20;
+  const int w = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * CHUNK;
+  const int r0 = min(n, c0 + w * SUBCH), r1 = min(n, r0 + SUBCH);
+  const int64_t base = row * (int64_t)n + r0;
+  const uint32_t c = collect_pass(s, r0, r1, aligned, lo, cbits + base, cpos + base, (uint32_t)SUBCH);
+  if (lane_id() == 0) ccount[(row * nch + blockIdx.x) * SW + w] = c;
+}
+
+// Dynamic LDS: nseg segment offsets.
+__global__ __launch_bounds__(256) void select_finish_kernel(const float* __restrict__ S, int n, int64_t stride,
+                                                            int k, const uint32_t* __restrict__ ghist,
+                                                            const uint32_t* __restrict__ cbits,
+                                                            const int32_t* __restrict__ cpos,
+                                                            const uint32_t* __restrict__ ccount,
+                                                            uint32_t* __restrict__ catb, int32_t* __restrict__ catp,
+                                                            int nch, int32_t* __restrict__ idx,
+                                                            float* __restrict__ sel) {
+  __shared__ SelSmem sm;
+  extern __shared__ uint32_t segoff[];
+  const int64_t row = blockIdx.x;
+  const float* s = S + row * stride;
+  int32_t* oidx = idx + row * k;
+  float* osel = sel ? sel + row * k : nullptr;
+  const int kk = min(k, n);
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  for (int j = kk + t; j < k; j += ST) {
+    oidx[j] = -1;
+    if (osel) osel[j] = -INFINITY;
+  }
+  if (kk <= 0) return;
+  if (kk == n) {
+    for (int p = t; p < n; p += ST) {
+      oidx[p] = p;
+      if (osel) osel[p] = s[p];
+    }
+    return;
+  }
+  const uint32_t* gh = ghist + row * NB0;
+  for (int i = t; i < NB0; i += ST) sm.hist[i] = gh[i];
+  __syncthreads();
+  find_bin(sm.hist, NB0, (uint32_t)kk, sm);
+  const uint32_t prefix = sm.res[0], above = sm.res[1];
+  __syncthreads();
+  // offsets of the (chunk, wave) segments, in position order
+  const int nseg = nch * SW;
+  const uint32_t* cc = ccount + row * (int64_t)nseg;
+  const int per = (nseg + ST - 1) / ST;
+  uint32_t loc = 0;
+  for (int i = 0; i < per; ++i) {
+    const int sg = t * per + i;
+    loc += sg < nseg ? cc[sg] : 0u;
+  }
+  uint32_t total;
+  const uint32_t incl = block_incl_scan(loc, sm, &total);
+  uint32_t run = incl - loc;
+  for (int i = 0; i < per; ++i) {
+    const int sg = t * per + i;
+    if (sg < nseg) {
+      segoff[sg] = run;
+      run += cc[sg];
+    }
+  }
+  __syncthreads();
+  uint32_t* rb = catb + row * (int64_t)n;
+  int32_t* rp = catp + row * (int64_t)n;
+  for (int sg = w; sg < nseg; sg += SW) {
+    const int64_t src = row * (int64_t)n + (int64_t)(sg / SW) * CHUNK + (sg % SW) * SUBCH;
+    const uint32_t cnt = cc[sg], dst = segoff[sg];
+    for (uint32_t e = lane; e < cnt; e += 64) {
+      rb[dst + e] = cbits[src + e];
+      rp[dst + e] = cpos[src + e];
+    }
+  }
+  __syncthreads();
+  const uint32_t q = (total + SW - 1) / SW;
+  const uint32_t off = min(total, (uint32_t)w * q);
+  const uint32_t cnt = min(total, off + q) - off;
+  refine_candidates(rb, off, cnt, 0, prefix, (uint32_t)kk - above, sm);
+  const uint32_t T = sm.res[0], need_eq = sm.res[1];
+  __syncthreads();
+  emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = rb[off + e]; pos = rp[off + e]; }, cnt, T,
+                need_eq, sm, oidx, osel, (uint32_t)kk);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static bool use_split(int64_t n_rows, int n) { return n_rows < 128 && n > 4 * CHUNK; }
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SplitLayout {
+  size_t ghist, cbits, cpos, ccount, catb, catp, total;
+};
+
+static SplitLayout split_layout(int64_t n_rows, int n) {
+  const int64_t nch = (n + CHUNK - 1) / CHUNK;
+  SplitLayout L;
+  size_t o = 0;
+  L.ghist = o; o += al256(sizeof(uint32_t) * n_rows * NB0);
+  L.cbits = o; o += al256(sizeof(uint32_t) * n_rows * (size_t)n);
+  L.cpos = o; o += al256(sizeof(int32_t) * n_rows * (size_t)n);
+  L.ccount = o; o += al256(sizeof(uint32_t) * n_rows * nch * SW);
+  L.catb = o; o += al256(sizeof(uint32_t) * n_rows * (size_t)n);
+  L.catp = o; o += al256(sizeof(int32_t) * n_rows * (size_t)n);
+  L.total = o;
+  return L;
+}
+
+size_t select_workspace_bytes(int64_t n_rows, int n, int k) {
+  (void)k;
+  if (!use_split(n_rows, n)) return 0;
+  return split_layout(n_rows, n).total;
+}
+
+static int max_lds_bytes() {
+  static int cached[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+      v = 64 * 1024;
+    (void)hipFuncSetAttribute((const void*)select_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
+  if (a.n_rows <= 0) return;
+  if (!use_split(a.n_rows, a.n)) {
+    const int kk = a.k < a.n ? a.k : a.n;
+    int capw = 64;
+    while (capw < 2048 && (int64_t)SW * capw < (int64_t)kk + kk / 2 + 64) capw <<= 1;
+    const size_t head = (sizeof(SelSmem) + 15) & ~(size_t)15;
+    const int lds_max = max_lds_bytes();
+    while (capw > 64 && head + (size_t)SW * capw * 8 > (size_t)lds_max) capw >>= 1;
+    const size_t lds = head + (size_t)SW * capw * 8;
+    hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride,
+                       a.k, a.idx, a.sel, capw);
+    return;
+  }
+  const SplitLayout L = split_layout(a.n_rows, a.n);
+  char* base = static_cast<char*>(ws);
+  uint32_t* ghist = reinterpret_cast<uint32_t*>(base + L.ghist);
+  uint32_t* cbits = reinterpret_cast<uint32_t*>(base + L.cbits);
+  int32_t* cpos = reinterpret_cast<int32_t*>(base + L.cpos);
+  uint32_t* ccount = reinterpret_cast<uint32_t*>(base + L.ccount);
+  uint32_t* catb = reinterpret_cast<uint32_t*>(base + L.catb);
+  int32_t* catp = reinterpret_cast<int32_t*>(base + L.catp);
+  const int nch = (a.n + CHUNK - 1) / CHUNK;
+  const int64_t nh = a.n_rows * NB0;
+  hipLaunchKernelGGL(select_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
+                     dim3(256), 0, st, ghist, nh);
+  hipLaunchKernelGGL(select_chunk_hist_kernel, dim3(nch, (unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n,
+                     a.stride, a.k, ghist);
+  hipLaunchKernelGGL(select_chunk_collect_kernel, dim3(nch, (unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n,
+                     a.stride, a.k, ghist, cbits, cpos, ccount, nch);
+  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.n_rows), dim3(ST), sizeof(uint32_t) * nch * SW, st,
+                     a.scores, a.n, a.stride, a.k, ghist, cbits, cpos, ccount, catb, catp, nch, a.idx, a.sel);
+}
+
+}  // namespace tka
