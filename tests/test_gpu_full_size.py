@@ -55,12 +55,13 @@ def test_full_size_workload(name):
         rows = [0]
     elif w.mode == fx.MODE_BLOCK:
         scores = m.topk_attn_score(p, qt, kw["proxy_keys"])
-        rows = sorted({0, 1, w.Hq + 5, (w.B - 1) * w.Hq + w.Hq - 1})
+        rows = sorted({r for r in (0, 1, w.Hq + 5, w.B * w.Hq - 1) if r < w.B * w.Hq})
     else:
         scores = m.topk_attn_score(p, qt, Kt)
         nr = w.B * w.Hq
-        rows = sorted({0, nr // 3 + 1, nr // 2 + 7, nr - 1})
+        rows = sorted({r for r in (0, nr // 3 + 1, nr // 2 + 7, nr - 1) if r < nr})
     S = scores.reshape(-1, n)
+    assert all(0 <= r < S.shape[0] for r in rows), rows  # checked on the host before indexing on the GPU
     gs = gpu_scores_np(S[rows])
     gi = idx2[rows].cpu().numpy()
     if w.mode == fx.MODE_INDEXER:

@@ -117,6 +117,7 @@ ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys
   a.Hkv = p->n_kv_heads;
   a.G = p->n_q_heads / p->n_kv_heads;
   a.d = p->head_dim;
+  a.q_bf16 = p->qkv_dtype == TKA_BF16;
   if (p->mode == TKA_SCORE_BLOCK_MEAN) {
     const int64_t m = n_blocks(p);
     a.nrows = (int)(m - 1);

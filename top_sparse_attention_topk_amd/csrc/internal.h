@@ -13,7 +13,8 @@ struct ScoreArgs {
   int B, Hq, Hkv, G, d, nrows;
   int64_t sb, sh, sl;
   float scale;
-  int bf16;  // 1: bf16 rows and q, 0: fp32
+  int bf16;    // rows: 1 bf16, 0 fp32
+  int q_bf16;  // query: 1 bf16, 0 fp32
 };
 
 struct IndexerArgs {

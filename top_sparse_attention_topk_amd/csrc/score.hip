@@ -99,14 +99,15 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 // A row of D elements is 16*LPR bytes: LPR lanes load 16 B each, RPW = 64/LPR
 // rows per wave load. Each lane keeps its 16-byte slice of q for every head,
 // the partial dots are reduced across the LPR lanes with xor shuffles.
-// Used for G = 1 heads, fp32 caches and the fp32 block-mean cache.
+// Used for G = 1 heads, fp32 caches and the fp32 block-mean cache (whose
+// query stays bf16: q_bf16 gives the query's dtype, BF16 the rows').
 // Grid (chunks, B*Hkv*htiles), 256 threads.
 // ---------------------------------------------------------------------------
 template <bool BF16, int D, int NH>
 __global__ __launch_bounds__(256) void score_vec_kernel(const void* __restrict__ qv, const void* __restrict__ Kv,
                                                         float* __restrict__ S, int Hq, int Hkv, int G, int nrows,
                                                         int64_t sb, int64_t sh, int64_t sl, float scale, int chunk,
-                                                        int htiles) {
+                                                        int htiles, int q_bf16) {
   using U = Unpack<BF16>;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPL = U::N;
@@ -125,12 +126,14 @@ __global__ __launch_bounds__(256) void score_vec_kernel(const void* __restrict__
   float qf[NH][EPL];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    if (h < nh) {
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(qv) + ((int64_t)(b * Hq + h0 + h) * D + sub * EPL) * ES;
-      U::run(ld16(qp), qf[h]);
-    } else {
+    const int64_t q0 = (int64_t)(b * Hq + h0 + h) * D + sub * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[h][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) {
+      float x = 0.f;
+      if (h < nh)
+        x = q_bf16 ? bf16_lo(reinterpret_cast<const uint16_t*>(qv)[q0 + e])
+                   : reinterpret_cast<const float*>(qv)[q0 + e];
+      qf[h][e] = x;
     }
   }
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(Kv) + ((int64_t)b * sb + (int64_t)g * sh) * ES;
@@ -329,7 +332,7 @@ static void launch_vec_nh(const ScoreArgs& a, hipStream_t st) {
   const int chunk = pick_chunk(a.nrows, (int64_t)a.B * a.Hkv * htiles, gran, gran, 4096);
   dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv * htiles);
   hipLaunchKernelGGL((score_vec_kernel<BF16, D, NH>), grid, dim3(256), 0, st, a.q, a.keys, a.scores, a.Hq, a.Hkv,
-                     a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, htiles);
+                     a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, htiles, a.q_bf16);
 }
 
 template <bool BF16, int D>
