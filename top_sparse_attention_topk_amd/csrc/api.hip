@@ -293,13 +293,50 @@ tka_status check_gather_ptrs(const tka_problem* p, const void* q, const void* K,
   return TKA_OK;
 }
 
+// ---- fused exact step: candidate prefilter plan ----
+// Used for the bf16 MFMA scan when the kept fraction is small (k' <= L/8) and
+// the row is long. Samples are the first 64 positions of every sample chunk;
+// the threshold is the r-th largest sample with r = 1.75 k' nsamp / L (about
+// 1.75 k' candidates expected), the chunk being chosen so that r >= 200
+// (a shortfall below k' is then a > 6 sigma event for exchangeable scores;
+// it is detected and repaired by a full rescore of the row anyway).
+struct PrefilterPlan {
+  bool on;
+  int sample_chunk, nsamp, r, capg;
+};
+
+int64_t sample_count(int64_t L, int64_t sc) {
+  const int64_t nch = (L + sc - 1) / sc;
+  const int64_t last = L - (nch - 1) * sc;
+  return 64 * (nch - 1) + (last < 64 ? last : 64);
+}
+
+PrefilterPlan prefilter_plan(const tka_problem* p) {
+  PrefilterPlan pf{};
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (p->mode != TKA_SCORE_EXACT || p->qkv_dtype != TKA_BF16 || !score_uses_mfma(1, G)) return pf;
+  const int64_t L = p->seq_len, kk = p->top_k < p->seq_len ? p->top_k : p->seq_len;
+  if (L < 8192 || L > 262144 || kk * 8 > L) return pf;
+  int64_t sc = 4096;
+  while (sc > 128 && 7 * kk * sample_count(L, sc) < 4 * 200 * L) sc >>= 1;
+  pf.sample_chunk = (int)sc;
+  pf.nsamp = (int)sample_count(L, sc);
+  pf.r = (int)((7 * kk * pf.nsamp + 4 * L - 1) / (4 * L));
+  if (pf.r < 1) pf.r = 1;
+  pf.capg = (int)(3 * kk);
+  pf.on = true;
+  return pf;
+}
+
 // ---- fused step: workspace layout ----
 struct DecodeLayout {
   size_t scores, sel_ws, idx, selv, gather_ws, total;
+  size_t samp, T, cnt, row_flag, group_flag, cbits, cpos;
   int64_t rows;
   int32_t len;
   int32_t k;
   GatherPlan gp;
+  PrefilterPlan pf;
   int unit, shared;
 };
 
@@ -323,6 +360,24 @@ DecodeLayout decode_layout(const tka_problem* p) {
   d.gp = plan_gather(ga);
   d.gather_ws = o;
   o += al256(d.gp.ws_bytes);
+  d.pf = prefilter_plan(p);
+  if (d.pf.on) {
+    const size_t R = (size_t)d.rows;
+    d.samp = o;
+    o += al256(sizeof(float) * R * d.pf.nsamp);
+    d.T = o;
+    o += al256(sizeof(uint32_t) * R);
+    d.cnt = o;
+    o += al256(sizeof(uint32_t) * R);
+    d.row_flag = o;
+    o += al256(sizeof(uint32_t) * R);
+    d.group_flag = o;
+    o += al256(sizeof(uint32_t) * (size_t)p->batch * p->n_kv_heads);
+    d.cbits = o;
+    o += al256(sizeof(uint32_t) * R * d.pf.capg);
+    d.cpos = o;
+    o += al256(sizeof(int32_t) * R * d.pf.capg);
+  }
   d.total = o;
   return d;
 }
@@ -459,12 +514,38 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
   float* selv = reinterpret_cast<float*>(base + d.selv);
   const bool exact = p->mode == TKA_SCORE_EXACT;
 
-  // 1. score
-  if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);
-  else if (d.len > 0) run_score(p, q, exact ? k_cache : proxy_keys, nullptr, scores, st);
-  // 2. select
   SelectArgs sa{scores, d.rows, d.len, (int64_t)d.len, d.k, idx, exact ? selv : nullptr};
-  launch_select(sa, base + d.sel_ws, st);
+  if (d.pf.on) {
+    // 1+2. sampled threshold, candidate scan, exact select on the candidates;
+    // rows whose candidates cannot hold the answer are rescored in full
+    const ScoreArgs sc = dense_score_args(p, q, k_cache, scores);
+    float* samp = reinterpret_cast<float*>(base + d.samp);
+    uint32_t* T = reinterpret_cast<uint32_t*>(base + d.T);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base + d.cnt);
+    uint32_t* row_flag = reinterpret_cast<uint32_t*>(base + d.row_flag);
+    uint32_t* group_flag = reinterpret_cast<uint32_t*>(base + d.group_flag);
+    uint32_t* cbits = reinterpret_cast<uint32_t*>(base + d.cbits);
+    int32_t* cpos = reinterpret_cast<int32_t*>(base + d.cpos);
+    const int G = p->n_q_heads / p->n_kv_heads;
+    launch_score_mfma_sample(sc, d.pf.sample_chunk, d.pf.nsamp, samp, st);
+    launch_prefilter_threshold(samp, d.rows, d.pf.nsamp, d.pf.r, T, cnt, row_flag, group_flag, G, st);
+    MfmaOut mo{};
+    mo.T = T;
+    mo.cnt = cnt;
+    mo.cbits = cbits;
+    mo.cpos = cpos;
+    mo.capg = d.pf.capg;
+    launch_score_mfma_cand(sc, mo, st);
+    launch_prefilter_finish(cbits, cpos, cnt, d.pf.capg, d.rows, d.len, d.k, G, idx, selv, row_flag, group_flag, st);
+    launch_score_mfma_guarded(sc, group_flag, st);
+    launch_select_rows_flagged(sa, row_flag, st);
+  } else {
+    // 1. score
+    if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);
+    else if (d.len > 0) run_score(p, q, exact ? k_cache : proxy_keys, nullptr, scores, st);
+    // 2. select
+    launch_select(sa, base + d.sel_ws, st);
+  }
   // 3. gather
   GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, d.k, d.unit, d.shared, exact ? selv : nullptr, out);
   launch_gather(ga, d.gp, base + d.gather_ws, st);

@@ -57,13 +57,39 @@ struct GatherArgs {
   int n_idx, unit, shared;
 };
 
+// Outputs of the exact bf16 MFMA scan (see score.hip for the modes).
+struct MfmaOut {
+  float* S;                     // full scores [B*Hq, L], or sample scores [B*Hq, nsamp]
+  int nsamp;
+  const uint32_t* T;            // candidate mode: key threshold per row
+  uint32_t* cnt;                // candidate mode: candidates found per row
+  uint32_t* cbits;              // candidate mode: [B*Hq, capg] score bits
+  int32_t* cpos;                // candidate mode: [B*Hq, capg] positions
+  int capg;
+  int stage;                    // candidate mode: LDS staging entries per head
+  const uint32_t* group_flag;   // guarded mode: [B*Hkv], nonzero = rescore the group
+};
+
 bool score_uses_mfma(int dtype_bf16, int G);
+int mfma_scan_chunk(const ScoreArgs& a);
+void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, float* samp, hipStream_t st);
+void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st);
+void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st);
 void launch_score_dense(const ScoreArgs& a, hipStream_t st);
 void launch_score_indexer(const IndexerArgs& a, hipStream_t st);
 void launch_block_mean(const BlockMeanArgs& a, hipStream_t st);
 
 size_t select_workspace_bytes(int64_t n_rows, int n, int k);
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
+// one workgroup per row, only rows whose flag is nonzero
+void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st);
+
+// candidate prefilter of the fused exact step (select.hip)
+void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, uint32_t* T, uint32_t* cnt,
+                                uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st);
+void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, int capg,
+                             int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel, uint32_t* row_flag,
+                             uint32_t* group_flag, hipStream_t st);
 
 // gather planning is shared by the workspace query and the launch
 struct GatherPlan {

@@ -20,20 +20,45 @@ namespace tka {
 // v_mfma_f32_16x16x32_bf16 tile = 16 positions x 16 heads (G used) x 32 dims.
 // A = 16 key rows (lane l: row l%16, dims 8*(l/16)+[0,8) of each 32-dim step),
 // B = q^T of the group (lane l: head l%16, same dims), C[pos][head]: lane l
-// holds head l%16 for positions 4*(l/16)+[0,4).
+// holds head l%16 for positions 4*(l/16)+[0,4). A position always sits in
+// lane row pos%16 and the dims are summed in one fixed order, so every mode
+// below produces bit-identical scores.
 // Grid (chunks, B*Hkv), 256 threads; each wave takes 64 positions per round.
+//   MFMA_FULL    - write every score, [B*Hq, L].
+//   MFMA_SAMPLE  - only the first 64 positions of every chunk; wave w of
+//                  workgroup x takes chunk 4x+w; scores to [B*Hq, nsamp].
+//   MFMA_CAND    - keep the scores whose key is >= T[row] as (bits, position)
+//                  candidates: staged per head in LDS, appended to the row's
+//                  list with one atomic per head and workgroup.
+//   MFMA_GUARDED - MFMA_FULL for the groups whose flag is set, else nothing.
 // ---------------------------------------------------------------------------
-template <int D>
+enum { MFMA_FULL = 0, MFMA_SAMPLE = 1, MFMA_CAND = 2, MFMA_GUARDED = 3 };
+
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ K,
-                                                               float* __restrict__ S, int Hq, int Hkv, int G, int L,
-                                                               int64_t sb, int64_t sh, int64_t sl, float scale,
-                                                               int chunk) {
+                                                               const uint16_t* __restrict__ K, int Hq, int Hkv, int G,
+                                                               int L, int64_t sb, int64_t sh, int64_t sl, float scale,
+                                                               int chunk, MfmaOut o) {
   constexpr int KS = D / 32;
   const int task = blockIdx.y;
+  if (MODE == MFMA_GUARDED && o.group_flag[task] == 0) return;
   const int b = task / Hkv, g = task % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
+  const int64_t row = (int64_t)b * Hq + g * G + (n < G ? n : 0);
+
+  extern __shared__ uint32_t stage[];  // MFMA_CAND: cnt[16], base[16], bits[G][o.stage], pos[G][o.stage]
+  uint32_t* lcnt = stage;
+  uint32_t* lbase = stage + 16;
+  uint32_t* lbits = stage + 32;
+  const int ST_H = o.stage;
+  int32_t* lpos = reinterpret_cast<int32_t*>(lbits + G * ST_H);
+  uint32_t Tn = 0;
+  if (MODE == MFMA_CAND) {
+    if (threadIdx.x < 16) lcnt[threadIdx.x] = 0;
+    if (n < G) Tn = o.T[row];
+    __syncthreads();
+  }
 
   bf16x8_t bq[KS];
 #pragma unroll
@@ -43,29 +68,37 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
     bq[s] = __builtin_bit_cast(bf16x8_t, v);
   }
   const uint16_t* Kb = K + (int64_t)b * sb + (int64_t)g * sh;
-  const int p0 = blockIdx.x * chunk;
-  const int p1 = min(p0 + chunk, L);
-  float* Srow = S + ((int64_t)(b * Hq + g * G + (n < G ? n : 0))) * L;
+  int p0, p1, base, step;
+  if (MODE == MFMA_SAMPLE) {
+    const int c = blockIdx.x * 4 + wave;
+    p0 = c * chunk;
+    p1 = min(p0 + 64, L);
+    base = p0;
+    step = 64;
+  } else {
+    p0 = blockIdx.x * chunk;
+    p1 = min(p0 + chunk, L);
+    base = p0 + wave * 64;
+    step = 256;
+  }
   const bool vec_store = (L & 3) == 0;
 
-  auto load = [&](uint4 (&a)[4][KS], int base) {
+  auto load = [&](uint4 (&a)[4][KS], int at) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int pos = min(base + 16 * t + n, L - 1);
-      const uint16_t* row = Kb + (int64_t)pos * sl + 8 * kg;
+      const int pos = min(at + 16 * t + n, L - 1);
+      const uint16_t* rp = Kb + (int64_t)pos * sl + 8 * kg;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a[t][s] = ld16_stream(row + 32 * s);
+      for (int s = 0; s < KS; ++s) a[t][s] = ld16_stream(rp + 32 * s);
     }
   };
 
-  int base = p0 + wave * 64;
-  if (base >= p1) return;
   uint4 cur[4][KS];
-  load(cur, base);
-  for (; base < p1; base += 256) {
+  if (base < p1) load(cur, base);
+  for (; base < p1; base += step) {
     uint4 nxt[4][KS];
-    const bool more = base + 256 < p1;
-    if (more) load(nxt, base + 256);
+    const bool more = base + step < p1;
+    if (more) load(nxt, base + step);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -74,14 +107,41 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[t][s]), bq[s], acc, 0, 0,
                                                       0);
       const int pos = base + 16 * t + 4 * kg;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = acc[i] * scale;
       if (n < G) {
-        if (vec_store && pos + 3 < p1) {
-          *reinterpret_cast<float4*>(Srow + pos) =
-              make_float4(acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale);
-        } else {
+        if (MODE == MFMA_FULL || MODE == MFMA_GUARDED) {
+          float* Srow = o.S + row * L;
+          if (vec_store && pos + 3 < p1) {
+            *reinterpret_cast<float4*>(Srow + pos) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (pos + i < p1) Srow[pos + i] = v[i];
+          }
+        } else if (MODE == MFMA_SAMPLE) {
+          float* Srow = o.S + row * o.nsamp + (p0 / chunk) * 64 - p0;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (pos + i < p1) Srow[pos + i] = acc[i] * scale;
+            if (pos + i < p1) Srow[pos + i] = v[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (pos + i < p1 && score_key(v[i]) >= Tn) {
+              const uint32_t slot = atomicAdd(&lcnt[n], 1u);
+              if (slot < ST_H) {
+                lbits[n * ST_H + slot] = __float_as_uint(v[i]);
+                lpos[n * ST_H + slot] = pos + i;
+              } else {  // stage full: append directly
+                const uint32_t gs = atomicAdd(&o.cnt[row], 1u);
+                if (gs < (uint32_t)o.capg) {
+                  o.cbits[row * o.capg + gs] = __float_as_uint(v[i]);
+                  o.cpos[row * o.capg + gs] = pos + i;
+                }
+              }
+            }
+          }
         }
       }
     }
@@ -90,6 +150,26 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int s = 0; s < KS; ++s) cur[t][s] = nxt[t][s];
+    }
+  }
+  if (MODE == MFMA_CAND) {
+    __syncthreads();
+    if (threadIdx.x < G) {
+      const int64_t r = (int64_t)b * Hq + g * G + threadIdx.x;
+      const uint32_t c = min(lcnt[threadIdx.x], (uint32_t)ST_H);
+      lcnt[threadIdx.x] = c;
+      lbase[threadIdx.x] = c ? atomicAdd(&o.cnt[r], c) : 0u;
+    }
+    __syncthreads();
+    for (int h = 0; h < G; ++h) {
+      const int64_t r = (int64_t)b * Hq + g * G + h;
+      const uint32_t c = lcnt[h], bse = lbase[h];
+      for (uint32_t j = threadIdx.x; j < c; j += 256) {
+        if (bse + j < (uint32_t)o.capg) {
+          o.cbits[r * o.capg + bse + j] = lbits[h * ST_H + j];
+          o.cpos[r * o.capg + bse + j] = lpos[h * ST_H + j];
+        }
+      }
     }
   }
 }
@@ -315,12 +395,46 @@ static int pick_chunk(int64_t rows_per_task, int64_t tasks, int granule, int lo,
   return (int)(c < granule ? granule : c);
 }
 
-template <int D>
-static void launch_mfma_d(const ScoreArgs& a, hipStream_t st) {
-  const int chunk = pick_chunk(a.nrows, (int64_t)a.B * a.Hkv, 256, 256, 4096);
-  dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv);
-  hipLaunchKernelGGL(score_exact_mfma_kernel<D>, grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.keys, a.scores, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk);
+template <int D, int MODE>
+static void launch_mfma_mode(const ScoreArgs& a, int chunk, unsigned gx, const MfmaOut& o, hipStream_t st) {
+  const size_t lds = MODE == MFMA_CAND ? sizeof(uint32_t) * (32 + 2 * (size_t)a.G * o.stage) : 0;
+  dim3 grid(gx, a.B * a.Hkv);
+  hipLaunchKernelGGL((score_exact_mfma_kernel<D, MODE>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, o);
+}
+
+template <int MODE>
+static void launch_mfma(const ScoreArgs& a, int chunk, unsigned gx, const MfmaOut& o, hipStream_t st) {
+  switch (a.d) {
+    case 64: launch_mfma_mode<64, MODE>(a, chunk, gx, o, st); break;
+    case 128: launch_mfma_mode<128, MODE>(a, chunk, gx, o, st); break;
+    default: launch_mfma_mode<256, MODE>(a, chunk, gx, o, st); break;
+  }
+}
+
+int mfma_scan_chunk(const ScoreArgs& a) { return pick_chunk(a.nrows, (int64_t)a.B * a.Hkv, 256, 256, 4096); }
+
+void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, float* samp, hipStream_t st) {
+  MfmaOut o{};
+  o.S = samp;
+  o.nsamp = nsamp;
+  const int nch = (a.nrows + sample_chunk - 1) / sample_chunk;
+  launch_mfma<MFMA_SAMPLE>(a, sample_chunk, (unsigned)((nch + 3) / 4), o, st);
+}
+
+void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o_in, hipStream_t st) {
+  MfmaOut o = o_in;
+  o.stage = a.G <= 8 ? 512 : 256;  // per head and workgroup; at most 32 KiB of LDS
+  const int chunk = mfma_scan_chunk(a);
+  launch_mfma<MFMA_CAND>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
+}
+
+void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st) {
+  MfmaOut o{};
+  o.S = a.scores;
+  o.group_flag = group_flag;
+  const int chunk = 8192;
+  launch_mfma<MFMA_GUARDED>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
 }
 
 template <bool BF16, int D, int NH>
@@ -357,11 +471,10 @@ bool score_uses_mfma(int dtype_bf16, int G) { return dtype_bf16 && G >= 2 && G <
 void launch_score_dense(const ScoreArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return;
   if (score_uses_mfma(a.bf16, a.G)) {
-    switch (a.d) {
-      case 64: launch_mfma_d<64>(a, st); break;
-      case 128: launch_mfma_d<128>(a, st); break;
-      default: launch_mfma_d<256>(a, st); break;
-    }
+    MfmaOut o{};
+    o.S = a.scores;
+    const int chunk = mfma_scan_chunk(a);
+    launch_mfma<MFMA_FULL>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
   } else if (a.bf16) {
     launch_vec<true>(a, st);
   } else {

@@ -161,31 +161,40 @@ __device__ uint32_t collect_pass(const float* s, int r0, int r1, bool aligned, u
   return cnt;
 }
 
-// Continue the radix search inside the candidates (each wave owns
-// [off, off+cnt) of cb) through levels lv+1..2. Returns T in sm.res[0] and
-// the number of keys == T to keep in sm.res[1].
-__device__ void refine_candidates(const uint32_t* cb, uint32_t off, uint32_t cnt, int lv, uint32_t prefix,
-                                  uint32_t need, SelSmem& sm) {
+// Radix search for the need-th largest key among the elements wave w owns
+// ([0, cnt) through key_of(e)), through levels l0..2, starting from the
+// digits `prefix` fixed above level l0. Returns T in sm.res[0] and the
+// number of keys == T to keep in sm.res[1].
+template <typename KeyOf>
+__device__ void radix_kth(KeyOf key_of, uint32_t cnt, int l0, uint32_t prefix, uint32_t need, SelSmem& sm) {
   const int lane = lane_id();
-  for (int l = lv + 1; l <= 2; ++l) {
-    for (int i = threadIdx.x; i < NB1; i += ST) sm.hist[i] = 0;
+  for (int l = l0; l <= 2; ++l) {
+    const int nb = lv_bins(l);
+    for (int i = threadIdx.x; i < nb; i += ST) sm.hist[i] = 0;
     __syncthreads();
     for (uint32_t e = lane; e < cnt; e += 64) {
-      const uint32_t key = score_key(__uint_as_float(cb[off + e]));
+      const uint32_t key = key_of(e);
       if (lv_in_range(key, l, prefix)) atomicAdd(&sm.hist[lv_digit(key, l)], 1u);
     }
     __syncthreads();
-    find_bin(sm.hist, NB1, need, sm);
+    find_bin(sm.hist, nb, need, sm);
     const uint32_t bin = sm.res[0], above = sm.res[1];
     __syncthreads();
     need -= above;
-    prefix = (prefix << 10) | bin;
+    prefix = (prefix << lv_bits(l)) | bin;
   }
   if (threadIdx.x == 0) {
     sm.res[0] = prefix;
     sm.res[1] = need;
   }
   __syncthreads();
+}
+
+// Continue the radix search inside candidates (each wave owns [off, off+cnt)
+// of cb) through levels lv+1..2.
+__device__ void refine_candidates(const uint32_t* cb, uint32_t off, uint32_t cnt, int lv, uint32_t prefix,
+                                  uint32_t need, SelSmem& sm) {
+  radix_kth([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, cnt, lv + 1, prefix, need, sm);
 }
 
 // Emit, in position order, every element with key > T and the first need_eq
@@ -253,7 +262,8 @@ __device__ void emit_segments(Get get, uint32_t cnt, uint32_t T, uint32_t need_e
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void select_rows_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                          int capw) {
+                                                          int capw, const uint32_t* __restrict__ row_flag) {
+  if (row_flag && row_flag[blockIdx.x] == 0) return;  // only the rows flagged for a full select
   extern __shared__ uint4 smem_raw[];
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem_raw);
   uint32_t* cb = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(smem_raw) + ((sizeof(SelSmem) + 15) & ~15));
@@ -461,6 +471,139 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Candidate prefilter for the fused exact step. A sampled scoring pass gives
+// each row a key threshold T (the r-th largest sample key); the scan keeps
+// only scores with key >= T. If at least k' of them were kept, every one of
+// the k' largest keys is among them (the k'-th largest key is then >= T), so
+// the exact answer comes from the candidates alone; otherwise the row is
+// flagged and rescored in full.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* __restrict__ samp, int nsamp, int r,
+                                                                  uint32_t* __restrict__ T, uint32_t* __restrict__ cnt,
+                                                                  uint32_t* __restrict__ row_flag,
+                                                                  uint32_t* __restrict__ group_flag, int G) {
+  __shared__ SelSmem sm;
+  const int64_t row = blockIdx.x;
+  const int w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) {
+    cnt[row] = 0;
+    row_flag[row] = 0;
+    if (row % G == 0) group_flag[row / G] = 0;
+  }
+  const float* s = samp + row * nsamp;
+  const uint32_t q4 = (uint32_t)(nsamp + SW - 1) / SW;
+  const uint32_t off = min((uint32_t)nsamp, (uint32_t)w * q4);
+  const uint32_t c = min((uint32_t)nsamp, off + q4) - off;
+  if (r > nsamp) {
+    if (threadIdx.x == 0) T[row] = 0u;  // too few samples: keep everything
+    return;
+  }
+  radix_kth([&](uint32_t e) { return score_key(s[off + e]); }, c, 0, 0u, (uint32_t)r, sm);
+  if (threadIdx.x == 0) T[row] = sm.res[0];
+}
+
+// Exact top-k of a row from its (unordered) candidates. Kept positions are
+// marked in an LDS bitmap over the row; popcount prefix sums give each one
+// its output slot in ascending position order. Dynamic LDS: 3 * ceil(n/32)
+// words (kept bitmap, tie bitmap, prefix counts).
+__global__ __launch_bounds__(256) void prefilter_finish_kernel(const uint32_t* __restrict__ cbits,
+                                                               const int32_t* __restrict__ cpos,
+                                                               const uint32_t* __restrict__ cnt, int capg, int n,
+                                                               int k, int G, int32_t* __restrict__ idx,
+                                                               float* __restrict__ sel,
+                                                               uint32_t* __restrict__ row_flag,
+                                                               uint32_t* __restrict__ group_flag) {
+  __shared__ SelSmem sm;
+  extern __shared__ uint32_t dyn[];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int kk = min(k, n);
+  int32_t* oidx = idx + row * k;
+  float* osel = sel ? sel + row * k : nullptr;
+  for (int j = kk + t; j < k; j += ST) {
+    oidx[j] = -1;
+    if (osel) osel[j] = -INFINITY;
+  }
+  const uint32_t nc = cnt[row];
+  if (nc < (uint32_t)kk || nc > (uint32_t)capg) {  // threshold too high or too many ties: full rescore
+    if (t == 0) {
+      row_flag[row] = 1u;
+      atomicOr(&group_flag[row / G], 1u);
+    }
+    return;
+  }
+  const uint32_t* cb = cbits + row * capg;
+  const int32_t* cp = cpos + row * capg;
+  const uint32_t q4 = (nc + SW - 1) / SW;
+  const uint32_t off = min(nc, (uint32_t)w * q4);
+  const uint32_t c = min(nc, off + q4) - off;
+  radix_kth([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, c, 0, 0u, (uint32_t)kk, sm);
+  const uint32_t T = sm.res[0], need_eq = sm.res[1];
+  const int words = (n + 31) >> 5;
+  uint32_t* bm = dyn;
+  uint32_t* tbm = dyn + words;
+  uint32_t* pre = dyn + 2 * words;
+  uint32_t neq = 0;
+  for (uint32_t e = lane; e < c; e += 64) neq += score_key(__uint_as_float(cb[off + e])) == T;
+  neq = wave_sum(neq);
+  if (lane == 0) sm.eq[w] = neq;
+  for (int i = t; i < words; i += ST) {
+    bm[i] = 0u;
+    tbm[i] = 0u;
+  }
+  __syncthreads();
+  const uint32_t neq_all = sm.eq[0] + sm.eq[1] + sm.eq[2] + sm.eq[3];
+  const bool excess = neq_all > need_eq;
+  for (uint32_t e = lane; e < c; e += 64) {
+    const uint32_t key = score_key(__uint_as_float(cb[off + e]));
+    const int32_t p = cp[off + e];
+    if (key > T || (key == T && !excess)) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    else if (key == T) atomicOr(&tbm[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  const int per = (words + ST - 1) / ST;
+  auto prefix_counts = [&](const uint32_t* bits) {
+    uint32_t loc = 0;
+    for (int i = 0; i < per; ++i) {
+      const int wd = t * per + i;
+      if (wd < words) loc += __popc(bits[wd]);
+    }
+    uint32_t total;
+    uint32_t run = block_incl_scan(loc, sm, &total) - loc;
+    for (int i = 0; i < per; ++i) {
+      const int wd = t * per + i;
+      if (wd < words) {
+        pre[wd] = run;
+        run += __popc(bits[wd]);
+      }
+    }
+    __syncthreads();
+  };
+  if (excess) {  // keep the need_eq lowest positions among the ties
+    prefix_counts(tbm);
+    for (uint32_t e = lane; e < c; e += 64) {
+      const uint32_t key = score_key(__uint_as_float(cb[off + e]));
+      if (key != T) continue;
+      const int32_t p = cp[off + e];
+      const uint32_t rank = pre[p >> 5] + __popc(tbm[p >> 5] & ((1u << (p & 31)) - 1u));
+      if (rank < need_eq) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+  }
+  prefix_counts(bm);
+  for (uint32_t e = lane; e < c; e += 64) {
+    const int32_t p = cp[off + e];
+    const uint32_t word = bm[p >> 5];
+    if (!((word >> (p & 31)) & 1u)) continue;
+    const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
+    if (slot < (uint32_t)kk) {
+      oidx[slot] = p;
+      if (osel) osel[slot] = __uint_as_float(cb[off + e]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static bool use_split(int64_t n_rows, int n) { return n_rows < 128 && n > 4 * CHUNK; }
@@ -501,23 +644,39 @@ static int max_lds_bytes() {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
       v = 64 * 1024;
     (void)hipFuncSetAttribute((const void*)select_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+    (void)hipFuncSetAttribute((const void*)prefilter_finish_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              v - (int)sizeof(SelSmem));
     cached[dev] = v;
   }
   return cached[dev];
 }
 
+static int rows_capw(int n, int k, size_t* lds) {
+  const int kk = k < n ? k : n;
+  int capw = 64;
+  while (capw < 2048 && (int64_t)SW * capw < (int64_t)kk + kk / 2 + 64) capw <<= 1;
+  const size_t head = (sizeof(SelSmem) + 15) & ~(size_t)15;
+  const int lds_max = max_lds_bytes();
+  while (capw > 64 && head + (size_t)SW * capw * 8 > (size_t)lds_max) capw >>= 1;
+  *lds = head + (size_t)SW * capw * 8;
+  return capw;
+}
+
+void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st) {
+  if (a.n_rows <= 0) return;
+  size_t lds;
+  const int capw = rows_capw(a.n, a.k, &lds);
+  hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k,
+                     a.idx, a.sel, capw, row_flag);
+}
+
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   if (a.n_rows <= 0) return;
   if (!use_split(a.n_rows, a.n)) {
-    const int kk = a.k < a.n ? a.k : a.n;
-    int capw = 64;
-    while (capw < 2048 && (int64_t)SW * capw < (int64_t)kk + kk / 2 + 64) capw <<= 1;
-    const size_t head = (sizeof(SelSmem) + 15) & ~(size_t)15;
-    const int lds_max = max_lds_bytes();
-    while (capw > 64 && head + (size_t)SW * capw * 8 > (size_t)lds_max) capw >>= 1;
-    const size_t lds = head + (size_t)SW * capw * 8;
+    size_t lds;
+    const int capw = rows_capw(a.n, a.k, &lds);
     hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride,
-                       a.k, a.idx, a.sel, capw);
+                       a.k, a.idx, a.sel, capw, (const uint32_t*)nullptr);
     return;
   }
   const SplitLayout L = split_layout(a.n_rows, a.n);
@@ -538,6 +697,22 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
                      a.stride, a.k, ghist, cbits, cpos, ccount, nch);
   hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.n_rows), dim3(ST), sizeof(uint32_t) * nch * SW, st,
                      a.scores, a.n, a.stride, a.k, ghist, cbits, cpos, ccount, catb, catp, nch, a.idx, a.sel);
+}
+
+void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, uint32_t* T, uint32_t* cnt,
+                                uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st) {
+  hipLaunchKernelGGL(prefilter_threshold_kernel, dim3((unsigned)n_rows), dim3(ST), 0, st, samp, nsamp, r, T, cnt,
+                     row_flag, group_flag, G);
+}
+
+static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 3 * (size_t)((n + 31) / 32); }
+
+void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, int capg,
+                             int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel, uint32_t* row_flag,
+                             uint32_t* group_flag, hipStream_t st) {
+  (void)max_lds_bytes();
+  hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(ST), prefilter_finish_lds(n), st, cbits,
+                     cpos, cnt, capg, n, k, G, idx, sel, row_flag, group_flag);
 }
 
 }  // namespace tka
