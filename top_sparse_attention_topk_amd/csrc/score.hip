@@ -33,13 +33,37 @@ namespace tka {
 //   MFMA_GUARDED - MFMA_FULL for the groups whose flag is set, else nothing.
 // ---------------------------------------------------------------------------
 enum { MFMA_FULL = 0, MFMA_SAMPLE = 1, MFMA_CAND = 2, MFMA_GUARDED = 3 };
+// How K reaches the MFMA operand registers:
+//   KLOAD_DIRECT    - each lane loads its own operand slice (16 rows x 64 B per
+//                     load instruction), non-temporal.
+//   KLOAD_DIRECT_RT - the same with ordinary (cached) loads.
+//   KLOAD_STAGED    - fully coalesced non-temporal loads (every instruction
+//                     reads whole rows, 1 KiB contiguous per wave) into a
+//                     wave-private LDS area whose rows are padded by 16 B, then
+//                     operand reads from LDS without bank conflicts.
+enum { KLOAD_DIRECT = 0, KLOAD_DIRECT_RT = 1, KLOAD_STAGED = 2 };
+#ifndef TKA_SCAN_KLOAD
+#define TKA_SCAN_KLOAD KLOAD_STAGED
+#endif
 
-template <int D, int MODE>
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int MODE, int KL>
 __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ K, int Hq, int Hkv, int G,
                                                                int L, int64_t sb, int64_t sh, int64_t sl, float scale,
                                                                int chunk, MfmaOut o) {
   constexpr int KS = D / 32;
+  constexpr int TILES = KL == KLOAD_STAGED ? 2 : 4;  // 16-position tiles per wave round
+  constexpr int P = 16 * TILES;
+  constexpr int RB = D * 2;              // bytes of a key row
+  constexpr int PADB = RB + 16;          // LDS row stride
+  constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;         // rows per coalesced load instruction
+  constexpr int NI = KL == KLOAD_STAGED ? P / RPI : TILES * KS;  // load instructions per round
   const int task = blockIdx.y;
   if (MODE == MFMA_GUARDED && o.group_flag[task] == 0) return;
   const int b = task / Hkv, g = task % Hkv;
@@ -47,10 +71,14 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
   const int n = lane & 15, kg = lane >> 4;
   const int64_t row = (int64_t)b * Hq + g * G + (n < G ? n : 0);
 
-  extern __shared__ uint32_t stage[];  // MFMA_CAND: cnt[16], base[16], bits[G][o.stage], pos[G][o.stage]
-  uint32_t* lcnt = stage;
-  uint32_t* lbase = stage + 16;
-  uint32_t* lbits = stage + 32;
+  // dynamic LDS: [staging: 4 waves x P rows x PADB][candidates: cnt[16], base[16], bits[G][stage], pos[G][stage]]
+  extern __shared__ uint4 smem_raw[];
+  uint8_t* stage_rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
+  uint32_t* cstage = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) +
+                                                 (KL == KLOAD_STAGED ? (size_t)4 * P * PADB : 0));
+  uint32_t* lcnt = cstage;
+  uint32_t* lbase = cstage + 16;
+  uint32_t* lbits = cstage + 32;
   const int ST_H = o.stage;
   int32_t* lpos = reinterpret_cast<int32_t*>(lbits + G * ST_H);
   uint32_t Tn = 0;
@@ -74,38 +102,56 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
     p0 = c * chunk;
     p1 = min(p0 + 64, L);
     base = p0;
-    step = 64;
+    step = P;
   } else {
     p0 = blockIdx.x * chunk;
     p1 = min(p0 + chunk, L);
-    base = p0 + wave * 64;
-    step = 256;
+    base = p0 + wave * P;
+    step = 4 * P;
   }
   const bool vec_store = (L & 3) == 0;
 
-  auto load = [&](uint4 (&a)[4][KS], int at) {
+  auto load = [&](uint4 (&a)[NI], int at) {
+    if (KL == KLOAD_STAGED) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int pos = min(at + 16 * t + n, L - 1);
-      const uint16_t* rp = Kb + (int64_t)pos * sl + 8 * kg;
+      for (int j = 0; j < NI; ++j) {
+        const int pos = min(at + j * RPI + lane / CPR, L - 1);
+        a[j] = ld16_stream(Kb + (int64_t)pos * sl + (lane % CPR) * 8);
+      }
+    } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a[t][s] = ld16_stream(rp + 32 * s);
+      for (int t = 0; t < TILES; ++t) {
+        const int pos = min(at + 16 * t + n, L - 1);
+        const uint16_t* rp = Kb + (int64_t)pos * sl + 8 * kg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          a[t * KS + s] = KL == KLOAD_DIRECT ? ld16_stream(rp + 32 * s) : ld16(rp + 32 * s);
+      }
     }
   };
 
-  uint4 cur[4][KS];
+  uint4 cur[NI];
   if (base < p1) load(cur, base);
   for (; base < p1; base += step) {
-    uint4 nxt[4][KS];
+    uint4 nxt[NI];
     const bool more = base + step < p1;
     if (more) load(nxt, base + step);
+    if (KL == KLOAD_STAGED) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+      for (int j = 0; j < NI; ++j)
+        *reinterpret_cast<uint4*>(stage_rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = cur[j];
+      lds_wave_sync();
+    }
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[t][s]), bq[s], acc, 0, 0,
-                                                      0);
+      for (int s = 0; s < KS; ++s) {
+        uint4 a;
+        if (KL == KLOAD_STAGED) a = *reinterpret_cast<const uint4*>(stage_rows + (16 * t + n) * PADB + (kg + 4 * s) * 16);
+        else a = cur[t * KS + s];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bq[s], acc, 0, 0, 0);
+      }
       const int pos = base + 16 * t + 4 * kg;
       float v[4];
 #pragma unroll
@@ -130,7 +176,7 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
           for (int i = 0; i < 4; ++i) {
             if (pos + i < p1 && score_key(v[i]) >= Tn) {
               const uint32_t slot = atomicAdd(&lcnt[n], 1u);
-              if (slot < ST_H) {
+              if (slot < (uint32_t)ST_H) {
                 lbits[n * ST_H + slot] = __float_as_uint(v[i]);
                 lpos[n * ST_H + slot] = pos + i;
               } else {  // stage full: append directly
@@ -145,11 +191,10 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
         }
       }
     }
+    if (KL == KLOAD_STAGED) __builtin_amdgcn_wave_barrier();  // reads of this round precede the next writes
     if (more) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) cur[t][s] = nxt[t][s];
+      for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
     }
   }
   if (MODE == MFMA_CAND) {
@@ -397,9 +442,11 @@ static int pick_chunk(int64_t rows_per_task, int64_t tasks, int granule, int lo,
 
 template <int D, int MODE>
 static void launch_mfma_mode(const ScoreArgs& a, int chunk, unsigned gx, const MfmaOut& o, hipStream_t st) {
-  const size_t lds = MODE == MFMA_CAND ? sizeof(uint32_t) * (32 + 2 * (size_t)a.G * o.stage) : 0;
+  constexpr int KL = TKA_SCAN_KLOAD;
+  const size_t stage_rows = KL == KLOAD_STAGED ? (size_t)4 * 32 * (D * 2 + 16) : 0;
+  const size_t lds = stage_rows + (MODE == MFMA_CAND ? sizeof(uint32_t) * (32 + 2 * (size_t)a.G * o.stage) : 0);
   dim3 grid(gx, a.B * a.Hkv);
-  hipLaunchKernelGGL((score_exact_mfma_kernel<D, MODE>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
+  hipLaunchKernelGGL((score_exact_mfma_kernel<D, MODE, KL>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, o);
 }
 
@@ -424,7 +471,7 @@ void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, f
 
 void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o_in, hipStream_t st) {
   MfmaOut o = o_in;
-  o.stage = a.G <= 8 ? 512 : 256;  // per head and workgroup; at most 32 KiB of LDS
+  o.stage = a.G <= 8 ? 256 : 128;  // per head and workgroup; at most 16 KiB of LDS
   const int chunk = mfma_scan_chunk(a);
   launch_mfma<MFMA_CAND>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
 }

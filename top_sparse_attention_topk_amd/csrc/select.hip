@@ -46,21 +46,22 @@ __device__ __forceinline__ bool lv_in_range(uint32_t key, int lv, uint32_t prefi
 
 struct SelSmem {
   uint32_t hist[NB0];
-  uint32_t scan[SW];
+  uint32_t scan[16];
   uint32_t res[2];
   uint32_t cnt[SW];
   uint32_t gt[SW], eq[SW];
   uint32_t obase[SW], eqbase[SW];
 };
 
-__device__ uint32_t block_incl_scan(uint32_t v, SelSmem& sm, uint32_t* total) {
+template <int NW>
+__device__ uint32_t block_incl_scan_t(uint32_t v, SelSmem& sm, uint32_t* total) {
   const int w = threadIdx.x >> 6, l = lane_id();
   uint32_t x = wave_incl_scan(v);
   if (l == 63) sm.scan[w] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < SW; ++i) {
+  for (int i = 0; i < NW; ++i) {
     off += (i < w) ? sm.scan[i] : 0u;
     tot += sm.scan[i];
   }
@@ -69,15 +70,20 @@ __device__ uint32_t block_incl_scan(uint32_t v, SelSmem& sm, uint32_t* total) {
   return x + off;
 }
 
+__device__ uint32_t block_incl_scan(uint32_t v, SelSmem& sm, uint32_t* total) {
+  return block_incl_scan_t<SW>(v, sm, total);
+}
+
 // Bin b with above(b) < need <= above(b) + hist[b], above(b) = sum of the
 // bins over b. Result in sm.res (bin, above). need must not exceed the total.
-__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, SelSmem& sm) {
+template <int NW>
+__device__ void find_bin_t(const uint32_t* hist, int nb, uint32_t need, SelSmem& sm) {
   const int t = threadIdx.x;
-  const int per = nb / ST;
+  const int per = nb / (64 * NW);
   uint32_t s = 0;
   for (int i = 0; i < per; ++i) s += hist[t * per + i];
   uint32_t tot;
-  const uint32_t incl = block_incl_scan(s, sm, &tot);
+  const uint32_t incl = block_incl_scan_t<NW>(s, sm, &tot);
   const uint32_t above = tot - incl;
   if (above < need && need <= above + s) {
     uint32_t acc = above;
@@ -92,6 +98,10 @@ __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, SelSmem& s
     }
   }
   __syncthreads();
+}
+
+__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, SelSmem& sm) {
+  find_bin_t<SW>(hist, nb, need, sm);
 }
 
 __device__ __forceinline__ void load4(const float* s, int p, int end, bool aligned, float (&v)[4]) {
@@ -165,19 +175,27 @@ __device__ uint32_t collect_pass(const float* s, int r0, int r1, bool aligned, u
 // ([0, cnt) through key_of(e)), through levels l0..2, starting from the
 // digits `prefix` fixed above level l0. Returns T in sm.res[0] and the
 // number of keys == T to keep in sm.res[1].
-template <typename KeyOf>
-__device__ void radix_kth(KeyOf key_of, uint32_t cnt, int l0, uint32_t prefix, uint32_t need, SelSmem& sm) {
+template <int NW, typename KeyOf>
+__device__ void radix_kth_t(KeyOf key_of, uint32_t cnt, int l0, uint32_t prefix, uint32_t need, SelSmem& sm) {
+  constexpr int U = 8;  // independent loads in flight per lane
   const int lane = lane_id();
   for (int l = l0; l <= 2; ++l) {
     const int nb = lv_bins(l);
-    for (int i = threadIdx.x; i < nb; i += ST) sm.hist[i] = 0;
+    for (int i = threadIdx.x; i < nb; i += 64 * NW) sm.hist[i] = 0;
     __syncthreads();
-    for (uint32_t e = lane; e < cnt; e += 64) {
-      const uint32_t key = key_of(e);
-      if (lv_in_range(key, l, prefix)) atomicAdd(&sm.hist[lv_digit(key, l)], 1u);
+    for (uint32_t e0 = 0; e0 < cnt; e0 += 64 * U) {
+      uint32_t key[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t e = e0 + u * 64 + lane;
+        key[u] = e < cnt ? key_of(e) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (e0 + u * 64 + lane < cnt && lv_in_range(key[u], l, prefix)) atomicAdd(&sm.hist[lv_digit(key[u], l)], 1u);
     }
     __syncthreads();
-    find_bin(sm.hist, nb, need, sm);
+    find_bin_t<NW>(sm.hist, nb, need, sm);
     const uint32_t bin = sm.res[0], above = sm.res[1];
     __syncthreads();
     need -= above;
@@ -188,6 +206,11 @@ __device__ void radix_kth(KeyOf key_of, uint32_t cnt, int l0, uint32_t prefix, u
     sm.res[1] = need;
   }
   __syncthreads();
+}
+
+template <typename KeyOf>
+__device__ void radix_kth(KeyOf key_of, uint32_t cnt, int l0, uint32_t prefix, uint32_t need, SelSmem& sm) {
+  radix_kth_t<SW>(key_of, cnt, l0, prefix, need, sm);
 }
 
 // Continue the radix search inside candidates (each wave owns [off, off+cnt)
@@ -478,10 +501,14 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
 // the exact answer comes from the candidates alone; otherwise the row is
 // flagged and rescored in full.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* __restrict__ samp, int nsamp, int r,
-                                                                  uint32_t* __restrict__ T, uint32_t* __restrict__ cnt,
-                                                                  uint32_t* __restrict__ row_flag,
-                                                                  uint32_t* __restrict__ group_flag, int G) {
+constexpr int PF_NW = 16;  // waves of the prefilter kernels (1024 threads)
+constexpr int PF_T = 64 * PF_NW;
+
+__global__ __launch_bounds__(1024) void prefilter_threshold_kernel(const float* __restrict__ samp, int nsamp, int r,
+                                                                   uint32_t* __restrict__ T,
+                                                                   uint32_t* __restrict__ cnt,
+                                                                   uint32_t* __restrict__ row_flag,
+                                                                   uint32_t* __restrict__ group_flag, int G) {
   __shared__ SelSmem sm;
   const int64_t row = blockIdx.x;
   const int w = threadIdx.x >> 6;
@@ -491,28 +518,30 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
     if (row % G == 0) group_flag[row / G] = 0;
   }
   const float* s = samp + row * nsamp;
-  const uint32_t q4 = (uint32_t)(nsamp + SW - 1) / SW;
-  const uint32_t off = min((uint32_t)nsamp, (uint32_t)w * q4);
-  const uint32_t c = min((uint32_t)nsamp, off + q4) - off;
   if (r > nsamp) {
     if (threadIdx.x == 0) T[row] = 0u;  // too few samples: keep everything
     return;
   }
-  radix_kth([&](uint32_t e) { return score_key(s[off + e]); }, c, 0, 0u, (uint32_t)r, sm);
+  const uint32_t q = (uint32_t)(nsamp + PF_NW - 1) / PF_NW;
+  const uint32_t off = min((uint32_t)nsamp, (uint32_t)w * q);
+  const uint32_t c = min((uint32_t)nsamp, off + q) - off;
+  radix_kth_t<PF_NW>([&](uint32_t e) { return score_key(s[off + e]); }, c, 0, 0u, (uint32_t)r, sm);
   if (threadIdx.x == 0) T[row] = sm.res[0];
 }
 
 // Exact top-k of a row from its (unordered) candidates. Kept positions are
 // marked in an LDS bitmap over the row; popcount prefix sums give each one
 // its output slot in ascending position order. Dynamic LDS: 3 * ceil(n/32)
-// words (kept bitmap, tie bitmap, prefix counts).
-__global__ __launch_bounds__(256) void prefilter_finish_kernel(const uint32_t* __restrict__ cbits,
-                                                               const int32_t* __restrict__ cpos,
-                                                               const uint32_t* __restrict__ cnt, int capg, int n,
-                                                               int k, int G, int32_t* __restrict__ idx,
-                                                               float* __restrict__ sel,
-                                                               uint32_t* __restrict__ row_flag,
-                                                               uint32_t* __restrict__ group_flag) {
+// words (kept bitmap, tie bitmap, prefix counts). Every pass over the
+// candidates keeps 8 loads per lane in flight.
+__global__ __launch_bounds__(1024) void prefilter_finish_kernel(const uint32_t* __restrict__ cbits,
+                                                                const int32_t* __restrict__ cpos,
+                                                                const uint32_t* __restrict__ cnt, int capg, int n,
+                                                                int k, int G, int32_t* __restrict__ idx,
+                                                                float* __restrict__ sel,
+                                                                uint32_t* __restrict__ row_flag,
+                                                                uint32_t* __restrict__ group_flag) {
+  constexpr int U = 8;
   __shared__ SelSmem sm;
   extern __shared__ uint32_t dyn[];
   const int64_t row = blockIdx.x;
@@ -520,7 +549,7 @@ __global__ __launch_bounds__(256) void prefilter_finish_kernel(const uint32_t* _
   const int kk = min(k, n);
   int32_t* oidx = idx + row * k;
   float* osel = sel ? sel + row * k : nullptr;
-  for (int j = kk + t; j < k; j += ST) {
+  for (int j = kk + t; j < k; j += PF_T) {
     oidx[j] = -1;
     if (osel) osel[j] = -INFINITY;
   }
@@ -534,34 +563,51 @@ __global__ __launch_bounds__(256) void prefilter_finish_kernel(const uint32_t* _
   }
   const uint32_t* cb = cbits + row * capg;
   const int32_t* cp = cpos + row * capg;
-  const uint32_t q4 = (nc + SW - 1) / SW;
-  const uint32_t off = min(nc, (uint32_t)w * q4);
-  const uint32_t c = min(nc, off + q4) - off;
-  radix_kth([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, c, 0, 0u, (uint32_t)kk, sm);
+  const uint32_t q = (nc + PF_NW - 1) / PF_NW;
+  const uint32_t off = min(nc, (uint32_t)w * q);
+  const uint32_t c = min(nc, off + q) - off;
+  radix_kth_t<PF_NW>([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, c, 0, 0u, (uint32_t)kk,
+                     sm);
   const uint32_t T = sm.res[0], need_eq = sm.res[1];
   const int words = (n + 31) >> 5;
   uint32_t* bm = dyn;
   uint32_t* tbm = dyn + words;
   uint32_t* pre = dyn + 2 * words;
-  uint32_t neq = 0;
-  for (uint32_t e = lane; e < c; e += 64) neq += score_key(__uint_as_float(cb[off + e])) == T;
-  neq = wave_sum(neq);
-  if (lane == 0) sm.eq[w] = neq;
-  for (int i = t; i < words; i += ST) {
+  for (int i = t; i < words; i += PF_T) {
     bm[i] = 0u;
     tbm[i] = 0u;
   }
   __syncthreads();
-  const uint32_t neq_all = sm.eq[0] + sm.eq[1] + sm.eq[2] + sm.eq[3];
-  const bool excess = neq_all > need_eq;
-  for (uint32_t e = lane; e < c; e += 64) {
-    const uint32_t key = score_key(__uint_as_float(cb[off + e]));
-    const int32_t p = cp[off + e];
-    if (key > T || (key == T && !excess)) atomicOr(&bm[p >> 5], 1u << (p & 31));
-    else if (key == T) atomicOr(&tbm[p >> 5], 1u << (p & 31));
+  // mark keys > T; keys == T go to the tie bitmap
+  uint32_t neq = 0;
+  for (uint32_t e0 = 0; e0 < c; e0 += 64 * U) {
+    uint32_t key[U];
+    int32_t pp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t e = e0 + u * 64 + lane;
+      key[u] = e < c ? score_key(__uint_as_float(cb[off + e])) : 0u;
+      pp[u] = e < c ? cp[off + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (e0 + u * 64 + lane >= c) continue;
+      const int32_t p = pp[u];
+      if (key[u] > T) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      else if (key[u] == T) {
+        atomicOr(&tbm[p >> 5], 1u << (p & 31));
+        ++neq;
+      }
+    }
   }
+  neq = wave_sum(neq);
+  if (lane == 0) sm.scan[w] = neq;
   __syncthreads();
-  const int per = (words + ST - 1) / ST;
+  uint32_t neq_all = 0;
+#pragma unroll
+  for (int i = 0; i < PF_NW; ++i) neq_all += sm.scan[i];
+  __syncthreads();
+  const int per = (words + PF_T - 1) / PF_T;
   auto prefix_counts = [&](const uint32_t* bits) {
     uint32_t loc = 0;
     for (int i = 0; i < per; ++i) {
@@ -569,7 +615,7 @@ __global__ __launch_bounds__(256) void prefilter_finish_kernel(const uint32_t* _
       if (wd < words) loc += __popc(bits[wd]);
     }
     uint32_t total;
-    uint32_t run = block_incl_scan(loc, sm, &total) - loc;
+    uint32_t run = block_incl_scan_t<PF_NW>(loc, sm, &total) - loc;
     for (int i = 0; i < per; ++i) {
       const int wd = t * per + i;
       if (wd < words) {
@@ -579,26 +625,46 @@ __global__ __launch_bounds__(256) void prefilter_finish_kernel(const uint32_t* _
     }
     __syncthreads();
   };
-  if (excess) {  // keep the need_eq lowest positions among the ties
-    prefix_counts(tbm);
-    for (uint32_t e = lane; e < c; e += 64) {
-      const uint32_t key = score_key(__uint_as_float(cb[off + e]));
-      if (key != T) continue;
-      const int32_t p = cp[off + e];
-      const uint32_t rank = pre[p >> 5] + __popc(tbm[p >> 5] & ((1u << (p & 31)) - 1u));
-      if (rank < need_eq) atomicOr(&bm[p >> 5], 1u << (p & 31));
+  // ties: keep the need_eq lowest positions (all of them when there is no excess)
+  if (neq_all > need_eq) prefix_counts(tbm);
+  for (int i = t; i < words; i += PF_T) {
+    uint32_t tw = tbm[i];
+    if (tw == 0u) continue;
+    if (neq_all > need_eq) {
+      uint32_t rank = pre[i], keep = 0u;
+      while (tw) {
+        const int bpos = __ffs(tw) - 1;
+        if (rank < need_eq) keep |= 1u << bpos;
+        ++rank;
+        tw &= tw - 1u;
+      }
+      tw = keep;
     }
-    __syncthreads();
+    bm[i] |= tw;
   }
+  __syncthreads();
   prefix_counts(bm);
-  for (uint32_t e = lane; e < c; e += 64) {
-    const int32_t p = cp[off + e];
-    const uint32_t word = bm[p >> 5];
-    if (!((word >> (p & 31)) & 1u)) continue;
-    const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
-    if (slot < (uint32_t)kk) {
-      oidx[slot] = p;
-      if (osel) osel[slot] = __uint_as_float(cb[off + e]);
+  // write every kept candidate to its slot
+  for (uint32_t e0 = 0; e0 < c; e0 += 64 * U) {
+    uint32_t bits[U];
+    int32_t pp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t e = e0 + u * 64 + lane;
+      bits[u] = e < c ? cb[off + e] : 0u;
+      pp[u] = e < c ? cp[off + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (e0 + u * 64 + lane >= c) continue;
+      const int32_t p = pp[u];
+      const uint32_t word = bm[p >> 5];
+      if (!((word >> (p & 31)) & 1u)) continue;
+      const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
+      if (slot < (uint32_t)kk) {
+        oidx[slot] = p;
+        if (osel) osel[slot] = __uint_as_float(bits[u]);
+      }
     }
   }
 }
@@ -701,7 +767,7 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
 
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, uint32_t* T, uint32_t* cnt,
                                 uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st) {
-  hipLaunchKernelGGL(prefilter_threshold_kernel, dim3((unsigned)n_rows), dim3(ST), 0, st, samp, nsamp, r, T, cnt,
+  hipLaunchKernelGGL(prefilter_threshold_kernel, dim3((unsigned)n_rows), dim3(PF_T), 0, st, samp, nsamp, r, T, cnt,
                      row_flag, group_flag, G);
 }
 
@@ -711,7 +777,7 @@ void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const u
                              int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel, uint32_t* row_flag,
                              uint32_t* group_flag, hipStream_t st) {
   (void)max_lds_bytes();
-  hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(ST), prefilter_finish_lds(n), st, cbits,
+  hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(PF_T), prefilter_finish_lds(n), st, cbits,
                      cpos, cnt, capg, n, k, G, idx, sel, row_flag, group_flag);
 }
 
