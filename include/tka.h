@@ -105,6 +105,24 @@ tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys
                            float* scores, void* stream);
 
 /*
+ * Thresholded scoring pass: scores every cached key as topk_attn_score does
+ * (EXACT, bytewise the same fp32 values) and keeps, per row r = b*Hq + h, the
+ * (score, position) pairs that rank at or above thresholds[r] in the
+ * topk_select order (so a score equal to the threshold is kept). Any
+ * threshold not above the row's k-th largest score keeps all of the row's k
+ * largest ("Sparse Attention in LLM Inference", "The Role of the Indexer":
+ * only a small candidate set goes on to the exact computation).
+ * Append semantics: pairs found for row r are written to
+ * cand_scores/cand_pos [r*capacity + counts[r] ...] in no particular order
+ * and counts[r] is increased by their number; pairs that would land at or
+ * beyond capacity are counted but not stored. Needs bf16 caches and
+ * 2 <= Hq/Hkv <= 16 (TKA_ERR_UNSUPPORTED otherwise).
+ */
+tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const void* k_cache,
+                                     const float* thresholds, uint32_t* counts, float* cand_scores, int32_t* cand_pos,
+                                     int32_t capacity, void* stream);
+
+/*
  * Exact top-k of each score row ("Sparse Attention Landscape", "Block Sparse
  * Attention", the TopK_j s_j operator). Order: i before j when s_i > s_j, or
  * s_i == s_j and i < j; -0 equals +0; NaN ranks below every number. Row r

@@ -29,6 +29,13 @@ CASES = {
     "C3-small": fx.shrink(W["C3"], 6000, B=2, k=512),
     "C4-small": fx.shrink(W["C4"], 64 * 150 + 17, B=2),
     "C5-small": fx.shrink(W["C5"], 50001),
+    # other head sizes and groupings of the same exact recipe
+    "d64-g16": fx.Workload("exact-bf16-d64-g16", fx.MODE_EXACT, 1, 16, 1, 64, 20000, 1000, fx.BF16, 21,
+                           fx.PLANT_ALIGN, 200, 0.5),
+    "d256-g2": fx.Workload("exact-bf16-d256-g2", fx.MODE_EXACT, 1, 4, 2, 256, 9000, 512, fx.BF16, 22,
+                           fx.PLANT_ALIGN, 90, 0.5),
+    "f32-d128-g4": fx.Workload("exact-f32-d128-g4", fx.MODE_EXACT, 2, 8, 2, 128, 3000, 200, fx.F32, 23,
+                               fx.PLANT_SCALE, 30, 3.0),
 }
 
 

@@ -71,3 +71,21 @@ def test_prefilter_repair_threshold_too_high(groups):
             K[b, g, hot] = fx.encode(mag[:, None] * d[None, :], fx.BF16)
     say(f"[prefilter] hot keys at sampled positions ({groups})")
     _run_both(w, q, K, V)
+
+
+def test_prefilter_repair_crowded_tie_bin():
+    """2500 identical top keys per KV head: the k-th score sits in a tie run
+    longer than the stash, so the row goes to the full select."""
+    w = BASE
+    q, K, V = fx.make_attn(w)
+    qf = fx.bf16_bits_to_f32(q).astype(np.float64)
+    G = w.Hq // w.Hkv
+    rng = np.random.default_rng(3)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            d = qf[b, g * G:(g + 1) * G].sum(0)
+            d = 8.0 * d / np.linalg.norm(d)
+            pos = np.sort(rng.choice(w.L, 2500, replace=False))
+            K[b, g, pos] = fx.encode(np.tile(d, (len(pos), 1)), fx.BF16)
+    say("[prefilter] crowded tie bin")
+    _run_both(w, q, K, V)

@@ -1,0 +1,54 @@
+"""topk_attn_score_threshold: the kept (score, position) pairs of each row are
+exactly the scores of topk_attn_score that rank at or above the row's
+threshold (IEEE order, -0 == +0), bit for bit, and a second call appends the
+same set after the first."""
+import numpy as np
+import pytest
+import torch
+
+import fixtures as fx
+from tests.gpu_common import dev, problem, say, tka
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("L,k", [(9000, 300), (40000, 2048)])
+def test_threshold_scan_keeps_exactly_the_ranked_set(L, k):
+    w = fx.shrink(fx.WORKLOADS["C3"], L, B=2, k=k)
+    m = tka()
+    q, K, V = fx.make_attn(w)
+    qt, Kt = dev(q), dev(K)
+    p = problem(w)
+    rows = w.B * w.Hq
+    s = m.topk_attn_score(p, qt, Kt).reshape(rows, L)
+    srt = torch.sort(s, dim=1, descending=True).values
+    thr = srt[:, k - 1].contiguous()                 # the k-th largest score of each row
+    thr[0] = srt[0, 0]                                # a row keeping only its maximum
+    thr[1] = -torch.inf                               # a row keeping everything
+    cap = L
+    counts = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    cs = torch.empty((rows, cap), dtype=torch.float32, device="cuda")
+    cp = torch.empty((rows, cap), dtype=torch.int32, device="cuda")
+    say(f"[threshold] L={L} k={k}")
+    m.topk_attn_score_threshold(p, qt, Kt, thr, counts, cs, cp)
+    torch.cuda.synchronize()
+    s_np, thr_np = s.cpu().numpy(), thr.cpu().numpy()
+    c_np, cs_np, cp_np = counts.cpu().numpy(), cs.cpu().numpy(), cp.cpu().numpy()
+    for r in range(rows):
+        want = np.nonzero(s_np[r] >= thr_np[r])[0]
+        assert c_np[r] == len(want), r
+        got = np.sort(cp_np[r, : c_np[r]])
+        assert np.array_equal(got, want), r
+        order = np.argsort(cp_np[r, : c_np[r]])
+        assert np.array_equal(cs_np[r, : c_np[r]][order].view(np.uint32), s_np[r, want].view(np.uint32))
+    # append: the same pairs again after the first batch (rows that still fit)
+    before = counts.clone()
+    m.topk_attn_score_threshold(p, qt, Kt, thr, counts, cs, cp)
+    torch.cuda.synchronize()
+    assert torch.equal(counts, 2 * before)
+    c2 = counts.cpu().numpy()
+    cp2 = cp.cpu().numpy()
+    for r in range(rows):
+        n1 = before[r].item()
+        if 2 * n1 <= cap:
+            assert np.array_equal(np.sort(cp2[r, n1: 2 * n1]), np.sort(cp_np[r, :n1]))

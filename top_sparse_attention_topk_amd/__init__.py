@@ -39,12 +39,16 @@ class Problem(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m top_sparse_attention_topk_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python top_sparse_attention_topk_amd/build.py`")
+    # torch first: libtka then binds the HIP runtime torch already loaded (one runtime per
+    # process, shared with the tensors whose pointers it receives)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     P = ctypes.POINTER(Problem)
     sig = {
         "topk_attn_score": [P, vp, vp, vp, vp, vp],
+        "topk_attn_score_threshold": [P, vp, vp, vp, vp, vp, vp, i32, vp],
         "topk_select": [vp, i64, i32, i64, i32, vp, vp, vp, sz, vp],
         "topk_select_workspace_size": [i64, i32, i32, ctypes.POINTER(sz)],
         "sparse_attn_gather": [P, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
@@ -67,7 +71,7 @@ def _load():
 
 
 LIB = _load()
-EXPORTS = ["topk_attn_score", "topk_select", "topk_select_workspace_size", "sparse_attn_gather",
+EXPORTS = ["topk_attn_score", "topk_attn_score_threshold", "topk_select", "topk_select_workspace_size", "sparse_attn_gather",
            "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
            "topk_block_mean_build", "tka_status_str", "tka_last_error", "tka_abi_version"]
 
@@ -127,6 +131,15 @@ def topk_attn_score(p: Problem, q, keys, idx_w=None, scores=None, stream=None):
     _check(LIB.topk_attn_score(ctypes.byref(p), _ptr(q), _ptr(keys), _ptr(idx_w), _ptr(scores), _stream(stream)),
            "topk_attn_score")
     return scores
+
+
+def topk_attn_score_threshold(p: Problem, q, k_cache, thresholds, counts, cand_scores, cand_pos, stream=None):
+    """Append (score, position) pairs ranking at or above thresholds[row]; see include/tka.h."""
+    capacity = cand_scores.shape[-1]
+    _check(LIB.topk_attn_score_threshold(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(thresholds), _ptr(counts),
+                                         _ptr(cand_scores), _ptr(cand_pos), capacity, _stream(stream)),
+           "topk_attn_score_threshold")
+    return counts
 
 
 def topk_select_workspace_size(n_rows: int, row_len: int, k: int) -> int:

@@ -1,6 +1,7 @@
 """Build libtka.so (gfx950) in-tree with hipcc.
 
-Usage: python -m top_sparse_attention_topk_amd.build
+Usage: python top_sparse_attention_topk_amd/build.py   (run as a file: it must not
+import the package, whose binding loads the library being built)
 Each .hip source is compiled to an object in _build/ (in parallel), then
 linked into top_sparse_attention_topk_amd/libtka.so.
 """

@@ -324,6 +324,8 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
   pf.r = (int)((7 * kk * pf.nsamp + 4 * L - 1) / (4 * L));
   if (pf.r < 1) pf.r = 1;
   pf.capg = (int)(3 * kk);
+  // the threshold and finish kernels hold the samples and the candidates in registers
+  if (pf.nsamp > 8192 || pf.capg > 12288) return PrefilterPlan{};
   pf.on = true;
   return pf;
 }
@@ -409,6 +411,43 @@ tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys
   if (score_len(p) <= 0) return ok();
   run_score(p, q, keys, idx_w, scores, as_stream(stream));
   return launched("topk_attn_score");
+}
+
+tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const void* k_cache,
+                                     const float* thresholds, uint32_t* counts, float* cand_scores, int32_t* cand_pos,
+                                     int32_t capacity, void* stream) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (p->mode != TKA_SCORE_EXACT) return fail(TKA_ERR_INVALID_ARG, "mode must be TKA_SCORE_EXACT");
+  if (p->qkv_dtype != TKA_BF16 || !score_uses_mfma(1, G))
+    return fail(TKA_ERR_UNSUPPORTED, "thresholded scan needs bf16 caches and 2 <= Hq/Hkv <= 16");
+  if (capacity < 1) return fail(TKA_ERR_INVALID_ARG, "capacity must be >= 1 (got %d)", capacity);
+  if ((s = need_ptr(q, "q")) || (s = need_ptr(k_cache, "k_cache")) ||
+      (s = need_ptr(thresholds, "thresholds", false)) || (s = need_ptr(counts, "counts", false)) ||
+      (s = need_ptr(cand_scores, "cand_scores", false)) || (s = need_ptr(cand_pos, "cand_pos", false)))
+    return s;
+  if ((reinterpret_cast<uintptr_t>(thresholds) | reinterpret_cast<uintptr_t>(counts) |
+       reinterpret_cast<uintptr_t>(cand_scores) | reinterpret_cast<uintptr_t>(cand_pos)) & 3)
+    return fail(TKA_ERR_ALIGNMENT, "thresholds, counts and candidate arrays must be 4-byte aligned");
+  const size_t rows = (size_t)p->batch * p->n_q_heads;
+  const Range co = span_of(counts, sizeof(uint32_t) * rows);
+  const Range cs = span_of(cand_scores, sizeof(float) * rows * (size_t)capacity);
+  const Range cp = span_of(cand_pos, sizeof(int32_t) * rows * (size_t)capacity);
+  const Range ins[3] = {span_of(q, attn_q_bytes(p)), span_of(k_cache, kv_bytes(p)),
+                        span_of(thresholds, sizeof(float) * rows)};
+  for (const Range& in : ins)
+    if (overlap(in, co) || overlap(in, cs) || overlap(in, cp))
+      return fail(TKA_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(co, cs) || overlap(co, cp) || overlap(cs, cp)) return fail(TKA_ERR_INVALID_ARG, "outputs overlap");
+  MfmaOut mo{};
+  mo.T = thresholds;
+  mo.cnt = counts;
+  mo.cbits = reinterpret_cast<uint32_t*>(cand_scores);
+  mo.cpos = cand_pos;
+  mo.capg = capacity;
+  launch_score_mfma_cand(dense_score_args(p, q, k_cache, nullptr), mo, as_stream(stream));
+  return launched("topk_attn_score_threshold");
 }
 
 tka_status topk_select_workspace_size(int64_t n_rows, int32_t row_len, int32_t k, size_t* bytes) {
@@ -520,7 +559,7 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     // rows whose candidates cannot hold the answer are rescored in full
     const ScoreArgs sc = dense_score_args(p, q, k_cache, scores);
     float* samp = reinterpret_cast<float*>(base + d.samp);
-    uint32_t* T = reinterpret_cast<uint32_t*>(base + d.T);
+    float* T = reinterpret_cast<float*>(base + d.T);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(base + d.cnt);
     uint32_t* row_flag = reinterpret_cast<uint32_t*>(base + d.row_flag);
     uint32_t* group_flag = reinterpret_cast<uint32_t*>(base + d.group_flag);
@@ -536,7 +575,8 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     mo.cpos = cpos;
     mo.capg = d.pf.capg;
     launch_score_mfma_cand(sc, mo, st);
-    launch_prefilter_finish(cbits, cpos, cnt, d.pf.capg, d.rows, d.len, d.k, G, idx, selv, row_flag, group_flag, st);
+    launch_prefilter_finish(cbits, cpos, cnt, T, d.pf.capg, d.rows, d.len, d.k, G, idx, selv, row_flag, group_flag,
+                            st);
     launch_score_mfma_guarded(sc, group_flag, st);
     launch_select_rows_flagged(sa, row_flag, st);
   } else {

@@ -61,7 +61,7 @@ struct GatherArgs {
 struct MfmaOut {
   float* S;                     // full scores [B*Hq, L], or sample scores [B*Hq, nsamp]
   int nsamp;
-  const uint32_t* T;            // candidate mode: key threshold per row
+  const float* T;               // candidate scan: score threshold per row (kept: ranks >= T)
   uint32_t* cnt;                // candidate mode: candidates found per row
   uint32_t* cbits;              // candidate mode: [B*Hq, capg] score bits
   int32_t* cpos;                // candidate mode: [B*Hq, capg] positions
@@ -69,6 +69,11 @@ struct MfmaOut {
   int stage;                    // candidate mode: LDS staging entries per head
   const uint32_t* group_flag;   // guarded mode: [B*Hkv], nonzero = rescore the group
 };
+
+// Largest LDS a workgroup may take on the current device, and a one-time
+// (per kernel and device) permission for a kernel to use more than 64 KiB.
+int device_lds_limit();
+void ensure_dynamic_lds(const void* kernel, size_t bytes);
 
 bool score_uses_mfma(int dtype_bf16, int G);
 int mfma_scan_chunk(const ScoreArgs& a);
@@ -85,11 +90,11 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st);
 
 // candidate prefilter of the fused exact step (select.hip)
-void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, uint32_t* T, uint32_t* cnt,
+void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
                                 uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st);
-void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, int capg,
-                             int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel, uint32_t* row_flag,
-                             uint32_t* group_flag, hipStream_t st);
+void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, const float* T,
+                             int capg, int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel,
+                             uint32_t* row_flag, uint32_t* group_flag, hipStream_t st);
 
 // gather planning is shared by the workspace query and the launch
 struct GatherPlan {

@@ -27,12 +27,9 @@ namespace tka {
 //   MFMA_FULL    - write every score, [B*Hq, L].
 //   MFMA_SAMPLE  - only the first 64 positions of every chunk; wave w of
 //                  workgroup x takes chunk 4x+w; scores to [B*Hq, nsamp].
-//   MFMA_CAND    - keep the scores whose key is >= T[row] as (bits, position)
-//                  candidates: staged per head in LDS, appended to the row's
-//                  list with one atomic per head and workgroup.
 //   MFMA_GUARDED - MFMA_FULL for the groups whose flag is set, else nothing.
 // ---------------------------------------------------------------------------
-enum { MFMA_FULL = 0, MFMA_SAMPLE = 1, MFMA_CAND = 2, MFMA_GUARDED = 3 };
+enum { MFMA_FULL = 0, MFMA_SAMPLE = 1, MFMA_GUARDED = 3 };
 // How K reaches the MFMA operand registers:
 //   KLOAD_DIRECT    - each lane loads its own operand slice (16 rows x 64 B per
 //                     load instruction), non-temporal.
@@ -71,22 +68,9 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
   const int n = lane & 15, kg = lane >> 4;
   const int64_t row = (int64_t)b * Hq + g * G + (n < G ? n : 0);
 
-  // dynamic LDS: [staging: 4 waves x P rows x PADB][candidates: cnt[16], base[16], bits[G][stage], pos[G][stage]]
+  // dynamic LDS: staging rows, 4 waves x P rows x PADB
   extern __shared__ uint4 smem_raw[];
   uint8_t* stage_rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
-  uint32_t* cstage = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) +
-                                                 (KL == KLOAD_STAGED ? (size_t)4 * P * PADB : 0));
-  uint32_t* lcnt = cstage;
-  uint32_t* lbase = cstage + 16;
-  uint32_t* lbits = cstage + 32;
-  const int ST_H = o.stage;
-  int32_t* lpos = reinterpret_cast<int32_t*>(lbits + G * ST_H);
-  uint32_t Tn = 0;
-  if (MODE == MFMA_CAND) {
-    if (threadIdx.x < 16) lcnt[threadIdx.x] = 0;
-    if (n < G) Tn = o.T[row];
-    __syncthreads();
-  }
 
   bf16x8_t bq[KS];
 #pragma unroll
@@ -171,23 +155,6 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (pos + i < p1) Srow[pos + i] = v[i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (pos + i < p1 && score_key(v[i]) >= Tn) {
-              const uint32_t slot = atomicAdd(&lcnt[n], 1u);
-              if (slot < (uint32_t)ST_H) {
-                lbits[n * ST_H + slot] = __float_as_uint(v[i]);
-                lpos[n * ST_H + slot] = pos + i;
-              } else {  // stage full: append directly
-                const uint32_t gs = atomicAdd(&o.cnt[row], 1u);
-                if (gs < (uint32_t)o.capg) {
-                  o.cbits[row * o.capg + gs] = __float_as_uint(v[i]);
-                  o.cpos[row * o.capg + gs] = pos + i;
-                }
-              }
-            }
-          }
         }
       }
     }
@@ -197,26 +164,166 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
       for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
     }
   }
-  if (MODE == MFMA_CAND) {
-    __syncthreads();
-    if (threadIdx.x < G) {
-      const int64_t r = (int64_t)b * Hq + g * G + threadIdx.x;
-      const uint32_t c = min(lcnt[threadIdx.x], (uint32_t)ST_H);
-      lcnt[threadIdx.x] = c;
-      lbase[threadIdx.x] = c ? atomicAdd(&o.cnt[r], c) : 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Candidate scan, persistent form (the hot loop of the fused exact step).
+// One workgroup per CU; workgroup i owns a contiguous, balanced range of
+// 32-position tiles of the flattened (batch * KV head, position) space, and
+// its waves take every fourth tile, so each wave streams K without gaps
+// (next tile prefetched while the current one is scored). K goes through the
+// wave's padded LDS rows as in KLOAD_STAGED. Kept scores (key >= T[row]) are
+// staged per head in wave-private LDS and appended to the row's list when a
+// head's stage would overflow, when the wave moves to another KV head, and at
+// the end: one atomic per head per flush, no workgroup barriers. Kept means
+// "ranks at or above T[row]" in the select order (score key >= key of T).
+// ---------------------------------------------------------------------------
+#ifndef TKA_PS_STAGE
+#define TKA_PS_STAGE 128
+#endif
+#ifndef TKA_PS_DEPTH
+#define TKA_PS_DEPTH 1
+#endif
+#ifndef TKA_PS_WPC
+#define TKA_PS_WPC 2
+#endif
+constexpr int PS_STAGE = TKA_PS_STAGE;  // staged candidates per head and wave
+constexpr int PS_DEPTH = TKA_PS_DEPTH;  // tiles in flight per wave beyond the one being scored
+constexpr int PS_WPC = TKA_PS_WPC;      // workgroups per CU
+
+template <int D>
+__global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16_t* __restrict__ q,
+                                                                    const uint16_t* __restrict__ K, int Hq, int Hkv,
+                                                                    int G, int L, int64_t sb, int64_t sh, int64_t sl,
+                                                                    float scale, int64_t ntiles, int tpg, MfmaOut o) {
+  constexpr int KS = D / 32;
+  constexpr int P = 32;
+  constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  extern __shared__ uint4 smem_raw[];
+  uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
+  uint32_t* sbits = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB) +
+                    (size_t)wave * 2 * G * PS_STAGE;
+  int32_t* spos = reinterpret_cast<int32_t*>(sbits + G * PS_STAGE);
+
+  const int64_t per = ntiles / gridDim.x, extra = ntiles % gridDim.x;
+  const int64_t r0 = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
+  const int64_t r1 = r0 + per + ((int64_t)blockIdx.x < extra ? 1 : 0);
+
+  int grp = -1;           // KV group (b * Hkv + g) whose fragments are loaded
+  bf16x8_t bq[KS];
+  uint32_t Tn = 0;
+  uint32_t scnt = 0;      // staged candidates of head n (lanes with n < G)
+
+  auto flush_head = [&](int h) {
+    const uint32_t c = (uint32_t)__shfl((int)scnt, h, kWave);
+    if (c == 0) return;
+    const int b = grp / Hkv, g = grp % Hkv;
+    const int64_t r = (int64_t)b * Hq + g * G + h;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&o.cnt[r], c);
+    base = (uint32_t)__shfl((int)base, 0, kWave);
+    for (uint32_t e = lane; e < c; e += 64)
+      if (base + e < (uint32_t)o.capg) {
+        o.cbits[r * o.capg + base + e] = sbits[h * PS_STAGE + e];
+        o.cpos[r * o.capg + base + e] = spos[h * PS_STAGE + e];
+      }
+    if (n == h) scnt = 0;
+  };
+  auto flush_all = [&]() {
+    for (int h = 0; h < G; ++h) flush_head(h);
+  };
+  auto kbase = [&](int64_t t) {
+    const int gg = (int)(t / tpg);
+    return K + (int64_t)(gg / Hkv) * sb + (int64_t)(gg % Hkv) * sh;
+  };
+  auto load = [&](uint4 (&a)[NI], int64_t t) {
+    const uint16_t* Kb = kbase(t);
+    const int at = (int)(t % tpg) * P;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int pos = min(at + j * RPI + lane / CPR, L - 1);
+      a[j] = ld16_stream(Kb + (int64_t)pos * sl + (lane % CPR) * 8);
     }
-    __syncthreads();
-    for (int h = 0; h < G; ++h) {
-      const int64_t r = (int64_t)b * Hq + g * G + h;
-      const uint32_t c = lcnt[h], bse = lbase[h];
-      for (uint32_t j = threadIdx.x; j < c; j += 256) {
-        if (bse + j < (uint32_t)o.capg) {
-          o.cbits[r * o.capg + bse + j] = lbits[h * ST_H + j];
-          o.cpos[r * o.capg + bse + j] = lpos[h * ST_H + j];
-        }
+  };
+
+  int64_t t = r0 + wave;
+  uint4 buf[PS_DEPTH + 1][NI];
+#pragma unroll
+  for (int i = 0; i < PS_DEPTH; ++i)
+    if (t + 4 * i < r1) load(buf[i], t + 4 * i);
+  for (; t < r1; t += 4) {
+    const int tg = (int)(t / tpg);
+    if (tg != grp) {  // new KV group: hand over the old group's candidates, load the new fragments
+      if (grp >= 0) flush_all();
+      grp = tg;
+      const int b = grp / Hkv, g = grp % Hkv;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n < G) v = ld16(q + ((int64_t)(b * Hq + g * G + n)) * D + 32 * s + 8 * kg);
+        bq[s] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      Tn = n < G ? score_key(o.T[(int64_t)b * Hq + g * G + n]) : 0u;
+    }
+    if (t + 4 * PS_DEPTH < r1) load(buf[PS_DEPTH], t + 4 * PS_DEPTH);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      *reinterpret_cast<uint4*>(rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = buf[0][j];
+    lds_wave_sync();
+    const int pos0 = (int)(t % tpg) * P;
+    bool f[2][4];
+    float v[2][4];
+    uint32_t c = 0;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 a = *reinterpret_cast<const uint4*>(rows + (16 * tt + n) * PADB + (kg + 4 * s) * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bq[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[tt][i] = acc[i] * scale;
+        const int pos = pos0 + 16 * tt + 4 * kg + i;
+        f[tt][i] = n < G && pos < L && score_key(v[tt][i]) >= Tn;
+        c += f[tt][i];
       }
     }
+    __builtin_amdgcn_wave_barrier();  // operand reads of this tile precede the next tile's writes
+    // per head: total over the four lanes holding it, and this lane's offset among them (kg order)
+    const uint32_t a1 = (uint32_t)__shfl_xor((int)c, 16, kWave);
+    const uint32_t pair = c + a1;
+    const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
+    const uint32_t tot = pair + a2;
+    const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
+    uint64_t full = ballot(lane < 16 && n < G && scnt + tot > (uint32_t)PS_STAGE);
+    while (full) {  // wave-uniform
+      const int h = __builtin_ctzll(full);
+      full &= full - 1;
+      flush_head(h);
+    }
+    if (n < G) {
+      uint32_t slot = scnt + pre;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (f[tt][i]) {
+            sbits[n * PS_STAGE + slot] = __float_as_uint(v[tt][i]);
+            spos[n * PS_STAGE + slot] = pos0 + 16 * tt + 4 * kg + i;
+            ++slot;
+          }
+      scnt += tot;
+    }
+#pragma unroll
+    for (int i = 0; i < PS_DEPTH; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) buf[i][j] = buf[i + 1][j];
   }
+  if (grp >= 0) flush_all();
 }
 
 // ---------------------------------------------------------------------------
@@ -443,9 +550,9 @@ static int pick_chunk(int64_t rows_per_task, int64_t tasks, int granule, int lo,
 template <int D, int MODE>
 static void launch_mfma_mode(const ScoreArgs& a, int chunk, unsigned gx, const MfmaOut& o, hipStream_t st) {
   constexpr int KL = TKA_SCAN_KLOAD;
-  const size_t stage_rows = KL == KLOAD_STAGED ? (size_t)4 * 32 * (D * 2 + 16) : 0;
-  const size_t lds = stage_rows + (MODE == MFMA_CAND ? sizeof(uint32_t) * (32 + 2 * (size_t)a.G * o.stage) : 0);
+  const size_t lds = KL == KLOAD_STAGED ? (size_t)4 * 32 * (D * 2 + 16) : 0;
   dim3 grid(gx, a.B * a.Hkv);
+  ensure_dynamic_lds((const void*)score_exact_mfma_kernel<D, MODE, KL>, lds);
   hipLaunchKernelGGL((score_exact_mfma_kernel<D, MODE, KL>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, o);
 }
@@ -469,11 +576,45 @@ void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, f
   launch_mfma<MFMA_SAMPLE>(a, sample_chunk, (unsigned)((nch + 3) / 4), o, st);
 }
 
-void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o_in, hipStream_t st) {
-  MfmaOut o = o_in;
-  o.stage = a.G <= 8 ? 256 : 128;  // per head and workgroup; at most 16 KiB of LDS
-  const int chunk = mfma_scan_chunk(a);
-  launch_mfma<MFMA_CAND>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
+#ifndef TKA_CAND_CHUNK
+#define TKA_CAND_CHUNK 1024  // positions per workgroup: many short workgroups, no long tail
+#endif
+
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = 256;
+    }
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+template <int D>
+static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
+  const int tpg = (a.nrows + 31) / 32;
+  const int64_t ntiles = (int64_t)a.B * a.Hkv * tpg;
+  int64_t grid = (int64_t)device_cus() * PS_WPC;
+  if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
+  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * 2 * a.G * PS_STAGE * sizeof(uint32_t);
+  ensure_dynamic_lds((const void*)score_cand_persistent_kernel<D>, lds);
+  hipLaunchKernelGGL((score_cand_persistent_kernel<D>), dim3((unsigned)grid), dim3(256), lds, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl,
+                     a.scale, ntiles, tpg, o);
+}
+
+void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
+  switch (a.d) {
+    case 64: launch_cand_persistent<64>(a, o, st); break;
+    case 128: launch_cand_persistent<128>(a, o, st); break;
+    default: launch_cand_persistent<256>(a, o, st); break;
+  }
 }
 
 void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st) {

@@ -20,6 +20,10 @@
 //    one workgroup per row finishes on the (small) candidate list.
 #include <math.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -42,6 +46,11 @@ __device__ __forceinline__ uint32_t lv_digit(uint32_t key, int lv) {
 // the digits above level lv equal `prefix`
 __device__ __forceinline__ bool lv_in_range(uint32_t key, int lv, uint32_t prefix) {
   return lv == 0 || (key >> lv_shift(lv - 1)) == prefix;
+}
+
+// A float whose score key is `key` (inverse of score_key up to -0 and NaN payloads).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 struct SelSmem {
@@ -503,49 +512,151 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 constexpr int PF_NW = 16;  // waves of the prefilter kernels (1024 threads)
 constexpr int PF_T = 64 * PF_NW;
+constexpr int PF_RS = 8;   // samples held per thread: nsamp <= 8192
+constexpr int PF_RC = 12;  // candidates held per thread: capacity <= 12288
 
+constexpr int PF_STASH = 2048;  // elements of the critical bin ranked one by one
+
+struct PfSmem {
+  uint32_t skey[PF_STASH];
+  uint32_t sidx[PF_STASH];
+  int32_t spos[PF_STASH];
+  uint32_t scnt;
+  uint32_t red[PF_NW];
+  uint32_t tval;
+};
+
+// One-pass bin search over register-held keys (thread t holds elements
+// t + PF_T*j, j < R, valid below cnt). The digit is taken relative to the
+// keys' own range [lo, hi]: d = (key - lo) >> shift < 4096, so the critical
+// bin usually holds a handful of elements. Returns (bin, above) in sm.res and
+// the shift in *shift_out.
+template <int R, typename KeyOf>
+__device__ void relative_bin(KeyOf key_of, uint32_t cnt, uint32_t lo, uint32_t hi, uint32_t need, SelSmem& sm,
+                             int* shift_out) {
+  const int t = threadIdx.x;
+  const uint32_t span = hi - lo;
+  const int shift = span >= 4096u ? (32 - __clz(span)) - 12 : 0;
+  for (int i = t; i < NB0; i += PF_T) sm.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if ((uint32_t)(t + PF_T * j) < cnt) atomicAdd(&sm.hist[(key_of(j) - lo) >> shift], 1u);
+  __syncthreads();
+  find_bin_t<PF_NW>(sm.hist, NB0, need, sm);
+  *shift_out = shift;
+}
+
+template <int R, typename KeyOf>
+__device__ void block_min_max(KeyOf key_of, uint32_t cnt, PfSmem& ps, uint32_t* mn_out, uint32_t* mx_out) {
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if ((uint32_t)(t + PF_T * j) < cnt) {
+      const uint32_t k = key_of(j);
+      mn = min(mn, k);
+      mx = max(mx, k);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  }
+  if (lane == 0) ps.red[w] = mx;
+  __syncthreads();
+  uint32_t gmx = 0u;
+#pragma unroll
+  for (int i = 0; i < PF_NW; ++i) gmx = max(gmx, ps.red[i]);
+  __syncthreads();
+  if (lane == 0) ps.red[w] = mn;
+  __syncthreads();
+  uint32_t gmn = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < PF_NW; ++i) gmn = min(gmn, ps.red[i]);
+  __syncthreads();
+  *mn_out = gmn;
+  *mx_out = gmx;
+}
+
+// Threshold of a row: the key of its r-th largest sample (the sample's
+// value, ties irrelevant). Also clears the row's counters and flags.
 __global__ __launch_bounds__(1024) void prefilter_threshold_kernel(const float* __restrict__ samp, int nsamp, int r,
-                                                                   uint32_t* __restrict__ T,
+                                                                   float* __restrict__ T,
                                                                    uint32_t* __restrict__ cnt,
                                                                    uint32_t* __restrict__ row_flag,
                                                                    uint32_t* __restrict__ group_flag, int G) {
   __shared__ SelSmem sm;
+  __shared__ PfSmem ps;
   const int64_t row = blockIdx.x;
-  const int w = threadIdx.x >> 6;
-  if (threadIdx.x == 0) {
+  const int t = threadIdx.x;
+  if (t == 0) {
     cnt[row] = 0;
     row_flag[row] = 0;
     if (row % G == 0) group_flag[row / G] = 0;
+    ps.scnt = 0;
   }
-  const float* s = samp + row * nsamp;
   if (r > nsamp) {
-    if (threadIdx.x == 0) T[row] = 0u;  // too few samples: keep everything
+    if (t == 0) T[row] = key_value(0u);  // too few samples: keep everything
     return;
   }
-  const uint32_t q = (uint32_t)(nsamp + PF_NW - 1) / PF_NW;
-  const uint32_t off = min((uint32_t)nsamp, (uint32_t)w * q);
-  const uint32_t c = min((uint32_t)nsamp, off + q) - off;
-  radix_kth_t<PF_NW>([&](uint32_t e) { return score_key(s[off + e]); }, c, 0, 0u, (uint32_t)r, sm);
-  if (threadIdx.x == 0) T[row] = sm.res[0];
+  const float* s = samp + row * nsamp;
+  uint32_t key[PF_RS];
+#pragma unroll
+  for (int j = 0; j < PF_RS; ++j) {
+    const int e = t + PF_T * j;
+    key[j] = e < nsamp ? score_key(s[e]) : 0u;
+  }
+  auto key_of = [&](int j) { return key[j]; };
+  uint32_t mn, mx;
+  block_min_max<PF_RS>(key_of, (uint32_t)nsamp, ps, &mn, &mx);
+  int shift;
+  relative_bin<PF_RS>(key_of, (uint32_t)nsamp, mn, mx, (uint32_t)r, sm, &shift);
+  const uint32_t bin = sm.res[0], need = (uint32_t)r - sm.res[1];
+#pragma unroll
+  for (int j = 0; j < PF_RS; ++j)
+    if (t + PF_T * j < nsamp && ((key[j] - mn) >> shift) == bin) {
+      const uint32_t slot = atomicAdd(&ps.scnt, 1u);
+      if (slot < PF_STASH) ps.skey[slot] = key[j];
+    }
+  __syncthreads();
+  const uint32_t m = ps.scnt;
+  if (m > PF_STASH) {  // a crowded bin: its lower edge is a valid (lower) threshold
+    if (t == 0) T[row] = key_value(mn + (bin << shift));
+    return;
+  }
+  for (uint32_t i = t; i < m; i += PF_T) {
+    const uint32_t v = ps.skey[i];
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t u = 0; u < m; ++u) {
+      gt += ps.skey[u] > v;
+      ge += ps.skey[u] >= v;
+    }
+    if (gt < need && need <= ge) ps.tval = v;  // every writer stores the same key
+  }
+  __syncthreads();
+  if (t == 0) T[row] = key_value(ps.tval);
 }
 
-// Exact top-k of a row from its (unordered) candidates. Kept positions are
-// marked in an LDS bitmap over the row; popcount prefix sums give each one
-// its output slot in ascending position order. Dynamic LDS: 3 * ceil(n/32)
-// words (kept bitmap, tie bitmap, prefix counts). Every pass over the
-// candidates keeps 8 loads per lane in flight.
-__global__ __launch_bounds__(1024) void prefilter_finish_kernel(const uint32_t* __restrict__ cbits,
+// Exact top-k of a row from its (unordered) candidates, whose keys are all
+// >= T[row]. One relative-digit histogram finds the bin holding the k'-th
+// key; its few elements are ranked one by one (key, then lower position
+// first). Kept positions are marked in an LDS bitmap over the row and
+// popcount prefix sums give each its output slot in ascending position
+// order. Dynamic LDS: 2 * ceil(n/32) words (kept bitmap, prefix counts).
+__global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_t* __restrict__ cbits,
                                                                 const int32_t* __restrict__ cpos,
-                                                                const uint32_t* __restrict__ cnt, int capg, int n,
+                                                                const uint32_t* __restrict__ cnt,
+                                                                const float* __restrict__ Tv, int capg, int n,
                                                                 int k, int G, int32_t* __restrict__ idx,
                                                                 float* __restrict__ sel,
                                                                 uint32_t* __restrict__ row_flag,
                                                                 uint32_t* __restrict__ group_flag) {
-  constexpr int U = 8;
   __shared__ SelSmem sm;
+  __shared__ PfSmem ps;
   extern __shared__ uint32_t dyn[];
   const int64_t row = blockIdx.x;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int t = threadIdx.x;
   const int kk = min(k, n);
   int32_t* oidx = idx + row * k;
   float* osel = sel ? sel + row * k : nullptr;
@@ -554,118 +665,94 @@ __global__ __launch_bounds__(1024) void prefilter_finish_kernel(const uint32_t* 
     if (osel) osel[j] = -INFINITY;
   }
   const uint32_t nc = cnt[row];
-  if (nc < (uint32_t)kk || nc > (uint32_t)capg) {  // threshold too high or too many ties: full rescore
-    if (t == 0) {
-      row_flag[row] = 1u;
-      atomicOr(&group_flag[row / G], 1u);
-    }
-    return;
-  }
-  const uint32_t* cb = cbits + row * capg;
-  const int32_t* cp = cpos + row * capg;
-  const uint32_t q = (nc + PF_NW - 1) / PF_NW;
-  const uint32_t off = min(nc, (uint32_t)w * q);
-  const uint32_t c = min(nc, off + q) - off;
-  radix_kth_t<PF_NW>([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, c, 0, 0u, (uint32_t)kk,
-                     sm);
-  const uint32_t T = sm.res[0], need_eq = sm.res[1];
-  const int words = (n + 31) >> 5;
-  uint32_t* bm = dyn;
-  uint32_t* tbm = dyn + words;
-  uint32_t* pre = dyn + 2 * words;
-  for (int i = t; i < words; i += PF_T) {
-    bm[i] = 0u;
-    tbm[i] = 0u;
-  }
-  __syncthreads();
-  // mark keys > T; keys == T go to the tie bitmap
-  uint32_t neq = 0;
-  for (uint32_t e0 = 0; e0 < c; e0 += 64 * U) {
-    uint32_t key[U];
-    int32_t pp[U];
+  bool repair = nc < (uint32_t)kk || nc > (uint32_t)capg;  // threshold too high, or too many candidates
+  if (!repair) {
+    const uint32_t* cb = cbits + row * capg;
+    const int32_t* cp = cpos + row * capg;
+    const uint32_t T0 = score_key(Tv[row]);
+    uint32_t bits[PF_RC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t e = e0 + u * 64 + lane;
-      key[u] = e < c ? score_key(__uint_as_float(cb[off + e])) : 0u;
-      pp[u] = e < c ? cp[off + e] : 0;
+    for (int j = 0; j < PF_RC; ++j) {
+      const uint32_t e = t + PF_T * j;
+      bits[j] = e < nc ? cb[e] : 0u;
     }
+    auto key_of = [&](int j) { return score_key(__uint_as_float(bits[j])); };
+    const int words = (n + 31) >> 5;
+    uint32_t* bm = dyn;
+    uint32_t* pre = dyn + words;
+    for (int i = t; i < words; i += PF_T) bm[i] = 0u;
+    if (t == 0) ps.scnt = 0;
+    uint32_t mn, mx;
+    block_min_max<PF_RC>(key_of, nc, ps, &mn, &mx);
+    (void)mn;
+    int shift;
+    relative_bin<PF_RC>(key_of, nc, T0, mx, (uint32_t)kk, sm, &shift);
+    const uint32_t bin = sm.res[0], need = (uint32_t)kk - sm.res[1];
+    // keys above the critical bin are kept; the bin's elements go to the stash
+    // (positions are read here and again below rather than held: fewer registers)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (e0 + u * 64 + lane >= c) continue;
-      const int32_t p = pp[u];
-      if (key[u] > T) atomicOr(&bm[p >> 5], 1u << (p & 31));
-      else if (key[u] == T) {
-        atomicOr(&tbm[p >> 5], 1u << (p & 31));
-        ++neq;
-      }
-    }
-  }
-  neq = wave_sum(neq);
-  if (lane == 0) sm.scan[w] = neq;
-  __syncthreads();
-  uint32_t neq_all = 0;
-#pragma unroll
-  for (int i = 0; i < PF_NW; ++i) neq_all += sm.scan[i];
-  __syncthreads();
-  const int per = (words + PF_T - 1) / PF_T;
-  auto prefix_counts = [&](const uint32_t* bits) {
-    uint32_t loc = 0;
-    for (int i = 0; i < per; ++i) {
-      const int wd = t * per + i;
-      if (wd < words) loc += __popc(bits[wd]);
-    }
-    uint32_t total;
-    uint32_t run = block_incl_scan_t<PF_NW>(loc, sm, &total) - loc;
-    for (int i = 0; i < per; ++i) {
-      const int wd = t * per + i;
-      if (wd < words) {
-        pre[wd] = run;
-        run += __popc(bits[wd]);
+    for (int j = 0; j < PF_RC; ++j) {
+      const uint32_t e = t + PF_T * j;
+      if (e >= nc) continue;
+      const uint32_t d = (key_of(j) - T0) >> shift;
+      if (d < bin) continue;
+      const int32_t p = cp[e];
+      if (d > bin) {
+        atomicOr(&bm[p >> 5], 1u << (p & 31));
+      } else {
+        const uint32_t slot = atomicAdd(&ps.scnt, 1u);
+        if (slot < PF_STASH) {
+          ps.skey[slot] = key_of(j);
+          ps.spos[slot] = p;
+        }
       }
     }
     __syncthreads();
-  };
-  // ties: keep the need_eq lowest positions (all of them when there is no excess)
-  if (neq_all > need_eq) prefix_counts(tbm);
-  for (int i = t; i < words; i += PF_T) {
-    uint32_t tw = tbm[i];
-    if (tw == 0u) continue;
-    if (neq_all > need_eq) {
-      uint32_t rank = pre[i], keep = 0u;
-      while (tw) {
-        const int bpos = __ffs(tw) - 1;
-        if (rank < need_eq) keep |= 1u << bpos;
-        ++rank;
-        tw &= tw - 1u;
+    const uint32_t m = ps.scnt;
+    repair = m > PF_STASH;  // heavy ties in one bin: leave the row to the full select
+    if (!repair) {
+      for (uint32_t i = t; i < m; i += PF_T) {
+        const uint32_t v = ps.skey[i];
+        const int32_t pv = ps.spos[i];
+        uint32_t rank = 0;
+        for (uint32_t u = 0; u < m; ++u) rank += ps.skey[u] > v || (ps.skey[u] == v && ps.spos[u] < pv);
+        if (rank < need) atomicOr(&bm[pv >> 5], 1u << (pv & 31));
       }
-      tw = keep;
+      __syncthreads();
+      const int per = (words + PF_T - 1) / PF_T;
+      uint32_t loc = 0;
+      for (int i = 0; i < per; ++i) {
+        const int wd = t * per + i;
+        if (wd < words) loc += __popc(bm[wd]);
+      }
+      uint32_t total;
+      uint32_t run = block_incl_scan_t<PF_NW>(loc, sm, &total) - loc;
+      for (int i = 0; i < per; ++i) {
+        const int wd = t * per + i;
+        if (wd < words) {
+          pre[wd] = run;
+          run += __popc(bm[wd]);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PF_RC; ++j) {
+        const uint32_t e = t + PF_T * j;
+        if (e >= nc || ((key_of(j) - T0) >> shift) < bin) continue;
+        const int32_t p = cp[e];
+        const uint32_t word = bm[p >> 5];
+        if (!((word >> (p & 31)) & 1u)) continue;
+        const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
+        if (slot < (uint32_t)kk) {
+          oidx[slot] = p;
+          if (osel) osel[slot] = __uint_as_float(bits[j]);
+        }
+      }
     }
-    bm[i] |= tw;
   }
-  __syncthreads();
-  prefix_counts(bm);
-  // write every kept candidate to its slot
-  for (uint32_t e0 = 0; e0 < c; e0 += 64 * U) {
-    uint32_t bits[U];
-    int32_t pp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t e = e0 + u * 64 + lane;
-      bits[u] = e < c ? cb[off + e] : 0u;
-      pp[u] = e < c ? cp[off + e] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (e0 + u * 64 + lane >= c) continue;
-      const int32_t p = pp[u];
-      const uint32_t word = bm[p >> 5];
-      if (!((word >> (p & 31)) & 1u)) continue;
-      const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
-      if (slot < (uint32_t)kk) {
-        oidx[slot] = p;
-        if (osel) osel[slot] = __uint_as_float(bits[u]);
-      }
-    }
+  if (repair && t == 0) {
+    row_flag[row] = 1u;
+    atomicOr(&group_flag[row / G], 1u);
   }
 }
 
@@ -700,6 +787,20 @@ size_t select_workspace_bytes(int64_t n_rows, int n, int k) {
   return split_layout(n_rows, n).total;
 }
 
+// Let a kernel take dynamic LDS up to the device limit minus its own static
+// LDS (read from the code object, alignment padding included). A refused
+// request is cleared so it cannot surface as a later launch error.
+static void allow_dynamic_lds(const void* kernel, int limit) {
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, kernel) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  const int dyn = limit - (int)fa.sharedSizeBytes;
+  if (dyn <= 0 || hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, dyn) != hipSuccess)
+    (void)hipGetLastError();
+}
+
 static int max_lds_bytes() {
   static int cached[64];
   int dev = 0;
@@ -707,14 +808,30 @@ static int max_lds_bytes() {
   if (dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] == 0) {
     int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
       v = 64 * 1024;
-    (void)hipFuncSetAttribute((const void*)select_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, v);
-    (void)hipFuncSetAttribute((const void*)prefilter_finish_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              v - (int)sizeof(SelSmem));
+    }
+    allow_dynamic_lds((const void*)select_rows_kernel, v);
+    allow_dynamic_lds((const void*)prefilter_finish_kernel, v);
     cached[dev] = v;
   }
   return cached[dev];
+}
+
+int device_lds_limit() { return max_lds_bytes(); }
+
+void ensure_dynamic_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return;
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto& e : done)
+    if (e.first == kernel && e.second == dev) return;
+  allow_dynamic_lds(kernel, max_lds_bytes());
+  done.emplace_back(kernel, dev);
 }
 
 static int rows_capw(int n, int k, size_t* lds) {
@@ -765,20 +882,20 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
                      a.scores, a.n, a.stride, a.k, ghist, cbits, cpos, ccount, catb, catp, nch, a.idx, a.sel);
 }
 
-void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, uint32_t* T, uint32_t* cnt,
+void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
                                 uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st) {
   hipLaunchKernelGGL(prefilter_threshold_kernel, dim3((unsigned)n_rows), dim3(PF_T), 0, st, samp, nsamp, r, T, cnt,
                      row_flag, group_flag, G);
 }
 
-static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 3 * (size_t)((n + 31) / 32); }
+static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((n + 31) / 32); }
 
-void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, int capg,
-                             int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel, uint32_t* row_flag,
-                             uint32_t* group_flag, hipStream_t st) {
+void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, const float* T,
+                             int capg, int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel,
+                             uint32_t* row_flag, uint32_t* group_flag, hipStream_t st) {
   (void)max_lds_bytes();
   hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(PF_T), prefilter_finish_lds(n), st, cbits,
-                     cpos, cnt, capg, n, k, G, idx, sel, row_flag, group_flag);
+                     cpos, cnt, T, capg, n, k, G, idx, sel, row_flag, group_flag);
 }
 
 }  // namespace tka
