@@ -17,6 +17,8 @@ on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -29,6 +31,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
 METRIC = "decode queries/sec and HBM GB/s (% of roofline) at L=128K, k=4096, 1 MI355X"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+CSRC = os.path.join(ROOT, "top_sparse_attention_topk_amd", "csrc")
+COPY_BYTES = 1 << 30  # calibration kernel: torch.neg over 1 GiB of fp32 reads and writes this many bytes
+COPY_KERNEL = "torch.neg (copy calibration)"
 
 
 def log(*a):
@@ -69,19 +74,111 @@ def score_kernel_bytes(w) -> int:
     return w.B * w.L * w.dI + w.B * w.HI * (w.dI + 4) + 4 * w.B * w.L
 
 
-def traffic_from_profiles(kernel: str, source: str):
+def source_digest() -> str:
+    """sha256 over every kernel source: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(kernel: str):
     """Measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated),
-    if profiles/counters.json holds them for the current kernel source."""
+    if profiles/counters.json holds them for the current kernel sources."""
     try:
         with open(COUNTERS) as f:
-            rec = json.load(f)[kernel]
-        with open(source, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+            rec = json.load(f)
+        if rec.get("source_sha256") != source_digest():
             return None
-        return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+        k = rec["kernels"][kernel]
+        return int(k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def short_name(name: str) -> str:
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    for c in "<(":
+        name = name.split(c)[0]
+    return name.strip()
+
+
+def copy_calibration(launches: int = 3):
+    """A plain elementwise kernel of known traffic (torch.neg over 1 GiB of
+    fp32: 1 GiB read, 1 GiB written) to scale the HBM byte counters by."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def summarize_trace(trace_dir: str, tail: int) -> None:
+    """Per-kernel dispatch count and mean/min/max duration from a rocprofv3
+    --kernel-trace csv, plus the mean of each kernel's last `tail` dispatches
+    (the standalone timing loops run last)."""
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    per = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                per.setdefault(short_name(r["Kernel_Name"]), []).append((int(r["Start_Timestamp"]), ns))
+    print(f"{'kernel':40s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'last%d_us' % tail:>9s}")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(ns for _, ns in kv[1])):
+        v.sort()
+        ns = [d for _, d in v]
+        last = ns[-tail:]
+        print(f"{name[:40]:40s} {len(ns):6d} {sum(ns) / len(ns) / 1e3:9.1f} {min(ns) / 1e3:9.1f} "
+              f"{max(ns) / 1e3:9.1f} {sum(last) / len(last) / 1e3:9.1f}")
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, tail: int) -> None:
+    """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per
+    dispatch), each divided by what the same counter reads for the copy
+    calibration kernel over its known size; the mean over each kernel's last
+    `tail` dispatches. Writes profiles/counters.json and prints a table."""
+    vals = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    name = COPY_KERNEL if "neg_kernel" in r["Kernel_Name"] else short_name(r["Kernel_Name"])
+                    disp = vals.setdefault(name, {}).setdefault(counter, {})
+                    key = int(r["Dispatch_Id"])
+                    disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"])
+
+    def mean_tail(kernel, counter):
+        d = vals[kernel][counter]
+        v = [d[i] * 1024.0 for i in sorted(d)][-tail:]
+        return sum(v) / len(v)
+
+    if COPY_KERNEL not in vals:
+        raise SystemExit(f"no copy calibration dispatches (torch.neg) among {sorted(vals)}")
+    cf = mean_tail(COPY_KERNEL, "FETCH_SIZE") / COPY_BYTES
+    cw = mean_tail(COPY_KERNEL, "WRITE_SIZE") / COPY_BYTES
+    out = {"source_sha256": source_digest(),
+           "calibration": {"kernel": COPY_KERNEL, "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                           "fetch_factor": round(cf, 5), "write_factor": round(cw, 5)},
+           "kernels": {}}
+    print(f"calibration {COPY_KERNEL}: FETCH_SIZE/{COPY_BYTES} = {cf:.4f}, WRITE_SIZE/{COPY_BYTES} = {cw:.4f}")
+    print(f"{'kernel':40s} {'fetch_raw_MB':>13s} {'write_raw_MB':>13s} {'fetch_MB':>10s} {'write_MB':>10s}")
+    for name in sorted(vals):
+        if name == COPY_KERNEL or "FETCH_SIZE" not in vals[name] or "WRITE_SIZE" not in vals[name]:
+            continue
+        f_raw, w_raw = mean_tail(name, "FETCH_SIZE"), mean_tail(name, "WRITE_SIZE")
+        out["kernels"][name] = {"fetch_bytes_per_launch": round(f_raw / cf), "write_bytes_per_launch": round(w_raw / cw),
+                                "fetch_raw_bytes": round(f_raw), "write_raw_bytes": round(w_raw)}
+        print(f"{name[:40]:40s} {f_raw / 1e6:13.1f} {w_raw / 1e6:13.1f} {f_raw / cf / 1e6:10.1f} {w_raw / cw / 1e6:10.1f}")
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
 
 
 def time_loop(fn, steps: int) -> float:
@@ -125,7 +222,19 @@ def main():
     ap.add_argument("--workload", default="C3", help="fixtures.WORKLOADS key (C3 is the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run the known-size copy kernel that HBM byte counters are scaled by")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="print kernel durations from a rocprofv3 trace; no GPU")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/counters.json from FETCH_SIZE / WRITE_SIZE runs; no GPU")
+    ap.add_argument("--tail", type=int, default=3, help="summaries: mean over each kernel's last N dispatches")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.tail)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.tail)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode.",
               file=sys.stderr)
@@ -207,8 +316,9 @@ def main():
     t_thr = None
     if exact and dt == tka.TKA_BF16 and 2 <= w.G <= 16:
         # the fused step's scan: every key scored, pairs ranking at or above the
-        # row's threshold kept. Timed alone with the k-th score as threshold.
-        thr = sel_val[:, w.k - 1].contiguous()
+        # row's threshold kept. Timed alone with the row's k-th largest score
+        # (the smallest selected one; selections come in index order) as threshold.
+        thr = sel_val.min(dim=1).values.contiguous()
         cnt = torch.zeros(rows, dtype=torch.int32, device="cuda")
         cap = 3 * w.k
         cs = torch.empty((rows, cap), dtype=torch.float32, device="cuda")
@@ -224,6 +334,7 @@ def main():
         torch.cuda.synchronize()
         t_thr = sum(a.elapsed_time(b) for a, b in times) / len(times)
         kept = int(cnt.sum().item())
+        assert int(cnt.min().item()) >= w.k, "thresholded scan kept fewer than k pairs in a row"
         kname = "score_cand_persistent_kernel"
         kbytes = (w.B * w.Hkv * w.L * w.d * 2 + w.B * w.Hq * w.d * 2 + 8 * rows + 8 * kept)
         kms = t_thr
@@ -234,11 +345,12 @@ def main():
         kbytes = score_kernel_bytes(w)
         kms = t_score
     achieved = kbytes / (kms / 1e3) / 1e9
-    traffic = traffic_from_profiles(kname, os.path.join(ROOT, "top_sparse_attention_topk_amd", "csrc",
-                                                        "score.hip"))
+    traffic = traffic_from_profiles(kname)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                 "kernel": kname, "algorithmic_bytes": kbytes, "avg_launch_ms": round(kms, 4)}
+    if t_thr is not None:
+        roofline["kept_pairs"] = kept
 
     result = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
@@ -255,6 +367,9 @@ def main():
     }
     del Kt, Vt, sc, ws
     torch.cuda.empty_cache()
+    if args.copy_calibration:
+        log("[bench] copy calibration kernel")
+        copy_calibration()
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, q, K, V, args.cpu_budget)
