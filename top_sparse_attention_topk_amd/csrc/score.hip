@@ -168,34 +168,37 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 
 // ---------------------------------------------------------------------------
 // Candidate scan, persistent form (the hot loop of the fused exact step).
-// One workgroup per CU; workgroup i owns a contiguous, balanced range of
+// PS_WPC workgroups per CU; workgroup i owns a contiguous, balanced range of
 // 32-position tiles of the flattened (batch * KV head, position) space, and
 // its waves take every fourth tile, so each wave streams K without gaps
 // (next tile prefetched while the current one is scored). K goes through the
-// wave's padded LDS rows as in KLOAD_STAGED. Kept scores (key >= T[row]) are
-// staged per head in wave-private LDS and appended to the row's list when a
-// head's stage would overflow, when the wave moves to another KV head, and at
-// the end: one atomic per head per flush, no workgroup barriers. Kept means
-// "ranks at or above T[row]" in the select order (score key >= key of T).
+// wave's padded LDS rows as in KLOAD_STAGED. Kept means "ranks at or above
+// T[row]" in the select order: key(s) >= key(T), which for fp32 is s >= T,
+// plus everything when T is NaN (NaN scores never rank at or above a number).
+// Kept (score, position) pairs are staged per head in wave-private LDS and
+// handed to the rows' lists when a head's stage could overflow on the next
+// tile, before the wave moves to another KV head, and at the end. A flush is
+// split around the next tile's loads: lanes 0..G-1 reserve list space for
+// all heads with one atomic instruction, the loads go out, then the staged
+// pairs are copied, so waiting for the reservation never drains the wave's
+// loads. Tile addresses and the (group, tile) cursor advance incrementally.
 // ---------------------------------------------------------------------------
-#ifndef TKA_PS_STAGE
-#define TKA_PS_STAGE 128
-#endif
-#ifndef TKA_PS_DEPTH
-#define TKA_PS_DEPTH 1
-#endif
 #ifndef TKA_PS_WPC
 #define TKA_PS_WPC 2
 #endif
-constexpr int PS_STAGE = TKA_PS_STAGE;  // staged candidates per head and wave
-constexpr int PS_DEPTH = TKA_PS_DEPTH;  // tiles in flight per wave beyond the one being scored
-constexpr int PS_WPC = TKA_PS_WPC;      // workgroups per CU
+#ifndef TKA_PS_STAGE_BYTES
+#define TKA_PS_STAGE_BYTES 11264
+#endif
+constexpr int PS_WPC = TKA_PS_WPC;                  // workgroups per CU
+constexpr int PS_STAGE_BYTES = TKA_PS_STAGE_BYTES;  // candidate stage per wave (G heads x 8 B x slots)
+constexpr int PS_TILE_MAX = 32;                     // most pairs one head can keep from one tile
 
 template <int D>
 __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16_t* __restrict__ q,
                                                                     const uint16_t* __restrict__ K, int Hq, int Hkv,
                                                                     int G, int L, int64_t sb, int64_t sh, int64_t sl,
-                                                                    float scale, int64_t ntiles, int tpg, MfmaOut o) {
+                                                                    float scale, int64_t ntiles, int tpg, int S,
+                                                                    MfmaOut o) {
   constexpr int KS = D / 32;
   constexpr int P = 32;
   constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
@@ -203,9 +206,10 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
   const int n = lane & 15, kg = lane >> 4;
   extern __shared__ uint4 smem_raw[];
   uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
+  // S slots per head: score bits [G][S], then positions [G][S]
   uint32_t* sbits = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB) +
-                    (size_t)wave * 2 * G * PS_STAGE;
-  int32_t* spos = reinterpret_cast<int32_t*>(sbits + G * PS_STAGE);
+                    (size_t)wave * 2 * G * S;
+  int32_t* spos = reinterpret_cast<int32_t*>(sbits + G * S);
 
   const int64_t per = ntiles / gridDim.x, extra = ntiles % gridDim.x;
   const int64_t r0 = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
@@ -213,66 +217,102 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 
   int grp = -1;           // KV group (b * Hkv + g) whose fragments are loaded
   bf16x8_t bq[KS];
-  uint32_t Tn = 0;
-  uint32_t scnt = 0;      // staged candidates of head n (lanes with n < G)
+  float Tf = 0.f;         // head n's threshold
+  bool tnan = false;
+  uint32_t scnt = 0;      // staged pairs of head n (lanes with n < G)
+  const bool hl = n < G;  // this lane holds a head
 
-  auto flush_head = [&](int h) {
-    const uint32_t c = (uint32_t)__shfl((int)scnt, h, kWave);
-    if (c == 0) return;
+  // reserve list space for every head's staged pairs: lane h < G holds head h's count
+  auto reserve = [&]() -> uint32_t {
     const int b = grp / Hkv, g = grp % Hkv;
-    const int64_t r = (int64_t)b * Hq + g * G + h;
     uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(&o.cnt[r], c);
-    base = (uint32_t)__shfl((int)base, 0, kWave);
-    for (uint32_t e = lane; e < c; e += 64)
-      if (base + e < (uint32_t)o.capg) {
-        o.cbits[r * o.capg + base + e] = sbits[h * PS_STAGE + e];
-        o.cpos[r * o.capg + base + e] = spos[h * PS_STAGE + e];
-      }
-    if (n == h) scnt = 0;
+    if (lane < G && scnt != 0) base = atomicAdd(&o.cnt[(int64_t)b * Hq + g * G + lane], scnt);
+    return base;
   };
-  auto flush_all = [&]() {
-    for (int h = 0; h < G; ++h) flush_head(h);
+  // copy the staged pairs to the reserved slots (counts and bases broadcast from lane h)
+  auto copy_out = [&](uint32_t base) {
+    const int b = grp / Hkv, g = grp % Hkv;
+    const int64_t rg = (int64_t)b * Hq + g * G;
+    for (int h = 0; h < G; ++h) {
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)scnt, h);
+      if (c == 0) continue;
+      const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)base, h);
+      const int64_t r = rg + h;
+      for (uint32_t e = lane; e < c; e += 64)
+        if (bh + e < (uint32_t)o.capg) {  // streaming stores: the lists are read once, by another kernel
+          __builtin_nontemporal_store(sbits[h * S + e], o.cbits + r * o.capg + bh + e);
+          __builtin_nontemporal_store(spos[h * S + e], o.cpos + r * o.capg + bh + e);
+        }
+    }
+    scnt = 0;
   };
-  auto kbase = [&](int64_t t) {
-    const int gg = (int)(t / tpg);
-    return K + (int64_t)(gg / Hkv) * sb + (int64_t)(gg % Hkv) * sh;
-  };
-  auto load = [&](uint4 (&a)[NI], int64_t t) {
-    const uint16_t* Kb = kbase(t);
-    const int at = (int)(t % tpg) * P;
+  // K rows of tile `tin` of group `g`: whole tiles step by a fixed stride, the last
+  // (partial) tile of a group clamps its rows to L-1
+  const int64_t jstep = (int64_t)RPI * sl;
+  int lg = -1;
+  const uint16_t* lK = K;
+  auto load = [&](uint4 (&a)[NI], int g, int tin) {
+    if (g != lg) {
+      lg = g;
+      lK = K + (int64_t)(g / Hkv) * sb + (int64_t)(g % Hkv) * sh + (lane % CPR) * 8;
+    }
+    const int at = tin * P;
+    if (at + P <= L) {
+      const uint16_t* p = lK + (int64_t)(at + lane / CPR) * sl;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int pos = min(at + j * RPI + lane / CPR, L - 1);
-      a[j] = ld16_stream(Kb + (int64_t)pos * sl + (lane % CPR) * 8);
+      for (int j = 0; j < NI; ++j) a[j] = ld16_stream(p + j * jstep);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int pos = min(at + j * RPI + lane / CPR, L - 1);
+        a[j] = ld16_stream(lK + (int64_t)pos * sl);
+      }
     }
   };
 
+  // tile t = cg * tpg + ct; each wave takes every fourth tile of [r0, r1)
   int64_t t = r0 + wave;
-  uint4 buf[PS_DEPTH + 1][NI];
-#pragma unroll
-  for (int i = 0; i < PS_DEPTH; ++i)
-    if (t + 4 * i < r1) load(buf[i], t + 4 * i);
+  int cg = 0, ct = 0;
+  uint4 cur[NI];
+  if (t < r1) {
+    cg = (int)(t / tpg);
+    ct = (int)(t % tpg);
+    load(cur, cg, ct);
+  }
+  bool pend = false;  // wave-uniform: flush the stage before this tile's pairs are staged
   for (; t < r1; t += 4) {
-    const int tg = (int)(t / tpg);
-    if (tg != grp) {  // new KV group: hand over the old group's candidates, load the new fragments
-      if (grp >= 0) flush_all();
-      grp = tg;
+    int ng = cg, nt = ct + 4;  // the wave's next tile
+    while (nt >= tpg) {
+      nt -= tpg;
+      ++ng;
+    }
+    const uint32_t base = pend ? reserve() : 0u;
+    uint4 nxt[NI];
+    const bool more = t + 4 < r1;
+    if (more) load(nxt, ng, nt);
+    if (pend) {
+      copy_out(base);
+      pend = false;
+    }
+    if (cg != grp) {  // new KV group (its stage is empty): load the fragments and thresholds
+      grp = cg;
       const int b = grp / Hkv, g = grp % Hkv;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < G) v = ld16(q + ((int64_t)(b * Hq + g * G + n)) * D + 32 * s + 8 * kg);
+        if (hl) v = ld16(q + ((int64_t)(b * Hq + g * G + n)) * D + 32 * s + 8 * kg);
         bq[s] = __builtin_bit_cast(bf16x8_t, v);
       }
-      Tn = n < G ? score_key(o.T[(int64_t)b * Hq + g * G + n]) : 0u;
+      const float tv = hl ? o.T[(int64_t)b * Hq + g * G + n] : 0.f;
+      Tf = tv;
+      tnan = tv != tv;
     }
-    if (t + 4 * PS_DEPTH < r1) load(buf[PS_DEPTH], t + 4 * PS_DEPTH);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      *reinterpret_cast<uint4*>(rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = buf[0][j];
+      *reinterpret_cast<uint4*>(rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = cur[j];
     lds_wave_sync();
-    const int pos0 = (int)(t % tpg) * P;
+    const int pos0 = ct * P;
+    const bool whole = pos0 + P <= L;
     bool f[2][4];
     float v[2][4];
     uint32_t c = 0;
@@ -288,8 +328,8 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       for (int i = 0; i < 4; ++i) {
         v[tt][i] = acc[i] * scale;
         const int pos = pos0 + 16 * tt + 4 * kg + i;
-        f[tt][i] = n < G && pos < L && score_key(v[tt][i]) >= Tn;
-        c += f[tt][i];
+        f[tt][i] = hl & (tnan | (v[tt][i] >= Tf)) & (whole | (pos < L));
+        c += f[tt][i] ? 1u : 0u;
       }
     }
     __builtin_amdgcn_wave_barrier();  // operand reads of this tile precede the next tile's writes
@@ -299,31 +339,29 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
     const uint32_t tot = pair + a2;
     const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
-    uint64_t full = ballot(lane < 16 && n < G && scnt + tot > (uint32_t)PS_STAGE);
-    while (full) {  // wave-uniform
-      const int h = __builtin_ctzll(full);
-      full &= full - 1;
-      flush_head(h);
-    }
-    if (n < G) {
+    if (hl) {  // scnt + tot <= S: the stage was flushed when it could not take a whole tile
       uint32_t slot = scnt + pre;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (f[tt][i]) {
-            sbits[n * PS_STAGE + slot] = __float_as_uint(v[tt][i]);
-            spos[n * PS_STAGE + slot] = pos0 + 16 * tt + 4 * kg + i;
+            sbits[n * S + slot] = __float_as_uint(v[tt][i]);
+            spos[n * S + slot] = pos0 + 16 * tt + 4 * kg + i;
             ++slot;
           }
       scnt += tot;
     }
+    // flush before the next tile if a head could overflow on it or it starts another group
+    pend = more && (ng != cg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
+    if (more) {
 #pragma unroll
-    for (int i = 0; i < PS_DEPTH; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) buf[i][j] = buf[i + 1][j];
+      for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
+    }
+    cg = ng;
+    ct = nt;
   }
-  if (grp >= 0) flush_all();
+  if (grp >= 0) copy_out(reserve());
 }
 
 // ---------------------------------------------------------------------------
@@ -600,13 +638,16 @@ template <int D>
 static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
   const int tpg = (a.nrows + 31) / 32;
   const int64_t ntiles = (int64_t)a.B * a.Hkv * tpg;
-  int64_t grid = (int64_t)device_cus() * PS_WPC;
+  // stage slots per head: PS_STAGE_BYTES per wave over G heads x (bits, position)
+  const int S = PS_STAGE_BYTES / (8 * a.G);
+  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * 2 * a.G * S * sizeof(uint32_t);
+  const int fit = (int)(device_lds_limit() / lds);  // workgroups whose LDS fits one CU
+  int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
-  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * 2 * a.G * PS_STAGE * sizeof(uint32_t);
   ensure_dynamic_lds((const void*)score_cand_persistent_kernel<D>, lds);
   hipLaunchKernelGGL((score_cand_persistent_kernel<D>), dim3((unsigned)grid), dim3(256), lds, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl,
-                     a.scale, ntiles, tpg, o);
+                     a.scale, ntiles, tpg, S, o);
 }
 
 void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
