@@ -297,9 +297,11 @@ tka_status check_gather_ptrs(const tka_problem* p, const void* q, const void* K,
 // Used for the bf16 MFMA scan when the kept fraction is small (k' <= L/8) and
 // the row is long. Samples are the first 64 positions of every sample chunk;
 // the threshold is the r-th largest sample with r = 1.75 k' nsamp / L (about
-// 1.75 k' candidates expected), the chunk being chosen so that r >= 200
-// (a shortfall below k' is then a > 6 sigma event for exchangeable scores;
-// it is detected and repaired by a full rescore of the row anyway).
+// 1.75 k' candidates expected), the chunk being chosen so that r >= 100. The
+// fraction of keys at or above the threshold then has a relative spread of
+// about 1/sqrt(r) < 10% for exchangeable scores, so a shortfall below k' is a
+// > 4 sigma event and more than the 3 k' list capacity a > 7 sigma one; both
+// are detected and repaired by a full rescore of the row's group anyway.
 struct PrefilterPlan {
   bool on;
   int sample_chunk, nsamp, r, capg;
@@ -318,7 +320,7 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
   const int64_t L = p->seq_len, kk = p->top_k < p->seq_len ? p->top_k : p->seq_len;
   if (L < 8192 || L > 262144 || kk * 8 > L) return pf;
   int64_t sc = 4096;
-  while (sc > 128 && 7 * kk * sample_count(L, sc) < 4 * 200 * L) sc >>= 1;
+  while (sc > 128 && 7 * kk * sample_count(L, sc) < 4 * 100 * L) sc >>= 1;
   pf.sample_chunk = (int)sc;
   pf.nsamp = (int)sample_count(L, sc);
   pf.r = (int)((7 * kk * pf.nsamp + 4 * L - 1) / (4 * L));

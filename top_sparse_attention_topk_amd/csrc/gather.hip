@@ -14,7 +14,8 @@
 //      groups reduce with xor shuffles) - or takes them from the selected
 //      scores when the caller passes them, skipping the K rows,
 //   3. max / exp / sum per head in fp32 (fixed-order wave reductions),
-//   4. gathers the V rows and accumulates w * V in fp32,
+//   4. gathers the V rows and accumulates w * V in fp32 (K and V rows are read
+//      once: non-temporal loads),
 //   5. writes o (one split) or (M, l, acc) partials merged in split order.
 #include <math.h>
 
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
       for (int u = 0; u < UNR; ++u) {
         const int i = ib + u * RPW + grp;
         const int tk = i < ne ? tok[i] : -1;
-        raw[u] = tk >= 0 ? ld16(Kb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
+        raw[u] = tk >= 0 ? ld16_stream(Kb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
     for (int u = 0; u < UNR; ++u) {
       const int i = ib + u * RPW + grp;
       const int tk = i < ne ? tok[i] : -1;
-      raw[u] = tk >= 0 ? ld16(Vb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
+      raw[u] = tk >= 0 ? ld16_stream(Vb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
