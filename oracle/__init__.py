@@ -52,6 +52,8 @@ def lib():
         L.orc_score.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]
         L.orc_select_f64.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
         L.orc_select_f32.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
+        L.orc_select_adaptive_f32.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
+        L.orc_select_adaptive_f64.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_attend.argtypes = [P, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int32, _vp, _i64, _vp]
         L.orc_decode.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp]
         L.orc_diag_exact.argtypes = [P, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp]
@@ -112,6 +114,28 @@ def select(scores, k: int):
     if rc != 0:
         raise ValueError("bad select arguments")
     return idx
+
+
+def select_adaptive(scores, eps: float, k_min: int, k_max: int):
+    """Certified top-k per row of logits: the smallest k whose top-k keeps >= 1 - eps of the
+    softmax mass, clamped to [max(k_min, 1), min(k_max, len)]. Returns (idx [rows, k_max]
+    ascending then -1, k [rows], tau [rows] = discarded mass of the final k). fp32 input is
+    compared as fp32; masses in fp64."""
+    s = np.ascontiguousarray(scores)
+    if s.ndim == 1:
+        s = s[None, :]
+    n_rows, n = s.shape
+    idx = np.empty((n_rows, k_max), np.int32)
+    k = np.empty(n_rows, np.int32)
+    tau = np.empty(n_rows, np.float64)
+    if s.dtype == np.float32:
+        rc = lib().orc_select_adaptive_f32(_ptr(s), n_rows, n, n, eps, k_min, k_max, _ptr(idx), _ptr(k), _ptr(tau))
+    else:
+        s = s.astype(np.float64)
+        rc = lib().orc_select_adaptive_f64(_ptr(s), n_rows, n, n, eps, k_min, k_max, _ptr(idx), _ptr(k), _ptr(tau))
+    if rc != 0:
+        raise ValueError("bad adaptive select arguments")
+    return idx, k, tau
 
 
 def attend(p: Problem, q, K, V, idx, unit=0, list_mode=2, rows=None):

@@ -214,6 +214,79 @@ int orc_select_f32(const float* s, int64_t n_rows, int64_t len, int64_t stride, 
   return 0;
 }
 
+/* ---- step 2, certified variant: the smallest k meeting a total-variation budget ----
+ * "A Mathematical Theory of Top-k Sparse Attention via Total Variation Distance"
+ * (abstract): the TV distance between the softmax P of a row and its top-k
+ * truncation equals the softmax mass the truncation discards, so the smallest k
+ * with TV <= eps is the smallest k whose top-k (in the select order) holds at
+ * least 1 - eps of the mass. Masses are exp(s_i - max s) in fp64 (NaN: no mass;
+ * an element equal to the maximum has mass 1, also when the maximum is +inf),
+ * the discarded mass of the first k is the sum of the masses after them, added
+ * from the smallest up. k is then clamped to [max(k_min, 1), min(k_max, len)];
+ * tau = discarded mass / total for the final k (NaN when no element has mass).
+ * Kept positions ascending, then -1 up to k_max. */
+static void adaptive_row(vi_t* tmp, int64_t len, double eps, int64_t k_min, int64_t k_max, int32_t* idx,
+                         int32_t* k_out, double* tau_out) {
+  qsort(tmp, (size_t)len, sizeof(vi_t), cmp_rank);
+  double* tail = (double*)malloc(sizeof(double) * (size_t)(len + 1));
+  const double M = (len > 0 && !isnan(tmp[0].v)) ? tmp[0].v : NAN;
+  tail[len] = 0.0;
+  for (int64_t j = len - 1; j >= 0; --j) {
+    const double v = tmp[j].v;
+    const double w = isnan(v) || isnan(M) ? 0.0 : (v == M ? 1.0 : exp(v - M));
+    tail[j] = tail[j + 1] + w;
+  }
+  const double Z = tail[0];
+  int64_t k = len;
+  for (int64_t j = 0; j <= len; ++j)  /* a row without mass needs no key: k = 0 before the clamp */
+    if (tail[j] <= eps * Z) {
+      k = j;
+      break;
+    }
+  int64_t lo = k_min > 1 ? k_min : 1, hi = k_max < len ? k_max : len;
+  if (k < lo) k = lo;
+  if (k > hi) k = hi;
+  *k_out = (int32_t)k;
+  *tau_out = Z > 0.0 ? tail[k] / Z : NAN;
+  for (int64_t j = 0; j < k; ++j) idx[j] = (int32_t)tmp[j].i;
+  qsort(idx, (size_t)k, sizeof(int32_t), cmp_i32);
+  for (int64_t j = k; j < k_max; ++j) idx[j] = -1;
+  free(tail);
+}
+
+/* fp32 logits (exact in double), rows of len at the given stride */
+int orc_select_adaptive_f32(const float* s, int64_t n_rows, int64_t len, int64_t stride, double eps, int64_t k_min,
+                            int64_t k_max, int32_t* idx, int32_t* k_out, double* tau_out) {
+  if (k_max <= 0 || len < 0 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    vi_t* tmp = (vi_t*)malloc(sizeof(vi_t) * (size_t)(len > 0 ? len : 1));
+    for (int64_t i = 0; i < len; ++i) {
+      tmp[i].v = (double)s[r * stride + i];
+      tmp[i].i = i;
+    }
+    adaptive_row(tmp, len, eps, k_min, k_max, idx + r * k_max, k_out + r, tau_out + r);
+    free(tmp);
+  }
+  return 0;
+}
+
+int orc_select_adaptive_f64(const double* s, int64_t n_rows, int64_t len, int64_t stride, double eps, int64_t k_min,
+                            int64_t k_max, int32_t* idx, int32_t* k_out, double* tau_out) {
+  if (k_max <= 0 || len < 0 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    vi_t* tmp = (vi_t*)malloc(sizeof(vi_t) * (size_t)(len > 0 ? len : 1));
+    for (int64_t i = 0; i < len; ++i) {
+      tmp[i].v = s[r * stride + i];
+      tmp[i].i = i;
+    }
+    adaptive_row(tmp, len, eps, k_min, k_max, idx + r * k_max, k_out + r, tau_out + r);
+    free(tmp);
+  }
+  return 0;
+}
+
 /* ---- step 3: exact softmax attention over a kept set ---- */
 
 /* token list of one row: unit 0 = positions; unit b >= 1 = block ids of b keys, plus the current block */
