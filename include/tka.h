@@ -139,6 +139,31 @@ tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int
 tka_status topk_select_workspace_size(int64_t n_rows, int32_t row_len, int32_t k, size_t* bytes);
 
 /*
+ * Certified adaptive top-k ("A Mathematical Theory of Top-k Sparse Attention
+ * via Total Variation Distance", abstract: the total-variation distance
+ * between a softmax P and its top-k truncation equals the softmax mass the
+ * truncation discards). Each row of n = row_len fp32 logits s (P_i ~ exp s_i)
+ * keeps the smallest k whose top-k, in the topk_select order, holds at least
+ * 1 - eps of the mass, clamped to [max(k_min, 1), min(k_max, n)] (a row with
+ * no mass keeps max(k_min, 1)).
+ *   idx_out        [n_rows, k_max] int32: the kept positions ascending, then -1.
+ *   k_out          [n_rows] int32: the kept count k.
+ *   tau_out        [n_rows] fp32: the discarded mass of the kept set over the
+ *                  row total (the certified TV distance; <= eps unless k_max
+ *                  or k_min bound k); NaN for a row with no mass.
+ *   sel_scores_out [n_rows, k_max] fp32 or NULL, as topk_select.
+ * Masses are exp(s_i - max s) in fp32 (an element equal to the maximum has
+ * mass 1, NaN has none) summed in 2^-40 fixed point, so k and tau do not
+ * depend on the order of the parallel sums. eps must be finite and >= 0.
+ * ws/ws_bytes: scratch of at least topk_select_adaptive_workspace_size bytes.
+ */
+tka_status topk_select_adaptive(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, float eps,
+                                int32_t k_min, int32_t k_max, int32_t* idx_out, int32_t* k_out, float* tau_out,
+                                float* sel_scores_out, void* ws, size_t ws_bytes, void* stream);
+
+tka_status topk_select_adaptive_workspace_size(int64_t n_rows, int32_t row_len, int32_t k_max, size_t* bytes);
+
+/*
  * Exact softmax attention over kept positions only ("Sparse Attention in LLM
  * Inference", "Changes in Caching Strategy": batch reads of the KV cache
  * through a position index built from the Top-K result; "Computational and
@@ -178,6 +203,21 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 tka_status topk_decode_workspace_size(const tka_problem* p, size_t* bytes);
+
+/*
+ * The certified step (TKA_SCORE_EXACT only): full exact scores, the adaptive
+ * k of topk_select_adaptive with k_max = p->top_k, then the gather over the
+ * kept positions with their scores as logits. Same kernels as
+ * topk_attn_score -> topk_select_adaptive -> sparse_attn_gather (bitwise
+ * equal results).
+ *   out [B,Hq,d] fp32; idx_out [B,Hq,top_k] (or NULL), k_out [B,Hq] (or NULL),
+ *   tau_out [B,Hq] (or NULL): as topk_select_adaptive.
+ */
+tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                                float eps, int32_t k_min, float* out, int32_t* idx_out, int32_t* k_out,
+                                float* tau_out, void* ws, size_t ws_bytes, void* stream);
+
+tka_status topk_decode_adaptive_workspace_size(const tka_problem* p, size_t* bytes);
 
 /*
  * Block-mean key cache for BLOCK_MEAN ("Sparse Attention Landscape", "Block

@@ -148,3 +148,34 @@ def test_workspace_sizes_scale_with_problem():
     n = tka.topk_decode_workspace_size(c3)
     # score array (repair path) + candidate lists (3k per row) + samples + small buffers
     assert 16 * 64 * 131072 * 4 <= n < 16 * 64 * 131072 * 4 + (192 << 20)
+
+
+def test_adaptive_checks():
+    sel = lambda **kw: LIB.topk_select_adaptive(kw.get("scores", FAKE), kw.get("n_rows", 4), kw.get("row_len", 100),
+                                                kw.get("stride", 100), kw.get("eps", 0.1), kw.get("k_min", 1),
+                                                kw.get("k_max", 10), kw.get("idx", FAKE * 2), kw.get("k", FAKE * 3),
+                                                kw.get("tau", FAKE * 4), kw.get("sel"), kw.get("ws", FAKE * 5),
+                                                kw.get("ws_bytes", 1 << 20), None)
+    assert sel(eps=float("nan")) == tka.TKA_ERR_INVALID_ARG
+    assert sel(eps=-0.1) == tka.TKA_ERR_INVALID_ARG
+    assert sel(eps=float("inf")) == tka.TKA_ERR_INVALID_ARG
+    assert sel(k_max=0) == tka.TKA_ERR_INVALID_ARG
+    assert sel(k_min=-1) == tka.TKA_ERR_INVALID_ARG
+    assert sel(k=None) == tka.TKA_ERR_INVALID_ARG
+    assert sel(tau=FAKE * 3 + 8) == tka.TKA_ERR_INVALID_ARG  # tau_out overlaps k_out
+    assert sel(k=FAKE * 3 + 2) == tka.TKA_ERR_ALIGNMENT
+    need = tka.topk_select_adaptive_workspace_size(4, 100, 10)
+    assert need >= 4 * 12
+    assert sel(ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
+    assert sel(ws=None) == tka.TKA_ERR_WORKSPACE
+    # the certified step is defined on exact attention logits only
+    pb = _p(mode=tka.BLOCK_MEAN, block_size=64)
+    dec = lambda p, **kw: LIB.topk_decode_adaptive(ctypes.byref(p), FAKE, FAKE * 2, FAKE * 3, kw.get("eps", 0.1), 1,
+                                                    FAKE * 5, None, None, None, kw.get("ws", FAKE * 8),
+                                                    kw.get("ws_bytes", 1 << 30), None)
+    assert dec(pb) == tka.TKA_ERR_INVALID_ARG
+    p = _p()
+    need = tka.topk_decode_adaptive_workspace_size(p)
+    assert need >= 2 * 8 * 1000 * 4
+    assert dec(p, ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
+    assert dec(p, eps=float("nan")) == tka.TKA_ERR_INVALID_ARG

@@ -44,7 +44,7 @@ def _load():
     # process, shared with the tensors whose pointers it receives)
     import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     P = ctypes.POINTER(Problem)
     sig = {
         "topk_attn_score": [P, vp, vp, vp, vp, vp],
@@ -56,6 +56,10 @@ def _load():
         "topk_decode": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "topk_decode_workspace_size": [P, ctypes.POINTER(sz)],
         "topk_block_mean_build": [P, vp, vp, vp],
+        "topk_select_adaptive": [vp, i64, i32, i64, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
+        "topk_select_adaptive_workspace_size": [i64, i32, i32, ctypes.POINTER(sz)],
+        "topk_decode_adaptive": [P, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, sz, vp],
+        "topk_decode_adaptive_workspace_size": [P, ctypes.POINTER(sz)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -73,7 +77,9 @@ def _load():
 LIB = _load()
 EXPORTS = ["topk_attn_score", "topk_attn_score_threshold", "topk_select", "topk_select_workspace_size", "sparse_attn_gather",
            "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
-           "topk_block_mean_build", "tka_status_str", "tka_last_error", "tka_abi_version"]
+           "topk_block_mean_build", "topk_select_adaptive", "topk_select_adaptive_workspace_size",
+           "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "tka_status_str", "tka_last_error",
+           "tka_abi_version"]
 
 
 def _check(status: int, fn: str):
@@ -169,6 +175,40 @@ def topk_select(scores, k: int, row_len: int | None = None, row_stride: int | No
     return idx_out, sel_out
 
 
+def topk_select_adaptive_workspace_size(n_rows: int, row_len: int, k_max: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.topk_select_adaptive_workspace_size(n_rows, row_len, k_max, ctypes.byref(n)),
+           "topk_select_adaptive_workspace_size")
+    return n.value
+
+
+def topk_select_adaptive(scores, eps: float, k_min: int, k_max: int, row_len: int | None = None,
+                         row_stride: int | None = None, idx_out=None, k_out=None, tau_out=None, sel_out=None,
+                         want_sel: bool = False, ws=None, stream=None):
+    """Certified top-k of logit rows [..., row_len] fp32 -> (idx [n_rows, k_max], k [n_rows], tau [n_rows],
+    sel [n_rows, k_max] or None)."""
+    import torch
+    row_len = scores.shape[-1] if row_len is None else row_len
+    row_stride = (scores.stride(-2) if scores.dim() > 1 else row_len) if row_stride is None else row_stride
+    n_rows = 1
+    for dim in scores.shape[:-1]:
+        n_rows *= int(dim)
+    if idx_out is None:
+        idx_out = _empty((n_rows, k_max), torch.int32, scores)
+    if k_out is None:
+        k_out = _empty((n_rows,), torch.int32, scores)
+    if tau_out is None:
+        tau_out = _empty((n_rows,), torch.float32, scores)
+    if sel_out is None and want_sel:
+        sel_out = _empty((n_rows, k_max), torch.float32, scores)
+    if ws is None:
+        ws = _ws(topk_select_adaptive_workspace_size(n_rows, row_len, k_max), scores)
+    _check(LIB.topk_select_adaptive(_ptr(scores), n_rows, row_len, row_stride, eps, k_min, k_max, _ptr(idx_out),
+                                    _ptr(k_out), _ptr(tau_out), _ptr(sel_out), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "topk_select_adaptive")
+    return idx_out, k_out, tau_out, sel_out
+
+
 def sparse_attn_gather_workspace_size(p: Problem, n_idx: int, idx_unit: int = 0, shared: bool = False) -> int:
     n = ctypes.c_size_t(0)
     _check(LIB.sparse_attn_gather_workspace_size(ctypes.byref(p), n_idx, idx_unit, int(shared), ctypes.byref(n)),
@@ -212,6 +252,33 @@ def topk_decode(p: Problem, q, k_cache, v_cache, proxy_keys=None, q_idx=None, id
                            _ptr(idx_w), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)),
            "topk_decode")
     return out, idx_out
+
+
+def topk_decode_adaptive_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.topk_decode_adaptive_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "topk_decode_adaptive_workspace_size")
+    return n.value
+
+
+def topk_decode_adaptive(p: Problem, q, k_cache, v_cache, eps: float, k_min: int = 1, out=None, idx_out=None,
+                         k_out=None, tau_out=None, ws=None, stream=None):
+    """Certified decode step (exact scores; k_max = p.top_k). Returns (out, idx, k, tau)."""
+    import torch
+    if out is None:
+        out = _empty((p.batch, p.n_q_heads, p.head_dim), torch.float32, q)
+    if idx_out is None:
+        idx_out = _empty((p.batch, p.n_q_heads, p.top_k), torch.int32, q)
+    if k_out is None:
+        k_out = _empty((p.batch, p.n_q_heads), torch.int32, q)
+    if tau_out is None:
+        tau_out = _empty((p.batch, p.n_q_heads), torch.float32, q)
+    if ws is None:
+        ws = _ws(topk_decode_adaptive_workspace_size(p), q)
+    _check(LIB.topk_decode_adaptive(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), eps, k_min, _ptr(out),
+                                    _ptr(idx_out), _ptr(k_out), _ptr(tau_out), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "topk_decode_adaptive")
+    return out, idx_out, k_out, tau_out
 
 
 def topk_block_mean_build(p: Problem, k_cache, means=None, stream=None):

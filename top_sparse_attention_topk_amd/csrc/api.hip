@@ -473,6 +473,62 @@ tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int
   return launched("topk_select");
 }
 
+// ---- certified adaptive k ----
+namespace {
+struct AdaptiveScratch {
+  size_t W, M, total;
+};
+AdaptiveScratch adaptive_scratch(int64_t n_rows) {
+  AdaptiveScratch a;
+  a.W = 0;
+  a.M = al256(sizeof(uint64_t) * (size_t)n_rows);
+  a.total = a.M + al256(sizeof(float) * (size_t)n_rows);
+  return a;
+}
+tka_status check_adaptive_args(float eps, int32_t k_min, int64_t n_rows, const int32_t* k_out, const float* tau_out,
+                               Range scores_in, Range idx_range) {
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(TKA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (k_min < 0) return fail(TKA_ERR_INVALID_ARG, "k_min must be >= 0");
+  if (n_rows == 0) return TKA_OK;
+  if (!k_out || !tau_out) return fail(TKA_ERR_INVALID_ARG, "k_out and tau_out must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(k_out) & 3) || (reinterpret_cast<uintptr_t>(tau_out) & 3))
+    return fail(TKA_ERR_ALIGNMENT, "k_out and tau_out must be 4-byte aligned");
+  const Range ko = span_of(k_out, sizeof(int32_t) * (size_t)n_rows);
+  const Range to = span_of(tau_out, sizeof(float) * (size_t)n_rows);
+  if (overlap(ko, to) || overlap(ko, scores_in) || overlap(to, scores_in) || overlap(ko, idx_range) ||
+      overlap(to, idx_range))
+    return fail(TKA_ERR_INVALID_ARG, "k_out or tau_out overlaps another buffer");
+  return TKA_OK;
+}
+}  // namespace
+
+tka_status topk_select_adaptive_workspace_size(int64_t n_rows, int32_t row_len, int32_t k_max, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  if (n_rows < 0 || row_len < 0 || k_max < 1) return fail(TKA_ERR_INVALID_ARG, "bad n_rows, row_len or k_max");
+  *bytes = adaptive_scratch(n_rows).total;
+  return ok();
+}
+
+tka_status topk_select_adaptive(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, float eps,
+                                int32_t k_min, int32_t k_max, int32_t* idx_out, int32_t* k_out, float* tau_out,
+                                float* sel_scores_out, void* ws, size_t ws_bytes, void* stream) {
+  tka_status s = check_select_args(scores, n_rows, row_len, row_stride, k_max, idx_out, sel_scores_out);
+  if (s) return s;
+  const Range in = n_rows ? span_of(scores, sizeof(float) * (size_t)((n_rows - 1) * row_stride + row_len)) : Range{};
+  const Range io = n_rows ? span_of(idx_out, sizeof(int32_t) * (size_t)n_rows * k_max) : Range{};
+  if ((s = check_adaptive_args(eps, k_min, n_rows, k_out, tau_out, in, io))) return s;
+  const AdaptiveScratch sc = adaptive_scratch(n_rows);
+  if (!ws || ws_bytes < sc.total)
+    return fail(TKA_ERR_WORKSPACE, "adaptive select needs %zu workspace bytes (got %zu)", sc.total, ws_bytes);
+  if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (n_rows == 0) return ok();
+  char* base = static_cast<char*>(ws);
+  SelectArgs a{scores, n_rows, row_len, row_stride, k_max, idx_out, sel_scores_out};
+  launch_select_adaptive(a, eps, k_min, k_out, reinterpret_cast<uint64_t*>(base + sc.W),
+                         reinterpret_cast<float*>(base + sc.M), tau_out, as_stream(stream));
+  return launched("topk_select_adaptive");
+}
+
 tka_status sparse_attn_gather_workspace_size(const tka_problem* p, int32_t n_idx, int32_t idx_unit,
                                              int32_t shared_across_heads, size_t* bytes) {
   if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
@@ -592,6 +648,102 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
   GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, d.k, d.unit, d.shared, exact ? selv : nullptr, out);
   launch_gather(ga, d.gp, base + d.gather_ws, st);
   return launched("topk_decode");
+}
+
+// ---- certified adaptive step: full exact scores -> adaptive k -> gather ----
+namespace {
+struct AdaptiveLayout {
+  size_t scores, idx, selv, kout, tau, scratch, gather_ws, total;
+  int64_t rows;
+  GatherPlan gp;
+};
+AdaptiveLayout adaptive_layout(const tka_problem* p) {
+  AdaptiveLayout d;
+  d.rows = score_rows(p);
+  const int32_t len = score_len(p);
+  size_t o = 0;
+  d.scores = o;
+  o += al256(sizeof(float) * (size_t)d.rows * (len > 0 ? len : 1));
+  d.idx = o;
+  o += al256(sizeof(int32_t) * (size_t)d.rows * p->top_k);
+  d.selv = o;
+  o += al256(sizeof(float) * (size_t)d.rows * p->top_k);
+  d.kout = o;
+  o += al256(sizeof(int32_t) * (size_t)d.rows);
+  d.tau = o;
+  o += al256(sizeof(float) * (size_t)d.rows);
+  d.scratch = o;
+  o += adaptive_scratch(d.rows).total;
+  d.gather_ws = o;
+  GatherArgs ga = gather_args(p, nullptr, nullptr, nullptr, nullptr, p->top_k, 0, 0, nullptr, nullptr);
+  d.gp = plan_gather(ga);
+  o += al256(d.gp.ws_bytes);
+  d.total = o;
+  return d;
+}
+tka_status check_adaptive_problem(const tka_problem* p) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  if (p->mode != TKA_SCORE_EXACT) return fail(TKA_ERR_INVALID_ARG, "the adaptive step needs TKA_SCORE_EXACT");
+  return check_gather_shape(p, p->top_k, 0, 0, nullptr);
+}
+}  // namespace
+
+tka_status topk_decode_adaptive_workspace_size(const tka_problem* p, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  tka_status s = check_adaptive_problem(p);
+  if (s) return s;
+  *bytes = adaptive_layout(p).total;
+  return ok();
+}
+
+tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                                float eps, int32_t k_min, float* out, int32_t* idx_out, int32_t* k_out,
+                                float* tau_out, void* ws, size_t ws_bytes, void* stream) {
+  tka_status s = check_adaptive_problem(p);
+  if (s) return s;
+  if ((s = check_attn_ptrs(p, q, k_cache, v_cache, out))) return s;
+  const AdaptiveLayout d = adaptive_layout(p);
+  const Range o = span_of(out, out_bytes(p));
+  const Range kv = span_of(k_cache, kv_bytes(p)), vv = span_of(v_cache, kv_bytes(p)), qq = span_of(q, attn_q_bytes(p));
+  Range io{};
+  if (idx_out) {
+    if (reinterpret_cast<uintptr_t>(idx_out) & 3) return fail(TKA_ERR_ALIGNMENT, "idx_out is not 4-byte aligned");
+    io = span_of(idx_out, sizeof(int32_t) * (size_t)d.rows * p->top_k);
+    if (overlap(io, o) || overlap(io, kv) || overlap(io, vv) || overlap(io, qq))
+      return fail(TKA_ERR_INVALID_ARG, "idx_out overlaps another buffer");
+  }
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(TKA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (k_min < 0) return fail(TKA_ERR_INVALID_ARG, "k_min must be >= 0");
+  for (const void* ptr : {(const void*)k_out, (const void*)tau_out}) {
+    if (!ptr) continue;
+    if (reinterpret_cast<uintptr_t>(ptr) & 3) return fail(TKA_ERR_ALIGNMENT, "k_out / tau_out not 4-byte aligned");
+    const Range r = span_of(ptr, sizeof(int32_t) * (size_t)d.rows);
+    if (overlap(r, o) || overlap(r, kv) || overlap(r, vv) || overlap(r, qq) || (idx_out && overlap(r, io)))
+      return fail(TKA_ERR_INVALID_ARG, "k_out or tau_out overlaps another buffer");
+  }
+  if (k_out && tau_out && overlap(span_of(k_out, 4 * (size_t)d.rows), span_of(tau_out, 4 * (size_t)d.rows)))
+    return fail(TKA_ERR_INVALID_ARG, "k_out overlaps tau_out");
+  if (!ws || ws_bytes < d.total)
+    return fail(TKA_ERR_WORKSPACE, "adaptive decode needs %zu workspace bytes (got %zu)", d.total, ws_bytes);
+  if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + d.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx);
+  float* selv = reinterpret_cast<float*>(base + d.selv);
+  int32_t* kk = k_out ? k_out : reinterpret_cast<int32_t*>(base + d.kout);
+  float* tau = tau_out ? tau_out : reinterpret_cast<float*>(base + d.tau);
+  const AdaptiveScratch sc = adaptive_scratch(d.rows);
+  const int32_t len = score_len(p);
+  run_score(p, q, k_cache, nullptr, scores, st);
+  SelectArgs sa{scores, d.rows, len, (int64_t)len, p->top_k, idx, selv};
+  launch_select_adaptive(sa, eps, k_min, kk, reinterpret_cast<uint64_t*>(base + d.scratch + sc.W),
+                         reinterpret_cast<float*>(base + d.scratch + sc.M), tau, st);
+  GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, p->top_k, 0, 0, selv, out);
+  launch_gather(ga, d.gp, base + d.gather_ws, st);
+  return launched("topk_decode_adaptive");
 }
 
 tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, float* means, void* stream) {

@@ -87,6 +87,10 @@ void launch_block_mean(const BlockMeanArgs& a, hipStream_t st);
 size_t select_workspace_bytes(int64_t n_rows, int n, int k);
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 // one workgroup per row, only rows whose flag is nonzero
+// certified adaptive k per row (a.k = k_max): counts to kout, then the kept positions
+// (row select with per-row counts), then tau; W [n_rows] and M [n_rows] are scratch
+void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
+                            float* tau, hipStream_t st);
 void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st);
 
 // candidate prefilter of the fused exact step (select.hip)

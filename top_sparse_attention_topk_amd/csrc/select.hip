@@ -294,7 +294,8 @@ __device__ void emit_segments(Get get, uint32_t cnt, uint32_t T, uint32_t need_e
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void select_rows_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                          int capw, const uint32_t* __restrict__ row_flag) {
+                                                          int capw, const uint32_t* __restrict__ row_flag,
+                                                          const int32_t* __restrict__ krow) {
   if (row_flag && row_flag[blockIdx.x] == 0) return;  // only the rows flagged for a full select
   extern __shared__ uint4 smem_raw[];
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem_raw);
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float* __restric
   const float* s = S + row * stride;
   int32_t* oidx = idx + row * k;
   float* osel = sel ? sel + row * k : nullptr;
-  const int kk = min(k, n);
+  const int kk = min(krow ? min(krow[row], k) : k, n);  // krow: a count per row, at most k (the row stride)
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   for (int j = kk + t; j < k; j += ST) {
     oidx[j] = -1;
@@ -781,6 +782,195 @@ static SplitLayout split_layout(int64_t n_rows, int n) {
   return L;
 }
 
+// ---------------------------------------------------------------------------
+// Certified adaptive k ("A Mathematical Theory of Top-k Sparse Attention via
+// Total Variation Distance", abstract): the total-variation distance between
+// a row's softmax P and its top-k truncation is the mass the truncation
+// discards, so the smallest k with TV <= eps is the smallest prefix of the
+// select order holding at least 1 - eps of the mass. Found by the same radix
+// search over score keys, with histograms of mass next to the counts.
+// Masses: w = exp(s - max) in fp32 (an element equal to the maximum: 1; NaN:
+// 0), as floor(w * 2^40) in uint64, so every sum is exact and independent of
+// the order of the atomics. The kept mass must reach need = W - floor(eps W)
+// (W: the row total). Elements with the threshold key T all carry the same
+// mass w_T, so after the keys above T the ties (lowest positions first, as in
+// the select order) are taken ceil(rest / w_T) at a time. k is clamped to
+// [max(k_min, 1), min(k_max, n)]; a row without mass keeps max(k_min, 1).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t ak_mass(float v, float M) {
+  if (v != v) return 0;
+  const float w = (v == M) ? 1.f : expf(v - M);
+  return (uint64_t)(w * 1099511627776.f);  // 2^40: exact scaling, the conversion truncates
+}
+
+struct AkSmem {
+  uint64_t mass[NB0];
+  uint32_t cnt[NB0];
+  uint64_t wm[SW];
+  uint32_t wc[SW];
+  uint32_t wk[SW];
+  uint64_t res_mass;
+  uint32_t res_bin, res_cnt;
+};
+
+// Bin b (of nb, bins ascending with the key) where the mass of the bins above
+// it stays below need and reaching into b meets it. Writes the bin, the mass
+// and the count of the bins above it to sm.res_*.
+__device__ void ak_find_bin(AkSmem& sm, int nb, uint64_t need) {
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int per = nb / ST;
+  uint64_t m = 0;
+  uint32_t c = 0;
+  for (int i = 0; i < per; ++i) {
+    m += sm.mass[t * per + i];
+    c += sm.cnt[t * per + i];
+  }
+  // inclusive prefix over threads (bins ascending), then the part above this thread's bins
+  uint64_t im = m;
+  uint32_t ic = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t ym = __shfl_up(im, o, kWave);
+    const uint32_t yc = __shfl_up(ic, o, kWave);
+    if (lane >= o) {
+      im += ym;
+      ic += yc;
+    }
+  }
+  if (lane == 63) {
+    sm.wm[w] = im;
+    sm.wc[w] = ic;
+  }
+  __syncthreads();
+  uint64_t tm = 0;
+  uint32_t tc = 0;
+  for (int i = 0; i < SW; ++i) {
+    if (i < w) {
+      im += sm.wm[i];
+      ic += sm.wc[i];
+    }
+    tm += sm.wm[i];
+    tc += sm.wc[i];
+  }
+  const uint64_t above = tm - im;
+  uint32_t cabove = tc - ic;
+  if (above < need && need <= above + m) {
+    uint64_t acc = above;
+    for (int i = per - 1; i >= 0; --i) {
+      const int b = t * per + i;
+      if (acc + sm.mass[b] >= need) {
+        sm.res_bin = (uint32_t)b;
+        sm.res_mass = acc;
+        sm.res_cnt = cabove;
+        break;
+      }
+      acc += sm.mass[b];
+      cabove += sm.cnt[b];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict__ S, int n, int64_t stride, float eps,
+                                                         int k_min, int k_max, int32_t* __restrict__ kout,
+                                                         uint64_t* __restrict__ Wout, float* __restrict__ Mout) {
+  __shared__ AkSmem sm;
+  const int64_t row = blockIdx.x;
+  const float* s = S + row * stride;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  // 1. the row maximum in the select order (NaN lowest)
+  uint32_t mk = 0;
+  for (int p = t; p < n; p += ST) mk = max(mk, score_key(s[p]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, kWave));
+  if (lane == 0) sm.wk[w] = mk;
+  __syncthreads();
+  mk = 0;
+  for (int i = 0; i < SW; ++i) mk = max(mk, sm.wk[i]);
+  const float M = mk ? key_value(mk) : __int_as_float(0x7fc00000);  // no number in the row: no mass
+  // 2. digit by digit: mass and count histograms of the keys inside the current prefix
+  uint64_t need = 0, W = 0, m_gt = 0;
+  uint32_t c_gt = 0, prefix = 0;
+  int64_t k_eps = 0;
+  bool found = true;
+  for (int lv = 0; lv <= 2; ++lv) {
+    const int nb = lv_bins(lv);
+    for (int i = t; i < nb; i += ST) {
+      sm.mass[i] = 0;
+      sm.cnt[i] = 0;
+    }
+    __syncthreads();
+    for (int p = t; p < n; p += ST) {
+      const float v = s[p];
+      const uint32_t key = score_key(v);
+      if (lv_in_range(key, lv, prefix)) {
+        const uint32_t d = lv_digit(key, lv);
+        atomicAdd(&sm.cnt[d], 1u);
+        const uint64_t m = ak_mass(v, M);
+        if (m) atomicAdd(reinterpret_cast<unsigned long long*>(&sm.mass[d]), (unsigned long long)m);
+      }
+    }
+    __syncthreads();
+    if (lv == 0) {
+      uint64_t part = 0;
+      for (int i = t; i < nb; i += ST) part += sm.mass[i];
+      part = wave_sum(part);
+      if (lane == 0) sm.wm[w] = part;
+      __syncthreads();
+      for (int i = 0; i < SW; ++i) W += sm.wm[i];
+      __syncthreads();
+      const double drop = floor((double)eps * (double)W);
+      need = drop >= (double)W ? 0 : W - (uint64_t)drop;
+      if (need == 0) {
+        found = false;  // nothing to keep for the budget
+        break;
+      }
+    }
+    ak_find_bin(sm, nb, need - m_gt);
+    m_gt += sm.res_mass;
+    c_gt += sm.res_cnt;
+    prefix = (prefix << lv_bits(lv)) | sm.res_bin;
+    __syncthreads();
+  }
+  if (found) {  // the ties at T: ceil(rest / w_T) of them
+    const uint64_t wT = ak_mass(key_value(prefix), M);
+    const uint64_t rest = need - m_gt;
+    k_eps = (int64_t)c_gt + (int64_t)((rest + wT - 1) / wT);
+  }
+  if (t == 0) {
+    const int64_t lo = k_min > 1 ? k_min : 1, hi = k_max < n ? k_max : n;
+    int64_t k = k_eps < lo ? lo : k_eps;
+    if (k > hi) k = hi;
+    kout[row] = (int32_t)k;
+    Wout[row] = W;
+    Mout[row] = M;
+  }
+}
+
+// tau = 1 - (mass of the kept positions) / W, the kept mass summed exactly.
+__global__ __launch_bounds__(256) void adaptive_tau_kernel(const float* __restrict__ S, int64_t stride,
+                                                           const int32_t* __restrict__ idx, int k_max,
+                                                           const int32_t* __restrict__ kout,
+                                                           const uint64_t* __restrict__ W,
+                                                           const float* __restrict__ Mrow, float* __restrict__ tau) {
+  __shared__ uint64_t part[SW];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const float M = Mrow[row];
+  const int ke = kout[row];
+  uint64_t kept = 0;
+  for (int j = t; j < ke; j += ST) kept += ak_mass(S[row * stride + idx[row * k_max + j]], M);
+  kept = wave_sum(kept);
+  if (lane == 0) part[w] = kept;
+  __syncthreads();
+  if (t == 0) {
+    uint64_t tot = 0;
+    for (int i = 0; i < SW; ++i) tot += part[i];
+    const uint64_t Wr = W[row];
+    tau[row] = Wr ? (float)((double)(Wr - tot) / (double)Wr) : __int_as_float(0x7fc00000);
+  }
+}
+
 size_t select_workspace_bytes(int64_t n_rows, int n, int k) {
   (void)k;
   if (!use_split(n_rows, n)) return 0;
@@ -850,7 +1040,21 @@ void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, h
   size_t lds;
   const int capw = rows_capw(a.n, a.k, &lds);
   hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k,
-                     a.idx, a.sel, capw, row_flag);
+                     a.idx, a.sel, capw, row_flag, (const int32_t*)nullptr);
+}
+
+void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
+                            float* tau, hipStream_t st) {
+  if (a.n_rows <= 0) return;
+  const unsigned rows = (unsigned)a.n_rows;
+  hipLaunchKernelGGL(adaptive_k_kernel, dim3(rows), dim3(ST), 0, st, a.scores, a.n, a.stride, eps, k_min, a.k, kout,
+                     W, M);
+  size_t lds;
+  const int capw = rows_capw(a.n, a.k, &lds);
+  hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel,
+                     capw, (const uint32_t*)nullptr, (const int32_t*)kout);
+  hipLaunchKernelGGL(adaptive_tau_kernel, dim3(rows), dim3(ST), 0, st, a.scores, a.stride, a.idx, a.k,
+                     (const int32_t*)kout, (const uint64_t*)W, (const float*)M, tau);
 }
 
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
@@ -859,7 +1063,7 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
     size_t lds;
     const int capw = rows_capw(a.n, a.k, &lds);
     hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride,
-                       a.k, a.idx, a.sel, capw, (const uint32_t*)nullptr);
+                       a.k, a.idx, a.sel, capw, (const uint32_t*)nullptr, (const int32_t*)nullptr);
     return;
   }
   const SplitLayout L = split_layout(a.n_rows, a.n);
