@@ -365,6 +365,32 @@ def main():
                       "score_threshold": None if t_thr is None else round(t_thr, 4)},
         "roofline": roofline,
     }
+    # adjacent paths on the same inputs (each timed alone on the launch stream)
+    extras = {}
+    if exact:
+        log("[bench] certified adaptive k")
+        eps = 0.9  # the synthetic caches spread their softmax mass widely: tau(k = 4096) is about 0.8
+        ak_idx = torch.empty((rows, w.k), dtype=torch.int32, device="cuda")
+        ak_k = torch.empty(rows, dtype=torch.int32, device="cuda")
+        ak_tau = torch.empty(rows, dtype=torch.float32, device="cuda")
+        ak_ws = torch.empty(max(tka.topk_select_adaptive_workspace_size(rows, sc.shape[-1], w.k), 1),
+                            dtype=torch.uint8, device="cuda")
+        t_ak = time_loop(lambda: tka.topk_select_adaptive(sc.reshape(rows, -1), eps, 1, w.k, idx_out=ak_idx,
+                                                          k_out=ak_k, tau_out=ak_tau, ws=ak_ws), args.steps)
+        del ak_ws
+        torch.cuda.empty_cache()
+        ad_out = torch.empty_like(out)
+        ad_ws = torch.empty(tka.topk_decode_adaptive_workspace_size(p), dtype=torch.uint8, device="cuda")
+        t_ad = time_loop(lambda: tka.topk_decode_adaptive(p, qt, Kt, Vt, eps, 1, out=ad_out, idx_out=ak_idx,
+                                                          k_out=ak_k, tau_out=ak_tau, ws=ad_ws), args.steps)
+        kf = ak_k.float()
+        extras["adaptive"] = {"eps": eps, "k_max": w.k, "select_ms": round(t_ak, 4),
+                              "select_score_gbps": round(4 * rows * sc.shape[-1] / (t_ak / 1e3) / 1e9, 1),
+                              "decode_ms": round(t_ad, 4), "decode_queries_per_s": round(w.B / (t_ad / 1e3), 1),
+                              "k_mean": round(float(kf.mean()), 1), "k_min": int(ak_k.min()),
+                              "k_max_seen": int(ak_k.max()), "tau_max": round(float(ak_tau.max()), 5)}
+        del ad_ws, ak_idx
+    result["extras"] = extras
     del Kt, Vt, sc, ws
     torch.cuda.empty_cache()
     if args.copy_calibration:

@@ -52,6 +52,7 @@ def lib():
         L.orc_score.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]
         L.orc_select_f64.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
         L.orc_select_f32.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
+        L.orc_encode_e4m3.argtypes = [_vp, _i64, _vp]
         L.orc_select_adaptive_f32.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_select_adaptive_f64.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_attend.argtypes = [P, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int32, _vp, _i64, _vp]
@@ -136,6 +137,14 @@ def select_adaptive(scores, eps: float, k_min: int, k_max: int):
     if rc != 0:
         raise ValueError("bad adaptive select arguments")
     return idx, k, tau
+
+
+def encode_e4m3(x):
+    """fp32 values -> OCP E4M3FN codes (nearest, ties to even mantissa, saturating at +-448, NaN -> 0x7f)."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_encode_e4m3(_ptr(x), x.size, _ptr(out))
+    return out
 
 
 def attend(p: Problem, q, K, V, idx, unit=0, list_mode=2, rows=None):

@@ -70,6 +70,33 @@ double orc_dec_e4m3(uint8_t c) {
   return s ? -v : v;
 }
 
+/* Encoding to OCP E4M3FN for keys stored in the indexer cache (the appended
+ * low-dimensional key of "Sparse Attention Landscape", "Token Sparse
+ * Attention"): the finite code nearest to |x|, a tie going to the code with an
+ * even mantissa; |x| >= 448 (the largest finite value, infinities included)
+ * saturates to 448; NaN encodes as 0x7f; the sign bit is kept (also for 0).
+ * Found by looking at every code: plain and slow on purpose. */
+static uint8_t enc_e4m3(double x) {
+  if (isnan(x)) return 0x7f;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs(x);
+  if (a >= 448.0) return sign | 0x7e;
+  int best = 0;
+  double dbest = a;
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double dc = fabs(orc_dec_e4m3((uint8_t)c) - a);
+    if (dc < dbest || (dc == dbest && (c & 1) == 0)) {
+      best = c;
+      dbest = dc;
+    }
+  }
+  return sign | (uint8_t)best;
+}
+
+void orc_encode_e4m3(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = enc_e4m3((double)x[i]);
+}
+
 static double ld(const void* p, int dt, int64_t i) {
   if (dt == ODT_F32) return (double)((const float*)p)[i];
   if (dt == ODT_BF16) return orc_dec_bf16(((const uint16_t*)p)[i]);
