@@ -53,6 +53,7 @@ def lib():
         L.orc_select_f64.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
         L.orc_select_f32.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
         L.orc_encode_e4m3.argtypes = [_vp, _i64, _vp]
+        L.orc_block_means.argtypes = [P, _vp, _vp]
         L.orc_select_adaptive_f32.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_select_adaptive_f64.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_attend.argtypes = [P, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int32, _vp, _i64, _vp]
@@ -137,6 +138,14 @@ def select_adaptive(scores, eps: float, k_min: int, k_max: int):
     if rc != 0:
         raise ValueError("bad adaptive select arguments")
     return idx, k, tau
+
+
+def block_means(p: Problem, K):
+    """fp64 block-mean keys [B, Hkv, ceil(L/b), d] of the block variant (partial last block included)."""
+    m = (p.L + p.block - 1) // p.block
+    out = np.empty((p.B, p.Hkv, m, p.d), np.float64)
+    lib().orc_block_means(ctypes.byref(p), _ptr(K), _ptr(out))
+    return out
 
 
 def encode_e4m3(x):

@@ -181,6 +181,26 @@ int orc_score(const orc_problem* p, const void* q, const void* K, const void* qI
   return 0;
 }
 
+/* Block-mean keys of the block variant, all m = ceil(L/b) blocks (the partial
+ * last one over its own keys): means[b,g,j,c] = (1/n_j) sum over block j of
+ * K[b,g,i,c] ("Sparse Attention Landscape", "Block Sparse Attention": MoBA
+ * mean-pools the keys of each block). fp64, [B,Hkv,m,d] contiguous. */
+int orc_block_means(const orc_problem* p, const void* K, double* means) {
+  const int64_t m = n_blocks(p);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < p->B; ++b)
+    for (int64_t g = 0; g < p->Hkv; ++g)
+      for (int64_t j = 0; j < m; ++j) {
+        const int64_t i0 = j * p->block, i1 = (i0 + p->block < p->L) ? i0 + p->block : p->L;
+        double* mu = means + ((b * p->Hkv + g) * m + j) * p->d;
+        for (int64_t c = 0; c < p->d; ++c) mu[c] = 0;
+        for (int64_t i = i0; i < i1; ++i)
+          for (int64_t c = 0; c < p->d; ++c) mu[c] += ld(K, p->dt, kv_off(p, b, g, i) + c);
+        for (int64_t c = 0; c < p->d; ++c) mu[c] /= (double)(i1 - i0);
+      }
+  return 0;
+}
+
 /* ---- step 2: exact top-k under the total order ---- */
 
 typedef struct {

@@ -169,3 +169,26 @@ def test_indexer_single_head_relu_order_and_all_negative():
     s2 = orc.score(p, qI=qI, kI=kneg, w=w)[0]
     assert (s2 == 0).all()
     assert orc.select(s2, k)[0].tolist() == list(range(k))
+
+
+def test_block_means_pins():
+    """Block-mean keys: b = 1 gives K itself; a block of equal keys has that key as its mean;
+    the partial last block divides by its own length; <q, mean_j> is the block score."""
+    w = fx.shrink(fx.WORKLOADS["C4"], 64 * 5 + 9, B=1)
+    q, K, _ = fx.make_attn(w)
+    p = orc.problem_for(w)
+    Kd = orc.decode_values(w.dtype, K).reshape(w.B, w.Hkv, w.L, w.d)
+    qd = orc.decode_values(w.dtype, q).reshape(w.B, w.Hq, w.d)
+    mu = orc.block_means(p, K)
+    m = mu.shape[2]
+    assert m == 6
+    np.testing.assert_allclose(mu[:, :, -1], Kd[:, :, 5 * 64:].sum(2) / 9, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(mu[:, :, 2], Kd[:, :, 128:192].sum(2) / 64, rtol=1e-13, atol=1e-13)
+    s = orc.score(p, q, K)
+    want = np.stack([mu[0, h // w.G, : m - 1] @ qd[0, h] for h in range(w.Hq)])
+    np.testing.assert_allclose(s, want, rtol=1e-12, atol=1e-12)
+    p.block = 1
+    assert np.array_equal(orc.block_means(p, K), Kd)
+    p.block = w.block
+    const = np.repeat(K[:, :, :1], w.L, axis=2).copy()  # every key equal to the first
+    assert np.array_equal(orc.block_means(p, const), np.repeat(Kd[:, :, :1], m, axis=2))
