@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TKA_ABI_VERSION 1
+#define TKA_ABI_VERSION 2
 
 typedef enum {
   TKA_OK = 0,
@@ -89,15 +89,21 @@ typedef struct {
   int32_t n_idx_heads; /* INDEXER: H_I in [1, 128] */
   int32_t idx_dim;     /* INDEXER: d_I, a multiple of 64 up to 256 */
   tka_dtype idx_dtype; /* INDEXER: TKA_FP8_E4M3 */
+  int32_t block_capacity; /* BLOCK_MEAN: block slots per (b, KV head) of the block-mean buffer, >= ceil(L/b),
+                             so a buffer sized for the longest sequence serves every length; 0 = ceil(L/b) */
+  int32_t idx_capacity;   /* INDEXER: positions per sequence of the indexer-key buffer, >= L (the same for the
+                             indexer keys of every length); 0 = L */
 } tka_problem;
 
 /*
  * Scoring pass (one of the three variants above), writes fp32 scores.
  *   EXACT:      q [B,Hq,d]; keys = K cache; scores [B,Hq,L].
- *   BLOCK_MEAN: q [B,Hq,d]; keys = block means [B,Hkv,m,d] fp32 contiguous (from
- *               topk_block_mean_build); scores [B,Hq,m-1] (the current block does
- *               not compete). Nothing is written when m == 1.
- *   INDEXER:    q = qI [B,H_I,d_I] E4M3FN; keys = kI [B,L,d_I] E4M3FN;
+ *   BLOCK_MEAN: q [B,Hq,d]; keys = block means [B,Hkv,mc,d] fp32 contiguous (from
+ *               topk_block_mean_build; mc = block_capacity, or m if 0); scores
+ *               [B,Hq,m-1] (the current block does not compete). Nothing is
+ *               written when m == 1.
+ *   INDEXER:    q = qI [B,H_I,d_I] E4M3FN; keys = kI [B,Lc,d_I] E4M3FN (Lc =
+ *               idx_capacity, or L if 0; positions >= L unread);
  *               idx_w [B,H_I] fp32; scores [B,L].
  * idx_w must be NULL unless mode is INDEXER.
  */
@@ -192,9 +198,9 @@ tka_status sparse_attn_gather_workspace_size(const tka_problem* p, int32_t n_idx
  * the same kernels and launch shapes as the three calls above (bitwise equal
  * results).
  *   EXACT:      proxy_keys, q_idx, idx_w NULL; the gather uses the selected scores.
- *   BLOCK_MEAN: proxy_keys = block means [B,Hkv,m,d] fp32; idx_out (if given)
+ *   BLOCK_MEAN: proxy_keys = block means [B,Hkv,mc,d] fp32; idx_out (if given)
  *               [B,Hq,k] block ids without the current block.
- *   INDEXER:    proxy_keys = kI [B,L,d_I], q_idx = qI [B,H_I,d_I], idx_w [B,H_I];
+ *   INDEXER:    proxy_keys = kI [B,Lc,d_I], q_idx = qI [B,H_I,d_I], idx_w [B,H_I];
  *               idx_out (if given) [B,k].
  * idx_out may be NULL (the indices then live in the workspace).
  */
@@ -222,11 +228,32 @@ tka_status topk_decode_adaptive_workspace_size(const tka_problem* p, size_t* byt
 /*
  * Block-mean key cache for BLOCK_MEAN ("Sparse Attention Landscape", "Block
  * Sparse Attention": MoBA mean-pools the keys of each block): means[b,g,j,:] =
- * (1/n_j) sum over the n_j keys of block j of K[b,g,i,:], fp32, [B,Hkv,m,d]
- * contiguous, m = ceil(L/b) (the last block may be partial). Built once, off
- * the decode step.
+ * (1/n_j) sum over the n_j keys of block j of K[b,g,i,:], fp32, [B,Hkv,mc,d]
+ * contiguous (mc = block_capacity, or m = ceil(L/b) if 0), blocks j < m
+ * written (the last block may be partial; slots j >= m are left as they are).
+ * Built once, off the decode step; topk_cache_append keeps it current.
  */
 tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, float* means, void* stream);
+
+/*
+ * Append one decode step to the caches ("Sparse Attention in LLM Inference",
+ * "Changes in Caching Strategy": the sparse layer reads its cache through a
+ * position index, so the caches hold one row per position). p->seq_len = L is
+ * the length after the append; the new token goes to position L-1. Any group
+ * below may be skipped by passing NULL for all of its pointers.
+ *   k_new, v_new [B,Hkv,d] in qkv_dtype, contiguous: to row L-1 of every
+ *     (b, KV head) of k_cache / v_cache (strides from p).
+ *   means (BLOCK_MEAN only) [B,Hkv,mc,d] fp32 (as topk_block_mean_build): the mean of block
+ *     (L-1)/b is recomputed from k_cache after the append, bitwise what
+ *     topk_block_mean_build writes for length L ("Sparse Attention Landscape",
+ *     "Block Sparse Attention": MoBA mean-pools each block's keys).
+ *   kI_new (INDEXER only) [B,d_I] fp32 -> kI_cache [B,Lc,d_I] row L-1 as OCP
+ *     E4M3FN: nearest code, ties to even, |x| >= 448 saturates to 448, NaN ->
+ *     0x7f (the low-dimensional indexer keys of "Sparse Attention Landscape",
+ *     "Token Sparse Attention").
+ */
+tka_status topk_cache_append(const tka_problem* p, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const float* kI_new, void* kI_cache, float* means, void* stream);
 
 const char* tka_status_str(tka_status s);
 /* detail of the last failed argument check in the calling thread ("" if none) */

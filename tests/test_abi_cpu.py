@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     missing = [n for n in names if n not in exported]
     assert not missing, missing
-    assert LIB.tka_abi_version() == 1
+    assert LIB.tka_abi_version() == 2
 
 
 def _status(code):
@@ -179,3 +179,27 @@ def test_adaptive_checks():
     assert need >= 2 * 8 * 1000 * 4
     assert dec(p, ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
     assert dec(p, eps=float("nan")) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_cache_append_checks():
+    p = _p()
+    app = lambda p, **kw: LIB.topk_cache_append(ctypes.byref(p), kw.get("kn", FAKE), kw.get("vn", FAKE * 2),
+                                                kw.get("K", FAKE * 3), kw.get("V", FAKE * 4), kw.get("kin"),
+                                                kw.get("kic"), kw.get("means"), None)
+    assert app(p, vn=None) == tka.TKA_ERR_INVALID_ARG          # both new rows or neither
+    assert app(p, K=None) == tka.TKA_ERR_INVALID_ARG
+    assert app(p, kn=FAKE + 8) == tka.TKA_ERR_ALIGNMENT
+    assert app(p, vn=FAKE * 3 + 256) == tka.TKA_ERR_INVALID_ARG  # v_new inside the K cache
+    assert app(p, means=FAKE * 6) == tka.TKA_ERR_INVALID_ARG     # means only for the block variant
+    assert app(p, kin=FAKE * 6, kic=FAKE * 7) == tka.TKA_ERR_INVALID_ARG  # indexer keys only for the indexer
+    pb = _p(mode=tka.BLOCK_MEAN, block_size=64)
+    assert app(pb, means=FAKE * 3 + 512) == tka.TKA_ERR_INVALID_ARG  # means overlapping the K cache
+    pi = _p(mode=tka.INDEXER, n_idx_heads=32, idx_dim=64)
+    assert app(pi, kin=FAKE * 6) == tka.TKA_ERR_INVALID_ARG      # kI_cache missing
+    assert app(pi, kin=FAKE * 6 + 2, kic=FAKE * 7) == tka.TKA_ERR_ALIGNMENT
+    # the block-mean capacity must hold every block
+    small = _p(mode=tka.BLOCK_MEAN, block_size=64, seq_len=1000)
+    small.block_capacity = 15  # ceil(1000 / 64) = 16
+    assert _score(small) == tka.TKA_ERR_INVALID_ARG
+    small.block_capacity = 16
+    assert _score(small) != tka.TKA_ERR_INVALID_ARG or LIB.tka_last_error().decode().find("capacity") < 0

@@ -5,9 +5,10 @@ Argument marshalling only: every step runs in the HIP kernels behind the C ABI
 HIP stream are handed to the library as integers. Importing this package
 raises ImportError when libtka.so has not been built - there is no fallback.
 
-The names match the C entry points: topk_attn_score, topk_select,
-sparse_attn_gather, topk_decode, topk_block_mean_build and the workspace-size
-queries.
+The names match the C entry points: topk_attn_score,
+topk_attn_score_threshold, topk_select, topk_select_adaptive,
+sparse_attn_gather, topk_decode, topk_decode_adaptive, topk_cache_append,
+topk_block_mean_build and the workspace-size queries.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ class Problem(ctypes.Structure):
                 ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
                 ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("mode", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
-                ("idx_dtype", ctypes.c_int32)]
+                ("idx_dtype", ctypes.c_int32), ("block_capacity", ctypes.c_int32), ("idx_capacity", ctypes.c_int32)]
 
 
 def _load():
@@ -56,6 +57,7 @@ def _load():
         "topk_decode": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "topk_decode_workspace_size": [P, ctypes.POINTER(sz)],
         "topk_block_mean_build": [P, vp, vp, vp],
+        "topk_cache_append": [P, vp, vp, vp, vp, vp, vp, vp, vp],
         "topk_select_adaptive": [vp, i64, i32, i64, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
         "topk_select_adaptive_workspace_size": [i64, i32, i32, ctypes.POINTER(sz)],
         "topk_decode_adaptive": [P, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, sz, vp],
@@ -78,7 +80,8 @@ LIB = _load()
 EXPORTS = ["topk_attn_score", "topk_attn_score_threshold", "topk_select", "topk_select_workspace_size", "sparse_attn_gather",
            "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
            "topk_block_mean_build", "topk_select_adaptive", "topk_select_adaptive_workspace_size",
-           "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "tka_status_str", "tka_last_error",
+           "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "topk_cache_append", "tka_status_str",
+           "tka_last_error",
            "tka_abi_version"]
 
 
@@ -104,11 +107,11 @@ def _stream(stream):
 
 def problem(mode: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int, top_k: int,
             dtype: int = TKA_BF16, scale: float = 0.0, block_size: int = 0, n_idx_heads: int = 0, idx_dim: int = 0,
-            strides=None) -> Problem:
+            strides=None, block_capacity: int = 0, idx_capacity: int = 0) -> Problem:
     """tka_problem; strides default to a contiguous [B, Hkv, L, d] cache."""
     sb, sh, sl = strides if strides is not None else (n_kv_heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     return Problem(batch, n_q_heads, n_kv_heads, head_dim, seq_len, top_k, sb, sh, sl, dtype, scale, mode,
-                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3)
+                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3, block_capacity, idx_capacity)
 
 
 def score_shape(p: Problem):
@@ -284,11 +287,18 @@ def topk_decode_adaptive(p: Problem, q, k_cache, v_cache, eps: float, k_min: int
 def topk_block_mean_build(p: Problem, k_cache, means=None, stream=None):
     import torch
     if means is None:
-        m = (p.seq_len + p.block_size - 1) // p.block_size
+        m = p.block_capacity or (p.seq_len + p.block_size - 1) // p.block_size
         means = _empty((p.batch, p.n_kv_heads, m, p.head_dim), torch.float32, k_cache)
     _check(LIB.topk_block_mean_build(ctypes.byref(p), _ptr(k_cache), _ptr(means), _stream(stream)),
            "topk_block_mean_build")
     return means
+
+
+def topk_cache_append(p: Problem, k_new=None, v_new=None, k_cache=None, v_cache=None, kI_new=None, kI_cache=None,
+                      means=None, stream=None):
+    """Append the step's new rows at position p.seq_len - 1 (and refresh the block mean / encode the indexer key)."""
+    _check(LIB.topk_cache_append(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(kI_new), _ptr(kI_cache), _ptr(means), _stream(stream)), "topk_cache_append")
 
 
 def abi_version() -> int:

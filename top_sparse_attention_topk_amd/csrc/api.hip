@@ -82,6 +82,11 @@ tka_status check_attn_shape(const tka_problem* p) {
     return fail(TKA_ERR_ALIGNMENT, "KV strides must be multiples of 16 bytes");
   if (p->mode == TKA_SCORE_BLOCK_MEAN && p->block_size < 1)
     return fail(TKA_ERR_INVALID_ARG, "block_size must be >= 1 (got %d)", p->block_size);
+  if (p->block_capacity < 0 ||
+      (p->mode == TKA_SCORE_BLOCK_MEAN && p->block_capacity > 0 && p->block_capacity < n_blocks(p)))
+    return fail(TKA_ERR_INVALID_ARG, "block_capacity %d is below ceil(seq_len / block_size)", p->block_capacity);
+  if (p->idx_capacity < 0 || (p->mode == TKA_SCORE_INDEXER && p->idx_capacity > 0 && p->idx_capacity < p->seq_len))
+    return fail(TKA_ERR_INVALID_ARG, "idx_capacity %d is below seq_len", p->idx_capacity);
   if (p->mode == TKA_SCORE_INDEXER) {
     if (p->n_idx_heads < 1 || p->n_idx_heads > 128)
       return fail(p->n_idx_heads < 1 ? TKA_ERR_INVALID_ARG : TKA_ERR_UNSUPPORTED, "n_idx_heads %d not in [1, 128]",
@@ -107,6 +112,10 @@ tka_status launched(const char* what) {
   return ok();
 }
 
+// block slots per (b, KV head) in the block-mean buffer; positions per sequence in the indexer-key buffer
+int64_t mean_slots(const tka_problem* p) { return p->block_capacity > 0 ? p->block_capacity : n_blocks(p); }
+int64_t idx_slots(const tka_problem* p) { return p->idx_capacity > 0 ? p->idx_capacity : p->seq_len; }
+
 ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys, float* scores) {
   ScoreArgs a;
   a.q = q;
@@ -119,10 +128,10 @@ ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys
   a.d = p->head_dim;
   a.q_bf16 = p->qkv_dtype == TKA_BF16;
   if (p->mode == TKA_SCORE_BLOCK_MEAN) {
-    const int64_t m = n_blocks(p);
+    const int64_t m = n_blocks(p), mc = mean_slots(p);
     a.nrows = (int)(m - 1);
-    a.sb = (int64_t)p->n_kv_heads * m * p->head_dim;
-    a.sh = m * p->head_dim;
+    a.sb = (int64_t)p->n_kv_heads * mc * p->head_dim;
+    a.sh = mc * p->head_dim;
     a.sl = p->head_dim;
     a.scale = 1.0f;
     a.bf16 = 0;
@@ -152,8 +161,8 @@ size_t q_bytes(const tka_problem* p) {
 
 size_t proxy_bytes(const tka_problem* p) {
   if (p->mode == TKA_SCORE_BLOCK_MEAN)
-    return sizeof(float) * (size_t)p->batch * p->n_kv_heads * n_blocks(p) * p->head_dim;
-  if (p->mode == TKA_SCORE_INDEXER) return (size_t)p->batch * p->seq_len * p->idx_dim;
+    return sizeof(float) * (size_t)p->batch * p->n_kv_heads * mean_slots(p) * p->head_dim;
+  if (p->mode == TKA_SCORE_INDEXER) return (size_t)p->batch * idx_slots(p) * p->idx_dim;
   return kv_bytes(p);
 }
 
@@ -188,6 +197,7 @@ void run_score(const tka_problem* p, const void* q, const void* keys, const floa
     a.HI = p->n_idx_heads;
     a.dI = p->idx_dim;
     a.L = p->seq_len;
+    a.Lc = (int)idx_slots(p);
     launch_score_indexer(a, st);
   } else {
     launch_score_dense(dense_score_args(p, q, keys, scores), st);
@@ -476,13 +486,14 @@ tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int
 // ---- certified adaptive k ----
 namespace {
 struct AdaptiveScratch {
-  size_t W, M, total;
+  size_t W, M, flag, total;
 };
 AdaptiveScratch adaptive_scratch(int64_t n_rows) {
   AdaptiveScratch a;
   a.W = 0;
   a.M = al256(sizeof(uint64_t) * (size_t)n_rows);
-  a.total = a.M + al256(sizeof(float) * (size_t)n_rows);
+  a.flag = a.M + al256(sizeof(float) * (size_t)n_rows);
+  a.total = a.flag + al256(sizeof(uint32_t) * (size_t)n_rows);
   return a;
 }
 tka_status check_adaptive_args(float eps, int32_t k_min, int64_t n_rows, const int32_t* k_out, const float* tau_out,
@@ -525,7 +536,8 @@ tka_status topk_select_adaptive(const float* scores, int64_t n_rows, int32_t row
   char* base = static_cast<char*>(ws);
   SelectArgs a{scores, n_rows, row_len, row_stride, k_max, idx_out, sel_scores_out};
   launch_select_adaptive(a, eps, k_min, k_out, reinterpret_cast<uint64_t*>(base + sc.W),
-                         reinterpret_cast<float*>(base + sc.M), tau_out, as_stream(stream));
+                         reinterpret_cast<float*>(base + sc.M), reinterpret_cast<uint32_t*>(base + sc.flag), tau_out,
+                         as_stream(stream));
   return launched("topk_select_adaptive");
 }
 
@@ -740,7 +752,8 @@ tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void*
   run_score(p, q, k_cache, nullptr, scores, st);
   SelectArgs sa{scores, d.rows, len, (int64_t)len, p->top_k, idx, selv};
   launch_select_adaptive(sa, eps, k_min, kk, reinterpret_cast<uint64_t*>(base + d.scratch + sc.W),
-                         reinterpret_cast<float*>(base + d.scratch + sc.M), tau, st);
+                         reinterpret_cast<float*>(base + d.scratch + sc.M),
+                         reinterpret_cast<uint32_t*>(base + d.scratch + sc.flag), tau, st);
   GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, p->top_k, 0, 0, selv, out);
   launch_gather(ga, d.gp, base + d.gather_ws, st);
   return launched("topk_decode_adaptive");
@@ -761,13 +774,80 @@ tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, floa
   a.d = p->head_dim;
   a.L = p->seq_len;
   a.bsz = p->block_size;
-  a.m = (int)n_blocks(p);
+  a.m = (int)mean_slots(p);
   a.sb = p->kv_stride_b;
   a.sh = p->kv_stride_h;
   a.sl = p->kv_stride_l;
   a.bf16 = p->qkv_dtype == TKA_BF16;
+  a.j0 = 0;
+  a.j1 = (int)n_blocks(p);
   launch_block_mean(a, as_stream(stream));
   return launched("topk_block_mean_build");
+}
+
+tka_status topk_cache_append(const tka_problem* p, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const float* kI_new, void* kI_cache, float* means, void* stream) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  const bool kv = k_new || v_new;
+  if (kv) {
+    if ((s = need_ptr(k_new, "k_new")) || (s = need_ptr(v_new, "v_new")) || (s = need_ptr(k_cache, "k_cache")) ||
+        (s = need_ptr(v_cache, "v_cache")))
+      return s;
+  }
+  if (means) {
+    if (p->mode != TKA_SCORE_BLOCK_MEAN) return fail(TKA_ERR_INVALID_ARG, "means only with TKA_SCORE_BLOCK_MEAN");
+    if ((s = need_ptr(means, "means")) || (s = need_ptr(k_cache, "k_cache"))) return s;
+  }
+  if (kI_new || kI_cache) {
+    if (p->mode != TKA_SCORE_INDEXER) return fail(TKA_ERR_INVALID_ARG, "kI_new/kI_cache only with TKA_SCORE_INDEXER");
+    if ((s = need_ptr(kI_new, "kI_new", false)) || (s = need_ptr(kI_cache, "kI_cache", false))) return s;
+    if (reinterpret_cast<uintptr_t>(kI_new) & 3) return fail(TKA_ERR_ALIGNMENT, "kI_new is not 4-byte aligned");
+  }
+  const size_t row_bytes = (size_t)p->head_dim * esize(p->qkv_dtype);
+  const size_t new_bytes = row_bytes * (size_t)p->batch * p->n_kv_heads;
+  const Range kc = k_cache ? span_of(k_cache, kv_bytes(p)) : Range{}, vc = v_cache ? span_of(v_cache, kv_bytes(p)) : Range{};
+  if (kv) {
+    const Range kn = span_of(k_new, new_bytes), vn = span_of(v_new, new_bytes);
+    if (overlap(kc, vc) || overlap(kn, kc) || overlap(kn, vc) || overlap(vn, kc) || overlap(vn, vc))
+      return fail(TKA_ERR_INVALID_ARG, "the new rows or the caches overlap");
+  }
+  if (means) {
+    const Range mo = span_of(means, proxy_bytes(p));
+    if (overlap(mo, kc) || overlap(mo, vc)) return fail(TKA_ERR_INVALID_ARG, "means overlaps a cache");
+  }
+  if (kI_cache) {
+    const Range ko = span_of(kI_cache, proxy_bytes(p));
+    if (overlap(ko, span_of(kI_new, sizeof(float) * (size_t)p->batch * p->idx_dim)) || overlap(ko, kc) ||
+        overlap(ko, vc))
+      return fail(TKA_ERR_INVALID_ARG, "kI_cache overlaps another buffer");
+  }
+  hipStream_t st = as_stream(stream);
+  const int pos = p->seq_len - 1;
+  if (kv)
+    launch_append_rows(k_new, v_new, k_cache, v_cache, p->batch, p->n_kv_heads, (int)row_bytes,
+                       (int)esize(p->qkv_dtype), p->kv_stride_b, p->kv_stride_h, p->kv_stride_l, pos, st);
+  if (means) {  // the block holding pos, recomputed from the cache as topk_block_mean_build does
+    BlockMeanArgs a;
+    a.K = k_cache;
+    a.means = means;
+    a.B = p->batch;
+    a.Hkv = p->n_kv_heads;
+    a.d = p->head_dim;
+    a.L = p->seq_len;
+    a.bsz = p->block_size;
+    a.m = (int)mean_slots(p);
+    a.sb = p->kv_stride_b;
+    a.sh = p->kv_stride_h;
+    a.sl = p->kv_stride_l;
+    a.bf16 = p->qkv_dtype == TKA_BF16;
+    a.j0 = pos / p->block_size;
+    a.j1 = a.j0 + 1;
+    launch_block_mean(a, st);
+  }
+  if (kI_cache)
+    launch_append_indexer(kI_new, static_cast<uint8_t*>(kI_cache), p->batch, p->idx_dim, (int)idx_slots(p), pos, st);
+  return launched("topk_cache_append");
 }
 
 }  // extern "C"

@@ -19,10 +19,11 @@ struct ScoreArgs {
 
 struct IndexerArgs {
   const uint8_t* qI;  // [B,HI,dI]
-  const uint8_t* kI;  // [B,L,dI]
+  const uint8_t* kI;  // [B,Lc,dI]
   const float* w;     // [B,HI]
   float* scores;      // [B,L]
   int B, HI, dI, L;
+  int Lc;             // positions per sequence in kI (>= L)
 };
 
 struct BlockMeanArgs {
@@ -31,6 +32,7 @@ struct BlockMeanArgs {
   int B, Hkv, d, L, bsz, m;
   int64_t sb, sh, sl;
   int bf16;
+  int j0 = 0, j1 = 0;  // blocks [j0, j1) only (j1 = 0: all m)
 };
 
 struct SelectArgs {
@@ -83,14 +85,18 @@ void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, h
 void launch_score_dense(const ScoreArgs& a, hipStream_t st);
 void launch_score_indexer(const IndexerArgs& a, hipStream_t st);
 void launch_block_mean(const BlockMeanArgs& a, hipStream_t st);
+// append one position of every (b, KV head) row (16-byte rows) and/or encode indexer keys
+void launch_append_rows(const void* knew, const void* vnew, void* K, void* V, int B, int Hkv, int row_bytes, int es,
+                        int64_t sb, int64_t sh, int64_t sl, int pos, hipStream_t st);
+void launch_append_indexer(const float* kI_new, uint8_t* kI, int B, int dI, int Lc, int pos, hipStream_t st);
 
 size_t select_workspace_bytes(int64_t n_rows, int n, int k);
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 // one workgroup per row, only rows whose flag is nonzero
-// certified adaptive k per row (a.k = k_max): counts to kout, then the kept positions
-// (row select with per-row counts), then tau; W [n_rows] and M [n_rows] are scratch
+// certified adaptive k per row (a.k = k_max): counts to kout and the kept positions, then
+// tau; W, M and row_flag [n_rows] are scratch
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
-                            float* tau, hipStream_t st);
+                            uint32_t* row_flag, float* tau, hipStream_t st);
 void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st);
 
 // candidate prefilter of the fused exact step (select.hip)

@@ -456,7 +456,7 @@ template <int DI, int NT>
 __global__ __launch_bounds__(256) void score_indexer_kernel(const uint8_t* __restrict__ qI,
                                                             const uint8_t* __restrict__ kI,
                                                             const float* __restrict__ w, float* __restrict__ S,
-                                                            int HI, int L, int chunk) {
+                                                            int HI, int L, int Lc, int chunk) {
   constexpr int KS = DI / 64;
   constexpr int UNR = 4;
   const int b = blockIdx.y;
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(256) void score_indexer_kernel(const uint8_t* __res
         wt[t][4 * a + c] = hh < HI ? w[(int64_t)b * HI + hh] : 0.f;
       }
   }
-  const uint8_t* kb = kI + (int64_t)b * L * DI;
+  const uint8_t* kb = kI + (int64_t)b * Lc * DI;
   float* Sb = S + (int64_t)b * L;
   const int p0 = blockIdx.x * chunk;
   const int p1 = min(p0 + chunk, L);
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256) void score_indexer_kernel(const uint8_t* __res
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void block_mean_kernel(const void* __restrict__ Kv, float* __restrict__ means,
                                                          int Hkv, int L, int bsz, int m, int64_t sb, int64_t sh,
-                                                         int64_t sl) {
+                                                         int64_t sl, int j0, int j1) {
   using U = Unpack<BF16>;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPL = U::N;
@@ -546,8 +546,8 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const void* __restrict_
   const int b = task / Hkv, g = task % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPR, grp = lane / LPR;
-  const int j = blockIdx.x * 4 + wave;
-  if (j >= m) return;
+  const int j = j0 + blockIdx.x * 4 + wave;  // blocks [j0, j1) of the m
+  if (j >= j1) return;
   const int i0 = j * bsz, i1 = min(i0 + bsz, L);
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(Kv) + ((int64_t)b * sb + (int64_t)g * sh) * ES;
   float acc[EPL];
@@ -716,7 +716,7 @@ static void launch_idx_t(const IndexerArgs& a, hipStream_t st) {
   const int chunk = pick_chunk(a.L, a.B, 512, 512, 8192);
   dim3 grid((a.L + chunk - 1) / chunk, a.B);
   hipLaunchKernelGGL((score_indexer_kernel<DI, NT>), grid, dim3(256), 0, st, a.qI, a.kI, a.w, a.scores, a.HI, a.L,
-                     chunk);
+                     a.Lc > 0 ? a.Lc : a.L, chunk);
 }
 
 template <int DI>
@@ -733,19 +733,21 @@ void launch_score_indexer(const IndexerArgs& a, hipStream_t st) {
 
 template <bool BF16>
 static void launch_bm(const BlockMeanArgs& a, hipStream_t st) {
-  dim3 grid((a.m + 3) / 4, a.B * a.Hkv);
+  const int j0 = a.j0, j1 = a.j1 > 0 ? a.j1 : a.m;
+  if (j1 <= j0) return;
+  dim3 grid((j1 - j0 + 3) / 4, a.B * a.Hkv);
   switch (a.d) {
     case 64:
       hipLaunchKernelGGL((block_mean_kernel<BF16, 64>), grid, dim3(256), 0, st, a.K, a.means, a.Hkv, a.L, a.bsz, a.m,
-                         a.sb, a.sh, a.sl);
+                         a.sb, a.sh, a.sl, j0, j1);
       break;
     case 128:
       hipLaunchKernelGGL((block_mean_kernel<BF16, 128>), grid, dim3(256), 0, st, a.K, a.means, a.Hkv, a.L, a.bsz,
-                         a.m, a.sb, a.sh, a.sl);
+                         a.m, a.sb, a.sh, a.sl, j0, j1);
       break;
     default:
       hipLaunchKernelGGL((block_mean_kernel<BF16, 256>), grid, dim3(256), 0, st, a.K, a.means, a.Hkv, a.L, a.bsz,
-                         a.m, a.sb, a.sh, a.sl);
+                         a.m, a.sb, a.sh, a.sl, j0, j1);
       break;
   }
 }

@@ -812,6 +812,7 @@ struct AkSmem {
   uint64_t res_mass;
   uint32_t res_bin, res_cnt;
 };
+static_assert(sizeof(SelSmem) <= sizeof(uint64_t) * NB0, "the emission state lives in the mass histogram");
 
 // Bin b (of nb, bins ascending with the key) where the mass of the bins above
 // it stays below need and reaching into b meets it. Writes the bin, the mass
@@ -871,16 +872,36 @@ __device__ void ak_find_bin(AkSmem& sm, int nb, uint64_t need) {
   __syncthreads();
 }
 
+// One workgroup per row; wave w streams its own segment [r0, r1) of the row
+// (UNR float4 loads in flight per lane), as the count-based row select does.
+// Rows whose k is the unclamped budget answer emit their kept set here (every
+// key above T, then the first `ties` keys equal to T in position order);
+// rows held by k_min or k_max, or without mass, are flagged for the
+// count-based row select with their k.
 __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict__ S, int n, int64_t stride, float eps,
                                                          int k_min, int k_max, int32_t* __restrict__ kout,
-                                                         uint64_t* __restrict__ Wout, float* __restrict__ Mout) {
+                                                         uint64_t* __restrict__ Wout, float* __restrict__ Mout,
+                                                         int32_t* __restrict__ idx, float* __restrict__ sel,
+                                                         uint32_t* __restrict__ row_flag) {
   __shared__ AkSmem sm;
   const int64_t row = blockIdx.x;
   const float* s = S + row * stride;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  const int seg = ((n + 4 * SW - 1) / (4 * SW)) * 4;
+  const int r0 = min(n, w * seg), r1 = min(n, r0 + seg);
   // 1. the row maximum in the select order (NaN lowest)
   uint32_t mk = 0;
-  for (int p = t; p < n; p += ST) mk = max(mk, score_key(s[p]));
+  for (int base = r0; base < r1; base += 256 * UNR) {
+    float v[UNR][4];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (base + u * 256 + 4 * lane + j < r1) mk = max(mk, score_key(v[u][j]));
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, kWave));
   if (lane == 0) sm.wk[w] = mk;
@@ -900,15 +921,22 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
       sm.cnt[i] = 0;
     }
     __syncthreads();
-    for (int p = t; p < n; p += ST) {
-      const float v = s[p];
-      const uint32_t key = score_key(v);
-      if (lv_in_range(key, lv, prefix)) {
-        const uint32_t d = lv_digit(key, lv);
-        atomicAdd(&sm.cnt[d], 1u);
-        const uint64_t m = ak_mass(v, M);
-        if (m) atomicAdd(reinterpret_cast<unsigned long long*>(&sm.mass[d]), (unsigned long long)m);
-      }
+    for (int base = r0; base < r1; base += 256 * UNR) {
+      float v[UNR][4];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t key = score_key(v[u][j]);
+          if (base + u * 256 + 4 * lane + j < r1 && lv_in_range(key, lv, prefix)) {
+            const uint32_t d = lv_digit(key, lv);
+            atomicAdd(&sm.cnt[d], 1u);
+            const uint64_t m = ak_mass(v[u][j], M);
+            if (m) atomicAdd(reinterpret_cast<unsigned long long*>(&sm.mass[d]), (unsigned long long)m);
+          }
+        }
     }
     __syncthreads();
     if (lv == 0) {
@@ -932,19 +960,38 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
     prefix = (prefix << lv_bits(lv)) | sm.res_bin;
     __syncthreads();
   }
+  uint32_t ties = 0;
   if (found) {  // the ties at T: ceil(rest / w_T) of them
     const uint64_t wT = ak_mass(key_value(prefix), M);
     const uint64_t rest = need - m_gt;
-    k_eps = (int64_t)c_gt + (int64_t)((rest + wT - 1) / wT);
+    ties = (uint32_t)((rest + wT - 1) / wT);
+    k_eps = (int64_t)c_gt + ties;
   }
+  const int64_t lo = k_min > 1 ? k_min : 1, hi = k_max < n ? k_max : n;
+  int64_t k = k_eps < lo ? lo : k_eps;
+  if (k > hi) k = hi;
   if (t == 0) {
-    const int64_t lo = k_min > 1 ? k_min : 1, hi = k_max < n ? k_max : n;
-    int64_t k = k_eps < lo ? lo : k_eps;
-    if (k > hi) k = hi;
     kout[row] = (int32_t)k;
     Wout[row] = W;
     Mout[row] = M;
   }
+  const bool direct = found && k == k_eps;
+  if (t == 0) row_flag[row] = direct ? 0u : 1u;
+  if (!direct) return;  // workgroup-uniform
+  // 3. emit: every key above T and the first `ties` keys equal to T, in position order (the
+  // emission state reuses the mass histogram, whose last reads ended at the barrier above)
+  int32_t* oidx = idx + row * k_max;
+  float* osel = sel ? sel + row * k_max : nullptr;
+  for (int j = (int)k + t; j < k_max; j += ST) {
+    oidx[j] = -1;
+    if (osel) osel[j] = -INFINITY;
+  }
+  emit_segments(
+      [&](uint32_t e, uint32_t& bits, int32_t& pos) {
+        pos = r0 + (int)e;
+        bits = __float_as_uint(s[pos]);
+      },
+      (uint32_t)(r1 - r0), prefix, ties, *reinterpret_cast<SelSmem*>(sm.mass), oidx, osel, (uint32_t)k);
 }
 
 // tau = 1 - (mass of the kept positions) / W, the kept mass summed exactly.
@@ -1044,15 +1091,16 @@ void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, h
 }
 
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
-                            float* tau, hipStream_t st) {
+                            uint32_t* row_flag, float* tau, hipStream_t st) {
   if (a.n_rows <= 0) return;
   const unsigned rows = (unsigned)a.n_rows;
   hipLaunchKernelGGL(adaptive_k_kernel, dim3(rows), dim3(ST), 0, st, a.scores, a.n, a.stride, eps, k_min, a.k, kout,
-                     W, M);
+                     W, M, a.idx, a.sel, row_flag);
+  // rows whose k is held by k_min / k_max or that have no mass: the count-based row select
   size_t lds;
   const int capw = rows_capw(a.n, a.k, &lds);
   hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel,
-                     capw, (const uint32_t*)nullptr, (const int32_t*)kout);
+                     capw, (const uint32_t*)row_flag, (const int32_t*)kout);
   hipLaunchKernelGGL(adaptive_tau_kernel, dim3(rows), dim3(ST), 0, st, a.scores, a.stride, a.idx, a.k,
                      (const int32_t*)kout, (const uint64_t*)W, (const float*)M, tau);
 }
