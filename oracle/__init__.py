@@ -54,6 +54,7 @@ def lib():
         L.orc_select_f32.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
         L.orc_encode_e4m3.argtypes = [_vp, _i64, _vp]
         L.orc_block_means.argtypes = [P, _vp, _vp]
+        L.orc_hisa_decode.argtypes = [P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.orc_select_adaptive_f32.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_select_adaptive_f64.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_attend.argtypes = [P, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int32, _vp, _i64, _vp]
@@ -146,6 +147,23 @@ def block_means(p: Problem, K):
     out = np.empty((p.B, p.Hkv, m, p.d), np.float64)
     lib().orc_block_means(ctypes.byref(p), _ptr(K), _ptr(out))
     return out
+
+
+def hisa_decode(p: Problem, KB: int, q, K, V):
+    """Two-level selection (top-KB blocks by <q, block mean>, then top-k tokens among their keys by the
+    exact score) and attention over the kept tokens. Returns (out [B*Hq, d], idx [B*Hq, k] positions,
+    blk [B*Hq, KB] block ids, block scores [B*Hq, m])."""
+    m = (p.L + p.block - 1) // p.block
+    n = p.B * p.Hq
+    out = np.empty((n, p.d), np.float64)
+    idx = np.empty((n, p.k), np.int32)
+    blk = np.empty((n, KB), np.int32)
+    bs = np.empty((n, m), np.float64)
+    rc = lib().orc_hisa_decode(ctypes.byref(p), KB, _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(idx), _ptr(blk),
+                               _ptr(bs))
+    if rc != 0:
+        raise ValueError("oracle two-level decode failed")
+    return out, idx, blk, bs
 
 
 def encode_e4m3(x):

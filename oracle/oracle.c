@@ -429,6 +429,63 @@ int orc_decode(const orc_problem* p, const void* q, const void* K, const void* V
 }
 
 /*
+ * Two-level (hierarchical) selection, "Sparse Attention Landscape",
+ * "Hierarchical Sparse Attention": a coarse score r_j = f_block(q_t, B_j) for
+ * every block, the top-K_B blocks kept, token scores s_i = f_token(q_t, k_i)
+ * only for the tokens of those blocks, the top-k of them kept, attention over
+ * those. Here f_block = <q, mean of the block's keys> (no scale; the mean as
+ * in the block variant, the partial last block over its own keys; every one
+ * of the m = ceil(L/b) blocks competes) and f_token = scale * <q, k_i>. Both
+ * selections use the select order (ties to the lower block / position).
+ * All rows: blk_out [B*Hq, KB] (ascending, -1 pad), idx_out [B*Hq, k] token
+ * positions (ascending, -1 pad), out [B*Hq, d]; blk_scores [B*Hq, m] or NULL.
+ */
+int orc_hisa_decode(const orc_problem* p, int64_t KB, const void* q, const void* K, const void* V, double* out,
+                    int32_t* idx_out, int32_t* blk_out, double* blk_scores) {
+  if (KB < 1 || p->block < 1 || p->k < 1) return -1;
+  const int64_t m = n_blocks(p), n_rows = (int64_t)p->B * p->Hq, G = p->Hq / p->Hkv;
+  const double sc = attn_scale(p);
+  double* means = (double*)malloc(sizeof(double) * (size_t)(p->B * p->Hkv * m * p->d));
+  if (!means) return -2;
+  orc_block_means(p, K, means);
+  int rc = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t b = r / p->Hq, h = r % p->Hq, g = h / G;
+    double* rj = (double*)malloc(sizeof(double) * (size_t)m);
+    for (int64_t j = 0; j < m; ++j) {
+      const double* mu = means + ((b * p->Hkv + g) * m + j) * p->d;
+      double s = 0;
+      for (int64_t c = 0; c < p->d; ++c) s += ld(q, p->dt, (b * p->Hq + h) * p->d + c) * mu[c];
+      rj[j] = s;
+      if (blk_scores) blk_scores[r * m + j] = s;
+    }
+    int32_t* blk = blk_out + r * KB;
+    orc_select_f64(rj, 1, m, m, KB, blk);
+    /* candidate tokens of the kept blocks, ascending (blocks ascend, tokens inside ascend) */
+    int64_t nc = 0;
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)(KB * p->block));
+    for (int64_t j = 0; j < KB; ++j) {
+      if (blk[j] < 0) continue;
+      const int64_t i0 = (int64_t)blk[j] * p->block, i1 = (i0 + p->block < p->L) ? i0 + p->block : p->L;
+      for (int64_t i = i0; i < i1; ++i) tok[nc++] = i;
+    }
+    vi_t* tmp = (vi_t*)malloc(sizeof(vi_t) * (size_t)(nc > 0 ? nc : 1));
+    for (int64_t e = 0; e < nc; ++e) {
+      tmp[e].v = sc * qk(p, q, K, b, h, tok[e]);
+      tmp[e].i = tok[e];  /* ranked by position among equal scores */
+    }
+    select_row(tmp, nc, p->k, idx_out + r * p->k);
+    free(tmp);
+    free(tok);
+    free(rj);
+  }
+  free(means);
+  if (rc) return rc;
+  return orc_attend(p, q, K, V, idx_out, p->k, 0, 0, NULL, n_rows, out);
+}
+
+/*
  * Diagnostics of one exact-variant row given its kept set (token positions,
  * -1 ignored). Full softmax P over all L keys, P-hat = P / (1 - tau) on the
  * kept set and 0 elsewhere.
