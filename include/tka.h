@@ -71,14 +71,20 @@ typedef enum {
   /* I[b,i] = sum_j w[b,j] * max(0, <qI[b,j], kI[b,i]>), no scale; one kept set per
      sequence, shared by every head. ("Sparse Attention Landscape", "Token Sparse
      Attention", lightning indexer with query-dependent head weights.) */
-  TKA_SCORE_INDEXER = 2
+  TKA_SCORE_INDEXER = 2,
+  /* Two levels ("Sparse Attention Landscape", "Hierarchical Sparse Attention"):
+     r[b,h,j] = <q[b,h], mean of K[b,g(h)] over block j> for every block j < m
+     (no scale; the partial last block competes too), the top_blocks blocks
+     kept; then the exact scores scale * <q, K_i> of their tokens only, the
+     top_k tokens kept (topk_hisa_decode). */
+  TKA_SCORE_HISA = 3
 } tka_score_mode;
 
 typedef struct {
   int32_t batch;      /* B >= 1 */
   int32_t n_q_heads;  /* Hq >= 1, a multiple of n_kv_heads */
   int32_t n_kv_heads; /* Hkv >= 1 */
-  int32_t head_dim;   /* d: 32, 64, 128 or 256 */
+  int32_t head_dim;   /* d: 64, 128 or 256 */
   int32_t seq_len;    /* L >= 1 cached keys; the query sits at position L-1 (no causal mask) */
   int32_t top_k;      /* k >= 1 tokens (EXACT, INDEXER) or blocks (BLOCK_MEAN); k' = min(k, candidates) */
   int64_t kv_stride_b, kv_stride_h, kv_stride_l; /* element strides of the K and V caches */
@@ -93,6 +99,8 @@ typedef struct {
                              so a buffer sized for the longest sequence serves every length; 0 = ceil(L/b) */
   int32_t idx_capacity;   /* INDEXER: positions per sequence of the indexer-key buffer, >= L (the same for the
                              indexer keys of every length); 0 = L */
+  int32_t top_blocks;     /* HISA: K_B >= 1, the blocks kept by the coarse level (block_size, block_capacity
+                             as for BLOCK_MEAN) */
 } tka_problem;
 
 /*
@@ -102,6 +110,8 @@ typedef struct {
  *               topk_block_mean_build; mc = block_capacity, or m if 0); scores
  *               [B,Hq,m-1] (the current block does not compete). Nothing is
  *               written when m == 1.
+ *   HISA:       q [B,Hq,d]; keys = block means as for BLOCK_MEAN; scores
+ *               [B,Hq,m]: the coarse score of every block.
  *   INDEXER:    q = qI [B,H_I,d_I] E4M3FN; keys = kI [B,Lc,d_I] E4M3FN (Lc =
  *               idx_capacity, or L if 0; positions >= L unread);
  *               idx_w [B,H_I] fp32; scores [B,L].
@@ -224,6 +234,30 @@ tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void*
                                 float* tau_out, void* ws, size_t ws_bytes, void* stream);
 
 tka_status topk_decode_adaptive_workspace_size(const tka_problem* p, size_t* bytes);
+
+/*
+ * The two-level step (mode TKA_SCORE_HISA; "Sparse Attention Landscape",
+ * "Hierarchical Sparse Attention": the fine scores run only over the tokens
+ * of the top_blocks blocks with the best coarse scores, about K_B b of them
+ * instead of L). Coarse scores of every block from the block means, the top
+ * K_B blocks (select order), the exact scores of their tokens, the top
+ * k' = min(top_k, their token count) tokens (select order, ties to the lower
+ * position), attention over those with their exact scores as logits.
+ *   means [B,Hkv,mc,d] fp32 from topk_block_mean_build (mode HISA or
+ *     BLOCK_MEAN layout).
+ *   out [B,Hq,d] fp32; idx_out [B,Hq,top_k] token positions ascending, -1
+ *     after k' (or NULL).
+ *   Optional (NULL: kept in the workspace): blk_out [B,Hq,K_B] the kept
+ *     blocks ascending, -1 padded; block_scores_out [B,Hq,m] the coarse
+ *     scores; cand_scores_out [B,Hq,K_B*b]: entry j*b+i is the exact score of
+ *     token blk[j]*b+i, NaN where that is no token (blk[j] = -1 or past L).
+ */
+tka_status topk_hisa_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                            const float* means, float* out, int32_t* idx_out, int32_t* blk_out,
+                            float* block_scores_out, float* cand_scores_out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+tka_status topk_hisa_decode_workspace_size(const tka_problem* p, size_t* bytes);
 
 /*
  * Block-mean key cache for BLOCK_MEAN ("Sparse Attention Landscape", "Block

@@ -203,3 +203,22 @@ def test_cache_append_checks():
     assert _score(small) == tka.TKA_ERR_INVALID_ARG
     small.block_capacity = 16
     assert _score(small) != tka.TKA_ERR_INVALID_ARG or LIB.tka_last_error().decode().find("capacity") < 0
+
+
+def test_hisa_checks():
+    p = _p(mode=tka.HISA, block_size=64, top_blocks=8, top_k=100)
+    call = lambda p, **kw: LIB.topk_hisa_decode(ctypes.byref(p), FAKE, FAKE * 2, FAKE * 3, kw.get("means", FAKE * 6),
+                                                FAKE * 5, kw.get("idx"), kw.get("blk"), None, None,
+                                                kw.get("ws", FAKE * 8), kw.get("ws_bytes", 1 << 30), None)
+    need = tka.topk_hisa_decode_workspace_size(p)
+    assert need > 0
+    assert call(p, ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
+    assert call(p, means=None) == tka.TKA_ERR_INVALID_ARG
+    assert call(p, idx=FAKE * 5 + 4) == tka.TKA_ERR_INVALID_ARG    # idx_out inside out
+    assert call(p, blk=FAKE * 9, idx=FAKE * 9) == tka.TKA_ERR_INVALID_ARG  # two outputs overlapping
+    assert call(_p(mode=tka.HISA, block_size=64, top_blocks=0)) == tka.TKA_ERR_INVALID_ARG
+    assert call(_p(mode=tka.HISA, block_size=0, top_blocks=4)) == tka.TKA_ERR_INVALID_ARG
+    assert call(_p(mode=tka.BLOCK_MEAN, block_size=64)) == tka.TKA_ERR_INVALID_ARG  # wrong mode
+    # topk_decode leaves the two-level mode to topk_hisa_decode
+    assert LIB.topk_decode(ctypes.byref(p), FAKE, FAKE * 2, FAKE * 3, FAKE * 6, None, None, FAKE * 5, None, FAKE * 8,
+                           1 << 30, None) == tka.TKA_ERR_INVALID_ARG

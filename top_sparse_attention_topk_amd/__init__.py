@@ -7,8 +7,8 @@ raises ImportError when libtka.so has not been built - there is no fallback.
 
 The names match the C entry points: topk_attn_score,
 topk_attn_score_threshold, topk_select, topk_select_adaptive,
-sparse_attn_gather, topk_decode, topk_decode_adaptive, topk_cache_append,
-topk_block_mean_build and the workspace-size queries.
+sparse_attn_gather, topk_decode, topk_decode_adaptive, topk_hisa_decode,
+topk_cache_append, topk_block_mean_build and the workspace-size queries.
 """
 from __future__ import annotations
 
@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, "libtka.so")
 
 TKA_OK, TKA_ERR_INVALID_ARG, TKA_ERR_UNSUPPORTED, TKA_ERR_WORKSPACE, TKA_ERR_ALIGNMENT, TKA_ERR_HIP = range(6)
 TKA_F32, TKA_BF16, TKA_FP8_E4M3 = 0, 1, 2
-EXACT, BLOCK_MEAN, INDEXER = 0, 1, 2
+EXACT, BLOCK_MEAN, INDEXER, HISA = 0, 1, 2, 3
 
 
 class TkaError(RuntimeError):
@@ -35,7 +35,8 @@ class Problem(ctypes.Structure):
                 ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
                 ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("mode", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
-                ("idx_dtype", ctypes.c_int32), ("block_capacity", ctypes.c_int32), ("idx_capacity", ctypes.c_int32)]
+                ("idx_dtype", ctypes.c_int32), ("block_capacity", ctypes.c_int32), ("idx_capacity", ctypes.c_int32),
+                ("top_blocks", ctypes.c_int32)]
 
 
 def _load():
@@ -58,6 +59,8 @@ def _load():
         "topk_decode_workspace_size": [P, ctypes.POINTER(sz)],
         "topk_block_mean_build": [P, vp, vp, vp],
         "topk_cache_append": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+        "topk_hisa_decode": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "topk_hisa_decode_workspace_size": [P, ctypes.POINTER(sz)],
         "topk_select_adaptive": [vp, i64, i32, i64, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
         "topk_select_adaptive_workspace_size": [i64, i32, i32, ctypes.POINTER(sz)],
         "topk_decode_adaptive": [P, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, sz, vp],
@@ -80,7 +83,8 @@ LIB = _load()
 EXPORTS = ["topk_attn_score", "topk_attn_score_threshold", "topk_select", "topk_select_workspace_size", "sparse_attn_gather",
            "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
            "topk_block_mean_build", "topk_select_adaptive", "topk_select_adaptive_workspace_size",
-           "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "topk_cache_append", "tka_status_str",
+           "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "topk_cache_append", "topk_hisa_decode",
+           "topk_hisa_decode_workspace_size", "tka_status_str",
            "tka_last_error",
            "tka_abi_version"]
 
@@ -107,19 +111,19 @@ def _stream(stream):
 
 def problem(mode: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int, top_k: int,
             dtype: int = TKA_BF16, scale: float = 0.0, block_size: int = 0, n_idx_heads: int = 0, idx_dim: int = 0,
-            strides=None, block_capacity: int = 0, idx_capacity: int = 0) -> Problem:
+            strides=None, block_capacity: int = 0, idx_capacity: int = 0, top_blocks: int = 0) -> Problem:
     """tka_problem; strides default to a contiguous [B, Hkv, L, d] cache."""
     sb, sh, sl = strides if strides is not None else (n_kv_heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     return Problem(batch, n_q_heads, n_kv_heads, head_dim, seq_len, top_k, sb, sh, sl, dtype, scale, mode,
-                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3, block_capacity, idx_capacity)
+                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3, block_capacity, idx_capacity, top_blocks)
 
 
 def score_shape(p: Problem):
     if p.mode == INDEXER:
         return (p.batch, p.seq_len)
-    if p.mode == BLOCK_MEAN:
+    if p.mode in (BLOCK_MEAN, HISA):
         m = (p.seq_len + p.block_size - 1) // p.block_size
-        return (p.batch, p.n_q_heads, m - 1)
+        return (p.batch, p.n_q_heads, m - 1 if p.mode == BLOCK_MEAN else m)
     return (p.batch, p.n_q_heads, p.seq_len)
 
 
@@ -299,6 +303,35 @@ def topk_cache_append(p: Problem, k_new=None, v_new=None, k_cache=None, v_cache=
     """Append the step's new rows at position p.seq_len - 1 (and refresh the block mean / encode the indexer key)."""
     _check(LIB.topk_cache_append(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(kI_new), _ptr(kI_cache), _ptr(means), _stream(stream)), "topk_cache_append")
+
+
+def topk_hisa_decode_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.topk_hisa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)), "topk_hisa_decode_workspace_size")
+    return n.value
+
+
+def topk_hisa_decode(p: Problem, q, k_cache, v_cache, means, out=None, idx_out=None, want_parts: bool = False,
+                     ws=None, stream=None):
+    """Two-level step (mode HISA). Returns (out, idx) or, with want_parts, (out, idx, blk [B,Hq,K_B],
+    block scores [B,Hq,m], candidate scores [B,Hq,K_B*b])."""
+    import torch
+    if out is None:
+        out = _empty((p.batch, p.n_q_heads, p.head_dim), torch.float32, q)
+    if idx_out is None:
+        idx_out = _empty((p.batch, p.n_q_heads, p.top_k), torch.int32, q)
+    blk = bs = cs = None
+    if want_parts:
+        m = (p.seq_len + p.block_size - 1) // p.block_size
+        blk = _empty((p.batch, p.n_q_heads, p.top_blocks), torch.int32, q)
+        bs = _empty((p.batch, p.n_q_heads, m), torch.float32, q)
+        cs = _empty((p.batch, p.n_q_heads, p.top_blocks * p.block_size), torch.float32, q)
+    if ws is None:
+        ws = _ws(topk_hisa_decode_workspace_size(p), q)
+    _check(LIB.topk_hisa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(means), _ptr(out),
+                                _ptr(idx_out), _ptr(blk), _ptr(bs), _ptr(cs), _ptr(ws), ws.numel(), _stream(stream)),
+           "topk_hisa_decode")
+    return (out, idx_out, blk, bs, cs) if want_parts else (out, idx_out)
 
 
 def abi_version() -> int:

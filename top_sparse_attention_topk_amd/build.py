@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libtka.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "score.hip", "select.hip", "gather.hip", "cache.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "gather.hip", "cache.hip", "hisa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,7 +43,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],

@@ -68,7 +68,8 @@ tka_status check_attn_shape(const tka_problem* p) {
                 p->n_kv_heads);
   if (p->seq_len < 1) return fail(TKA_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", p->seq_len);
   if (p->top_k < 1) return fail(TKA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", p->top_k);
-  if (p->mode != TKA_SCORE_EXACT && p->mode != TKA_SCORE_BLOCK_MEAN && p->mode != TKA_SCORE_INDEXER)
+  if (p->mode != TKA_SCORE_EXACT && p->mode != TKA_SCORE_BLOCK_MEAN && p->mode != TKA_SCORE_INDEXER &&
+      p->mode != TKA_SCORE_HISA)
     return fail(TKA_ERR_INVALID_ARG, "unknown score mode %d", (int)p->mode);
   if (p->qkv_dtype != TKA_F32 && p->qkv_dtype != TKA_BF16)
     return fail(TKA_ERR_UNSUPPORTED, "qkv_dtype must be TKA_F32 or TKA_BF16 (got %d)", (int)p->qkv_dtype);
@@ -80,10 +81,14 @@ tka_status check_attn_shape(const tka_problem* p) {
   const int64_t es = (int64_t)esize(p->qkv_dtype);
   if ((p->kv_stride_l * es) % 16 || (p->kv_stride_h * es) % 16 || (p->kv_stride_b * es) % 16)
     return fail(TKA_ERR_ALIGNMENT, "KV strides must be multiples of 16 bytes");
-  if (p->mode == TKA_SCORE_BLOCK_MEAN && p->block_size < 1)
+  const bool blocks = p->mode == TKA_SCORE_BLOCK_MEAN || p->mode == TKA_SCORE_HISA;
+  if (blocks && p->block_size < 1)
     return fail(TKA_ERR_INVALID_ARG, "block_size must be >= 1 (got %d)", p->block_size);
-  if (p->block_capacity < 0 ||
-      (p->mode == TKA_SCORE_BLOCK_MEAN && p->block_capacity > 0 && p->block_capacity < n_blocks(p)))
+  if (p->mode == TKA_SCORE_HISA &&
+      (p->top_blocks < 1 || (int64_t)p->top_blocks * p->block_size > 0x7fffffff))
+    return fail(TKA_ERR_INVALID_ARG, "top_blocks must be >= 1 with top_blocks * block_size < 2^31 (got %d)",
+                p->top_blocks);
+  if (p->block_capacity < 0 || (blocks && p->block_capacity > 0 && p->block_capacity < n_blocks(p)))
     return fail(TKA_ERR_INVALID_ARG, "block_capacity %d is below ceil(seq_len / block_size)", p->block_capacity);
   if (p->idx_capacity < 0 || (p->mode == TKA_SCORE_INDEXER && p->idx_capacity > 0 && p->idx_capacity < p->seq_len))
     return fail(TKA_ERR_INVALID_ARG, "idx_capacity %d is below seq_len", p->idx_capacity);
@@ -127,9 +132,9 @@ ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys
   a.G = p->n_q_heads / p->n_kv_heads;
   a.d = p->head_dim;
   a.q_bf16 = p->qkv_dtype == TKA_BF16;
-  if (p->mode == TKA_SCORE_BLOCK_MEAN) {
+  if (p->mode == TKA_SCORE_BLOCK_MEAN || p->mode == TKA_SCORE_HISA) {
     const int64_t m = n_blocks(p), mc = mean_slots(p);
-    a.nrows = (int)(m - 1);
+    a.nrows = p->mode == TKA_SCORE_HISA ? (int)m : (int)(m - 1);
     a.sb = (int64_t)p->n_kv_heads * mc * p->head_dim;
     a.sh = mc * p->head_dim;
     a.sl = p->head_dim;
@@ -151,6 +156,7 @@ int64_t score_rows(const tka_problem* p) {
 }
 
 int32_t score_len(const tka_problem* p) {
+  if (p->mode == TKA_SCORE_HISA) return (int32_t)n_blocks(p);  // every block competes
   return p->mode == TKA_SCORE_BLOCK_MEAN ? (int32_t)(n_blocks(p) - 1) : p->seq_len;
 }
 
@@ -160,7 +166,7 @@ size_t q_bytes(const tka_problem* p) {
 }
 
 size_t proxy_bytes(const tka_problem* p) {
-  if (p->mode == TKA_SCORE_BLOCK_MEAN)
+  if (p->mode == TKA_SCORE_BLOCK_MEAN || p->mode == TKA_SCORE_HISA)
     return sizeof(float) * (size_t)p->batch * p->n_kv_heads * mean_slots(p) * p->head_dim;
   if (p->mode == TKA_SCORE_INDEXER) return (size_t)p->batch * idx_slots(p) * p->idx_dim;
   return kv_bytes(p);
@@ -581,6 +587,7 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
                        void* ws, size_t ws_bytes, void* stream) {
   tka_status s = check_attn_shape(p);
   if (s) return s;
+  if (p->mode == TKA_SCORE_HISA) return fail(TKA_ERR_INVALID_ARG, "TKA_SCORE_HISA runs through topk_hisa_decode");
   const int shared = p->mode == TKA_SCORE_INDEXER ? 1 : 0;
   if ((s = check_gather_shape(p, p->top_k, p->mode == TKA_SCORE_BLOCK_MEAN ? p->block_size : 0, shared, nullptr)))
     return s;
@@ -759,10 +766,139 @@ tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void*
   return launched("topk_decode_adaptive");
 }
 
+// ---- two-level step ----
+namespace {
+struct HisaLayout {
+  size_t bscores, blk, sel_ws, cand, krow, idx, selv, gather_ws, total;
+  int64_t rows, m, ncand;
+  GatherPlan gp;
+};
+HisaLayout hisa_layout(const tka_problem* p) {
+  HisaLayout d;
+  d.rows = (int64_t)p->batch * p->n_q_heads;
+  d.m = n_blocks(p);
+  d.ncand = (int64_t)p->top_blocks * p->block_size;
+  size_t o = 0;
+  d.bscores = o;
+  o += al256(sizeof(float) * (size_t)(d.rows * d.m));
+  d.blk = o;
+  o += al256(sizeof(int32_t) * (size_t)(d.rows * p->top_blocks));
+  d.sel_ws = o;
+  o += al256(select_workspace_bytes(d.rows, (int)d.m, p->top_blocks));
+  d.cand = o;
+  o += al256(sizeof(float) * (size_t)(d.rows * d.ncand));
+  d.krow = o;
+  o += al256(sizeof(int32_t) * (size_t)d.rows);
+  d.idx = o;
+  o += al256(sizeof(int32_t) * (size_t)(d.rows * p->top_k));
+  d.selv = o;
+  o += al256(sizeof(float) * (size_t)(d.rows * p->top_k));
+  d.gather_ws = o;
+  GatherArgs ga = gather_args(p, nullptr, nullptr, nullptr, nullptr, p->top_k, 0, 0, nullptr, nullptr);
+  d.gp = plan_gather(ga);
+  o += al256(d.gp.ws_bytes);
+  d.total = o;
+  return d;
+}
+tka_status check_hisa_problem(const tka_problem* p) {
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  if (p->mode != TKA_SCORE_HISA) return fail(TKA_ERR_INVALID_ARG, "topk_hisa_decode needs mode TKA_SCORE_HISA");
+  if ((int64_t)p->top_blocks * p->block_size > 0x7fffffff / 4)
+    return fail(TKA_ERR_UNSUPPORTED, "top_blocks * block_size too large");
+  return check_gather_shape(p, p->top_k, 0, 0, nullptr);
+}
+}  // namespace
+
+tka_status topk_hisa_decode_workspace_size(const tka_problem* p, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  tka_status s = check_hisa_problem(p);
+  if (s) return s;
+  *bytes = hisa_layout(p).total;
+  return ok();
+}
+
+tka_status topk_hisa_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                            const float* means, float* out, int32_t* idx_out, int32_t* blk_out,
+                            float* block_scores_out, float* cand_scores_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  tka_status s = check_hisa_problem(p);
+  if (s) return s;
+  if ((s = check_attn_ptrs(p, q, k_cache, v_cache, out))) return s;
+  if ((s = need_ptr(means, "means"))) return s;
+  const HisaLayout d = hisa_layout(p);
+  const Range o = span_of(out, out_bytes(p)), mo = span_of(means, proxy_bytes(p));
+  const Range kv = span_of(k_cache, kv_bytes(p)), vv = span_of(v_cache, kv_bytes(p)), qq = span_of(q, attn_q_bytes(p));
+  if (overlap(o, mo)) return fail(TKA_ERR_INVALID_ARG, "out overlaps means");
+  struct Opt {
+    const void* ptr;
+    size_t bytes;
+    const char* name;
+  } opts[4] = {{idx_out, sizeof(int32_t) * (size_t)(d.rows * p->top_k), "idx_out"},
+               {blk_out, sizeof(int32_t) * (size_t)(d.rows * p->top_blocks), "blk_out"},
+               {block_scores_out, sizeof(float) * (size_t)(d.rows * d.m), "block_scores_out"},
+               {cand_scores_out, sizeof(float) * (size_t)(d.rows * d.ncand), "cand_scores_out"}};
+  for (int i = 0; i < 4; ++i) {
+    if (!opts[i].ptr) continue;
+    if (reinterpret_cast<uintptr_t>(opts[i].ptr) & 3) return fail(TKA_ERR_ALIGNMENT, "%s not 4-byte aligned", opts[i].name);
+    const Range r = span_of(opts[i].ptr, opts[i].bytes);
+    if (overlap(r, o) || overlap(r, mo) || overlap(r, kv) || overlap(r, vv) || overlap(r, qq))
+      return fail(TKA_ERR_INVALID_ARG, "%s overlaps an input or out", opts[i].name);
+    for (int j = 0; j < i; ++j)
+      if (opts[j].ptr && overlap(r, span_of(opts[j].ptr, opts[j].bytes)))
+        return fail(TKA_ERR_INVALID_ARG, "%s overlaps %s", opts[i].name, opts[j].name);
+  }
+  if (!ws || ws_bytes < d.total)
+    return fail(TKA_ERR_WORKSPACE, "two-level decode needs %zu workspace bytes (got %zu)", d.total, ws_bytes);
+  if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* bscores = block_scores_out ? block_scores_out : reinterpret_cast<float*>(base + d.bscores);
+  int32_t* blk = blk_out ? blk_out : reinterpret_cast<int32_t*>(base + d.blk);
+  float* cand = cand_scores_out ? cand_scores_out : reinterpret_cast<float*>(base + d.cand);
+  int32_t* krow = reinterpret_cast<int32_t*>(base + d.krow);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx);
+  float* selv = reinterpret_cast<float*>(base + d.selv);
+  // coarse level: every block's score from the means, the top K_B blocks
+  run_score(p, q, means, nullptr, bscores, st);
+  SelectArgs sb{bscores, d.rows, (int)d.m, d.m, p->top_blocks, blk, nullptr};
+  launch_select(sb, base + d.sel_ws, st);
+  // fine level: exact scores of the kept blocks' tokens, the top k' of them
+  HisaArgs ha;
+  ha.q = q;
+  ha.K = k_cache;
+  ha.blk = blk;
+  ha.cand = cand;
+  ha.krow = krow;
+  ha.B = p->batch;
+  ha.Hq = p->n_q_heads;
+  ha.G = p->n_q_heads / p->n_kv_heads;
+  ha.d = p->head_dim;
+  ha.L = p->seq_len;
+  ha.KB = p->top_blocks;
+  ha.bsz = p->block_size;
+  ha.k = p->top_k;
+  ha.sb = p->kv_stride_b;
+  ha.sh = p->kv_stride_h;
+  ha.sl = p->kv_stride_l;
+  ha.scale = eff_scale(p);
+  ha.bf16 = p->qkv_dtype == TKA_BF16;
+  launch_hisa_token_scores(ha, st);
+  SelectArgs sc{cand, d.rows, (int)d.ncand, d.ncand, p->top_k, idx, selv};
+  launch_select_rows_counts(sc, krow, st);
+  launch_hisa_map(idx, blk, d.rows, p->top_k, p->top_blocks, p->block_size, st);
+  // attention over the kept tokens, their exact scores as logits
+  GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, p->top_k, 0, 0, selv, out);
+  launch_gather(ga, d.gp, base + d.gather_ws, st);
+  return launched("topk_hisa_decode");
+}
+
 tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, float* means, void* stream) {
   tka_status s = check_attn_shape(p);
   if (s) return s;
-  if (p->mode != TKA_SCORE_BLOCK_MEAN) return fail(TKA_ERR_INVALID_ARG, "mode must be TKA_SCORE_BLOCK_MEAN");
+  if (p->mode != TKA_SCORE_BLOCK_MEAN && p->mode != TKA_SCORE_HISA)
+    return fail(TKA_ERR_INVALID_ARG, "mode must be TKA_SCORE_BLOCK_MEAN or TKA_SCORE_HISA");
   if ((s = need_ptr(k_cache, "k_cache")) || (s = need_ptr(means, "means"))) return s;
   const Range mo = span_of(means, proxy_bytes(p));
   if (overlap(mo, span_of(k_cache, kv_bytes(p)))) return fail(TKA_ERR_INVALID_ARG, "means overlaps k_cache");
@@ -796,7 +932,8 @@ tka_status topk_cache_append(const tka_problem* p, const void* k_new, const void
       return s;
   }
   if (means) {
-    if (p->mode != TKA_SCORE_BLOCK_MEAN) return fail(TKA_ERR_INVALID_ARG, "means only with TKA_SCORE_BLOCK_MEAN");
+    if (p->mode != TKA_SCORE_BLOCK_MEAN && p->mode != TKA_SCORE_HISA)
+      return fail(TKA_ERR_INVALID_ARG, "means only with TKA_SCORE_BLOCK_MEAN or TKA_SCORE_HISA");
     if ((s = need_ptr(means, "means")) || (s = need_ptr(k_cache, "k_cache"))) return s;
   }
   if (kI_new || kI_cache) {

@@ -26,6 +26,18 @@ struct IndexerArgs {
   int Lc;             // positions per sequence in kI (>= L)
 };
 
+struct HisaArgs {
+  const void* q;      // [B,Hq,d]
+  const void* K;      // strided cache
+  const int32_t* blk; // [B*Hq, KB] kept blocks, ascending, -1 padded
+  float* cand;        // [B*Hq, KB*bsz]
+  int32_t* krow;      // [B*Hq]
+  int B, Hq, G, d, L, KB, bsz, k;
+  int64_t sb, sh, sl;
+  float scale;
+  int bf16;
+};
+
 struct BlockMeanArgs {
   const void* K;
   float* means;  // [B,Hkv,m,d]
@@ -97,6 +109,11 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 // tau; W, M and row_flag [n_rows] are scratch
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
                             uint32_t* row_flag, float* tau, hipStream_t st);
+// the two-level step's fine level: token scores of the kept blocks, and slot -> position
+void launch_hisa_token_scores(const HisaArgs& a, hipStream_t st);
+void launch_hisa_map(int32_t* idx, const int32_t* blk, int64_t rows, int k, int KB, int bsz, hipStream_t st);
+// row select with a count per row (krow[r] <= a.k; rows padded with -1 up to a.k)
+void launch_select_rows_counts(const SelectArgs& a, const int32_t* krow, hipStream_t st);
 void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st);
 
 // candidate prefilter of the fused exact step (select.hip)

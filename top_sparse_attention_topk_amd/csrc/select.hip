@@ -1082,6 +1082,14 @@ static int rows_capw(int n, int k, size_t* lds) {
   return capw;
 }
 
+void launch_select_rows_counts(const SelectArgs& a, const int32_t* krow, hipStream_t st) {
+  if (a.n_rows <= 0) return;
+  size_t lds;
+  const int capw = rows_capw(a.n, a.k, &lds);
+  hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k,
+                     a.idx, a.sel, capw, (const uint32_t*)nullptr, krow);
+}
+
 void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st) {
   if (a.n_rows <= 0) return;
   size_t lds;
