@@ -390,6 +390,23 @@ def main():
                               "k_mean": round(float(kf.mean()), 1), "k_min": int(ak_k.min()),
                               "k_max_seen": int(ak_k.max()), "tau_max": round(float(ak_tau.max()), 5)}
         del ad_ws, ak_idx
+        torch.cuda.empty_cache()
+        # the two-level step on the same caches: 128 blocks of 64 kept, then the top k tokens
+        log("[bench] two-level step")
+        KB, bsz = 128, 64
+        ph = tka.problem(tka.HISA, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, 0.0, bsz, top_blocks=KB)
+        hmeans = tka.topk_block_mean_build(ph, Kt)
+        h_out = torch.empty_like(out)
+        h_idx = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+        h_ws = torch.empty(tka.topk_hisa_decode_workspace_size(ph), dtype=torch.uint8, device="cuda")
+        t_h = time_loop(lambda: tka.topk_hisa_decode(ph, qt, Kt, Vt, hmeans, out=h_out, idx_out=h_idx, ws=h_ws),
+                        args.steps)
+        m_blocks = (w.L + bsz - 1) // bsz
+        h_bytes = (w.B * w.Hkv * m_blocks * w.d * 4 + rows * KB * bsz * w.d * 2 + rows * w.k * (w.d * 2 + 8))
+        extras["hisa"] = {"block_size": bsz, "top_blocks": KB, "top_k": w.k, "decode_ms": round(t_h, 4),
+                          "decode_queries_per_s": round(w.B / (t_h / 1e3), 1),
+                          "algorithmic_bytes": h_bytes, "gbps": round(h_bytes / (t_h / 1e3) / 1e9, 1)}
+        del h_ws, hmeans
     result["extras"] = extras
     del Kt, Vt, sc, ws
     torch.cuda.empty_cache()

@@ -55,6 +55,7 @@ def lib():
         L.orc_encode_e4m3.argtypes = [_vp, _i64, _vp]
         L.orc_block_means.argtypes = [P, _vp, _vp]
         L.orc_hisa_decode.argtypes = [P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.orc_decode_mq.argtypes = [P, _i64, _vp, _vp, _vp, _vp, _vp]
         L.orc_select_adaptive_f32.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_select_adaptive_f64.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]
         L.orc_attend.argtypes = [P, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int32, _vp, _i64, _vp]
@@ -147,6 +148,18 @@ def block_means(p: Problem, K):
     out = np.empty((p.B, p.Hkv, m, p.d), np.float64)
     lib().orc_block_means(ctypes.byref(p), _ptr(K), _ptr(out))
     return out
+
+
+def decode_mq(p: Problem, M: int, q, K, V):
+    """M causal queries per sequence at positions L-M .. L-1 (q [B, M, Hq, d]). Returns (out [B*M*Hq, d],
+    idx [B*M*Hq, k]); rows (b*M + t)*Hq + h, query t keeps the top min(k, L-M+t+1) of its visible keys."""
+    n = p.B * M * p.Hq
+    out = np.empty((n, p.d), np.float64)
+    idx = np.empty((n, p.k), np.int32)
+    rc = lib().orc_decode_mq(ctypes.byref(p), M, _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(idx))
+    if rc != 0:
+        raise ValueError("bad multi-query arguments")
+    return out, idx
 
 
 def hisa_decode(p: Problem, KB: int, q, K, V):

@@ -429,6 +429,52 @@ int orc_decode(const orc_problem* p, const void* q, const void* K, const void* V
 }
 
 /*
+ * Several query tokens per sequence ("Evolution of Sparse Attention in
+ * Long-Context LLMs", section 6: the attention matrix shrinks from "current
+ * length x full history" to "current length x K"): M queries per sequence sit
+ * at positions L-M .. L-1 of the cache and each attends causally, query t
+ * seeing the keys 0 .. L-M+t. Per (b, t, h): exact scores over its L_t =
+ * L-M+t+1 visible keys, the top k' = min(k, L_t) in the select order, softmax
+ * attention over them. q [B,M,Hq,d]; rows r = (b*M + t)*Hq + h;
+ * idx_out [B*M*Hq, k] (ascending, -1 pad), out [B*M*Hq, d].
+ */
+int orc_decode_mq(const orc_problem* p, int64_t M, const void* q, const void* K, const void* V, double* out,
+                  int32_t* idx_out) {
+  if (M < 1 || M > p->L || p->k < 1) return -1;
+  const int64_t n_rows = (int64_t)p->B * M * p->Hq, G = p->Hq / p->Hkv;
+  const double sc = attn_scale(p);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t h = r % p->Hq, bt = r / p->Hq, t = bt % M, b = bt / M, g = h / G;
+    const int64_t Lt = p->L - M + t + 1;
+    vi_t* tmp = (vi_t*)malloc(sizeof(vi_t) * (size_t)Lt);
+    double* z = (double*)malloc(sizeof(double) * (size_t)Lt);
+    for (int64_t i = 0; i < Lt; ++i) {
+      double dot = 0;
+      for (int64_t c = 0; c < p->d; ++c) dot += ld(q, p->dt, r * p->d + c) * ld(K, p->dt, kv_off(p, b, g, i) + c);
+      z[i] = sc * dot;
+      tmp[i].v = z[i];
+      tmp[i].i = i;
+    }
+    int32_t* idx = idx_out + r * p->k;
+    select_row(tmp, Lt, p->k, idx);
+    double M0 = -INFINITY;
+    for (int64_t j = 0; j < p->k && idx[j] >= 0; ++j) M0 = z[idx[j]] > M0 ? z[idx[j]] : M0;
+    double den = 0;
+    for (int64_t c = 0; c < p->d; ++c) out[r * p->d + c] = 0;
+    for (int64_t j = 0; j < p->k && idx[j] >= 0; ++j) {
+      const double wgt = exp(z[idx[j]] - M0);
+      den += wgt;
+      for (int64_t c = 0; c < p->d; ++c) out[r * p->d + c] += wgt * ld(V, p->dt, kv_off(p, b, g, idx[j]) + c);
+    }
+    for (int64_t c = 0; c < p->d; ++c) out[r * p->d + c] /= den;
+    free(z);
+    free(tmp);
+  }
+  return 0;
+}
+
+/*
  * Two-level (hierarchical) selection, "Sparse Attention Landscape",
  * "Hierarchical Sparse Attention": a coarse score r_j = f_block(q_t, B_j) for
  * every block, the top-K_B blocks kept, token scores s_i = f_token(q_t, k_i)
