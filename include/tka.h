@@ -101,6 +101,13 @@ typedef struct {
                              indexer keys of every length); 0 = L */
   int32_t top_blocks;     /* HISA: K_B >= 1, the blocks kept by the coarse level (block_size, block_capacity
                              as for BLOCK_MEAN) */
+  int32_t n_queries;      /* EXACT: M query tokens per sequence (0 or 1: one). With M > 1 the queries sit at
+                             positions L-M .. L-1 of the cache and attend causally: query t sees keys
+                             0 .. L-M+t and keeps min(k, L-M+t+1) of them ("Evolution of Sparse Attention in
+                             Long-Context LLMs", section 6: current length x K). Then q and out are
+                             [B,M,Hq,d], scores [B,M,Hq,L] (a position a query cannot see is NaN), index
+                             lists [B,M,Hq,n]; built for bf16 with M * Hq/Hkv <= 64 (topk_attn_score,
+                             sparse_attn_gather, topk_decode; TKA_ERR_UNSUPPORTED elsewhere). */
 } tka_problem;
 
 /*

@@ -36,7 +36,7 @@ class Problem(ctypes.Structure):
                 ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("mode", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
                 ("idx_dtype", ctypes.c_int32), ("block_capacity", ctypes.c_int32), ("idx_capacity", ctypes.c_int32),
-                ("top_blocks", ctypes.c_int32)]
+                ("top_blocks", ctypes.c_int32), ("n_queries", ctypes.c_int32)]
 
 
 def _load():
@@ -111,11 +111,13 @@ def _stream(stream):
 
 def problem(mode: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int, top_k: int,
             dtype: int = TKA_BF16, scale: float = 0.0, block_size: int = 0, n_idx_heads: int = 0, idx_dim: int = 0,
-            strides=None, block_capacity: int = 0, idx_capacity: int = 0, top_blocks: int = 0) -> Problem:
+            strides=None, block_capacity: int = 0, idx_capacity: int = 0, top_blocks: int = 0,
+            n_queries: int = 0) -> Problem:
     """tka_problem; strides default to a contiguous [B, Hkv, L, d] cache."""
     sb, sh, sl = strides if strides is not None else (n_kv_heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     return Problem(batch, n_q_heads, n_kv_heads, head_dim, seq_len, top_k, sb, sh, sl, dtype, scale, mode,
-                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3, block_capacity, idx_capacity, top_blocks)
+                   block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3, block_capacity, idx_capacity, top_blocks,
+                   n_queries)
 
 
 def score_shape(p: Problem):
@@ -124,7 +126,14 @@ def score_shape(p: Problem):
     if p.mode in (BLOCK_MEAN, HISA):
         m = (p.seq_len + p.block_size - 1) // p.block_size
         return (p.batch, p.n_q_heads, m - 1 if p.mode == BLOCK_MEAN else m)
+    if p.n_queries > 1:
+        return (p.batch, p.n_queries, p.n_q_heads, p.seq_len)
     return (p.batch, p.n_q_heads, p.seq_len)
+
+
+def _qrows(p: Problem):
+    """Leading dims of q / out: (B, M, Hq) with several queries per sequence, else (B, Hq)."""
+    return (p.batch, p.n_queries, p.n_q_heads) if p.n_queries > 1 else (p.batch, p.n_q_heads)
 
 
 def _empty(shape, dtype, like):
@@ -228,7 +237,7 @@ def sparse_attn_gather(p: Problem, q, k_cache, v_cache, idx, idx_unit: int = 0, 
     import torch
     n_idx = idx.shape[-1]
     if out is None:
-        out = _empty((p.batch, p.n_q_heads, p.head_dim), torch.float32, q)
+        out = _empty(_qrows(p) + (p.head_dim,), torch.float32, q)
     nbytes = sparse_attn_gather_workspace_size(p, n_idx, idx_unit, shared)
     if ws is None and nbytes:
         ws = _ws(nbytes, q)
@@ -246,12 +255,12 @@ def topk_decode_workspace_size(p: Problem) -> int:
 
 def topk_decode(p: Problem, q, k_cache, v_cache, proxy_keys=None, q_idx=None, idx_w=None, out=None, idx_out=None,
                 ws=None, want_idx: bool = True, stream=None):
-    """One fused decode step. Returns (out [B,Hq,d] fp32, idx or None)."""
+    """One fused decode step. Returns (out [B,Hq,d] fp32 ([B,M,Hq,d] with several queries), idx or None)."""
     import torch
     if out is None:
-        out = _empty((p.batch, p.n_q_heads, p.head_dim), torch.float32, q)
+        out = _empty(_qrows(p) + (p.head_dim,), torch.float32, q)
     if idx_out is None and want_idx:
-        shape = (p.batch, p.top_k) if p.mode == INDEXER else (p.batch, p.n_q_heads, p.top_k)
+        shape = (p.batch, p.top_k) if p.mode == INDEXER else _qrows(p) + (p.top_k,)
         idx_out = _empty(shape, torch.int32, q)
     if ws is None:
         ws = _ws(topk_decode_workspace_size(p), q)

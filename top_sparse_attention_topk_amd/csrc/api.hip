@@ -47,6 +47,8 @@ Range span_of(const void* p, size_t bytes) {
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 int64_t n_blocks(const tka_problem* p) { return ((int64_t)p->seq_len + p->block_size - 1) / p->block_size; }
+// query tokens per sequence
+int64_t nqry(const tka_problem* p) { return p->n_queries > 1 ? p->n_queries : 1; }
 
 // extent in bytes of a KV cache with the problem's strides
 size_t kv_bytes(const tka_problem* p) {
@@ -73,6 +75,13 @@ tka_status check_attn_shape(const tka_problem* p) {
     return fail(TKA_ERR_INVALID_ARG, "unknown score mode %d", (int)p->mode);
   if (p->qkv_dtype != TKA_F32 && p->qkv_dtype != TKA_BF16)
     return fail(TKA_ERR_UNSUPPORTED, "qkv_dtype must be TKA_F32 or TKA_BF16 (got %d)", (int)p->qkv_dtype);
+  if (p->n_queries < 0) return fail(TKA_ERR_INVALID_ARG, "n_queries must be >= 0 (got %d)", p->n_queries);
+  if (nqry(p) > 1) {
+    if (p->mode != TKA_SCORE_EXACT) return fail(TKA_ERR_INVALID_ARG, "several queries need TKA_SCORE_EXACT");
+    if (p->n_queries > p->seq_len) return fail(TKA_ERR_INVALID_ARG, "n_queries above seq_len");
+    if (p->qkv_dtype != TKA_BF16 || nqry(p) * (p->n_q_heads / p->n_kv_heads) > 64)
+      return fail(TKA_ERR_UNSUPPORTED, "several queries are built for bf16 with n_queries * Hq/Hkv <= 64");
+  }
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return fail(TKA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", p->head_dim);
   if (p->kv_stride_l < p->head_dim || p->kv_stride_h < 0 || p->kv_stride_b < 0)
@@ -132,6 +141,7 @@ ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys
   a.G = p->n_q_heads / p->n_kv_heads;
   a.d = p->head_dim;
   a.q_bf16 = p->qkv_dtype == TKA_BF16;
+  a.M = (int)nqry(p);
   if (p->mode == TKA_SCORE_BLOCK_MEAN || p->mode == TKA_SCORE_HISA) {
     const int64_t m = n_blocks(p), mc = mean_slots(p);
     a.nrows = p->mode == TKA_SCORE_HISA ? (int)m : (int)(m - 1);
@@ -152,7 +162,7 @@ ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys
 }
 
 int64_t score_rows(const tka_problem* p) {
-  return p->mode == TKA_SCORE_INDEXER ? p->batch : (int64_t)p->batch * p->n_q_heads;
+  return p->mode == TKA_SCORE_INDEXER ? p->batch : (int64_t)p->batch * nqry(p) * p->n_q_heads;
 }
 
 int32_t score_len(const tka_problem* p) {
@@ -162,7 +172,7 @@ int32_t score_len(const tka_problem* p) {
 
 size_t q_bytes(const tka_problem* p) {
   if (p->mode == TKA_SCORE_INDEXER) return (size_t)p->batch * p->n_idx_heads * p->idx_dim;
-  return (size_t)p->batch * p->n_q_heads * p->head_dim * esize(p->qkv_dtype);
+  return (size_t)p->batch * nqry(p) * p->n_q_heads * p->head_dim * esize(p->qkv_dtype);
 }
 
 size_t proxy_bytes(const tka_problem* p) {
@@ -243,7 +253,8 @@ GatherArgs gather_args(const tka_problem* p, const void* q, const void* K, const
   a.idx = idx;
   a.sel = sel;
   a.out = out;
-  a.B = p->batch;
+  a.B = (int)(p->batch * nqry(p));  // (sequence, query) pairs
+  a.M = (int)nqry(p);
   a.Hq = p->n_q_heads;
   a.Hkv = p->n_kv_heads;
   a.G = p->n_q_heads / p->n_kv_heads;
@@ -273,14 +284,18 @@ tka_status check_gather_shape(const tka_problem* p, int32_t n_idx, int32_t unit,
     return fail(TKA_ERR_UNSUPPORTED, "shared index lists need Hq/Hkv in {1,2,4,8,16} (got %d)", G);
   if (sel && (shared || unit != 0))
     return fail(TKA_ERR_INVALID_ARG, "sel_scores needs per-head token lists (shared 0, idx_unit 0)");
+  if (nqry(p) > 1 && (shared || unit != 0))
+    return fail(TKA_ERR_INVALID_ARG, "several queries take per-head token lists (shared 0, idx_unit 0)");
   return TKA_OK;
 }
 
 size_t attn_q_bytes(const tka_problem* p) {
-  return (size_t)p->batch * p->n_q_heads * p->head_dim * esize(p->qkv_dtype);
+  return (size_t)p->batch * nqry(p) * p->n_q_heads * p->head_dim * esize(p->qkv_dtype);
 }
 
-size_t out_bytes(const tka_problem* p) { return sizeof(float) * (size_t)p->batch * p->n_q_heads * p->head_dim; }
+size_t out_bytes(const tka_problem* p) {
+  return sizeof(float) * (size_t)p->batch * nqry(p) * p->n_q_heads * p->head_dim;
+}
 
 // q, K, V, out pointers of the attention part and out's overlap with them
 tka_status check_attn_ptrs(const tka_problem* p, const void* q, const void* K, const void* V, const float* out) {
@@ -334,7 +349,7 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
   const int G = p->n_q_heads / p->n_kv_heads;
   if (p->mode != TKA_SCORE_EXACT || p->qkv_dtype != TKA_BF16 || !score_uses_mfma(1, G)) return pf;
   const int64_t L = p->seq_len, kk = p->top_k < p->seq_len ? p->top_k : p->seq_len;
-  if (L < 8192 || L > 262144 || kk * 8 > L) return pf;
+  if (L < 8192 || L > 262144 || kk * 8 > L || nqry(p) > 1) return pf;
   int64_t sc = 4096;
   while (sc > 128 && 7 * kk * sample_count(L, sc) < 4 * 100 * L) sc >>= 1;
   pf.sample_chunk = (int)sc;
@@ -350,7 +365,7 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
 
 // ---- fused step: workspace layout ----
 struct DecodeLayout {
-  size_t scores, sel_ws, idx, selv, gather_ws, total;
+  size_t scores, sel_ws, idx, selv, gather_ws, krow, total;
   size_t samp, T, cnt, row_flag, group_flag, cbits, cpos;
   int64_t rows;
   int32_t len;
@@ -380,6 +395,8 @@ DecodeLayout decode_layout(const tka_problem* p) {
   d.gp = plan_gather(ga);
   d.gather_ws = o;
   o += al256(d.gp.ws_bytes);
+  d.krow = o;  // several queries: each row's count
+  if (nqry(p) > 1) o += al256(sizeof(int32_t) * (size_t)d.rows);
   d.pf = prefilter_plan(p);
   if (d.pf.on) {
     const size_t R = (size_t)d.rows;
@@ -434,6 +451,7 @@ tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys
 tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const void* k_cache,
                                      const float* thresholds, uint32_t* counts, float* cand_scores, int32_t* cand_pos,
                                      int32_t capacity, void* stream) {
+  if (p && p->n_queries > 1) return fail(TKA_ERR_UNSUPPORTED, "the thresholded scan takes one query per sequence");
   tka_status s = check_attn_shape(p);
   if (s) return s;
   const int G = p->n_q_heads / p->n_kv_heads;
@@ -660,8 +678,14 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     // 1. score
     if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);
     else if (d.len > 0) run_score(p, q, exact ? k_cache : proxy_keys, nullptr, scores, st);
-    // 2. select
-    launch_select(sa, base + d.sel_ws, st);
+    // 2. select (several queries: query t keeps min(k, L - M + t + 1) of its visible keys)
+    if (nqry(p) > 1) {
+      int32_t* krow = reinterpret_cast<int32_t*>(base + d.krow);
+      launch_mq_counts(krow, d.rows, (int)nqry(p), p->n_q_heads, p->seq_len, d.k, st);
+      launch_select_rows_counts(sa, krow, st);
+    } else {
+      launch_select(sa, base + d.sel_ws, st);
+    }
   }
   // 3. gather
   GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, d.k, d.unit, d.shared, exact ? selv : nullptr, out);
@@ -703,6 +727,7 @@ AdaptiveLayout adaptive_layout(const tka_problem* p) {
 tka_status check_adaptive_problem(const tka_problem* p) {
   tka_status s = check_attn_shape(p);
   if (s) return s;
+  if (nqry(p) > 1) return fail(TKA_ERR_UNSUPPORTED, "the certified step takes one query per sequence");
   if (p->mode != TKA_SCORE_EXACT) return fail(TKA_ERR_INVALID_ARG, "the adaptive step needs TKA_SCORE_EXACT");
   return check_gather_shape(p, p->top_k, 0, 0, nullptr);
 }
@@ -925,6 +950,7 @@ tka_status topk_cache_append(const tka_problem* p, const void* k_new, const void
                              void* v_cache, const float* kI_new, void* kI_cache, float* means, void* stream) {
   tka_status s = check_attn_shape(p);
   if (s) return s;
+  if (nqry(p) > 1) return fail(TKA_ERR_UNSUPPORTED, "append one position at a time (n_queries 0 or 1)");
   const bool kv = k_new || v_new;
   if (kv) {
     if ((s = need_ptr(k_new, "k_new")) || (s = need_ptr(v_new, "v_new")) || (s = need_ptr(k_cache, "k_cache")) ||

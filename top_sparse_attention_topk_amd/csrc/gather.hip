@@ -37,6 +37,7 @@ struct GatherK {
   float scale;
   int n_idx, unit, shared, nsplit, span;
   int64_t E;
+  int M;  // queries per sequence (causal): task's K/V sequence is b / M, its last visible key L - M + b % M
 };
 
 template <bool BF16, int D, int NH, bool SEL>
@@ -65,12 +66,14 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
     h0 = g * a.G;
     list = a.idx + (int64_t)b * a.n_idx;
   } else {
-    b = task / a.Hq;
+    b = task / a.Hq;  // a (sequence, query) pair when M > 1
     h0 = task % a.Hq;
     g = h0 / a.G;
     list = a.idx + (int64_t)task * a.n_idx;
     if (SEL) sl_list = a.sel + (int64_t)task * a.n_idx;
   }
+  const int bkv = b / a.M;                 // the sequence whose K/V rows it reads
+  const int lim = a.L - a.M + 1 + b % a.M;  // keys it may see (all L for one query per sequence)
   const int64_t e0 = (int64_t)split * a.span;
   const int ne = (int)max((int64_t)0, min(a.E, e0 + a.span) - e0);
 
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
     int tk = -1;
     if (a.unit == 0) {
       const int v = list[e];
-      tk = (v >= 0 && v < a.L) ? v : -1;
+      tk = (v >= 0 && v < lim) ? v : -1;
     } else if (e < nb) {
       const int j = list[e / a.unit];
       if (j >= 0 && j < a.m - 1) {
@@ -97,8 +100,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   }
   __syncthreads();
 
-  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.K) + ((int64_t)b * a.sb + (int64_t)g * a.sh) * ES;
-  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.V) + ((int64_t)b * a.sb + (int64_t)g * a.sh) * ES;
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.K) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
+  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.V) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
 
   // 2. logits from the K rows
   if (!SEL) {
@@ -345,6 +348,7 @@ void launch_gather(const GatherArgs& a, const GatherPlan& pl, void* ws, hipStrea
   k.nsplit = pl.nsplit;
   k.span = pl.span;
   k.E = pl.expanded;
+  k.M = a.M > 1 ? a.M : 1;
   const bool sel = a.sel != nullptr;
   if (a.bf16) launch_gb<true>(k, pl, a.d, sel, st);
   else launch_gb<false>(k, pl, a.d, sel, st);

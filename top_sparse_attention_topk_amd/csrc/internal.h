@@ -15,6 +15,7 @@ struct ScoreArgs {
   float scale;
   int bf16;    // rows: 1 bf16, 0 fp32
   int q_bf16;  // query: 1 bf16, 0 fp32
+  int M = 1;   // queries per sequence (q [B,M,Hq,d], scores [B,M,Hq,nrows], causal)
 };
 
 struct IndexerArgs {
@@ -69,6 +70,7 @@ struct GatherArgs {
   float scale;
   int bf16;
   int n_idx, unit, shared;
+  int M = 1;  // queries per sequence: B counts (sequence, query) pairs, K/V rows are those of B / M
 };
 
 // Outputs of the exact bf16 MFMA scan (see score.hip for the modes).
@@ -109,6 +111,10 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 // tau; W, M and row_flag [n_rows] are scratch
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
                             uint32_t* row_flag, float* tau, hipStream_t st);
+// several causal queries per sequence: exact scores (bf16, M*G <= 64 rows per KV head; a
+// position a query cannot see is NaN) and each row's count min(k, L - M + t + 1)
+void launch_score_mq(const ScoreArgs& a, hipStream_t st);
+void launch_mq_counts(int32_t* krow, int64_t rows, int M, int Hq, int L, int k, hipStream_t st);
 // the two-level step's fine level: token scores of the kept blocks, and slot -> position
 void launch_hisa_token_scores(const HisaArgs& a, hipStream_t st);
 void launch_hisa_map(int32_t* idx, const int32_t* blk, int64_t rows, int k, int KB, int bsz, hipStream_t st);

@@ -365,6 +365,115 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 }
 
 // ---------------------------------------------------------------------------
+// Several causal queries per sequence ("Evolution of Sparse Attention in
+// Long-Context LLMs", section 6: current length x K instead of current length
+// x full history): the M queries of sequence b sit at positions L-M .. L-1
+// and query t sees keys 0 .. L-M+t. The R = M*G (query, head) rows of a KV
+// group share every key row, so the score is a real contraction: a K tile is
+// staged once through LDS (as in KLOAD_STAGED) and each of its 16x32 operand
+// fragments feeds RT row tiles of 16 rows (v_mfma_f32_16x16x32_bf16; lane l of
+// row tile rt holds row rt*16 + l%16 = t*G + hh). Scores go to row
+// (b*M + t)*Hq + g*G + hh of [B*M*Hq, L]; positions past the query's own are
+// NaN (they rank below every number). Grid (chunks, B*Hkv), 256 threads.
+// ---------------------------------------------------------------------------
+template <int D, int RT>
+__global__ __launch_bounds__(256) void score_mq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
+                                                       int Hq, int Hkv, int G, int M, int L, int64_t sb, int64_t sh,
+                                                       int64_t sl, float scale, int chunk, float* __restrict__ S) {
+  constexpr int KS = D / 32;
+  constexpr int P = 32;
+  constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
+  const int task = blockIdx.y;
+  const int b = task / Hkv, g = task % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int R = M * G;
+  extern __shared__ uint4 smem_raw[];
+  uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
+
+  bf16x8_t bq[RT][KS];
+  int64_t srow[RT];
+  int last[RT];  // the last position row rt of this lane may see
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rr = rt * 16 + n;
+    const bool ok = rr < R;
+    const int t = ok ? rr / G : 0, hh = ok ? rr % G : 0;
+    const int64_t qr = ((int64_t)b * M + t) * Hq + g * G + hh;
+    srow[rt] = ok ? qr : -1;
+    last[rt] = L - M + t;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ok) v = ld16(q + qr * D + 32 * s + 8 * kg);
+      bq[rt][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  const uint16_t* Kb = K + (int64_t)b * sb + (int64_t)g * sh;
+  const int p0 = blockIdx.x * chunk, p1 = min(p0 + chunk, L);
+  const bool vec_store = (L & 3) == 0;
+  auto load = [&](uint4 (&a)[NI], int at) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int pos = min(at + j * RPI + lane / CPR, L - 1);
+      a[j] = ld16_stream(Kb + (int64_t)pos * sl + (lane % CPR) * 8);
+    }
+  };
+  int base = p0 + wave * P;
+  uint4 cur[NI];
+  if (base < p1) load(cur, base);
+  for (; base < p1; base += 4 * P) {
+    uint4 nxt[NI];
+    const bool more = base + 4 * P < p1;
+    if (more) load(nxt, base + 4 * P);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      *reinterpret_cast<uint4*>(rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = cur[j];
+    lds_wave_sync();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      uint4 a[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        a[s] = *reinterpret_cast<const uint4*>(rows + (16 * tt + n) * PADB + (kg + 4 * s) * 16);
+      const int pos = base + 16 * tt + 4 * kg;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[s]), bq[rt][s], acc, 0, 0, 0);
+        if (srow[rt] >= 0) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = pos + i <= last[rt] ? acc[i] * scale : __int_as_float(0x7fc00000);
+          float* Srow = S + srow[rt] * L;
+          if (vec_store && pos + 3 < p1) {
+            *reinterpret_cast<float4*>(Srow + pos) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (pos + i < p1) Srow[pos + i] = v[i];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // reads of this round precede the next writes
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
+    }
+  }
+}
+
+__global__ void mq_counts_kernel(int32_t* __restrict__ krow, int64_t rows, int M, int Hq, int L, int k) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)((r / Hq) % M);
+    krow[r] = min(k, L - M + t + 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Wave dot-reduction scores for fp32 or bf16 rows, NH query heads per task.
 // A row of D elements is 16*LPR bytes: LPR lanes load 16 B each, RPW = 64/LPR
 // rows per wave load. Each lane keeps its 16-byte slice of q for every head,
@@ -614,9 +723,6 @@ void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, f
   launch_mfma<MFMA_SAMPLE>(a, sample_chunk, (unsigned)((nch + 3) / 4), o, st);
 }
 
-#ifndef TKA_CAND_CHUNK
-#define TKA_CAND_CHUNK 1024  // positions per workgroup: many short workgroups, no long tail
-#endif
 
 static int device_cus() {
   static int cached[64];
@@ -656,6 +762,41 @@ void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st
     case 128: launch_cand_persistent<128>(a, o, st); break;
     default: launch_cand_persistent<256>(a, o, st); break;
   }
+}
+
+template <int D, int RT>
+static void launch_mq_t(const ScoreArgs& a, hipStream_t st) {
+  const int chunk = mfma_scan_chunk(a);
+  const size_t lds = (size_t)4 * 32 * (D * 2 + 16);
+  ensure_dynamic_lds((const void*)score_mq_kernel<D, RT>, lds);
+  dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv);
+  hipLaunchKernelGGL((score_mq_kernel<D, RT>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.M, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk,
+                     a.scores);
+}
+
+template <int D>
+static void launch_mq_d(const ScoreArgs& a, hipStream_t st) {
+  const int R = a.M * a.G;
+  if (R <= 16) launch_mq_t<D, 1>(a, st);
+  else if (R <= 32) launch_mq_t<D, 2>(a, st);
+  else launch_mq_t<D, 4>(a, st);
+}
+
+void launch_score_mq(const ScoreArgs& a, hipStream_t st) {
+  if (a.nrows <= 0) return;
+  switch (a.d) {
+    case 64: launch_mq_d<64>(a, st); break;
+    case 128: launch_mq_d<128>(a, st); break;
+    default: launch_mq_d<256>(a, st); break;
+  }
+}
+
+void launch_mq_counts(int32_t* krow, int64_t rows, int M, int Hq, int L, int k, hipStream_t st) {
+  if (rows <= 0) return;
+  const int64_t blocks = (rows + 255) / 256;
+  hipLaunchKernelGGL(mq_counts_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, krow, rows,
+                     M, Hq, L, k);
 }
 
 void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st) {
@@ -699,6 +840,10 @@ bool score_uses_mfma(int dtype_bf16, int G) { return dtype_bf16 && G >= 2 && G <
 
 void launch_score_dense(const ScoreArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return;
+  if (a.M > 1) {
+    launch_score_mq(a, st);
+    return;
+  }
   if (score_uses_mfma(a.bf16, a.G)) {
     MfmaOut o{};
     o.S = a.scores;
