@@ -406,7 +406,37 @@ def main():
         extras["hisa"] = {"block_size": bsz, "top_blocks": KB, "top_k": w.k, "decode_ms": round(t_h, 4),
                           "decode_queries_per_s": round(w.B / (t_h / 1e3), 1),
                           "algorithmic_bytes": h_bytes, "gbps": round(h_bytes / (t_h / 1e3) / 1e9, 1)}
+        # the step's cache append on the same caches: row L-1 rewritten with its own values (no change),
+        # alone and with the block-mean refresh of its block
+        kn = Kt[:, :, w.L - 1].contiguous()
+        vn = Vt[:, :, w.L - 1].contiguous()
+        t_app = time_loop(lambda: tka.topk_cache_append(ph, kn, vn, Kt, Vt), args.steps)
+        t_appm = time_loop(lambda: tka.topk_cache_append(ph, kn, vn, Kt, Vt, means=hmeans), args.steps)
+        extras["append"] = {"kv_rows_us": round(t_app * 1e3, 2), "kv_rows_and_block_mean_us": round(t_appm * 1e3, 2)}
         del h_ws, hmeans
+        torch.cuda.empty_cache()
+        # several causal queries per sequence (speculative or chunked decoding) on the same caches
+        if dt == tka.TKA_BF16 and 4 * w.G <= 64:
+            log("[bench] four queries per sequence")
+            M = 4
+            qm_np = fx.encode(fx.normal(97, 0, w.B * M * w.Hq * w.d), fx.BF16).reshape(w.B, M, w.Hq, w.d)
+            qm = torch.from_numpy(qm_np.view(np.int16)).view(torch.bfloat16).cuda()
+            pm = tka.problem(tka.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, n_queries=M)
+            mq_out = torch.empty((w.B, M, w.Hq, w.d), dtype=torch.float32, device="cuda")
+            mq_idx = torch.empty((w.B, M, w.Hq, w.k), dtype=torch.int32, device="cuda")
+            mq_ws = torch.empty(tka.topk_decode_workspace_size(pm), dtype=torch.uint8, device="cuda")
+            t_mq = time_loop(lambda: tka.topk_decode(pm, qm, Kt, Vt, out=mq_out, idx_out=mq_idx, ws=mq_ws),
+                             args.steps)
+            mq_sc = torch.empty(tka.score_shape(pm), dtype=torch.float32, device="cuda")
+            t_mqs = time_loop(lambda: tka.topk_attn_score(pm, qm, Kt, scores=mq_sc), args.steps)
+            flops = 2.0 * w.B * M * w.Hq * w.L * w.d
+            sbytes = w.B * w.Hkv * w.L * w.d * 2 + w.B * M * w.Hq * w.L * 4
+            extras["multi_query"] = {"queries_per_seq": M, "decode_ms": round(t_mq, 4),
+                                     "query_tokens_per_s": round(w.B * M / (t_mq / 1e3), 1),
+                                     "score_ms": round(t_mqs, 4),
+                                     "score_tflops": round(flops / (t_mqs / 1e3) / 1e12, 2),
+                                     "score_gbps": round(sbytes / (t_mqs / 1e3) / 1e9, 1)}
+            del mq_ws, mq_sc
     result["extras"] = extras
     del Kt, Vt, sc, ws
     torch.cuda.empty_cache()
