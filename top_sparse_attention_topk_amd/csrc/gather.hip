@@ -13,9 +13,9 @@
 //   2. computes the logits z = scale <q, K_t> (16-byte row gathers, lane
 //      groups reduce with xor shuffles) - or takes them from the selected
 //      scores when the caller passes them, skipping the K rows,
-//   3. max / exp / sum per head in fp32 (fixed-order wave reductions),
-//   4. gathers the V rows and accumulates w * V in fp32 (K and V rows are read
-//      once: non-temporal loads),
+//   3. the maximum logit per head,
+//   4. gathers the V rows and accumulates p V and p, p = exp(z - max), in fp32
+//      (K and V rows are read once: non-temporal loads; sums in a fixed order),
 //   5. writes o (one split) or (M, l, acc) partials merged in split order.
 #include <math.h>
 
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   constexpr int UNR = 8;
   extern __shared__ uint4 smem_raw[];
   float* red = reinterpret_cast<float*>(smem_raw);  // [NH][D]
-  float* stat = red + NH * D;                      // M[NH], l[NH]
-  int32_t* tok = reinterpret_cast<int32_t*>(stat + 2 * NH);
+  float* stat = red + NH * D;                      // M[NH], l[NH], wave maxima [4][NH]
+  int32_t* tok = reinterpret_cast<int32_t*>(stat + 6 * NH);
   float* lg = reinterpret_cast<float*>(tok + a.span);  // [NH][span]
 
   const int task = blockIdx.y, split = blockIdx.x;
@@ -79,7 +79,25 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
 
   // 1. tokens (and the given logits)
   const int64_t nb = (int64_t)a.n_idx * (a.unit > 0 ? a.unit : 1);
-  for (int i = t; i < ne; i += 256) {
+  const bool vec = a.unit == 0 && (ne & 3) == 0 && ((reinterpret_cast<uintptr_t>(list + e0) & 15) == 0) &&
+                   (!SEL || (reinterpret_cast<uintptr_t>(sl_list + e0) & 15) == 0);
+  if (vec) {  // position lists: 16-byte loads, all of a thread's issued together
+#pragma unroll 4
+    for (int i = 4 * t; i < ne; i += 1024) {
+      const int4 v = *reinterpret_cast<const int4*>(list + e0 + i);
+      float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (SEL) z = *reinterpret_cast<const float4*>(sl_list + e0 + i);
+      const int tv[4] = {v.x, v.y, v.z, v.w};
+      const float zv[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int tk = (tv[c] >= 0 && tv[c] < lim) ? tv[c] : -1;
+        tok[i + c] = tk;
+        if (SEL) lg[i + c] = tk >= 0 ? zv[c] : -INFINITY;
+      }
+    }
+  }
+  for (int i = vec ? ne : t; i < ne; i += 256) {
     const int64_t e = e0 + i;
     int tk = -1;
     if (a.unit == 0) {
@@ -148,32 +166,36 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
     __syncthreads();
   }
 
-  // 3. softmax statistics per head (one wave per head, fixed order)
-  for (int h = w; h < NH; h += 4) {
-    float* lh = lg + h * a.span;
-    float mx = -INFINITY;
-    for (int i = lane; i < ne; i += 64) mx = fmaxf(mx, lh[i]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int i = lane; i < ne; i += 64) {
-      const float p = (mx == -INFINITY) ? 0.f : expf(lh[i] - mx);
-      lh[i] = p;
-      sum += p;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      stat[h] = mx;
-      stat[NH + h] = sum;
+  // 3. the maximum logit per head (every thread takes a strided share; waves combine through LDS)
+  float* wmax = stat + 2 * NH;  // [4][NH]
+  {
+    float mloc[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) mloc[h] = -INFINITY;
+    for (int i = t; i < ne; i += 256)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) mloc[h] = fmaxf(mloc[h], lg[h * a.span + i]);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float m = wave_max(mloc[h]);
+      if (lane == 0) wmax[w * NH + h] = m;
     }
   }
   __syncthreads();
-
-  // 4. V gather and weighted accumulation
-  float acc[NH][EPL];
+  float mx[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
+    mx[h] = fmaxf(fmaxf(wmax[h], wmax[NH + h]), fmaxf(wmax[2 * NH + h], wmax[3 * NH + h]));
+
+  // 4. V gather and weighted accumulation; the weights p = exp(z - max) are formed here, and each
+  //    lane group sums the weights of its own rows (the sums are combined in a fixed order below)
+  float acc[NH][EPL], psum[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    psum[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
   for (int ib = w * RPW * UNR; ib < ne; ib += 4 * RPW * UNR) {
     uint4 raw[UNR];
 #pragma unroll
@@ -190,7 +212,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
         U::run(raw[u], vf);
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-          const float p = lg[h * a.span + i];
+          const float z = lg[h * a.span + i];
+          const float p = (mx[h] == -INFINITY) ? 0.f : expf(z - mx[h]);
+          psum[h] += p;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
         }
@@ -200,22 +224,28 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
 #pragma unroll
   for (int o = LPR; o < 64; o <<= 1)
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int h = 0; h < NH; ++h) {
+      psum[h] += __shfl_xor(psum[h], o, kWave);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, kWave);
+    }
   // waves add their sums in a fixed order
   for (int ww = 0; ww < 4; ++ww) {
     if (w == ww && grp == 0) {
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int h = 0; h < NH; ++h) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           float* r = red + h * D + sub * EPL + e;
           *r = (ww == 0) ? acc[h][e] : *r + acc[h][e];
         }
+        if (sub == 0) stat[NH + h] = (ww == 0) ? psum[h] : stat[NH + h] + psum[h];
+      }
     }
     __syncthreads();
   }
+  if (t < NH) stat[t] = mx[t];
+  __syncthreads();
 
   // 5. output or partials
   if (a.nsplit == 1) {
@@ -293,7 +323,7 @@ GatherPlan plan_gather(const GatherArgs& a) {
 
 template <bool BF16, int D, int NH, bool SEL>
 static void launch_g(const GatherK& k, const GatherPlan& pl, hipStream_t st) {
-  const size_t lds = sizeof(float) * (NH * D + 2 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
+  const size_t lds = sizeof(float) * (NH * D + 6 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
   hipLaunchKernelGGL((gather_kernel<BF16, D, NH, SEL>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
   if (pl.nsplit > 1)
     hipLaunchKernelGGL((gather_merge_kernel<D, NH>), dim3(pl.tasks), dim3(256), 0, st, k.part, k.out, pl.nsplit,
