@@ -513,7 +513,6 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 constexpr int PF_NW = 16;  // waves of the prefilter kernels (1024 threads)
 constexpr int PF_T = 64 * PF_NW;
-constexpr int PF_RS = 8;   // samples held per thread: nsamp <= 8192
 constexpr int PF_RC = 12;  // candidates held per thread: capacity <= 12288
 
 constexpr int PF_STASH = 2048;  // elements of the critical bin ranked one by one
@@ -580,63 +579,129 @@ __device__ void block_min_max(KeyOf key_of, uint32_t cnt, PfSmem& ps, uint32_t* 
   *mx_out = gmx;
 }
 
-// Threshold of a row: the key of its r-th largest sample (the sample's
-// value, ties irrelevant). Also clears the row's counters and flags.
-__global__ __launch_bounds__(1024) void prefilter_threshold_kernel(const float* __restrict__ samp, int nsamp, int r,
-                                                                   float* __restrict__ T,
-                                                                   uint32_t* __restrict__ cnt,
-                                                                   uint32_t* __restrict__ row_flag,
-                                                                   uint32_t* __restrict__ group_flag, int G) {
-  __shared__ SelSmem sm;
-  __shared__ PfSmem ps;
-  const int64_t row = blockIdx.x;
-  const int t = threadIdx.x;
-  if (t == 0) {
+// Threshold of a row: the key of its r-th largest sample. One wave per row,
+// the row's samples held in registers (RS per lane, lane-strided). Radix
+// levels of 1024 bins over the current key range [lo, lo + span]: the bin
+// holding the r-th key (counting from the top) becomes the next range, until
+// it is one key wide or holds at most 64 samples, which are then ranked one
+// by one. The result is exact: every level narrows the range by 2^10. The
+// wave also clears the row's counters and flags. No workgroup barriers.
+template <int RS>
+__global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* __restrict__ samp, int nsamp, int r,
+                                                                  int64_t n_rows, float* __restrict__ T,
+                                                                  uint32_t* __restrict__ cnt,
+                                                                  uint32_t* __restrict__ row_flag,
+                                                                  uint32_t* __restrict__ group_flag, int G) {
+  __shared__ uint32_t hist_all[4][1024];
+  __shared__ uint32_t list_all[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= n_rows) return;
+  uint32_t* hist = hist_all[w];
+  uint32_t* lst = list_all[w];
+  if (lane == 0) {
     cnt[row] = 0;
     row_flag[row] = 0;
     if (row % G == 0) group_flag[row / G] = 0;
-    ps.scnt = 0;
   }
   if (r > nsamp) {
-    if (t == 0) T[row] = key_value(0u);  // too few samples: keep everything
+    if (lane == 0) T[row] = key_value(0u);  // too few samples: keep everything
     return;
   }
   const float* s = samp + row * nsamp;
-  uint32_t key[PF_RS];
+  uint32_t key[RS];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  float raw[RS];
 #pragma unroll
-  for (int j = 0; j < PF_RS; ++j) {
-    const int e = t + PF_T * j;
-    key[j] = e < nsamp ? score_key(s[e]) : 0u;
-  }
-  auto key_of = [&](int j) { return key[j]; };
-  uint32_t mn, mx;
-  block_min_max<PF_RS>(key_of, (uint32_t)nsamp, ps, &mn, &mx);
-  int shift;
-  relative_bin<PF_RS>(key_of, (uint32_t)nsamp, mn, mx, (uint32_t)r, sm, &shift);
-  const uint32_t bin = sm.res[0], need = (uint32_t)r - sm.res[1];
+  for (int j = 0; j < RS; ++j) raw[j] = s[min(lane + 64 * j, nsamp - 1)];  // all loads in flight together
 #pragma unroll
-  for (int j = 0; j < PF_RS; ++j)
-    if (t + PF_T * j < nsamp && ((key[j] - mn) >> shift) == bin) {
-      const uint32_t slot = atomicAdd(&ps.scnt, 1u);
-      if (slot < PF_STASH) ps.skey[slot] = key[j];
-    }
-  __syncthreads();
-  const uint32_t m = ps.scnt;
-  if (m > PF_STASH) {  // a crowded bin: its lower edge is a valid (lower) threshold
-    if (t == 0) T[row] = key_value(mn + (bin << shift));
-    return;
+  for (int j = 0; j < RS; ++j) {
+    const bool ok = lane + 64 * j < nsamp;
+    key[j] = ok ? score_key(raw[j]) : 0u;
+    mn = ok ? min(mn, key[j]) : mn;
+    mx = ok ? max(mx, key[j]) : mx;
   }
-  for (uint32_t i = t; i < m; i += PF_T) {
-    const uint32_t v = ps.skey[i];
-    uint32_t gt = 0, ge = 0;
-    for (uint32_t u = 0; u < m; ++u) {
-      gt += ps.skey[u] > v;
-      ge += ps.skey[u] >= v;
-    }
-    if (gt < need && need <= ge) ps.tval = v;  // every writer stores the same key
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
   }
-  __syncthreads();
-  if (t == 0) T[row] = key_value(ps.tval);
+  uint32_t lo = mn, span = mx - mn, need = (uint32_t)r, result = mn;
+  for (;;) {
+    const int shift = span >= 1024u ? (32 - __clz(span)) - 10 : 0;  // span >> shift < 1024
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hist[lane + 64 * i] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < RS; ++j)
+      if (lane + 64 * j < nsamp && key[j] - lo <= span) atomicAdd(&hist[(key[j] - lo) >> shift], 1u);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    // lane l owns bins [16 l, 16 l + 16); counts above a lane's bins from a prefix over lanes
+    uint32_t c[16], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      c[i] = hist[16 * lane + i];
+      sum += c[i];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t above = tot - incl;
+    const uint64_t hit = ballot(above < need && need <= above + sum);
+    if (hit == 0) {  // not reached: 1 <= need <= tot at every level
+      result = lo;
+      break;
+    }
+    const int h = (int)__builtin_ctzll(hit);
+    uint32_t bin = 0, abv = 0;
+    if (lane == h) {
+      uint32_t acc = above;
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        if (acc + c[i] >= need) {
+          bin = 16 * lane + i;
+          abv = acc;
+          break;
+        }
+        acc += c[i];
+      }
+    }
+    bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, h);
+    abv = (uint32_t)__builtin_amdgcn_readlane((int)abv, h);
+    need -= abv;  // rank of the answer inside the bin, from its top
+    const uint32_t blo = lo + (bin << shift);
+    if (shift == 0) {  // one key wide
+      result = blo;
+      break;
+    }
+    const uint32_t inbin = hist[bin];
+    if (inbin <= 64u) {  // rank the bin's samples one by one
+      uint32_t base = 0;
+#pragma unroll
+      for (int j = 0; j < RS; ++j) {
+        const bool in = lane + 64 * j < nsamp && key[j] - lo <= span && ((key[j] - lo) >> shift) == bin;
+        const uint64_t m = ballot(in);
+        if (in) lst[base + count_below(m)] = key[j];
+        base += (uint32_t)__builtin_popcountll(m);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t v = lane < (int)inbin ? lst[lane] : 0u;
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t u = 0; u < inbin; ++u) {
+        const uint32_t x = lst[u];
+        gt += x > v;
+        ge += x >= v;
+      }
+      const uint64_t ok = ballot(lane < (int)inbin && gt < need && need <= ge);
+      result = ok ? (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(ok)) : blo;
+      break;
+    }
+    lo = blo;
+    span = (1u << shift) - 1u;
+    __builtin_amdgcn_wave_barrier();  // this level's bin reads precede the next level's clearing
+  }
+  if (lane == 0) T[row] = key_value(result);
 }
 
 // Exact top-k of a row from its (unordered) candidates, whose keys are all
@@ -1144,8 +1209,17 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
 
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
                                 uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st) {
-  hipLaunchKernelGGL(prefilter_threshold_kernel, dim3((unsigned)n_rows), dim3(PF_T), 0, st, samp, nsamp, r, T, cnt,
-                     row_flag, group_flag, G);
+  if (n_rows <= 0) return;
+  const dim3 grid((unsigned)((n_rows + 3) / 4));
+  if (nsamp <= 2048)
+    hipLaunchKernelGGL(prefilter_threshold_kernel<32>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
+                       row_flag, group_flag, G);
+  else if (nsamp <= 4096)
+    hipLaunchKernelGGL(prefilter_threshold_kernel<64>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
+                       row_flag, group_flag, G);
+  else  // the plan keeps nsamp <= 8192
+    hipLaunchKernelGGL(prefilter_threshold_kernel<128>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
+                       row_flag, group_flag, G);
 }
 
 static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((n + 31) / 32); }
