@@ -736,11 +736,15 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
     const uint32_t* cb = cbits + row * capg;
     const int32_t* cp = cpos + row * capg;
     const uint32_t T0 = score_key(Tv[row]);
+    // the thread's candidates, every load of the batch in flight together (indices past the
+    // count re-read the last candidate and are masked below)
     uint32_t bits[PF_RC];
+    int32_t pos[PF_RC];
 #pragma unroll
     for (int j = 0; j < PF_RC; ++j) {
-      const uint32_t e = t + PF_T * j;
-      bits[j] = e < nc ? cb[e] : 0u;
+      const uint32_t e = min((uint32_t)(t + PF_T * j), nc - 1u);
+      bits[j] = cb[e];
+      pos[j] = cp[e];
     }
     auto key_of = [&](int j) { return score_key(__uint_as_float(bits[j])); };
     const int words = (n + 31) >> 5;
@@ -755,14 +759,13 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
     relative_bin<PF_RC>(key_of, nc, T0, mx, (uint32_t)kk, sm, &shift);
     const uint32_t bin = sm.res[0], need = (uint32_t)kk - sm.res[1];
     // keys above the critical bin are kept; the bin's elements go to the stash
-    // (positions are read here and again below rather than held: fewer registers)
 #pragma unroll
     for (int j = 0; j < PF_RC; ++j) {
       const uint32_t e = t + PF_T * j;
       if (e >= nc) continue;
       const uint32_t d = (key_of(j) - T0) >> shift;
       if (d < bin) continue;
-      const int32_t p = cp[e];
+      const int32_t p = pos[j];
       if (d > bin) {
         atomicOr(&bm[p >> 5], 1u << (p & 31));
       } else {
@@ -805,7 +808,7 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
       for (int j = 0; j < PF_RC; ++j) {
         const uint32_t e = t + PF_T * j;
         if (e >= nc || ((key_of(j) - T0) >> shift) < bin) continue;
-        const int32_t p = cp[e];
+        const int32_t p = pos[j];
         const uint32_t word = bm[p >> 5];
         if (!((word >> (p & 31)) & 1u)) continue;
         const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
