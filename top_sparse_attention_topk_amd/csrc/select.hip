@@ -871,28 +871,48 @@ __device__ __forceinline__ uint64_t ak_mass(float v, float M) {
   return (uint64_t)(w * 1099511627776.f);  // 2^40: exact scaling, the conversion truncates
 }
 
+// Radix levels of the adaptive search: 11, 11 and 10 bits of the key.
+__device__ __forceinline__ int ak_shift(int lv) { return lv == 0 ? 21 : (lv == 1 ? 10 : 0); }
+__device__ __forceinline__ int ak_bins(int lv) { return lv == 2 ? 1024 : 2048; }
+__device__ __forceinline__ uint32_t ak_digit(uint32_t key, int lv) { return (key >> ak_shift(lv)) & (ak_bins(lv) - 1); }
+__device__ __forceinline__ bool ak_in_range(uint32_t key, int lv, uint32_t prefix) {
+  return lv == 0 || (key >> ak_shift(lv - 1)) == prefix;
+}
+
+// 28 KiB of histograms, so that four rows fit one CU. Levels 0 and 1: mass[2048] then
+// cnt[2048]; level 2: mass[1024], cnt[1024], then a count histogram per wave [4][1024].
+constexpr int AK_BUF = 3584;
 struct AkSmem {
-  uint64_t mass[NB0];
-  uint32_t cnt[NB0];
+  uint64_t buf[AK_BUF];
   uint64_t wm[SW];
   uint32_t wc[SW];
   uint32_t wk[SW];
+  uint32_t egt[SW], eeq[SW];  // per wave: keys above T, keys equal to T
   uint64_t res_mass;
   uint32_t res_bin, res_cnt;
 };
-static_assert(sizeof(SelSmem) <= sizeof(uint64_t) * NB0, "the emission state lives in the mass histogram");
+__device__ __forceinline__ uint64_t* ak_mass_h(AkSmem& sm) { return sm.buf; }
+__device__ __forceinline__ uint32_t* ak_cnt_h(AkSmem& sm, int lv) {
+  return reinterpret_cast<uint32_t*>(sm.buf + (lv == 2 ? 1024 : 2048));
+}
+__device__ __forceinline__ uint32_t* ak_wave_h(AkSmem& sm, int w) {
+  return reinterpret_cast<uint32_t*>(sm.buf + 1536) + w * 1024;
+}
+static_assert(1536 + SW * 1024 / 2 <= AK_BUF && 2048 + 2048 / 2 <= AK_BUF, "histogram views exceed the buffer");
+constexpr int AK_UNR = 8;  // float4 loads in flight per lane in the streaming passes
+constexpr int AK_EJ = 16;  // lane-strided elements per lane per round of the emission pass
 
 // Bin b (of nb, bins ascending with the key) where the mass of the bins above
 // it stays below need and reaching into b meets it. Writes the bin, the mass
 // and the count of the bins above it to sm.res_*.
-__device__ void ak_find_bin(AkSmem& sm, int nb, uint64_t need) {
+__device__ void ak_find_bin(AkSmem& sm, const uint64_t* mass, const uint32_t* cnt, int nb, uint64_t need) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int per = nb / ST;
   uint64_t m = 0;
   uint32_t c = 0;
   for (int i = 0; i < per; ++i) {
-    m += sm.mass[t * per + i];
-    c += sm.cnt[t * per + i];
+    m += mass[t * per + i];
+    c += cnt[t * per + i];
   }
   // inclusive prefix over threads (bins ascending), then the part above this thread's bins
   uint64_t im = m;
@@ -927,14 +947,14 @@ __device__ void ak_find_bin(AkSmem& sm, int nb, uint64_t need) {
     uint64_t acc = above;
     for (int i = per - 1; i >= 0; --i) {
       const int b = t * per + i;
-      if (acc + sm.mass[b] >= need) {
+      if (acc + mass[b] >= need) {
         sm.res_bin = (uint32_t)b;
         sm.res_mass = acc;
         sm.res_cnt = cabove;
         break;
       }
-      acc += sm.mass[b];
-      cabove += sm.cnt[b];
+      acc += mass[b];
+      cabove += cnt[b];
     }
   }
   __syncthreads();
@@ -960,12 +980,12 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
   const int r0 = min(n, w * seg), r1 = min(n, r0 + seg);
   // 1. the row maximum in the select order (NaN lowest)
   uint32_t mk = 0;
-  for (int base = r0; base < r1; base += 256 * UNR) {
-    float v[UNR][4];
+  for (int base = r0; base < r1; base += 256 * AK_UNR) {
+    float v[AK_UNR][4];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+    for (int u = 0; u < AK_UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
+    for (int u = 0; u < AK_UNR; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (base + u * 256 + 4 * lane + j < r1) mk = max(mk, score_key(v[u][j]));
@@ -982,34 +1002,46 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
   uint32_t c_gt = 0, prefix = 0;
   int64_t k_eps = 0;
   bool found = true;
+  // the last level also counts, per wave, the keys above its range and its keys per digit (for
+  // the emission's per-wave output bases)
+  uint32_t* whist = ak_wave_h(sm, w);
+  uint64_t* mass = ak_mass_h(sm);
+  uint32_t wgt = 0;
   for (int lv = 0; lv <= 2; ++lv) {
-    const int nb = lv_bins(lv);
+    const int nb = ak_bins(lv);
+    uint32_t* cnt = ak_cnt_h(sm, lv);
     for (int i = t; i < nb; i += ST) {
-      sm.mass[i] = 0;
-      sm.cnt[i] = 0;
+      mass[i] = 0;
+      cnt[i] = 0;
     }
+    if (lv == 2)
+      for (int i = lane; i < 1024; i += 64) whist[i] = 0;
     __syncthreads();
-    for (int base = r0; base < r1; base += 256 * UNR) {
-      float v[UNR][4];
+    for (int base = r0; base < r1; base += 256 * AK_UNR) {
+      float v[AK_UNR][4];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+      for (int u = 0; u < AK_UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
+      for (int u = 0; u < AK_UNR; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t key = score_key(v[u][j]);
-          if (base + u * 256 + 4 * lane + j < r1 && lv_in_range(key, lv, prefix)) {
-            const uint32_t d = lv_digit(key, lv);
-            atomicAdd(&sm.cnt[d], 1u);
+          const bool valid = base + u * 256 + 4 * lane + j < r1;
+          if (valid && ak_in_range(key, lv, prefix)) {
+            const uint32_t d = ak_digit(key, lv);
+            atomicAdd(&cnt[d], 1u);
+            if (lv == 2) atomicAdd(&whist[d], 1u);
             const uint64_t m = ak_mass(v[u][j], M);
-            if (m) atomicAdd(reinterpret_cast<unsigned long long*>(&sm.mass[d]), (unsigned long long)m);
+            if (m) atomicAdd(reinterpret_cast<unsigned long long*>(&mass[d]), (unsigned long long)m);
+          } else if (lv == 2 && valid && (key >> ak_shift(1)) > prefix) {
+            ++wgt;
           }
         }
     }
     __syncthreads();
     if (lv == 0) {
       uint64_t part = 0;
-      for (int i = t; i < nb; i += ST) part += sm.mass[i];
+      for (int i = t; i < nb; i += ST) part += mass[i];
       part = wave_sum(part);
       if (lane == 0) sm.wm[w] = part;
       __syncthreads();
@@ -1022,10 +1054,10 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
         break;
       }
     }
-    ak_find_bin(sm, nb, need - m_gt);
+    ak_find_bin(sm, mass, cnt, nb, need - m_gt);
     m_gt += sm.res_mass;
     c_gt += sm.res_cnt;
-    prefix = (prefix << lv_bits(lv)) | sm.res_bin;
+    prefix = (prefix << (lv == 2 ? 10 : 11)) | sm.res_bin;
     __syncthreads();
   }
   uint32_t ties = 0;
@@ -1046,20 +1078,55 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
   const bool direct = found && k == k_eps;
   if (t == 0) row_flag[row] = direct ? 0u : 1u;
   if (!direct) return;  // workgroup-uniform
-  // 3. emit: every key above T and the first `ties` keys equal to T, in position order (the
-  // emission state reuses the mass histogram, whose last reads ended at the barrier above)
+  // 3. emit: every key above T and the first `ties` keys equal to T, in position order. Wave w's
+  // keys above T: those above the last level's range plus its digits above T's; equal: T's digit.
   int32_t* oidx = idx + row * k_max;
   float* osel = sel ? sel + row * k_max : nullptr;
   for (int j = (int)k + t; j < k_max; j += ST) {
     oidx[j] = -1;
     if (osel) osel[j] = -INFINITY;
   }
-  emit_segments(
-      [&](uint32_t e, uint32_t& bits, int32_t& pos) {
-        pos = r0 + (int)e;
-        bits = __float_as_uint(s[pos]);
-      },
-      (uint32_t)(r1 - r0), prefix, ties, *reinterpret_cast<SelSmem*>(sm.mass), oidx, osel, (uint32_t)k);
+  const uint32_t T = prefix, dT = T & (NB1 - 1);
+  {
+    uint32_t g = 0;
+    for (int i = lane; i < NB1; i += 64) g += (uint32_t)i > dT ? whist[i] : 0u;
+    g = wave_sum(g) + wave_sum(wgt);
+    if (lane == 0) {
+      sm.egt[w] = g;
+      sm.eeq[w] = whist[dT];
+    }
+  }
+  __syncthreads();
+  uint32_t run = 0, eqrun = 0;  // this wave's first output slot and first tie rank
+  for (int i = 0; i < w; ++i) {
+    const uint32_t take = ties > eqrun ? min(ties - eqrun, sm.eeq[i]) : 0u;
+    run += sm.egt[i] + take;
+    eqrun += sm.eeq[i];
+  }
+  // lane-strided rounds, so that a ballot over one element slot covers consecutive positions
+  for (int base = r0; base < r1; base += 64 * AK_EJ) {
+    float v[AK_EJ];
+#pragma unroll
+    for (int j = 0; j < AK_EJ; ++j) v[j] = s[min(base + 64 * j + lane, r1 - 1)];
+#pragma unroll
+    for (int j = 0; j < AK_EJ; ++j) {
+      const int p = base + 64 * j + lane;
+      const uint32_t key = score_key(v[j]);
+      const bool valid = p < r1;
+      const bool gt = valid && key > T;
+      const bool eq = valid && key == T;
+      const uint64_t be = ballot(eq);
+      const bool take = gt || (eq && eqrun + (uint32_t)count_below(be) < ties);
+      const uint64_t bs = ballot(take);
+      const uint32_t slot = run + (uint32_t)count_below(bs);
+      if (take && slot < (uint32_t)k) {  // exactly k keys are taken
+        oidx[slot] = p;
+        if (osel) osel[slot] = v[j];
+      }
+      run += (uint32_t)__popcll(bs);
+      eqrun += (uint32_t)__popcll(be);
+    }
+  }
 }
 
 // tau = 1 - (mass of the kept positions) / W, the kept mass summed exactly.
