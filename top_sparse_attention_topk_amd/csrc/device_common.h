@@ -85,4 +85,14 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// Workgroups are dispatched to the 8 XCDs (each with its own L2) in turn by
+// their linear id. This bijection on [0, total) gives consecutive logical ids
+// to the workgroups of one XCD, in their dispatch order, so that work sharing
+// data (the query heads of one KV group) shares an L2.
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ unsigned xcd_logical_id(unsigned hid, unsigned total) {
+  const unsigned xcd = hid % kXcds, i = hid / kXcds, q = total / kXcds, r = total % kXcds;
+  return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
+}
+
 }  // namespace tka

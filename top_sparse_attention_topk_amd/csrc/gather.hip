@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   int32_t* tok = reinterpret_cast<int32_t*>(stat + 6 * NH);
   float* lg = reinterpret_cast<float*>(tok + a.span);  // [NH][span]
 
-  const int task = blockIdx.y, split = blockIdx.x;
+  // workgroup ids remapped so that the tasks of one KV group share an XCD (and its L2)
+  const unsigned lid = xcd_logical_id(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int task = (int)(lid / gridDim.x), split = (int)(lid % gridDim.x);
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int sub = lane % LPR, grp = lane / LPR;
   int b, h0, g;

@@ -9,8 +9,10 @@
 
 namespace tka {
 
-// One row (b, query head) per blockIdx.y; blockIdx.x takes bpw of its K_B kept
-// blocks. Candidate slot t = j*bsz + i is token blk[j]*bsz + i; its score
+// One row (b, query head) per logical grid row; a workgroup takes bpw of its
+// K_B kept blocks. Workgroup ids are remapped so that the rows of one KV
+// group (which often keep the same blocks) run on one XCD and share its L2.
+// Candidate slot t = j*bsz + i is token blk[j]*bsz + i; its score
 // scale * <q, K_token> goes to cand[row, t], NaN where there is no token
 // (blk[j] = -1 or past L). A lane group of LPR lanes holds one key row
 // (16 bytes per lane), RPW rows per wave load, UNR loads in flight. The first
@@ -27,14 +29,17 @@ __global__ __launch_bounds__(256) void hisa_token_score_kernel(const void* __res
   constexpr int LPR = D * ES / 16;
   constexpr int RPW = 64 / LPR;
   constexpr int UNR = 4;
-  const int64_t row = blockIdx.y;
+  // logical (row, block slice): the rows of one KV group are adjacent, so they share an XCD
+  const unsigned lid = xcd_logical_id(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int64_t row = lid / gridDim.x;
+  const unsigned bx = lid % gridDim.x;
   const int b = (int)(row / Hq), h = (int)(row % Hq), g = h / G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPR, grp = lane / LPR;
   const int32_t* lb = blk + row * KB;
   const int64_t ncand = (int64_t)KB * bsz;
   float* crow = cand + row * ncand;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (bx == 0 && threadIdx.x == 0) {
     int64_t n = 0;
     for (int j = 0; j < KB; ++j)
       if (lb[j] >= 0) n += min((int64_t)bsz, (int64_t)L - (int64_t)lb[j] * bsz);
@@ -43,7 +48,7 @@ __global__ __launch_bounds__(256) void hisa_token_score_kernel(const void* __res
   float qf[EPL];
   U::run(ld16(reinterpret_cast<const uint8_t*>(qv) + (row * D + sub * EPL) * ES), qf);
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(Kv) + ((int64_t)b * sb + (int64_t)g * sh) * ES;
-  const int64_t t0 = (int64_t)blockIdx.x * bpw * bsz, t1 = min(t0 + (int64_t)bpw * bsz, ncand);
+  const int64_t t0 = (int64_t)bx * bpw * bsz, t1 = min(t0 + (int64_t)bpw * bsz, ncand);
   for (int64_t base = t0 + wave * RPW * UNR; base < t1; base += 4 * RPW * UNR) {
     uint4 raw[UNR];
     int pos[UNR];
