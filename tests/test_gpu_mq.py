@@ -19,13 +19,18 @@ from tests.gpu_common import dev, exact_score_bound, say, tka, tol
 
 pytestmark = pytest.mark.gpu
 
-# name: (B, M, Hq, Hkv, d, L, k)
+# name: (B, M, Hq, Hkv, d, L, k); from L = 8192 (and M <= 4, k <= L/8) the fused step takes the
+# candidate prefilter (sampled thresholds, one scan of K for all M queries, exact select on the
+# candidates), which must give what the dense composition gives, bitwise
 CASES = {
     "g4-m4": (2, 4, 8, 2, 128, 3000, 256),
     "g8-m8": (1, 8, 16, 2, 128, 5000, 512),
     "g1-m3": (2, 3, 4, 4, 64, 1000, 100),
     "k-above-visible": (1, 5, 4, 1, 128, 300, 298),
     "d256-m2": (1, 2, 16, 2, 256, 2000, 128),
+    "prefilter-g8-m4": (2, 4, 16, 2, 128, 16384, 512),
+    "prefilter-g16-m3": (1, 3, 32, 2, 128, 12000, 700),
+    "prefilter-g4-m2-d64": (2, 2, 8, 2, 64, 8192, 1024),
 }
 
 
@@ -41,6 +46,26 @@ def make(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_several_queries_against_oracle(name):
     w, M, q, K, V = make(name)
+    check_several_queries(name, w, M, q, K, V)
+
+
+def test_prefilter_repair_several_queries():
+    """Keys far above the rest planted exactly at the sampled positions of the first KV group of
+    each sequence (positions with p % 512 < 64 for L = 16384, k = 512): the sampled threshold of
+    its rows lands above their k-th score, so those rows take the full rescore and select."""
+    w, M, q, K, V = make("prefilter-g8-m4")
+    qf = fx.bf16_bits_to_f32(q).astype(np.float64)
+    pos = np.arange(w.L)
+    hot = (pos % 512) < 64
+    for b in range(w.B):
+        d = qf[b, :, :w.G].reshape(-1, w.d).sum(0)
+        d = d / np.linalg.norm(d)
+        mag = 12.0 + 0.01 * pos[hot]
+        K[b, 0, hot] = fx.encode(mag[:, None] * d[None, :], fx.BF16)
+    check_several_queries("prefilter-hot", w, M, q, K, V)
+
+
+def check_several_queries(name, w, M, q, K, V):
     m = tka()
     p = m.problem(m.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, m.TKA_BF16, n_queries=M)
     qt, Kt, Vt = dev(q), dev(K), dev(V)

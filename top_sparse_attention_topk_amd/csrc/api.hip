@@ -349,7 +349,8 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
   const int G = p->n_q_heads / p->n_kv_heads;
   if (p->mode != TKA_SCORE_EXACT || p->qkv_dtype != TKA_BF16 || !score_uses_mfma(1, G)) return pf;
   const int64_t L = p->seq_len, kk = p->top_k < p->seq_len ? p->top_k : p->seq_len;
-  if (L < 8192 || L > 262144 || kk * 8 > L || nqry(p) > 1) return pf;
+  // several queries per sequence: up to 4 (the scan's waves take one query each on shared tiles)
+  if (L < 8192 || L > 262144 || kk * 8 > L || nqry(p) > 4) return pf;
   int64_t sc = 4096;
   while (sc > 128 && 7 * kk * sample_count(L, sc) < 4 * 100 * L) sc >>= 1;
   pf.sample_chunk = (int)sc;
@@ -662,7 +663,9 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     int32_t* cpos = reinterpret_cast<int32_t*>(base + d.cpos);
     const int G = p->n_q_heads / p->n_kv_heads;
     launch_score_mfma_sample(sc, d.pf.sample_chunk, d.pf.nsamp, samp, st);
-    launch_prefilter_threshold(samp, d.rows, d.pf.nsamp, d.pf.r, T, cnt, row_flag, group_flag, G, st);
+    const int M = (int)nqry(p);
+    launch_prefilter_threshold(samp, d.rows, d.pf.nsamp, d.pf.r, T, cnt, row_flag, group_flag, G, p->n_q_heads, M,
+                               st);
     MfmaOut mo{};
     mo.T = T;
     mo.cnt = cnt;
@@ -670,10 +673,15 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     mo.cpos = cpos;
     mo.capg = d.pf.capg;
     launch_score_mfma_cand(sc, mo, st);
-    launch_prefilter_finish(cbits, cpos, cnt, T, d.pf.capg, d.rows, d.len, d.k, G, idx, selv, row_flag, group_flag,
-                            st);
+    launch_prefilter_finish(cbits, cpos, cnt, T, d.pf.capg, d.rows, d.len, d.k, G, p->n_q_heads, M, idx, selv,
+                            row_flag, group_flag, st);
     launch_score_mfma_guarded(sc, group_flag, st);
-    launch_select_rows_flagged(sa, row_flag, st);
+    int32_t* krow = nullptr;  // several queries: query t keeps min(k, L - M + t + 1)
+    if (M > 1) {
+      krow = reinterpret_cast<int32_t*>(base + d.krow);
+      launch_mq_counts(krow, d.rows, M, p->n_q_heads, p->seq_len, d.k, st);
+    }
+    launch_select_rows_flagged(sa, row_flag, krow, st);
   } else {
     // 1. score
     if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);

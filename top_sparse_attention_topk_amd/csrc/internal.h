@@ -120,13 +120,15 @@ void launch_hisa_token_scores(const HisaArgs& a, hipStream_t st);
 void launch_hisa_map(int32_t* idx, const int32_t* blk, int64_t rows, int k, int KB, int bsz, hipStream_t st);
 // row select with a count per row (krow[r] <= a.k; rows padded with -1 up to a.k)
 void launch_select_rows_counts(const SelectArgs& a, const int32_t* krow, hipStream_t st);
-void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st);
+// rows with row_flag set; krow (optional): each row's count, at most a.k
+void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, const int32_t* krow, hipStream_t st);
 
 // candidate prefilter of the fused exact step (select.hip)
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
-                                uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st);
+                                uint32_t* row_flag, uint32_t* group_flag, int G, int Hq, int M, hipStream_t st);
+// rows are (b, t, h) with M queries t per sequence; group flags are per (b, KV head)
 void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, const float* T,
-                             int capg, int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel,
+                             int capg, int64_t n_rows, int n, int k, int G, int Hq, int M, int32_t* idx, float* sel,
                              uint32_t* row_flag, uint32_t* group_flag, hipStream_t st);
 
 // gather planning is shared by the workspace query and the launch

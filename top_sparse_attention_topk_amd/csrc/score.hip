@@ -193,17 +193,23 @@ constexpr int PS_WPC = TKA_PS_WPC;                  // workgroups per CU
 constexpr int PS_STAGE_BYTES = TKA_PS_STAGE_BYTES;  // candidate stage per wave (G heads x 8 B x slots)
 constexpr int PS_TILE_MAX = 32;                     // most pairs one head can keep from one tile
 
-template <int D>
+template <int D, bool SH>
 __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16_t* __restrict__ q,
                                                                     const uint16_t* __restrict__ K, int Hq, int Hkv,
-                                                                    int G, int L, int64_t sb, int64_t sh, int64_t sl,
-                                                                    float scale, int64_t ntiles, int tpg, int S,
-                                                                    MfmaOut o) {
+                                                                    int G, int M, int L, int64_t sb, int64_t sh,
+                                                                    int64_t sl, float scale, int64_t ntiles, int tpg,
+                                                                    int S, MfmaOut o) {
   constexpr int KS = D / 32;
   constexpr int P = 32;
   constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
+  // M queries per sequence (M <= 4): wave w scores query tq = w % M on tile lane w / M of TL = 4 / M;
+  // the M waves of a tile lane read the same tiles (SH: cached loads, so the repeats hit the caches)
+  const int TL = 4 / M;
+  if (wave >= M * TL) return;
+  const int tq = wave % M;
+  const int lim = L - M + tq + 1;  // positions query tq may see
   extern __shared__ uint4 smem_raw[];
   uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
   // S slots per head: score bits [G][S], then positions [G][S]
@@ -226,13 +232,13 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
   auto reserve = [&]() -> uint32_t {
     const int b = grp / Hkv, g = grp % Hkv;
     uint32_t base = 0;
-    if (lane < G && scnt != 0) base = atomicAdd(&o.cnt[(int64_t)b * Hq + g * G + lane], scnt);
+    if (lane < G && scnt != 0) base = atomicAdd(&o.cnt[((int64_t)b * M + tq) * Hq + g * G + lane], scnt);
     return base;
   };
   // copy the staged pairs to the reserved slots (counts and bases broadcast from lane h)
   auto copy_out = [&](uint32_t base) {
     const int b = grp / Hkv, g = grp % Hkv;
-    const int64_t rg = (int64_t)b * Hq + g * G;
+    const int64_t rg = ((int64_t)b * M + tq) * Hq + g * G;
     for (int h = 0; h < G; ++h) {
       const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)scnt, h);
       if (c == 0) continue;
@@ -260,18 +266,18 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     if (at + P <= L) {
       const uint16_t* p = lK + (int64_t)(at + lane / CPR) * sl;
 #pragma unroll
-      for (int j = 0; j < NI; ++j) a[j] = ld16_stream(p + j * jstep);
+      for (int j = 0; j < NI; ++j) a[j] = SH ? ld16(p + j * jstep) : ld16_stream(p + j * jstep);
     } else {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int pos = min(at + j * RPI + lane / CPR, L - 1);
-        a[j] = ld16_stream(lK + (int64_t)pos * sl);
+        a[j] = SH ? ld16(lK + (int64_t)pos * sl) : ld16_stream(lK + (int64_t)pos * sl);
       }
     }
   };
 
-  // tile t = cg * tpg + ct; each wave takes every fourth tile of [r0, r1)
-  int64_t t = r0 + wave;
+  // tile t = cg * tpg + ct; each tile lane takes every TL-th tile of [r0, r1)
+  int64_t t = r0 + wave / M;
   int cg = 0, ct = 0;
   uint4 cur[NI];
   if (t < r1) {
@@ -280,15 +286,15 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     load(cur, cg, ct);
   }
   bool pend = false;  // wave-uniform: flush the stage before this tile's pairs are staged
-  for (; t < r1; t += 4) {
-    int ng = cg, nt = ct + 4;  // the wave's next tile
+  for (; t < r1; t += TL) {
+    int ng = cg, nt = ct + TL;  // the wave's next tile
     while (nt >= tpg) {
       nt -= tpg;
       ++ng;
     }
     const uint32_t base = pend ? reserve() : 0u;
     uint4 nxt[NI];
-    const bool more = t + 4 < r1;
+    const bool more = t + TL < r1;
     if (more) load(nxt, ng, nt);
     if (pend) {
       copy_out(base);
@@ -300,10 +306,10 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (hl) v = ld16(q + ((int64_t)(b * Hq + g * G + n)) * D + 32 * s + 8 * kg);
+        if (hl) v = ld16(q + (((int64_t)b * M + tq) * Hq + g * G + n) * D + 32 * s + 8 * kg);
         bq[s] = __builtin_bit_cast(bf16x8_t, v);
       }
-      const float tv = hl ? o.T[(int64_t)b * Hq + g * G + n] : 0.f;
+      const float tv = hl ? o.T[((int64_t)b * M + tq) * Hq + g * G + n] : 0.f;
       Tf = tv;
       tnan = tv != tv;
     }
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       *reinterpret_cast<uint4*>(rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = cur[j];
     lds_wave_sync();
     const int pos0 = ct * P;
-    const bool whole = pos0 + P <= L;
+    const bool whole = pos0 + P <= lim;
     bool f[2][4];
     float v[2][4];
     uint32_t c = 0;
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       for (int i = 0; i < 4; ++i) {
         v[tt][i] = acc[i] * scale;
         const int pos = pos0 + 16 * tt + 4 * kg + i;
-        f[tt][i] = hl & (tnan | (v[tt][i] >= Tf)) & (whole | (pos < L));
+        f[tt][i] = hl & (tnan | (v[tt][i] >= Tf)) & (whole | (pos < lim));
         c += f[tt][i] ? 1u : 0u;
       }
     }
@@ -376,14 +382,17 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 // (b*M + t)*Hq + g*G + hh of [B*M*Hq, L]; positions past the query's own are
 // NaN (they rank below every number). Grid (chunks, B*Hkv), 256 threads.
 // ---------------------------------------------------------------------------
-template <int D, int RT>
+enum { MQ_FULL = 0, MQ_SAMPLE = 1, MQ_GUARDED = 2 };
+template <int D, int RT, int MODE>
 __global__ __launch_bounds__(256) void score_mq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
                                                        int Hq, int Hkv, int G, int M, int L, int64_t sb, int64_t sh,
-                                                       int64_t sl, float scale, int chunk, float* __restrict__ S) {
+                                                       int64_t sl, float scale, int chunk, float* __restrict__ S,
+                                                       int nsamp, const uint32_t* __restrict__ group_flag) {
   constexpr int KS = D / 32;
   constexpr int P = 32;
   constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
   const int task = blockIdx.y;
+  if (MODE == MQ_GUARDED && group_flag[task] == 0) return;
   const int b = task / Hkv, g = task % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
@@ -410,8 +419,9 @@ __global__ __launch_bounds__(256) void score_mq_kernel(const uint16_t* __restric
     }
   }
   const uint16_t* Kb = K + (int64_t)b * sb + (int64_t)g * sh;
-  const int p0 = blockIdx.x * chunk, p1 = min(p0 + chunk, L);
-  const bool vec_store = (L & 3) == 0;
+  // sample mode: the first 64 positions of sample chunk blockIdx.x, to samples blockIdx.x*64 + ...
+  const int p0 = blockIdx.x * chunk, p1 = min(p0 + (MODE == MQ_SAMPLE ? 64 : chunk), L);
+  const bool vec_store = MODE != MQ_SAMPLE && (L & 3) == 0;
   auto load = [&](uint4 (&a)[NI], int at) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(256) void score_mq_kernel(const uint16_t* __restric
           float v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = pos + i <= last[rt] ? acc[i] * scale : __int_as_float(0x7fc00000);
-          float* Srow = S + srow[rt] * L;
+          float* Srow = MODE == MQ_SAMPLE ? S + srow[rt] * nsamp + (int64_t)blockIdx.x * 64 - p0 : S + srow[rt] * L;
           if (vec_store && pos + 3 < p1) {
             *reinterpret_cast<float4*>(Srow + pos) = make_float4(v[0], v[1], v[2], v[3]);
           } else {
@@ -715,7 +725,14 @@ static void launch_mfma(const ScoreArgs& a, int chunk, unsigned gx, const MfmaOu
 
 int mfma_scan_chunk(const ScoreArgs& a) { return pick_chunk(a.nrows, (int64_t)a.B * a.Hkv, 256, 256, 4096); }
 
+template <int MODE>
+static void launch_mq_mode(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* gf, hipStream_t st);
+
 void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, float* samp, hipStream_t st) {
+  if (a.M > 1) {
+    launch_mq_mode<MQ_SAMPLE>(a, sample_chunk, samp, nsamp, nullptr, st);
+    return;
+  }
   MfmaOut o{};
   o.S = samp;
   o.nsamp = nsamp;
@@ -750,10 +767,18 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   const int fit = (int)(device_lds_limit() / lds);  // workgroups whose LDS fits one CU
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
-  ensure_dynamic_lds((const void*)score_cand_persistent_kernel<D>, lds);
-  hipLaunchKernelGGL((score_cand_persistent_kernel<D>), dim3((unsigned)grid), dim3(256), lds, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl,
-                     a.scale, ntiles, tpg, S, o);
+  const int M = a.M > 1 ? a.M : 1;  // the caller keeps M <= 4
+  if (M == 1) {
+    ensure_dynamic_lds((const void*)score_cand_persistent_kernel<D, false>, lds);
+    hipLaunchKernelGGL((score_cand_persistent_kernel<D, false>), dim3((unsigned)grid), dim3(256), lds, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, 1, a.nrows, a.sb, a.sh,
+                       a.sl, a.scale, ntiles, tpg, S, o);
+  } else {
+    ensure_dynamic_lds((const void*)score_cand_persistent_kernel<D, true>, lds);
+    hipLaunchKernelGGL((score_cand_persistent_kernel<D, true>), dim3((unsigned)grid), dim3(256), lds, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh,
+                       a.sl, a.scale, ntiles, tpg, S, o);
+  }
 }
 
 void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
@@ -764,32 +789,39 @@ void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st
   }
 }
 
-template <int D, int RT>
-static void launch_mq_t(const ScoreArgs& a, hipStream_t st) {
-  const int chunk = mfma_scan_chunk(a);
+// chunk: positions per workgroup (full and guarded modes) or the sample chunk (sample mode,
+// which scores the first 64 positions of each, out = [rows, nsamp])
+template <int D, int RT, int MODE>
+static void launch_mq_t(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* group_flag,
+                        hipStream_t st) {
   const size_t lds = (size_t)4 * 32 * (D * 2 + 16);
-  ensure_dynamic_lds((const void*)score_mq_kernel<D, RT>, lds);
+  ensure_dynamic_lds((const void*)score_mq_kernel<D, RT, MODE>, lds);
   dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv);
-  hipLaunchKernelGGL((score_mq_kernel<D, RT>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.M, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk,
-                     a.scores);
+  hipLaunchKernelGGL((score_mq_kernel<D, RT, MODE>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.M, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, out,
+                     nsamp, group_flag);
 }
 
-template <int D>
-static void launch_mq_d(const ScoreArgs& a, hipStream_t st) {
+template <int D, int MODE>
+static void launch_mq_d(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* gf, hipStream_t st) {
   const int R = a.M * a.G;
-  if (R <= 16) launch_mq_t<D, 1>(a, st);
-  else if (R <= 32) launch_mq_t<D, 2>(a, st);
-  else launch_mq_t<D, 4>(a, st);
+  if (R <= 16) launch_mq_t<D, 1, MODE>(a, chunk, out, nsamp, gf, st);
+  else if (R <= 32) launch_mq_t<D, 2, MODE>(a, chunk, out, nsamp, gf, st);
+  else launch_mq_t<D, 4, MODE>(a, chunk, out, nsamp, gf, st);
+}
+
+template <int MODE>
+static void launch_mq_mode(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* gf, hipStream_t st) {
+  if (a.nrows <= 0) return;
+  switch (a.d) {
+    case 64: launch_mq_d<64, MODE>(a, chunk, out, nsamp, gf, st); break;
+    case 128: launch_mq_d<128, MODE>(a, chunk, out, nsamp, gf, st); break;
+    default: launch_mq_d<256, MODE>(a, chunk, out, nsamp, gf, st); break;
+  }
 }
 
 void launch_score_mq(const ScoreArgs& a, hipStream_t st) {
-  if (a.nrows <= 0) return;
-  switch (a.d) {
-    case 64: launch_mq_d<64>(a, st); break;
-    case 128: launch_mq_d<128>(a, st); break;
-    default: launch_mq_d<256>(a, st); break;
-  }
+  launch_mq_mode<MQ_FULL>(a, mfma_scan_chunk(a), a.scores, 0, nullptr, st);
 }
 
 void launch_mq_counts(int32_t* krow, int64_t rows, int M, int Hq, int L, int k, hipStream_t st) {
@@ -800,6 +832,10 @@ void launch_mq_counts(int32_t* krow, int64_t rows, int M, int Hq, int L, int k, 
 }
 
 void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st) {
+  if (a.M > 1) {
+    launch_mq_mode<MQ_GUARDED>(a, mfma_scan_chunk(a), a.scores, 0, group_flag, st);
+    return;
+  }
   MfmaOut o{};
   o.S = a.scores;
   o.group_flag = group_flag;

@@ -591,7 +591,8 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
                                                                   int64_t n_rows, float* __restrict__ T,
                                                                   uint32_t* __restrict__ cnt,
                                                                   uint32_t* __restrict__ row_flag,
-                                                                  uint32_t* __restrict__ group_flag, int G) {
+                                                                  uint32_t* __restrict__ group_flag, int G, int Hq,
+                                                                  int M) {
   __shared__ uint32_t hist_all[4][1024];
   __shared__ uint32_t list_all[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -602,7 +603,8 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
   if (lane == 0) {
     cnt[row] = 0;
     row_flag[row] = 0;
-    if (row % G == 0) group_flag[row / G] = 0;
+    // rows (b, t, h), several queries t per sequence: the group flag of (b, h / G) is cleared once
+    if ((row / Hq) % M == 0 && (row % Hq) % G == 0) group_flag[(row / ((int64_t)M * Hq)) * (Hq / G) + (row % Hq) / G] = 0;
   }
   if (r > nsamp) {
     if (lane == 0) T[row] = key_value(0u);  // too few samples: keep everything
@@ -714,7 +716,8 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
                                                                 const int32_t* __restrict__ cpos,
                                                                 const uint32_t* __restrict__ cnt,
                                                                 const float* __restrict__ Tv, int capg, int n,
-                                                                int k, int G, int32_t* __restrict__ idx,
+                                                                int k, int G, int Hq, int M,
+                                                                int32_t* __restrict__ idx,
                                                                 float* __restrict__ sel,
                                                                 uint32_t* __restrict__ row_flag,
                                                                 uint32_t* __restrict__ group_flag) {
@@ -821,7 +824,7 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
   }
   if (repair && t == 0) {
     row_flag[row] = 1u;
-    atomicOr(&group_flag[row / G], 1u);
+    atomicOr(&group_flag[(row / ((int64_t)M * Hq)) * (Hq / G) + (row % Hq) / G], 1u);  // group (b, h / G)
   }
 }
 
@@ -1225,12 +1228,12 @@ void launch_select_rows_counts(const SelectArgs& a, const int32_t* krow, hipStre
                      a.idx, a.sel, capw, (const uint32_t*)nullptr, krow);
 }
 
-void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, hipStream_t st) {
+void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, const int32_t* krow, hipStream_t st) {
   if (a.n_rows <= 0) return;
   size_t lds;
   const int capw = rows_capw(a.n, a.k, &lds);
   hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k,
-                     a.idx, a.sel, capw, row_flag, (const int32_t*)nullptr);
+                     a.idx, a.sel, capw, row_flag, krow);
 }
 
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
@@ -1278,28 +1281,28 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
 }
 
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
-                                uint32_t* row_flag, uint32_t* group_flag, int G, hipStream_t st) {
+                                uint32_t* row_flag, uint32_t* group_flag, int G, int Hq, int M, hipStream_t st) {
   if (n_rows <= 0) return;
   const dim3 grid((unsigned)((n_rows + 3) / 4));
   if (nsamp <= 2048)
     hipLaunchKernelGGL(prefilter_threshold_kernel<32>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
-                       row_flag, group_flag, G);
+                       row_flag, group_flag, G, Hq, M);
   else if (nsamp <= 4096)
     hipLaunchKernelGGL(prefilter_threshold_kernel<64>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
-                       row_flag, group_flag, G);
+                       row_flag, group_flag, G, Hq, M);
   else  // the plan keeps nsamp <= 8192
     hipLaunchKernelGGL(prefilter_threshold_kernel<128>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
-                       row_flag, group_flag, G);
+                       row_flag, group_flag, G, Hq, M);
 }
 
 static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((n + 31) / 32); }
 
 void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, const float* T,
-                             int capg, int64_t n_rows, int n, int k, int G, int32_t* idx, float* sel,
+                             int capg, int64_t n_rows, int n, int k, int G, int Hq, int M, int32_t* idx, float* sel,
                              uint32_t* row_flag, uint32_t* group_flag, hipStream_t st) {
   (void)max_lds_bytes();
   hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(PF_T), prefilter_finish_lds(n), st, cbits,
-                     cpos, cnt, T, capg, n, k, G, idx, sel, row_flag, group_flag);
+                     cpos, cnt, T, capg, n, k, G, Hq, M, idx, sel, row_flag, group_flag);
 }
 
 }  // namespace tka
