@@ -91,19 +91,24 @@ def traffic_from_profiles(kernel: str):
             rec = json.load(f)
         if rec.get("source_sha256") != source_digest():
             return None
-        k = rec["kernels"][kernel]
+        ks = rec["kernels"]
+        if kernel not in ks:  # a base name: the one instantiation that carries it
+            hits = [n for n in ks if n.split("<")[0] == kernel]
+            if len(hits) != 1:
+                return None
+            kernel = hits[0]
+        k = ks[kernel]
         return int(k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
 
 def short_name(name: str) -> str:
+    """Qualified kernel name with its template arguments (instantiations differ in work)."""
     name = name.strip()
     if name.startswith("void "):
         name = name[5:]
-    for c in "<(":
-        name = name.split(c)[0]
-    return name.strip()
+    return name.split("(")[0].strip()
 
 
 def copy_calibration(launches: int = 3):
@@ -128,12 +133,12 @@ def summarize_trace(trace_dir: str, tail: int) -> None:
             for r in csv.DictReader(f):
                 ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
                 per.setdefault(short_name(r["Kernel_Name"]), []).append((int(r["Start_Timestamp"]), ns))
-    print(f"{'kernel':40s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'last%d_us' % tail:>9s}")
+    print(f"{'kernel':56s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'last%d_us' % tail:>9s}")
     for name, v in sorted(per.items(), key=lambda kv: -sum(ns for _, ns in kv[1])):
         v.sort()
         ns = [d for _, d in v]
         last = ns[-tail:]
-        print(f"{name[:40]:40s} {len(ns):6d} {sum(ns) / len(ns) / 1e3:9.1f} {min(ns) / 1e3:9.1f} "
+        print(f"{name[:56]:56s} {len(ns):6d} {sum(ns) / len(ns) / 1e3:9.1f} {min(ns) / 1e3:9.1f} "
               f"{max(ns) / 1e3:9.1f} {sum(last) / len(last) / 1e3:9.1f}")
 
 
@@ -168,14 +173,14 @@ def summarize_counters(fetch_dir: str, write_dir: str, tail: int) -> None:
                            "fetch_factor": round(cf, 5), "write_factor": round(cw, 5)},
            "kernels": {}}
     print(f"calibration {COPY_KERNEL}: FETCH_SIZE/{COPY_BYTES} = {cf:.4f}, WRITE_SIZE/{COPY_BYTES} = {cw:.4f}")
-    print(f"{'kernel':40s} {'fetch_raw_MB':>13s} {'write_raw_MB':>13s} {'fetch_MB':>10s} {'write_MB':>10s}")
+    print(f"{'kernel':56s} {'fetch_raw_MB':>13s} {'write_raw_MB':>13s} {'fetch_MB':>10s} {'write_MB':>10s}")
     for name in sorted(vals):
         if name == COPY_KERNEL or "FETCH_SIZE" not in vals[name] or "WRITE_SIZE" not in vals[name]:
             continue
         f_raw, w_raw = mean_tail(name, "FETCH_SIZE"), mean_tail(name, "WRITE_SIZE")
         out["kernels"][name] = {"fetch_bytes_per_launch": round(f_raw / cf), "write_bytes_per_launch": round(w_raw / cw),
                                 "fetch_raw_bytes": round(f_raw), "write_raw_bytes": round(w_raw)}
-        print(f"{name[:40]:40s} {f_raw / 1e6:13.1f} {w_raw / 1e6:13.1f} {f_raw / cf / 1e6:10.1f} {w_raw / cw / 1e6:10.1f}")
+        print(f"{name[:56]:56s} {f_raw / 1e6:13.1f} {w_raw / 1e6:13.1f} {f_raw / cf / 1e6:10.1f} {w_raw / cw / 1e6:10.1f}")
     with open(COUNTERS, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -222,6 +227,8 @@ def main():
     ap.add_argument("--workload", default="C3", help="fixtures.WORKLOADS key (C3 is the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the adjacent paths (profiling runs: the roofline launches stay the last ones)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the known-size copy kernel that HBM byte counters are scaled by")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print kernel durations from a rocprofv3 trace; no GPU")
@@ -335,13 +342,13 @@ def main():
         t_thr = sum(a.elapsed_time(b) for a, b in times) / len(times)
         kept = int(cnt.sum().item())
         assert int(cnt.min().item()) >= w.k, "thresholded scan kept fewer than k pairs in a row"
-        kname = "score_cand_persistent_kernel"
+        kname = f"tka::score_cand_persistent_kernel<{w.d}, false>"
         kbytes = (w.B * w.Hkv * w.L * w.d * 2 + w.B * w.Hq * w.d * 2 + 8 * rows + 8 * kept)
         kms = t_thr
     else:
-        kname = {fx.MODE_EXACT: "score_exact_mfma_kernel" if dt == tka.TKA_BF16 and 2 <= w.G <= 16
-                 else "score_vec_kernel", fx.MODE_BLOCK: "score_vec_kernel",
-                 fx.MODE_INDEXER: "score_indexer_kernel"}[w.mode]
+        kname = {fx.MODE_EXACT: "tka::score_exact_mfma_kernel" if dt == tka.TKA_BF16 and 2 <= w.G <= 16
+                 else "tka::score_vec_kernel", fx.MODE_BLOCK: "tka::score_vec_kernel",
+                 fx.MODE_INDEXER: "tka::score_indexer_kernel"}[w.mode]
         kbytes = score_kernel_bytes(w)
         kms = t_score
     achieved = kbytes / (kms / 1e3) / 1e9
@@ -367,7 +374,7 @@ def main():
     }
     # adjacent paths on the same inputs (each timed alone on the launch stream)
     extras = {}
-    if exact:
+    if exact and not args.no_extras:
         log("[bench] certified adaptive k")
         eps = 0.9  # the synthetic caches spread their softmax mass widely: tau(k = 4096) is about 0.8
         ak_idx = torch.empty((rows, w.k), dtype=torch.int32, device="cuda")
