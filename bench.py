@@ -200,6 +200,44 @@ def time_loop(fn, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
+    """Fused step and scoring launch of a proxy-score workload (block means or indexer), each timed
+    alone on the launch stream; the scoring launch against the HBM roofline (its algorithmic bytes:
+    proxy keys read once, q read, fp32 scores written)."""
+    q, K, V = fx.make_attn(w)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    qt, Kt, Vt = to(q), to(K), to(V)
+    del K, V
+    p = tka.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, tka.TKA_BF16, 0.0, w.block, w.HI, w.dI)
+    res = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.L, "top_k": w.k}
+    if w.mode == fx.MODE_BLOCK:
+        means = tka.topk_block_mean_build(p, Kt)
+        res["block_size"] = w.block
+        res["mean_build_ms"] = round(time_loop(lambda: tka.topk_block_mean_build(p, Kt, means), steps), 4)
+        kw = dict(proxy_keys=means)
+        sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
+        score_call = lambda: tka.topk_attn_score(p, qt, means, scores=sc)
+        idx = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+    else:
+        qI, kI, wt = fx.make_indexer(w)
+        kw = dict(proxy_keys=torch.from_numpy(kI).cuda(), q_idx=torch.from_numpy(qI).cuda(),
+                  idx_w=torch.from_numpy(wt).cuda())
+        res["indexer_heads"], res["indexer_dim"] = w.HI, w.dI
+        sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
+        score_call = lambda: tka.topk_attn_score(p, kw["q_idx"], kw["proxy_keys"], idx_w=kw["idx_w"], scores=sc)
+        idx = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tka.topk_decode_workspace_size(p), dtype=torch.uint8, device="cuda")
+    t_dec = time_loop(lambda: tka.topk_decode(p, qt, Kt, Vt, out=out, idx_out=idx, ws=ws, **kw), steps)
+    t_sc = time_loop(score_call, steps)
+    sb = score_kernel_bytes(w)
+    res.update({"decode_ms": round(t_dec, 4), "decode_queries_per_s": round(w.B / (t_dec / 1e3), 1),
+                "score_ms": round(t_sc, 4), "score_algorithmic_bytes": sb,
+                "score_gbps": round(sb / (t_sc / 1e3) / 1e9, 1),
+                "score_frac": round(sb / (t_sc / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)})
+    return res
+
+
 def cpu_baseline(w, q, K, V, budget_s: float):
     """The fp64 oracle, as it stands, on whole queries (all heads of one
     sequence) of the same workload until about budget_s seconds have passed."""
@@ -346,7 +384,7 @@ def main():
         kbytes = (w.B * w.Hkv * w.L * w.d * 2 + w.B * w.Hq * w.d * 2 + 8 * rows + 8 * kept)
         kms = t_thr
     else:
-        kname = {fx.MODE_EXACT: "tka::score_exact_mfma_kernel" if dt == tka.TKA_BF16 and 2 <= w.G <= 16
+        kname = {fx.MODE_EXACT: f"tka::score_exact_mfma_kernel<{w.d}, 0, 2>" if dt == tka.TKA_BF16 and 2 <= w.G <= 16
                  else "tka::score_vec_kernel", fx.MODE_BLOCK: "tka::score_vec_kernel",
                  fx.MODE_INDEXER: "tka::score_indexer_kernel"}[w.mode]
         kbytes = score_kernel_bytes(w)
@@ -444,9 +482,16 @@ def main():
                                      "score_tflops": round(flops / (t_mqs / 1e3) / 1e12, 2),
                                      "score_gbps": round(sbytes / (t_mqs / 1e3) / 1e9, 1)}
             del mq_ws, mq_sc
-    result["extras"] = extras
     del Kt, Vt, sc, ws
     torch.cuda.empty_cache()
+    if exact and not args.no_extras and args.workload == "C3":
+        # the proxy-score variants at their own workload sizes: block means (MoBA-style, top 16 blocks
+        # of 64 at L = 128K) and the lightning indexer (E4M3 keys, top 2048 of L = 1M)
+        for wname, key in (("C4", "block_mean_C4"), ("C5", "indexer_C5")):
+            log(f"[bench] {key}")
+            extras[key] = proxy_variant(fx, tka, torch, np, fx.WORKLOADS[wname], args.steps)
+            torch.cuda.empty_cache()
+    result["extras"] = extras
     if args.copy_calibration:
         log("[bench] copy calibration kernel")
         copy_calibration()
