@@ -263,11 +263,17 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   }
 }
 
-// o = sum_s e^(M_s - M) acc_s / sum_s e^(M_s - M) l_s, splits in order.
+// o = sum_s e^(M_s - M) acc_s / sum_s e^(M_s - M) l_s, splits in order. A workgroup per
+// (task, head): the split weights e^(M_s - M) first (to LDS), then thread c accumulates output
+// column c over the splits with independent loads.
+constexpr int kMergeLdsSplits = 8192;
 template <int D, int NH>
 __global__ __launch_bounds__(256) void gather_merge_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                            int nsplit, int Hq, int Hkv, int G, int shared) {
-  const int task = blockIdx.x;
+  extern __shared__ float fw[];  // [nsplit] split weights (when nsplit <= kMergeLdsSplits)
+  __shared__ float red[4];
+  const int task = blockIdx.x, h = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   int b, h0;
   if (shared) {
     b = task / Hkv;
@@ -276,23 +282,50 @@ __global__ __launch_bounds__(256) void gather_merge_kernel(const float* __restri
     b = task / Hq;
     h0 = task % Hq;
   }
-  const float* p = part + (int64_t)task * nsplit * (NH * (D + 2));
-  for (int i = threadIdx.x; i < NH * D; i += 256) {
-    const int h = i / D;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (NH * (D + 2)) + NH * D + h]);
+  constexpr int PS = NH * (D + 2);  // floats per split partial
+  const float* p = part + (int64_t)task * nsplit * PS;
+  float m = -INFINITY;
+  for (int s = t; s < nsplit; s += blockDim.x) m = fmaxf(m, p[s * PS + NH * D + h]);
+  m = wave_max(m);
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int i = 0; i < (int)(blockDim.x + 63) / 64; ++i) M = fmaxf(M, red[i]);
+  const bool in_lds = nsplit <= kMergeLdsSplits;
+  auto weight = [&](int s) {
+    const float ms = p[s * PS + NH * D + h];
+    return (M == -INFINITY || ms == -INFINITY) ? 0.f : expf(ms - M);
+  };
+  if (in_lds)
+    for (int s = t; s < nsplit; s += blockDim.x) fw[s] = weight(s);
+  __syncthreads();
+  for (int c = t; c < D; c += 256) {
     float num = 0.f, den = 0.f;
     if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* ps = p + s * (NH * (D + 2));
-        const float ms = ps[NH * D + h];
-        if (ms == -INFINITY) continue;
-        const float f = expf(ms - M);
-        num = fmaf(f, ps[i], num);
-        den = fmaf(f, ps[NH * D + NH + h], den);
+      int s = 0;
+      for (; s + 8 <= nsplit; s += 8) {
+        float a[8], l[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          a[u] = p[(s + u) * PS + h * D + c];
+          l[u] = p[(s + u) * PS + NH * D + NH + h];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float f = in_lds ? fw[s + u] : weight(s + u);
+          if (f == 0.f) continue;
+          num = fmaf(f, a[u], num);
+          den = fmaf(f, l[u], den);
+        }
+      }
+      for (; s < nsplit; ++s) {
+        const float f = in_lds ? fw[s] : weight(s);
+        if (f == 0.f) continue;
+        num = fmaf(f, p[s * PS + h * D + c], num);
+        den = fmaf(f, p[s * PS + NH * D + NH + h], den);
       }
     }
-    out[((int64_t)b * Hq + h0 + h) * D + (i % D)] = den > 0.f ? num / den : 0.f;
+    out[((int64_t)b * Hq + h0 + h) * D + c] = den > 0.f ? num / den : 0.f;
   }
 }
 
@@ -328,7 +361,8 @@ static void launch_g(const GatherK& k, const GatherPlan& pl, hipStream_t st) {
   const size_t lds = sizeof(float) * (NH * D + 6 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
   hipLaunchKernelGGL((gather_kernel<BF16, D, NH, SEL>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
   if (pl.nsplit > 1)
-    hipLaunchKernelGGL((gather_merge_kernel<D, NH>), dim3(pl.tasks), dim3(256), 0, st, k.part, k.out, pl.nsplit,
+    hipLaunchKernelGGL((gather_merge_kernel<D, NH>), dim3(pl.tasks, NH), dim3(D < 256 ? D : 256),
+                       pl.nsplit <= kMergeLdsSplits ? sizeof(float) * pl.nsplit : 0, st, k.part, k.out, pl.nsplit,
                        k.Hq, k.Hkv, k.G, k.shared);
 }
 

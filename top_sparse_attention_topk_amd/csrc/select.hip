@@ -402,12 +402,10 @@ __global__ __launch_bounds__(256) void select_chunk_hist_kernel(const float* __r
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
 
-__global__ __launch_bounds__(256) void select_chunk_collect_kernel(const float* __restrict__ S, int n,
-                                                                   int64_t stride, int k,
-                                                                   const uint32_t* __restrict__ ghist,
-                                                                   uint32_t* __restrict__ cbits,
-                                                                   int32_t* __restrict__ cpos,
-                                                                   uint32_t* __restrict__ ccount, int nch) {
+// Level-1 digits of the keys inside the level-0 bin that holds the k'-th key.
+__global__ __launch_bounds__(256) void select_chunk_hist1_kernel(const float* __restrict__ S, int n, int64_t stride,
+                                                                 int k, const uint32_t* __restrict__ ghist,
+                                                                 uint32_t* __restrict__ ghist1) {
   __shared__ SelSmem sm;
   const int64_t row = blockIdx.y;
   const int kk = min(k, n);
@@ -418,7 +416,54 @@ __global__ __launch_bounds__(256) void select_chunk_collect_kernel(const float* 
   for (int i = threadIdx.x; i < NB0; i += ST) sm.hist[i] = gh[i];
   __syncthreads();
   find_bin(sm.hist, NB0, (uint32_t)kk, sm);
-  const uint32_t lo = sm.res[0] << 20;
+  const uint32_t bin0 = sm.res[0];
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB1; i += ST) sm.hist[i] = 0;
+  __syncthreads();
+  const int w = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * CHUNK;
+  const int r0 = min(n, c0 + w * SUBCH), r1 = min(n, r0 + SUBCH);
+  hist_pass(s, r0, r1, aligned, 1, bin0, sm.hist);
+  __syncthreads();
+  uint32_t* g1 = ghist1 + row * NB1;
+  for (int i = threadIdx.x; i < NB1; i += ST)
+    if (sm.hist[i]) atomicAdd(&g1[i], sm.hist[i]);
+}
+
+// The level-0 and level-1 bins that hold the k'-th key of a row, from the global histograms:
+// (bin0, bin1) and the counts of keys above each.
+__device__ void split_bins(const uint32_t* gh0, const uint32_t* gh1, uint32_t kk, SelSmem& sm, uint32_t* bin0,
+                           uint32_t* above0, uint32_t* bin1, uint32_t* above1) {
+  for (int i = threadIdx.x; i < NB0; i += ST) sm.hist[i] = gh0[i];
+  __syncthreads();
+  find_bin(sm.hist, NB0, kk, sm);
+  *bin0 = sm.res[0];
+  *above0 = sm.res[1];
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB1; i += ST) sm.hist[i] = gh1[i];
+  __syncthreads();
+  find_bin(sm.hist, NB1, kk - *above0, sm);
+  *bin1 = sm.res[0];
+  *above1 = sm.res[1];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void select_chunk_collect_kernel(const float* __restrict__ S, int n,
+                                                                   int64_t stride, int k,
+                                                                   const uint32_t* __restrict__ ghist,
+                                                                   const uint32_t* __restrict__ ghist1,
+                                                                   uint32_t* __restrict__ cbits,
+                                                                   int32_t* __restrict__ cpos,
+                                                                   uint32_t* __restrict__ ccount, int nch) {
+  __shared__ SelSmem sm;
+  const int64_t row = blockIdx.y;
+  const int kk = min(k, n);
+  if (kk == n) return;
+  const float* s = S + row * stride;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  uint32_t bin0, above0, bin1, above1;
+  split_bins(ghist + row * NB0, ghist1 + row * NB1, (uint32_t)kk, sm, &bin0, &above0, &bin1, &above1);
+  const uint32_t lo = (bin0 << 20) | (bin1 << 10);  // keys at or above the level-1 bin of the k'-th key
   const int w = threadIdx.x >> 6;
   const int c0 = blockIdx.x * CHUNK;
   const int r0 = min(n, c0 + w * SUBCH), r1 = min(n, r0 + SUBCH);
@@ -430,6 +475,7 @@ __global__ __launch_bounds__(256) void select_chunk_collect_kernel(const float* 
 // Dynamic LDS: nseg segment offsets.
 __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restrict__ S, int n, int64_t stride,
                                                             int k, const uint32_t* __restrict__ ghist,
+                                                            const uint32_t* __restrict__ ghist1,
                                                             const uint32_t* __restrict__ cbits,
                                                             const int32_t* __restrict__ cpos,
                                                             const uint32_t* __restrict__ ccount,
@@ -443,7 +489,7 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
   int32_t* oidx = idx + row * k;
   float* osel = sel ? sel + row * k : nullptr;
   const int kk = min(k, n);
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, w = t >> 6;
   for (int j = kk + t; j < k; j += ST) {
     oidx[j] = -1;
     if (osel) osel[j] = -INFINITY;
@@ -456,12 +502,9 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
     }
     return;
   }
-  const uint32_t* gh = ghist + row * NB0;
-  for (int i = t; i < NB0; i += ST) sm.hist[i] = gh[i];
-  __syncthreads();
-  find_bin(sm.hist, NB0, (uint32_t)kk, sm);
-  const uint32_t prefix = sm.res[0], above = sm.res[1];
-  __syncthreads();
+  uint32_t bin0, above0, bin1, above1;
+  split_bins(ghist + row * NB0, ghist1 + row * NB1, (uint32_t)kk, sm, &bin0, &above0, &bin1, &above1);
+  const uint32_t prefix = (bin0 << 10) | bin1, above = above0 + above1;
   // offsets of the (chunk, wave) segments, in position order
   const int nseg = nch * SW;
   const uint32_t* cc = ccount + row * (int64_t)nseg;
@@ -484,19 +527,24 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
   __syncthreads();
   uint32_t* rb = catb + row * (int64_t)n;
   int32_t* rp = catp + row * (int64_t)n;
-  for (int sg = w; sg < nseg; sg += SW) {
-    const int64_t src = row * (int64_t)n + (int64_t)(sg / SW) * CHUNK + (sg % SW) * SUBCH;
-    const uint32_t cnt = cc[sg], dst = segoff[sg];
-    for (uint32_t e = lane; e < cnt; e += 64) {
-      rb[dst + e] = cbits[src + e];
-      rp[dst + e] = cpos[src + e];
+  // concatenate the segments in position order: output e comes from the last segment whose
+  // offset is <= e (binary search over the offsets; independent loads across threads)
+  for (uint32_t e = t; e < total; e += ST) {
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (segoff[mid] <= e) lo = mid;
+      else hi = mid - 1;
     }
+    const int64_t src = row * (int64_t)n + (int64_t)(lo / SW) * CHUNK + (lo % SW) * SUBCH + (e - segoff[lo]);
+    rb[e] = cbits[src];
+    rp[e] = cpos[src];
   }
   __syncthreads();
   const uint32_t q = (total + SW - 1) / SW;
   const uint32_t off = min(total, (uint32_t)w * q);
   const uint32_t cnt = min(total, off + q) - off;
-  refine_candidates(rb, off, cnt, 0, prefix, (uint32_t)kk - above, sm);
+  refine_candidates(rb, off, cnt, 1, prefix, (uint32_t)kk - above, sm);
   const uint32_t T = sm.res[0], need_eq = sm.res[1];
   __syncthreads();
   emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = rb[off + e]; pos = rp[off + e]; }, cnt, T,
@@ -843,7 +891,7 @@ static SplitLayout split_layout(int64_t n_rows, int n) {
   const int64_t nch = (n + CHUNK - 1) / CHUNK;
   SplitLayout L;
   size_t o = 0;
-  L.ghist = o; o += al256(sizeof(uint32_t) * n_rows * NB0);
+  L.ghist = o; o += al256(sizeof(uint32_t) * n_rows * (NB0 + NB1));  // level 0 [rows][NB0], then level 1 [rows][NB1]
   L.cbits = o; o += al256(sizeof(uint32_t) * n_rows * (size_t)n);
   L.cpos = o; o += al256(sizeof(int32_t) * n_rows * (size_t)n);
   L.ccount = o; o += al256(sizeof(uint32_t) * n_rows * nch * SW);
@@ -1263,21 +1311,25 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   const SplitLayout L = split_layout(a.n_rows, a.n);
   char* base = static_cast<char*>(ws);
   uint32_t* ghist = reinterpret_cast<uint32_t*>(base + L.ghist);
+  uint32_t* ghist1 = ghist + a.n_rows * NB0;
   uint32_t* cbits = reinterpret_cast<uint32_t*>(base + L.cbits);
   int32_t* cpos = reinterpret_cast<int32_t*>(base + L.cpos);
   uint32_t* ccount = reinterpret_cast<uint32_t*>(base + L.ccount);
   uint32_t* catb = reinterpret_cast<uint32_t*>(base + L.catb);
   int32_t* catp = reinterpret_cast<int32_t*>(base + L.catp);
   const int nch = (a.n + CHUNK - 1) / CHUNK;
-  const int64_t nh = a.n_rows * NB0;
+  const int64_t nh = a.n_rows * (NB0 + NB1);
   hipLaunchKernelGGL(select_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
                      dim3(256), 0, st, ghist, nh);
   hipLaunchKernelGGL(select_chunk_hist_kernel, dim3(nch, (unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n,
                      a.stride, a.k, ghist);
+  hipLaunchKernelGGL(select_chunk_hist1_kernel, dim3(nch, (unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n,
+                     a.stride, a.k, ghist, ghist1);
   hipLaunchKernelGGL(select_chunk_collect_kernel, dim3(nch, (unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n,
-                     a.stride, a.k, ghist, cbits, cpos, ccount, nch);
+                     a.stride, a.k, ghist, ghist1, cbits, cpos, ccount, nch);
   hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.n_rows), dim3(ST), sizeof(uint32_t) * nch * SW, st,
-                     a.scores, a.n, a.stride, a.k, ghist, cbits, cpos, ccount, catb, catp, nch, a.idx, a.sel);
+                     a.scores, a.n, a.stride, a.k, ghist, ghist1, cbits, cpos, ccount, catb, catp, nch, a.idx,
+                     a.sel);
 }
 
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
