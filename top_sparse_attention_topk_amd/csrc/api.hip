@@ -367,7 +367,7 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
 // ---- fused step: workspace layout ----
 struct DecodeLayout {
   size_t scores, sel_ws, idx, selv, gather_ws, krow, total;
-  size_t samp, T, cnt, row_flag, group_flag, cbits, cpos;
+  size_t samp, T, cnt, row_flag, group_flag, cpair;
   int64_t rows;
   int32_t len;
   int32_t k;
@@ -411,10 +411,8 @@ DecodeLayout decode_layout(const tka_problem* p) {
     o += al256(sizeof(uint32_t) * R);
     d.group_flag = o;
     o += al256(sizeof(uint32_t) * (size_t)p->batch * p->n_kv_heads);
-    d.cbits = o;
-    o += al256(sizeof(uint32_t) * R * d.pf.capg);
-    d.cpos = o;
-    o += al256(sizeof(int32_t) * R * d.pf.capg);
+    d.cpair = o;  // (score bits, position) pairs
+    o += al256(sizeof(uint2) * R * d.pf.capg);
   }
   d.total = o;
   return d;
@@ -659,8 +657,7 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     uint32_t* cnt = reinterpret_cast<uint32_t*>(base + d.cnt);
     uint32_t* row_flag = reinterpret_cast<uint32_t*>(base + d.row_flag);
     uint32_t* group_flag = reinterpret_cast<uint32_t*>(base + d.group_flag);
-    uint32_t* cbits = reinterpret_cast<uint32_t*>(base + d.cbits);
-    int32_t* cpos = reinterpret_cast<int32_t*>(base + d.cpos);
+    uint2* cpair = reinterpret_cast<uint2*>(base + d.cpair);
     const int G = p->n_q_heads / p->n_kv_heads;
     launch_score_mfma_sample(sc, d.pf.sample_chunk, d.pf.nsamp, samp, st);
     const int M = (int)nqry(p);
@@ -669,11 +666,10 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     MfmaOut mo{};
     mo.T = T;
     mo.cnt = cnt;
-    mo.cbits = cbits;
-    mo.cpos = cpos;
+    mo.cpair = cpair;
     mo.capg = d.pf.capg;
     launch_score_mfma_cand(sc, mo, st);
-    launch_prefilter_finish(cbits, cpos, cnt, T, d.pf.capg, d.rows, d.len, d.k, G, p->n_q_heads, M, idx, selv,
+    launch_prefilter_finish(cpair, cnt, T, d.pf.capg, d.rows, d.len, d.k, G, p->n_q_heads, M, idx, selv,
                             row_flag, group_flag, st);
     launch_score_mfma_guarded(sc, group_flag, st);
     int32_t* krow = nullptr;  // several queries: query t keeps min(k, L - M + t + 1)

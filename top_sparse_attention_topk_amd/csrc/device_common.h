@@ -11,6 +11,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 // Order-preserving key of an fp32 score: larger key <=> ranks higher.
 // -0 and +0 share one key; every NaN maps to key 0, below -inf (0x007fffff).

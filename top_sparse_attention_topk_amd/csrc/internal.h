@@ -81,6 +81,7 @@ struct MfmaOut {
   uint32_t* cnt;                // candidate mode: candidates found per row
   uint32_t* cbits;              // candidate mode: [B*Hq, capg] score bits
   int32_t* cpos;                // candidate mode: [B*Hq, capg] positions
+  uint2* cpair;                 // candidate mode, packed (when set, instead of cbits/cpos): [B*Hq, capg] (bits, pos)
   int capg;
   int stage;                    // candidate mode: LDS staging entries per head
   const uint32_t* group_flag;   // guarded mode: [B*Hkv], nonzero = rescore the group
@@ -127,7 +128,7 @@ void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, c
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
                                 uint32_t* row_flag, uint32_t* group_flag, int G, int Hq, int M, hipStream_t st);
 // rows are (b, t, h) with M queries t per sequence; group flags are per (b, KV head)
-void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, const float* T,
+void launch_prefilter_finish(const uint2* cpair, const uint32_t* cnt, const float* T,
                              int capg, int64_t n_rows, int n, int k, int G, int Hq, int M, int32_t* idx, float* sel,
                              uint32_t* row_flag, uint32_t* group_flag, hipStream_t st);
 

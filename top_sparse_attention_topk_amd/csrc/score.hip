@@ -244,11 +244,19 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       if (c == 0) continue;
       const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)base, h);
       const int64_t r = rg + h;
-      for (uint32_t e = lane; e < c; e += 64)
-        if (bh + e < (uint32_t)o.capg) {  // streaming stores: the lists are read once, by another kernel
-          __builtin_nontemporal_store(sbits[h * S + e], o.cbits + r * o.capg + bh + e);
-          __builtin_nontemporal_store(spos[h * S + e], o.cpos + r * o.capg + bh + e);
-        }
+      if (o.cpair) {  // one 8-byte (bits, position) store per pair
+        for (uint32_t e = lane; e < c; e += 64)
+          if (bh + e < (uint32_t)o.capg) {  // streaming stores: the lists are read once, by another kernel
+            u32x2_t x = {sbits[h * S + e], (uint32_t)spos[h * S + e]};
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
+          }
+      } else {
+        for (uint32_t e = lane; e < c; e += 64)
+          if (bh + e < (uint32_t)o.capg) {
+            __builtin_nontemporal_store(sbits[h * S + e], o.cbits + r * o.capg + bh + e);
+            __builtin_nontemporal_store(spos[h * S + e], o.cpos + r * o.capg + bh + e);
+          }
+      }
     }
     scnt = 0;
   };

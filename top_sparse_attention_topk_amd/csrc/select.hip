@@ -760,8 +760,7 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
 // first). Kept positions are marked in an LDS bitmap over the row and
 // popcount prefix sums give each its output slot in ascending position
 // order. Dynamic LDS: 2 * ceil(n/32) words (kept bitmap, prefix counts).
-__global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_t* __restrict__ cbits,
-                                                                const int32_t* __restrict__ cpos,
+__global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint2* __restrict__ cpair,
                                                                 const uint32_t* __restrict__ cnt,
                                                                 const float* __restrict__ Tv, int capg, int n,
                                                                 int k, int G, int Hq, int M,
@@ -784,8 +783,7 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
   const uint32_t nc = cnt[row];
   bool repair = nc < (uint32_t)kk || nc > (uint32_t)capg;  // threshold too high, or too many candidates
   if (!repair) {
-    const uint32_t* cb = cbits + row * capg;
-    const int32_t* cp = cpos + row * capg;
+    const u32x2_t* cw = reinterpret_cast<const u32x2_t*>(cpair + row * capg);
     const uint32_t T0 = score_key(Tv[row]);
     // the thread's candidates, every load of the batch in flight together (indices past the
     // count re-read the last candidate and are masked below)
@@ -793,9 +791,9 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint32_
     int32_t pos[PF_RC];
 #pragma unroll
     for (int j = 0; j < PF_RC; ++j) {
-      const uint32_t e = min((uint32_t)(t + PF_T * j), nc - 1u);
-      bits[j] = cb[e];
-      pos[j] = cp[e];
+      const u32x2_t x = cw[min((uint32_t)(t + PF_T * j), nc - 1u)];  // (score bits, position)
+      bits[j] = x[0];
+      pos[j] = (int32_t)x[1];
     }
     auto key_of = [&](int j) { return score_key(__uint_as_float(bits[j])); };
     const int words = (n + 31) >> 5;
@@ -1349,12 +1347,12 @@ void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, in
 
 static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((n + 31) / 32); }
 
-void launch_prefilter_finish(const uint32_t* cbits, const int32_t* cpos, const uint32_t* cnt, const float* T,
+void launch_prefilter_finish(const uint2* cpair, const uint32_t* cnt, const float* T,
                              int capg, int64_t n_rows, int n, int k, int G, int Hq, int M, int32_t* idx, float* sel,
                              uint32_t* row_flag, uint32_t* group_flag, hipStream_t st) {
   (void)max_lds_bytes();
-  hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(PF_T), prefilter_finish_lds(n), st, cbits,
-                     cpos, cnt, T, capg, n, k, G, Hq, M, idx, sel, row_flag, group_flag);
+  hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(PF_T), prefilter_finish_lds(n), st, cpair,
+                     cnt, T, capg, n, k, G, Hq, M, idx, sel, row_flag, group_flag);
 }
 
 }  // namespace tka
