@@ -202,7 +202,8 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
   constexpr int KS = D / 32;
   constexpr int P = 32;
   constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: the tile cursor lives in SGPRs
   const int n = lane & 15, kg = lane >> 4;
   // M queries per sequence (M <= 4): wave w scores query tq = w % M on tile lane w / M of TL = 4 / M;
   // the M waves of a tile lane read the same tiles (SH: cached loads, so the repeats hit the caches)
@@ -212,10 +213,9 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
   const int lim = L - M + tq + 1;  // positions query tq may see
   extern __shared__ uint4 smem_raw[];
   uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
-  // S slots per head: score bits [G][S], then positions [G][S]
-  uint32_t* sbits = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB) +
-                    (size_t)wave * 2 * G * S;
-  int32_t* spos = reinterpret_cast<int32_t*>(sbits + G * S);
+  // S + 1 (score bits, position) slots per head; slot S takes the writes of pairs not kept
+  uint2* stg = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB) +
+               (size_t)wave * G * (S + 1);
 
   const int64_t per = ntiles / gridDim.x, extra = ntiles % gridDim.x;
   const int64_t r0 = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
@@ -247,14 +247,16 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       if (o.cpair) {  // one 8-byte (bits, position) store per pair
         for (uint32_t e = lane; e < c; e += 64)
           if (bh + e < (uint32_t)o.capg) {  // streaming stores: the lists are read once, by another kernel
-            u32x2_t x = {sbits[h * S + e], (uint32_t)spos[h * S + e]};
+            const uint2 y = stg[h * (S + 1) + e];
+            u32x2_t x = {y.x, y.y};
             __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
           }
       } else {
         for (uint32_t e = lane; e < c; e += 64)
           if (bh + e < (uint32_t)o.capg) {
-            __builtin_nontemporal_store(sbits[h * S + e], o.cbits + r * o.capg + bh + e);
-            __builtin_nontemporal_store(spos[h * S + e], o.cpos + r * o.capg + bh + e);
+            const uint2 y = stg[h * (S + 1) + e];
+            __builtin_nontemporal_store(y.x, o.cbits + r * o.capg + bh + e);
+            __builtin_nontemporal_store((int32_t)y.y, o.cpos + r * o.capg + bh + e);
           }
       }
     }
@@ -341,11 +343,19 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[tt][i] = acc[i] * scale;
-        const int pos = pos0 + 16 * tt + 4 * kg + i;
-        f[tt][i] = hl & (tnan | (v[tt][i] >= Tf)) & (whole | (pos < lim));
-        c += f[tt][i] ? 1u : 0u;
+        f[tt][i] = hl & (tnan | (v[tt][i] >= Tf));
       }
     }
+    if (!whole) {  // the last tile: rows past the query's limit (loaded as row L-1) are never kept
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[tt][i] = f[tt][i] & (pos0 + 16 * tt + 4 * kg + i < lim);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c += f[tt][i] ? 1u : 0u;
     __builtin_amdgcn_wave_barrier();  // operand reads of this tile precede the next tile's writes
     // per head: total over the four lanes holding it, and this lane's offset among them (kg order)
     const uint32_t a1 = (uint32_t)__shfl_xor((int)c, 16, kWave);
@@ -353,18 +363,19 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
     const uint32_t tot = pair + a2;
     const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
-    if (hl) {  // scnt + tot <= S: the stage was flushed when it could not take a whole tile
+    {  // scnt + tot <= S: the stage was flushed when it could not take a whole tile. No branches:
+       // a pair not kept (and every pair of a lane without a head) is written to the spare slot S
+      uint2* hs = stg + (hl ? n : 0) * (S + 1);
       uint32_t slot = scnt + pre;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (f[tt][i]) {
-            sbits[n * S + slot] = __float_as_uint(v[tt][i]);
-            spos[n * S + slot] = pos0 + 16 * tt + 4 * kg + i;
-            ++slot;
-          }
-      scnt += tot;
+        for (int i = 0; i < 4; ++i) {
+          hs[f[tt][i] ? slot : (uint32_t)S] =
+              make_uint2(__float_as_uint(v[tt][i]), (uint32_t)(pos0 + 16 * tt + 4 * kg + i));
+          slot += f[tt][i] ? 1u : 0u;
+        }
+      if (hl) scnt += tot;
     }
     // flush before the next tile if a head could overflow on it or it starts another group
     pend = more && (ng != cg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
@@ -771,7 +782,7 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   const int64_t ntiles = (int64_t)a.B * a.Hkv * tpg;
   // stage slots per head: PS_STAGE_BYTES per wave over G heads x (bits, position)
   const int S = PS_STAGE_BYTES / (8 * a.G);
-  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * 2 * a.G * S * sizeof(uint32_t);
+  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * a.G * (S + 1) * 8;
   const int fit = (int)(device_lds_limit() / lds);  // workgroups whose LDS fits one CU
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
