@@ -390,6 +390,183 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 }
 
 // ---------------------------------------------------------------------------
+// Candidate scan for several queries per sequence (2 <= M <= 4), persistent.
+// Workgroup i owns a contiguous range of 32-position tiles of the flattened
+// (batch * KV head, position) space, as above, but its four waves take every
+// tile together: the workgroup loads a tile once (each thread 16-byte chunks
+// of it), four tiles ahead in a ring of four register buffers written out by
+// hand, stores it to one of two LDS tile buffers, and after one barrier wave
+// w < M scores query w's G heads on it (the MFMA, threshold test, staging
+// and flushes of the one-query scan, with the query's causal limit).
+// ---------------------------------------------------------------------------
+#ifndef TKA_SHARED_SCAN
+#define TKA_SHARED_SCAN 1
+#endif
+
+template <int D>
+__global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ K, int Hq, int Hkv,
+                                                                int G, int M, int L, int64_t sb, int64_t sh,
+                                                                int64_t sl, float scale, int ntiles, int tpg, int S,
+                                                                MfmaOut o) {
+  constexpr int KS = D / 32;
+  constexpr int P = 32;
+  constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16;
+  constexpr int NT = P * CPR / 256;  // 16-byte chunks a thread loads per tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, kg = lane >> 4;
+  const bool act = wave < M;  // wave w scores query w
+  const int tq = act ? wave : 0;
+  const int lim = L - M + tq + 1;  // positions query tq may see
+  extern __shared__ uint4 smem_raw[];
+  uint8_t* tiles = reinterpret_cast<uint8_t*>(smem_raw);  // two tile buffers of P rows
+  uint2* stg = reinterpret_cast<uint2*>(tiles + 2 * P * PADB) + (size_t)wave * G * (S + 1);  // S + 1 per head
+
+  const int per = ntiles / (int)gridDim.x, extra = ntiles % (int)gridDim.x;
+  const int r0 = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
+  const int r1 = r0 + per + ((int)blockIdx.x < extra ? 1 : 0);
+  if (r0 >= r1) return;  // workgroup-uniform
+
+  int grp = -1;
+  bf16x8_t bq[KS];
+  float Tf = 0.f;
+  bool tnan = false;
+  uint32_t scnt = 0;
+  const bool hl = act && n < G;
+  auto reserve = [&]() -> uint32_t {
+    const int b = grp / Hkv, g = grp % Hkv;
+    uint32_t base = 0;
+    if (lane < G && scnt != 0) base = atomicAdd(&o.cnt[((int64_t)b * M + tq) * Hq + g * G + lane], scnt);
+    return base;
+  };
+  auto copy_out = [&](uint32_t base) {
+    const int b = grp / Hkv, g = grp % Hkv;
+    const int64_t rg = ((int64_t)b * M + tq) * Hq + g * G;
+    for (int h = 0; h < G; ++h) {
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)scnt, h);
+      if (c == 0) continue;
+      const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)base, h);
+      const int64_t r = rg + h;
+      for (uint32_t e = lane; e < c; e += 64)
+        if (bh + e < (uint32_t)o.capg) {  // the fused step's packed lists
+          const uint2 y = stg[h * (S + 1) + e];
+          u32x2_t x = {y.x, y.y};
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
+        }
+    }
+    scnt = 0;
+  };
+  // loads of tile u into a (rows past L-1 re-read row L-1); past the range's last tile the
+  // cursor stays on it, so every step issues the same number of loads
+  int ld = r0;
+  auto load_next = [&](uint4 (&a)[NT]) {
+    const int g = ld / tpg, tin = ld - g * tpg;
+    const uint16_t* base = K + (int64_t)(g / Hkv) * sb + (int64_t)(g % Hkv) * sh;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      const int pos = min(tin * P + c / CPR, L - 1);
+      a[j] = ld16(base + (int64_t)pos * sl + (c % CPR) * 8);
+    }
+    if (ld + 1 < r1) ++ld;
+  };
+  int u = r0;  // the tile being scored
+  bool pend = false;
+  // one tile: its registers to LDS, the buffer refilled SS_DEPTH tiles ahead, a barrier, the scoring
+  auto step = [&](uint4 (&a)[NT]) -> bool {
+    uint8_t* tb = tiles + (size_t)(u & 1) * P * PADB;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      *reinterpret_cast<uint4*>(tb + (c / CPR) * PADB + (c % CPR) * 16) = a[j];
+    }
+    load_next(a);
+    __syncthreads();  // the tile is in LDS; every wave is done with the buffer written next step
+    const int cg = u / tpg, ct = u - cg * tpg;
+    const bool more = u + 1 < r1;
+    if (act) {
+      if (pend) {
+        copy_out(reserve());
+        pend = false;
+      }
+      if (cg != grp) {  // new KV group (its stage is empty): the query's fragments and thresholds
+        grp = cg;
+        const int b = grp / Hkv, g = grp % Hkv;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (hl) v = ld16(q + (((int64_t)b * M + tq) * Hq + g * G + n) * D + 32 * s + 8 * kg);
+          bq[s] = __builtin_bit_cast(bf16x8_t, v);
+        }
+        const float tv = hl ? o.T[((int64_t)b * M + tq) * Hq + g * G + n] : 0.f;
+        Tf = tv;
+        tnan = tv != tv;
+      }
+      const int pos0 = ct * P;
+      const bool whole = pos0 + P <= lim;
+      bool f[2][4];
+      float v[2][4];
+      uint32_t c = 0;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const uint4 x = *reinterpret_cast<const uint4*>(tb + (16 * tt + n) * PADB + (kg + 4 * s) * 16);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), bq[s], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[tt][i] = acc[i] * scale;
+          f[tt][i] = hl & (tnan | (v[tt][i] >= Tf));
+        }
+      }
+      if (!whole) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[tt][i] = f[tt][i] & (pos0 + 16 * tt + 4 * kg + i < lim);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c += f[tt][i] ? 1u : 0u;
+      const uint32_t a1 = (uint32_t)__shfl_xor((int)c, 16, kWave);
+      const uint32_t pair = c + a1;
+      const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
+      const uint32_t tot = pair + a2;
+      const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
+      {
+        uint2* hs = stg + (hl ? n : 0) * (S + 1);
+        uint32_t slot = scnt + pre;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hs[f[tt][i] ? slot : (uint32_t)S] =
+                make_uint2(__float_as_uint(v[tt][i]), (uint32_t)(pos0 + 16 * tt + 4 * kg + i));
+            slot += f[tt][i] ? 1u : 0u;
+          }
+        if (hl) scnt += tot;
+      }
+      const int ng = (u + 1) / tpg;
+      pend = more && (ng != cg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
+    }
+    ++u;
+    return more;
+  };
+  uint4 a0[NT], a1[NT], a2[NT], a3[NT];
+  load_next(a0);
+  load_next(a1);
+  load_next(a2);
+  load_next(a3);
+  while (step(a0) && step(a1) && step(a2) && step(a3)) {
+  }
+  if (act && grp >= 0) copy_out(reserve());
+}
+
+// ---------------------------------------------------------------------------
 // Several causal queries per sequence ("Evolution of Sparse Attention in
 // Long-Context LLMs", section 6: current length x K instead of current length
 // x full history): the M queries of sequence b sit at positions L-M .. L-1
@@ -787,6 +964,19 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
   const int M = a.M > 1 ? a.M : 1;  // the caller keeps M <= 4
+  if (M > 1 && TKA_SHARED_SCAN && o.cpair) {
+    // two tile buffers and four wave stages sized to fit two workgroups per CU
+    const size_t tiles = (size_t)2 * 32 * (D * 2 + 16);
+    const int S2 = (int)(((size_t)device_lds_limit() / 2 - tiles - 256) / (4 * 8 * (size_t)a.G)) - 1;
+    const size_t lds2 = tiles + (size_t)4 * a.G * (S2 + 1) * 8;
+    int64_t g2 = (int64_t)device_cus() * 2;
+    if (g2 > ntiles) g2 = ntiles;
+    ensure_dynamic_lds((const void*)score_cand_shared_kernel<D>, lds2);
+    hipLaunchKernelGGL((score_cand_shared_kernel<D>), dim3((unsigned)g2), dim3(256), lds2, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh, a.sl, a.scale, (int)ntiles,
+                       tpg, S2, o);
+    return;
+  }
   if (M == 1) {
     ensure_dynamic_lds((const void*)score_cand_persistent_kernel<D, false>, lds);
     hipLaunchKernelGGL((score_cand_persistent_kernel<D, false>), dim3((unsigned)grid), dim3(256), lds, st,
