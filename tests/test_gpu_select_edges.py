@@ -44,6 +44,10 @@ def _rows(kind, n_rows, n, rng):
         return x
     if kind == "staircase":
         return np.tile(np.repeat(np.arange(n // 7 + 1, dtype=np.float32)[::-1], 7)[:n], (n_rows, 1))
+    if kind == "skew":  # the large values crowd into the first eighth of the row
+        x = rng.standard_normal((n_rows, n)).astype(np.float32)
+        x[:, : n // 8] += 3.0
+        return x
     raise ValueError(kind)
 
 
@@ -72,6 +76,24 @@ def test_select_adversarial(kind, shape):
         assert np.array_equal(gs[:, :kk].view(np.uint32), x[rows, gi[:, :kk]].view(np.uint32))
         assert np.all(np.isneginf(gs[:, kk:]))
         assert torch.equal(idx, idx2) and torch.equal(sel.view(torch.int32), sel2.view(torch.int32))
+
+
+@pytest.mark.parametrize("kind", ["normal", "dups", "tierun", "ascending", "special", "skew", "equal"])
+def test_select_long_rows_sampled_threshold(kind):
+    """Rows of 131072 with k' <= n/8 take the sampled threshold and one collecting pass; rows
+    where it cannot hold (ties, crowding) fall back to the digit search: bit-exact either way."""
+    n_rows, n = 128, 131072
+    rng = np.random.default_rng(hash((kind, "long")) % (1 << 32))
+    x = _rows(kind, n_rows, n, rng)
+    xt = torch.from_numpy(x).cuda()
+    m = tka()
+    for k in (512, 4096):
+        say(f"[select long rows] {kind} k={k}")
+        idx, sel = m.topk_select(xt, k)
+        gi = idx.cpu().numpy()
+        assert np.array_equal(gi, orc.select(x, k)), (kind, k)
+        rows = np.arange(n_rows)[:, None]
+        assert np.array_equal(sel.cpu().numpy().view(np.uint32), x[rows, gi].view(np.uint32))
 
 
 def test_select_strided_and_unaligned_rows():

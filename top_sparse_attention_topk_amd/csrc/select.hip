@@ -20,6 +20,7 @@
 //    one workgroup per row finishes on the (small) candidate list.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -35,6 +36,16 @@ constexpr int NB0 = 4096;
 constexpr int NB1 = 1024;
 constexpr int UNR = 4;          // float4 loads per lane per round
 constexpr int CHUNK = 4096;     // split mode: elements per workgroup
+constexpr int SEL_SAMPLES = 2048;       // row mode: samples for the threshold of long rows
+#ifndef TKA_SEL_SAMPLE_MIN_N
+#define TKA_SEL_SAMPLE_MIN_N 16384
+#endif
+constexpr int SEL_SAMPLE_MIN_N = TKA_SEL_SAMPLE_MIN_N;  // shortest row that takes the sampled threshold
+constexpr int SEL_SAMPLE_MAX_N = 262144;                // longest: a wave's segment fits 16-bit offsets
+#ifndef TKA_SEL_U
+#define TKA_SEL_U 16
+#endif
+constexpr int SEL_U = TKA_SEL_U;  // float4 loads per lane in flight in the sampled path's pass
 constexpr int SUBCH = CHUNK / SW;
 
 __device__ __forceinline__ int lv_shift(int lv) { return lv == 0 ? 20 : (lv == 1 ? 10 : 0); }
@@ -57,6 +68,7 @@ struct SelSmem {
   uint32_t hist[NB0];
   uint32_t scan[16];
   uint32_t res[2];
+  uint32_t aux;
   uint32_t cnt[SW];
   uint32_t gt[SW], eq[SW];
   uint32_t obase[SW], eqbase[SW];
@@ -141,18 +153,19 @@ __device__ void hist_pass(const float* s, int r0, int r1, bool aligned, int lv, 
   }
 }
 
-// Keys >= lo of [r0, r1), in position order, to cb/cp (first `cap` of them).
-// Returns the number found (the same value in every lane).
-__device__ uint32_t collect_pass(const float* s, int r0, int r1, bool aligned, uint32_t lo, uint32_t* cb,
-                                 int32_t* cp, uint32_t cap) {
+// Keys >= lo of [r0, r1), in position order, to cb/cp (first `cap` of them), U float4
+// loads per lane in flight. Returns the number found (the same value in every lane).
+template <int U>
+__device__ uint32_t collect_pass_t(const float* s, int r0, int r1, bool aligned, uint32_t lo, uint32_t* cb,
+                                   int32_t* cp, uint32_t cap) {
   const int lane = lane_id();
   uint32_t cnt = 0;
-  for (int base = r0; base < r1; base += 256 * UNR) {
-    float v[UNR][4];
+  for (int base = r0; base < r1; base += 256 * U) {
+    float v[U][4];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
+    for (int u = 0; u < U; ++u) load4(s, base + u * 256 + 4 * lane, r1, aligned, v[u]);
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
+    for (int u = 0; u < U; ++u) {
       bool f[4];
       uint32_t before = 0, tot = 0;
 #pragma unroll
@@ -170,6 +183,54 @@ __device__ uint32_t collect_pass(const float* s, int r0, int r1, bool aligned, u
           if (slot < cap) {
             cb[slot] = __float_as_uint(v[u][j]);
             cp[slot] = base + u * 256 + 4 * lane + j;
+          }
+          ++slot;
+        }
+      }
+      cnt += tot;
+    }
+  }
+  return cnt;
+}
+
+__device__ uint32_t collect_pass(const float* s, int r0, int r1, bool aligned, uint32_t lo, uint32_t* cb,
+                                 int32_t* cp, uint32_t cap) {
+  return collect_pass_t<UNR>(s, r0, r1, aligned, lo, cb, cp, cap);
+}
+
+// collect_pass for a 16-byte aligned row whose segment ends are multiples of 4: every load is
+// one float4 with no branch around it (past r1 the address is clamped to the last float4 of the
+// segment and the values masked), so all U of a round are in flight together - a load under a
+// condition makes the compiler wait for each one before the next.
+template <int U>
+__device__ __forceinline__ uint32_t collect_fast(const float* s, int r0, int r1, uint32_t lo, uint32_t* cb,
+                                                 uint16_t* cp, uint32_t cap) {
+  const int lane = lane_id();
+  uint32_t cnt = 0;
+  for (int base = r0; base < r1; base += 256 * U) {
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = *reinterpret_cast<const float4*>(s + min(base + u * 256 + 4 * lane, r1 - 4));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p0 = base + u * 256 + 4 * lane;
+      const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      bool f[4];
+      uint32_t before = 0, tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[j] = p0 < r1 && score_key(v[j]) >= lo;
+        const uint64_t bl = ballot(f[j]);
+        before += count_below(bl);
+        tot += __popcll(bl);
+      }
+      uint32_t slot = cnt + before;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (f[j]) {
+          if (slot < cap) {
+            cb[slot] = __float_as_uint(v[j]);
+            cp[slot] = (uint16_t)(p0 + j - r0);  // offset in the segment: positions as 16 bits
           }
           ++slot;
         }
@@ -227,6 +288,61 @@ __device__ void radix_kth(KeyOf key_of, uint32_t cnt, int l0, uint32_t prefix, u
 __device__ void refine_candidates(const uint32_t* cb, uint32_t off, uint32_t cnt, int lv, uint32_t prefix,
                                   uint32_t need, SelSmem& sm) {
   radix_kth([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, cnt, lv + 1, prefix, need, sm);
+}
+
+// The need-th largest key among candidates that are all >= lo (wave w owns cb[off, off + cnt)),
+// with one histogram of NB0 bins over the candidates' own range [lo, max] (bins spread over the
+// values actually present, so few atomics meet on one address), then the critical bin's
+// elements ranked one by one. Result as for radix_kth: sm.res[0] = the need-th largest key T,
+// sm.res[1] = how many keys == T to keep. Returns false, the result unset, when the critical
+// bin holds more than REL_STASH elements (heavy ties): the caller takes the digit search.
+constexpr uint32_t REL_STASH = 1024;
+__device__ bool relative_kth(const uint32_t* cb, uint32_t off, uint32_t cnt, uint32_t lo, uint32_t need,
+                             SelSmem& sm) {
+  const int t = threadIdx.x, w = t >> 6, lane = lane_id();
+  uint32_t mx = lo;
+  for (uint32_t e = lane; e < cnt; e += 64) mx = max(mx, score_key(__uint_as_float(cb[off + e])));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  if (lane == 0) sm.gt[w] = mx;
+  for (int i = t; i < NB0; i += ST) sm.hist[i] = 0;
+  __syncthreads();
+  uint32_t hi = lo;
+#pragma unroll
+  for (int i = 0; i < SW; ++i) hi = max(hi, sm.gt[i]);
+  const uint32_t span = hi - lo;
+  const int shift = span >= (uint32_t)NB0 ? (32 - __clz(span)) - 12 : 0;  // span >> shift < NB0
+  for (uint32_t e = lane; e < cnt; e += 64)
+    atomicAdd(&sm.hist[(score_key(__uint_as_float(cb[off + e])) - lo) >> shift], 1u);
+  __syncthreads();
+  find_bin_t<SW>(sm.hist, NB0, need, sm);
+  const uint32_t bin = sm.res[0], above = sm.res[1], inbin = sm.hist[bin];
+  __syncthreads();
+  if (inbin > REL_STASH) return false;  // workgroup-uniform
+  if (t == 0) sm.aux = 0u;
+  __syncthreads();
+  uint32_t* stash = sm.hist;  // the histogram is spent
+  for (uint32_t e = lane; e < cnt; e += 64) {
+    const uint32_t key = score_key(__uint_as_float(cb[off + e]));
+    if (((key - lo) >> shift) == bin) stash[atomicAdd(&sm.aux, 1u)] = key;
+  }
+  __syncthreads();
+  const uint32_t nd = need - above;  // 1 <= nd <= inbin
+  for (uint32_t i = t; i < inbin; i += ST) {
+    const uint32_t v = stash[i];
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < inbin; ++j) {
+      const uint32_t x = stash[j];
+      gt += x > v;
+      ge += x >= v;
+    }
+    if (gt < nd && nd <= ge) {  // v is the nd-th largest of the bin (every such i writes the same)
+      sm.res[0] = v;
+      sm.res[1] = nd - gt;
+    }
+  }
+  __syncthreads();
+  return true;
 }
 
 // Emit, in position order, every element with key > T and the first need_eq
@@ -322,6 +438,59 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float* __restric
       if (osel) osel[p] = s[p];
     }
     return;
+  }
+  // Sampled threshold (long rows, k' <= n/8): the key T of the r-th largest of ns samples, r a
+  // few standard deviations above the samples expected among the k' largest, so that one pass
+  // collecting the keys >= T almost always yields between k' and the LDS capacity of them. Then
+  // the k' largest are among them (the k'-th largest key is >= T) and the row is read once more
+  // only when it is not so (the digit-by-digit search below).
+  const int ns = min(SEL_SAMPLES, 4 * capw) & ~255;
+  if (n >= SEL_SAMPLE_MIN_N && n <= SEL_SAMPLE_MAX_N && (int64_t)kk * 8 <= n && ns >= 1024 && aligned &&
+      (n & 3) == 0 && (stride & 3) == 0) {
+    // candidates as 4-byte keys and 16-bit offsets in the wave's segment (at most 65536 long)
+    const uint32_t capf = (uint32_t)(capw * 8 / 6) & ~63u;
+    uint16_t* cq = reinterpret_cast<uint16_t*>(cb + SW * capf);
+    const int nch = ns / 64;  // chunks of 64 consecutive elements, spread over the row
+    const int per_w = ns / SW;
+    uint32_t* samp = cb;
+    for (int c = w; c < nch; c += SW) {
+      const int64_t at = (int64_t)c * n / nch;
+      samp[c * 64 + lane] = score_key(s[at + lane]);
+    }
+    __syncthreads();
+    const float E = (float)kk * (float)ns / (float)n;
+    const uint32_t r = min((uint32_t)ns, (uint32_t)ceilf(E + 4.5f * sqrtf(E)) + 2u);
+    // wave w owns the samples of chunks w, w + SW, ...
+    radix_kth_t<SW>([&](uint32_t e) { return samp[((e >> 6) * SW + w) * 64 + (e & 63)]; }, (uint32_t)per_w, 0, 0u,
+                    r, sm);
+    const uint32_t T = sm.res[0];
+    __syncthreads();  // every wave has T before the samples are overwritten
+    const uint32_t c = collect_fast<SEL_U>(s, r0, r1, T, cb + w * capf, cq + w * capf, capf);
+    if (lane == 0) sm.cnt[w] = c;
+    __syncthreads();
+    bool over = false;
+    uint32_t base = 0, total = 0;
+    for (int i = 0; i < SW; ++i) {
+      over |= sm.cnt[i] > capf;
+      base += (i < w) ? sm.cnt[i] : 0u;
+      total += sm.cnt[i];
+    }
+    __syncthreads();
+    if (total >= (uint32_t)kk && total <= SW * capf) {  // workgroup-uniform
+      uint32_t off = w * capf;
+      if (over) {  // uneven spread across waves: pack the waves' candidates back to back
+        collect_fast<SEL_U>(s, r0, r1, T, cb + base, cq + base, 0xffffffffu);
+        off = base;
+        __syncthreads();
+      }
+      if (!relative_kth(cb, off, c, T, (uint32_t)kk, sm))
+        radix_kth([&](uint32_t e) { return score_key(__uint_as_float(cb[off + e])); }, c, 0, 0u, (uint32_t)kk, sm);
+      const uint32_t Tk = sm.res[0], need_eq = sm.res[1];
+      __syncthreads();
+      emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = cb[off + e]; pos = r0 + (int)cq[off + e]; },
+                    c, Tk, need_eq, sm, oidx, osel, (uint32_t)kk);
+      return;
+    }
   }
   int lv = 0;
   uint32_t prefix = 0, need = (uint32_t)kk, cnt_above = 0;
@@ -1257,11 +1426,14 @@ void ensure_dynamic_lds(const void* kernel, size_t bytes) {
 
 static int rows_capw(int n, int k, size_t* lds) {
   const int kk = k < n ? k : n;
-  int capw = 64;
-  while (capw < 2048 && (int64_t)SW * capw < (int64_t)kk + kk / 2 + 64) capw <<= 1;
+  // candidates per wave: 1.5 k' + 64 over the waves, in multiples of 64, at most what lets two
+  // workgroups share a CU's LDS
   const size_t head = (sizeof(SelSmem) + 15) & ~(size_t)15;
   const int lds_max = max_lds_bytes();
-  while (capw > 64 && head + (size_t)SW * capw * 8 > (size_t)lds_max) capw >>= 1;
+  const int two = (int)(((size_t)lds_max / 2 - head) / (SW * 8)) & ~63;
+  int capw = (int)((((int64_t)kk + kk / 2 + 64 + SW - 1) / SW + 63) & ~(int64_t)63);
+  capw = std::max(64, std::min(capw, std::max(64, two)));
+  while (capw > 64 && head + (size_t)SW * capw * 8 > (size_t)lds_max) capw -= 64;
   *lds = head + (size_t)SW * capw * 8;
   return capw;
 }
