@@ -348,8 +348,8 @@ __device__ bool relative_kth(const uint32_t* cb, uint32_t off, uint32_t cnt, uin
 // Emit, in position order, every element with key > T and the first need_eq
 // elements with key == T. Wave w walks its own segment [0, cnt) through
 // get(e) -> (bits, position); segments are in position order by wave.
-template <typename Get>
-__device__ void emit_segments(Get get, uint32_t cnt, uint32_t T, uint32_t need_eq, SelSmem& sm, int32_t* oidx,
+template <typename Get, typename Sm>
+__device__ void emit_segments(Get get, uint32_t cnt, uint32_t T, uint32_t need_eq, Sm& sm, int32_t* oidx,
                               float* osel, uint32_t kk) {
   const int w = threadIdx.x >> 6, lane = lane_id();
   uint32_t ngt = 0, neq = 0;
@@ -1120,10 +1120,43 @@ static_assert(1536 + SW * 1024 / 2 <= AK_BUF && 2048 + 2048 / 2 <= AK_BUF, "hist
 constexpr int AK_UNR = 8;  // float4 loads in flight per lane in the streaming passes
 constexpr int AK_EJ = 16;  // lane-strided elements per lane per round of the emission pass
 
+// Sampled path of long rows: the keys >= T0 (T0 a sample quantile with about AKF_WANT keys above
+// it) are collected while the row's mass is summed, and the search runs on them in LDS.
+constexpr int AKF_WANT = 2048;  // expected candidates per row
+constexpr int AKF_CAP = 4096;   // candidates per row held in LDS (AKF_CAP / SW per wave)
+constexpr int AKF_NB = 1024;    // bins of the candidates' relative histogram
+struct AkCand {
+  uint32_t bits[AKF_CAP];     // score bits, per wave in position order
+  uint16_t off[AKF_CAP];      // position minus the wave's segment start
+  uint64_t hmass[AKF_NB];     // relative histogram: mass and count per bin
+  uint32_t hcnt[AKF_NB];      // (then the critical bin's keys)
+};
+struct AkFast {
+  SelSmem sel;
+  uint32_t samp[SEL_SAMPLES];
+};
+union AkShared {
+  AkSmem ak;
+  AkFast f;
+  AkCand c;
+};
+// reductions and results of the sampled path (outside the union)
+struct AkRed {
+  uint64_t wm[SW];
+  uint32_t wc[SW];
+  uint32_t wk[SW];
+  uint32_t gt[SW], eq[SW], obase[SW], eqbase[SW];
+  uint64_t res_mass;
+  uint32_t res_bin, res_cnt, aux;
+  uint32_t tkey, tcnt;
+  uint64_t tmass;
+};
+
 // Bin b (of nb, bins ascending with the key) where the mass of the bins above
 // it stays below need and reaching into b meets it. Writes the bin, the mass
 // and the count of the bins above it to sm.res_*.
-__device__ void ak_find_bin(AkSmem& sm, const uint64_t* mass, const uint32_t* cnt, int nb, uint64_t need) {
+template <typename Sm>
+__device__ void ak_find_bin(Sm& sm, const uint64_t* mass, const uint32_t* cnt, int nb, uint64_t need) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int per = nb / ST;
   uint64_t m = 0;
@@ -1189,13 +1222,196 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
                                                          uint64_t* __restrict__ Wout, float* __restrict__ Mout,
                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
                                                          uint32_t* __restrict__ row_flag) {
-  __shared__ AkSmem sm;
+  __shared__ AkShared shm;
+  __shared__ AkRed fr;
+  AkSmem& sm = shm.ak;
   const int64_t row = blockIdx.x;
   const float* s = S + row * stride;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
   const int seg = ((n + 4 * SW - 1) / (4 * SW)) * 4;
   const int r0 = min(n, w * seg), r1 = min(n, r0 + seg);
+  // 0. Long rows: two passes (the maximum; the mass total while the keys >= T0 are collected),
+  // then the search among the candidates in LDS. The result is the one the digit search below
+  // finds (the smallest k under the same integer masses), whenever the candidates hold the mass
+  // to keep; otherwise (or on crowding, ties, no mass) the row goes the digit-search way.
+  if (n >= SEL_SAMPLE_MIN_N && n <= SEL_SAMPLE_MAX_N && aligned && (n & 3) == 0 && (stride & 3) == 0) {
+    AkFast& f = shm.f;
+    const int ns = SEL_SAMPLES, nch = ns / 64;
+    for (int c = w; c < nch; c += SW) {
+      const int64_t at = (int64_t)c * n / nch;
+      f.samp[c * 64 + lane] = score_key(s[at + lane]);
+    }
+    __syncthreads();
+    const uint32_t rs = (uint32_t)max((int64_t)1, min((int64_t)ns, (int64_t)AKF_WANT * ns / n));
+    radix_kth_t<SW>([&](uint32_t e) { return f.samp[((e >> 6) * SW + w) * 64 + (e & 63)]; }, (uint32_t)(ns / SW),
+                    0, 0u, rs, f.sel);
+    const uint32_t T0 = f.sel.res[0];
+    __syncthreads();  // the samples are spent
+    // the row maximum (every load one float4 with no branch around it)
+    uint32_t mk = 0;
+    for (int base = r0; base < r1; base += 256 * AK_UNR) {
+      float4 x[AK_UNR];
+#pragma unroll
+      for (int u = 0; u < AK_UNR; ++u)
+        x[u] = *reinterpret_cast<const float4*>(s + min(base + u * 256 + 4 * lane, r1 - 4));
+#pragma unroll
+      for (int u = 0; u < AK_UNR; ++u)
+        if (base + u * 256 + 4 * lane < r1)
+          mk = max(max(max(mk, score_key(x[u].x)), score_key(x[u].y)), max(score_key(x[u].z), score_key(x[u].w)));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, kWave));
+    if (lane == 0) fr.wk[w] = mk;
+    __syncthreads();
+    mk = 0;
+    for (int i = 0; i < SW; ++i) mk = max(mk, fr.wk[i]);
+    if (mk != 0u) {  // workgroup-uniform; a row with no number has no mass (the digit-search way)
+      const float M = key_value(mk);
+      // the mass total and the candidates, in position order per wave
+      AkCand& cd = shm.c;
+      constexpr uint32_t capw = AKF_CAP / SW;
+      uint32_t* cb = cd.bits + w * capw;
+      uint16_t* co = cd.off + w * capw;
+      uint64_t wl = 0;
+      uint32_t cnt = 0;
+      for (int base = r0; base < r1; base += 256 * AK_UNR) {
+        float4 x[AK_UNR];
+#pragma unroll
+        for (int u = 0; u < AK_UNR; ++u)
+          x[u] = *reinterpret_cast<const float4*>(s + min(base + u * 256 + 4 * lane, r1 - 4));
+#pragma unroll
+        for (int u = 0; u < AK_UNR; ++u) {
+          const int p0 = base + u * 256 + 4 * lane;
+          const bool valid = p0 < r1;  // whole float4s: r1 is a multiple of 4
+          const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+          bool fk[4];
+          uint32_t before = 0, tot = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            wl += valid ? ak_mass(v[j], M) : 0ull;
+            fk[j] = valid && score_key(v[j]) >= T0;
+            const uint64_t bl = ballot(fk[j]);
+            before += count_below(bl);
+            tot += __popcll(bl);
+          }
+          uint32_t slot = cnt + before;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (fk[j]) {
+              if (slot < capw) {
+                cb[slot] = __float_as_uint(v[j]);
+                co[slot] = (uint16_t)(p0 + j - r0);
+              }
+              ++slot;
+            }
+          }
+          cnt += tot;
+        }
+      }
+      wl = wave_sum(wl);
+      if (lane == 0) {
+        fr.wm[w] = wl;
+        fr.wc[w] = cnt;
+      }
+      __syncthreads();
+      uint64_t W = 0;
+      bool over = false;
+      for (int i = 0; i < SW; ++i) {
+        W += fr.wm[i];
+        over |= fr.wc[i] > capw;
+      }
+      const double drop = floor((double)eps * (double)W);
+      const uint64_t need = drop >= (double)W ? 0 : W - (uint64_t)drop;
+      // the candidates' mass (all keys >= T0, when none was dropped)
+      uint64_t cm = 0;
+      if (!over)
+        for (uint32_t e = lane; e < cnt; e += 64) cm += ak_mass(__uint_as_float(cb[e]), M);
+      cm = wave_sum(cm);
+      __syncthreads();
+      if (lane == 0) fr.wm[w] = cm;
+      __syncthreads();
+      uint64_t CM = 0;
+      for (int i = 0; i < SW; ++i) CM += fr.wm[i];
+      if (!over && need > 0 && CM >= need) {  // workgroup-uniform: T >= T0, every key >= T is here
+        // relative histogram of the candidates over [T0, max]: mass and count per bin
+        const uint32_t span = mk - T0;
+        const int shift = span >= (uint32_t)AKF_NB ? (32 - __clz(span)) - 10 : 0;  // span >> shift < AKF_NB
+        for (int i = t; i < AKF_NB; i += ST) {
+          cd.hmass[i] = 0;
+          cd.hcnt[i] = 0;
+        }
+        __syncthreads();
+        for (uint32_t e = lane; e < cnt; e += 64) {
+          const float v = __uint_as_float(cb[e]);
+          const uint32_t d = (score_key(v) - T0) >> shift;
+          atomicAdd(&cd.hcnt[d], 1u);
+          const uint64_t m = ak_mass(v, M);
+          if (m) atomicAdd(reinterpret_cast<unsigned long long*>(&cd.hmass[d]), (unsigned long long)m);
+        }
+        __syncthreads();
+        ak_find_bin(fr, cd.hmass, cd.hcnt, AKF_NB, need);
+        const uint32_t bin = fr.res_bin, inbin = cd.hcnt[bin];
+        const uint64_t m_above = fr.res_mass;
+        const uint32_t c_above = fr.res_cnt;
+        __syncthreads();
+        if (inbin <= (uint32_t)AKF_NB) {  // workgroup-uniform; else heavy ties: the digit-search way
+          // the critical bin's keys, then T: the key where the mass from the top reaches need
+          uint32_t* stash = cd.hcnt;  // the counts are spent
+          if (t == 0) fr.aux = 0u;
+          __syncthreads();
+          for (uint32_t e = lane; e < cnt; e += 64) {
+            const uint32_t key = score_key(__uint_as_float(cb[e]));
+            if (((key - T0) >> shift) == bin) stash[atomicAdd(&fr.aux, 1u)] = key;
+          }
+          __syncthreads();
+          for (uint32_t i = t; i < inbin; i += ST) {
+            const uint32_t v = stash[i];
+            uint64_t gm = 0, em = 0;
+            uint32_t gc = 0;
+            for (uint32_t j = 0; j < inbin; ++j) {
+              const uint32_t x = stash[j];
+              const uint64_t m = ak_mass(key_value(x), M);
+              gm += x > v ? m : 0ull;
+              em += x == v ? m : 0ull;
+              gc += x > v;
+            }
+            if (m_above + gm < need && need <= m_above + gm + em) {  // every such i writes the same
+              fr.tkey = v;
+              fr.tmass = m_above + gm;
+              fr.tcnt = c_above + gc;
+            }
+          }
+          __syncthreads();
+          const uint32_t T = fr.tkey;
+          const uint64_t m_gt = fr.tmass;
+          const uint64_t wT = ak_mass(key_value(T), M);
+          const uint32_t ties = (uint32_t)((need - m_gt + wT - 1) / wT);
+          const int64_t k_eps = (int64_t)fr.tcnt + ties;
+          const int64_t lo = k_min > 1 ? k_min : 1, hi = k_max < n ? k_max : n;
+          int64_t k = k_eps < lo ? lo : k_eps;
+          if (k > hi) k = hi;
+          if (t == 0) {
+            kout[row] = (int32_t)k;
+            Wout[row] = W;
+            Mout[row] = M;
+            row_flag[row] = k == k_eps ? 0u : 1u;
+          }
+          if (k != k_eps) return;  // held by k_min or k_max: the count-based row select
+          int32_t* oidx = idx + row * k_max;
+          float* osel = sel ? sel + row * k_max : nullptr;
+          for (int j = (int)k + t; j < k_max; j += ST) {
+            oidx[j] = -1;
+            if (osel) osel[j] = -INFINITY;
+          }
+          emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = cb[e]; pos = r0 + (int)co[e]; }, cnt, T,
+                        ties, fr, oidx, osel, (uint32_t)k);
+          return;
+        }
+      }
+    }
+    __syncthreads();  // the union is handed to the digit search
+  }
   // 1. the row maximum in the select order (NaN lowest)
   uint32_t mk = 0;
   for (int base = r0; base < r1; base += 256 * AK_UNR) {
