@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 #define TKA_PS_WPC 2
 #endif
 #ifndef TKA_PS_STAGE_BYTES
-#define TKA_PS_STAGE_BYTES 11264
+#define TKA_PS_STAGE_BYTES 11776
 #endif
 constexpr int PS_WPC = TKA_PS_WPC;                  // workgroups per CU
 constexpr int PS_STAGE_BYTES = TKA_PS_STAGE_BYTES;  // candidate stage per wave (G heads x 8 B x slots)
@@ -213,9 +213,11 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
   const int lim = L - M + tq + 1;  // positions query tq may see
   extern __shared__ uint4 smem_raw[];
   uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
-  // S + 1 (score bits, position) slots per head; slot S takes the writes of pairs not kept
+  // S (score bits, position) slots per head, then one spare slot per lane that takes the writes
+  // of pairs not kept (a slot per lane: one shared slot would make every such write a conflict)
   uint2* stg = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB) +
-               (size_t)wave * G * (S + 1);
+               (size_t)wave * (G * S + 64);
+  uint2* const spare = stg + G * S + lane;
 
   const int64_t per = ntiles / gridDim.x, extra = ntiles % gridDim.x;
   const int64_t r0 = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
@@ -247,14 +249,14 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       if (o.cpair) {  // one 8-byte (bits, position) store per pair
         for (uint32_t e = lane; e < c; e += 64)
           if (bh + e < (uint32_t)o.capg) {  // streaming stores: the lists are read once, by another kernel
-            const uint2 y = stg[h * (S + 1) + e];
+            const uint2 y = stg[h * S + e];
             u32x2_t x = {y.x, y.y};
             __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
           }
       } else {
         for (uint32_t e = lane; e < c; e += 64)
           if (bh + e < (uint32_t)o.capg) {
-            const uint2 y = stg[h * (S + 1) + e];
+            const uint2 y = stg[h * S + e];
             __builtin_nontemporal_store(y.x, o.cbits + r * o.capg + bh + e);
             __builtin_nontemporal_store((int32_t)y.y, o.cpos + r * o.capg + bh + e);
           }
@@ -364,14 +366,14 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     const uint32_t tot = pair + a2;
     const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
     {  // scnt + tot <= S: the stage was flushed when it could not take a whole tile. No branches:
-       // a pair not kept (and every pair of a lane without a head) is written to the spare slot S
-      uint2* hs = stg + (hl ? n : 0) * (S + 1);
+       // a pair not kept (and every pair of a lane without a head) goes to the lane's spare slot
+      uint2* hs = stg + n * S;
       uint32_t slot = scnt + pre;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          hs[f[tt][i] ? slot : (uint32_t)S] =
+          *(f[tt][i] ? hs + slot : spare) =
               make_uint2(__float_as_uint(v[tt][i]), (uint32_t)(pos0 + 16 * tt + 4 * kg + i));
           slot += f[tt][i] ? 1u : 0u;
         }
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 #define TKA_SHARED_SCAN 1
 #endif
 
-template <int D>
+template <int D, int NTT>
 __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ K, int Hq, int Hkv,
                                                                 int G, int M, int L, int64_t sb, int64_t sh,
@@ -416,12 +418,23 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kg = lane >> 4;
-  const bool act = wave < M;  // wave w scores query w
-  const int tq = act ? wave : 0;
-  const int lim = L - M + tq + 1;  // positions query tq may see
+  // the R = M * G (query, head) rows of a KV group in blocks of 16 (lane column n: query t = row / G,
+  // head row % G), so every MFMA column and epilogue lane works. NTT = 2: wave w scores block w on
+  // both 16-position halves of a tile; NTT = 1 (at most two blocks): wave w scores block w / 2 on
+  // half w % 2, so that four waves share the work
+  const int R = M * G;
+  const int cb = NTT == 1 ? wave >> 1 : wave, half = NTT == 1 ? wave & 1 : 0;
+  const bool act = cb * 16 < R;
+  const int rr = cb * 16 + n;  // this lane's row (column) of the group
+  const bool hl = act && rr < R;
+  const int tl = hl ? rr / G : 0, hh = hl ? rr % G : 0;
+  const int lim = L - M + tl + 1;    // positions the lane's query may see
+  const int lim_all = L - M + 1;     // ... that every query may see
   extern __shared__ uint4 smem_raw[];
   uint8_t* tiles = reinterpret_cast<uint8_t*>(smem_raw);  // two tile buffers of P rows
-  uint2* stg = reinterpret_cast<uint2*>(tiles + 2 * P * PADB) + (size_t)wave * G * (S + 1);  // S + 1 per head
+  // S slots per row, then one spare slot per lane (pairs not kept); stages of the scoring waves only
+  uint2* stg = reinterpret_cast<uint2*>(tiles + 2 * P * PADB) + (size_t)(act ? wave : 0) * (16 * S + 64);
+  uint2* const spare = stg + 16 * S + lane;
 
   const int per = ntiles / (int)gridDim.x, extra = ntiles % (int)gridDim.x;
   const int r0 = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
@@ -433,24 +446,26 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
   float Tf = 0.f;
   bool tnan = false;
   uint32_t scnt = 0;
-  const bool hl = act && n < G;
-  auto reserve = [&]() -> uint32_t {
+  // list of the lane's row in group grp: ((b * M + t) * Hq + g * G + head)
+  auto row_of = [&](int t, int head) -> int64_t {
     const int b = grp / Hkv, g = grp % Hkv;
+    return ((int64_t)b * M + t) * Hq + g * G + head;
+  };
+  auto reserve = [&]() -> uint32_t {
     uint32_t base = 0;
-    if (lane < G && scnt != 0) base = atomicAdd(&o.cnt[((int64_t)b * M + tq) * Hq + g * G + lane], scnt);
+    if (lane < 16 && scnt != 0) base = atomicAdd(&o.cnt[row_of(tl, hh)], scnt);
     return base;
   };
   auto copy_out = [&](uint32_t base) {
-    const int b = grp / Hkv, g = grp % Hkv;
-    const int64_t rg = ((int64_t)b * M + tq) * Hq + g * G;
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < 16; ++h) {
       const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)scnt, h);
-      if (c == 0) continue;
+      if (c == 0) continue;  // (columns past R never count)
       const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)base, h);
-      const int64_t r = rg + h;
+      const int rc = cb * 16 + h;
+      const int64_t r = row_of(rc / G, rc % G);
       for (uint32_t e = lane; e < c; e += 64)
         if (bh + e < (uint32_t)o.capg) {  // the fused step's packed lists
-          const uint2 y = stg[h * (S + 1) + e];
+          const uint2 y = stg[h * S + e];
           u32x2_t x = {y.x, y.y};
           __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
         }
@@ -459,57 +474,69 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
   };
   // loads of tile u into a (rows past L-1 re-read row L-1); past the range's last tile the
   // cursor stays on it, so every step issues the same number of loads
-  int ld = r0;
+  // (tile cursors advance incrementally: a division per step costs dozens of scalar instructions)
+  int ld = r0, lg = r0 / tpg, lt = r0 - lg * tpg;
+  const uint16_t* lbase = K + (int64_t)(lg / Hkv) * sb + (int64_t)(lg % Hkv) * sh;
   auto load_next = [&](uint4 (&a)[NT]) {
-    const int g = ld / tpg, tin = ld - g * tpg;
-    const uint16_t* base = K + (int64_t)(g / Hkv) * sb + (int64_t)(g % Hkv) * sh;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int c = tid + 256 * j;
-      const int pos = min(tin * P + c / CPR, L - 1);
-      a[j] = ld16(base + (int64_t)pos * sl + (c % CPR) * 8);
+      const int pos = min(lt * P + c / CPR, L - 1);
+      a[j] = ld16(lbase + (int64_t)pos * sl + (c % CPR) * 8);
     }
-    if (ld + 1 < r1) ++ld;
+    if (ld + 1 < r1) {
+      ++ld;
+      if (++lt == tpg) {
+        lt = 0;
+        ++lg;
+        lbase = K + (int64_t)(lg / Hkv) * sb + (int64_t)(lg % Hkv) * sh;
+      }
+    }
   };
   int u = r0;  // the tile being scored
+  int cg = r0 / tpg, ct = r0 - cg * tpg;  // ... as (group, tile in group)
   bool pend = false;
-  // one tile: its registers to LDS, the buffer refilled SS_DEPTH tiles ahead, a barrier, the scoring
-  auto step = [&](uint4 (&a)[NT]) -> bool {
+  // one tile: its registers to LDS, the buffer refilled SS_DEPTH tiles ahead, a barrier, the scoring.
+  // Steps past the range (rounding the loop up to whole rounds) only load and meet the barrier.
+  auto step = [&](uint4 (&a)[NT]) {
+    const bool live = u < r1;  // workgroup-uniform
     uint8_t* tb = tiles + (size_t)(u & 1) * P * PADB;
+    if (live) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int c = tid + 256 * j;
-      *reinterpret_cast<uint4*>(tb + (c / CPR) * PADB + (c % CPR) * 16) = a[j];
+      for (int j = 0; j < NT; ++j) {
+        const int c = tid + 256 * j;
+        *reinterpret_cast<uint4*>(tb + (c / CPR) * PADB + (c % CPR) * 16) = a[j];
+      }
     }
     load_next(a);
     __syncthreads();  // the tile is in LDS; every wave is done with the buffer written next step
-    const int cg = u / tpg, ct = u - cg * tpg;
     const bool more = u + 1 < r1;
-    if (act) {
+    if (live && act) {
       if (pend) {
         copy_out(reserve());
         pend = false;
       }
-      if (cg != grp) {  // new KV group (its stage is empty): the query's fragments and thresholds
+      if (cg != grp) {  // new KV group (its stage is empty): the rows' fragments and thresholds
         grp = cg;
-        const int b = grp / Hkv, g = grp % Hkv;
+        const int64_t qr = row_of(tl, hh);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           uint4 v = make_uint4(0, 0, 0, 0);
-          if (hl) v = ld16(q + (((int64_t)b * M + tq) * Hq + g * G + n) * D + 32 * s + 8 * kg);
+          if (hl) v = ld16(q + qr * D + 32 * s + 8 * kg);
           bq[s] = __builtin_bit_cast(bf16x8_t, v);
         }
-        const float tv = hl ? o.T[((int64_t)b * M + tq) * Hq + g * G + n] : 0.f;
+        const float tv = hl ? o.T[qr] : 0.f;
         Tf = tv;
         tnan = tv != tv;
       }
       const int pos0 = ct * P;
-      const bool whole = pos0 + P <= lim;
-      bool f[2][4];
-      float v[2][4];
+      const bool whole = pos0 + P <= lim_all;  // wave-uniform
+      bool f[NTT][4];
+      float v[NTT][4];
       uint32_t c = 0;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int j = 0; j < NTT; ++j) {
+        const int tt = NTT == 1 ? half : j;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -518,50 +545,67 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[tt][i] = acc[i] * scale;
-          f[tt][i] = hl & (tnan | (v[tt][i] >= Tf));
+          v[j][i] = acc[i] * scale;
+          f[j][i] = hl & (tnan | (v[j][i] >= Tf));
         }
       }
       if (!whole) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int j = 0; j < NTT; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) f[tt][i] = f[tt][i] & (pos0 + 16 * tt + 4 * kg + i < lim);
+          for (int i = 0; i < 4; ++i)
+            f[j][i] = f[j][i] & (pos0 + 16 * (NTT == 1 ? half : j) + 4 * kg + i < lim);
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int j = 0; j < NTT; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c += f[tt][i] ? 1u : 0u;
+        for (int i = 0; i < 4; ++i) c += f[j][i] ? 1u : 0u;
       const uint32_t a1 = (uint32_t)__shfl_xor((int)c, 16, kWave);
       const uint32_t pair = c + a1;
       const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
       const uint32_t tot = pair + a2;
       const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
       {
-        uint2* hs = stg + (hl ? n : 0) * (S + 1);
+        uint2* hs = stg + n * S;
         uint32_t slot = scnt + pre;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int j = 0; j < NTT; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            hs[f[tt][i] ? slot : (uint32_t)S] =
-                make_uint2(__float_as_uint(v[tt][i]), (uint32_t)(pos0 + 16 * tt + 4 * kg + i));
-            slot += f[tt][i] ? 1u : 0u;
+            *(f[j][i] ? hs + slot : spare) =
+                make_uint2(__float_as_uint(v[j][i]), (uint32_t)(pos0 + 16 * (NTT == 1 ? half : j) + 4 * kg + i));
+            slot += f[j][i] ? 1u : 0u;
           }
         if (hl) scnt += tot;
       }
-      const int ng = (u + 1) / tpg;
-      pend = more && (ng != cg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
+      pend = more && (ct + 1 == tpg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
     }
     ++u;
-    return more;
+    if (++ct == tpg) {
+      ct = 0;
+      ++cg;
+    }
   };
+  // whole rounds of four steps, one exit at the bottom: a loop left from the middle of a round
+  // gets one merged exit test that can branch back to the top, and on that path the compiler
+  // must assume the buffer just refilled is needed at once, draining every load in flight
+  // (the scheduling barriers keep the four buffers' loads in this order: if the scheduler issued
+  // a0's last, the one wait the compiler places for a0 would have to drain everything)
   uint4 a0[NT], a1[NT], a2[NT], a3[NT];
   load_next(a0);
+  __builtin_amdgcn_sched_barrier(0);
   load_next(a1);
+  __builtin_amdgcn_sched_barrier(0);
   load_next(a2);
+  __builtin_amdgcn_sched_barrier(0);
   load_next(a3);
-  while (step(a0) && step(a1) && step(a2) && step(a3)) {
+  __builtin_amdgcn_sched_barrier(0);
+  const int rounds = (r1 - r0 + 3) / 4;
+  for (int rd = 0; rd < rounds; ++rd) {
+    step(a0);
+    step(a1);
+    step(a2);
+    step(a3);
   }
   if (act && grp >= 0) copy_out(reserve());
 }
@@ -957,9 +1001,9 @@ template <int D>
 static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
   const int tpg = (a.nrows + 31) / 32;
   const int64_t ntiles = (int64_t)a.B * a.Hkv * tpg;
-  // stage slots per head: PS_STAGE_BYTES per wave over G heads x (bits, position)
-  const int S = PS_STAGE_BYTES / (8 * a.G);
-  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * a.G * (S + 1) * 8;
+  // stage slots per head: PS_STAGE_BYTES per wave, less 64 spare slots, over G heads x (bits, position)
+  const int S = (PS_STAGE_BYTES / 8 - 64) / a.G;
+  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * (a.G * S + 64) * 8;
   const int fit = (int)(device_lds_limit() / lds);  // workgroups whose LDS fits one CU
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
@@ -967,14 +1011,25 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   if (M > 1 && TKA_SHARED_SCAN && o.cpair) {
     // two tile buffers and four wave stages sized to fit two workgroups per CU
     const size_t tiles = (size_t)2 * 32 * (D * 2 + 16);
-    const int S2 = (int)(((size_t)device_lds_limit() / 2 - tiles - 256) / (4 * 8 * (size_t)a.G)) - 1;
-    const size_t lds2 = tiles + (size_t)4 * a.G * (S2 + 1) * 8;
+    // stages for the scoring waves only, 16 rows each: ceil(M G / 16) blocks, two waves per block
+    // (one per tile half) when there are at most two blocks
+    const int ncb = (M * a.G + 15) / 16;
+    const int nst = ncb <= 2 ? 2 * ncb : ncb;
+    const int S2 = (int)((((size_t)device_lds_limit() / 2 - tiles - 256) / (8 * (size_t)nst) - 64) / 16);
+    const size_t lds2 = tiles + (size_t)nst * (16 * S2 + 64) * 8;
     int64_t g2 = (int64_t)device_cus() * 2;
     if (g2 > ntiles) g2 = ntiles;
-    ensure_dynamic_lds((const void*)score_cand_shared_kernel<D>, lds2);
-    hipLaunchKernelGGL((score_cand_shared_kernel<D>), dim3((unsigned)g2), dim3(256), lds2, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh, a.sl, a.scale, (int)ntiles,
-                       tpg, S2, o);
+    if (ncb <= 2) {
+      ensure_dynamic_lds((const void*)score_cand_shared_kernel<D, 1>, lds2);
+      hipLaunchKernelGGL((score_cand_shared_kernel<D, 1>), dim3((unsigned)g2), dim3(256), lds2, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh, a.sl,
+                         a.scale, (int)ntiles, tpg, S2, o);
+    } else {
+      ensure_dynamic_lds((const void*)score_cand_shared_kernel<D, 2>, lds2);
+      hipLaunchKernelGGL((score_cand_shared_kernel<D, 2>), dim3((unsigned)g2), dim3(256), lds2, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh, a.sl,
+                         a.scale, (int)ntiles, tpg, S2, o);
+    }
     return;
   }
   if (M == 1) {
