@@ -107,7 +107,7 @@ def edge_rows(n):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("n", [1, 37, 1000, 4099])
+@pytest.mark.parametrize("n", [1, 37, 1000, 4099, 20000, 65536])  # the last two: the sampled path of long rows
 @pytest.mark.parametrize("eps,k_min,k_max", [(0.0, 1, 5000), (0.05, 1, 5000), (0.3, 4, 9), (0.999, 2, 5000),
                                              (0.2, 0, 3)])
 def test_adaptive_select_edge_rows(n, eps, k_min, k_max):
