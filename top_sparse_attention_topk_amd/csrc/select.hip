@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -742,59 +743,11 @@ struct PfSmem {
   uint32_t red[PF_NW];
   uint32_t tval;
 };
-
-// One-pass bin search over register-held keys (thread t holds elements
-// t + PF_T*j, j < R, valid below cnt). The digit is taken relative to the
-// keys' own range [lo, hi]: d = (key - lo) >> shift < 4096, so the critical
-// bin usually holds a handful of elements. Returns (bin, above) in sm.res and
-// the shift in *shift_out.
-template <int R, typename KeyOf>
-__device__ void relative_bin(KeyOf key_of, uint32_t cnt, uint32_t lo, uint32_t hi, uint32_t need, SelSmem& sm,
-                             int* shift_out) {
-  const int t = threadIdx.x;
-  const uint32_t span = hi - lo;
-  const int shift = span >= 4096u ? (32 - __clz(span)) - 12 : 0;
-  for (int i = t; i < NB0; i += PF_T) sm.hist[i] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < R; ++j)
-    if ((uint32_t)(t + PF_T * j) < cnt) atomicAdd(&sm.hist[(key_of(j) - lo) >> shift], 1u);
-  __syncthreads();
-  find_bin_t<PF_NW>(sm.hist, NB0, need, sm);
-  *shift_out = shift;
-}
-
-template <int R, typename KeyOf>
-__device__ void block_min_max(KeyOf key_of, uint32_t cnt, PfSmem& ps, uint32_t* mn_out, uint32_t* mx_out) {
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-  for (int j = 0; j < R; ++j)
-    if ((uint32_t)(t + PF_T * j) < cnt) {
-      const uint32_t k = key_of(j);
-      mn = min(mn, k);
-      mx = max(mx, k);
-    }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-  }
-  if (lane == 0) ps.red[w] = mx;
-  __syncthreads();
-  uint32_t gmx = 0u;
-#pragma unroll
-  for (int i = 0; i < PF_NW; ++i) gmx = max(gmx, ps.red[i]);
-  __syncthreads();
-  if (lane == 0) ps.red[w] = mn;
-  __syncthreads();
-  uint32_t gmn = 0xffffffffu;
-#pragma unroll
-  for (int i = 0; i < PF_NW; ++i) gmn = min(gmn, ps.red[i]);
-  __syncthreads();
-  *mn_out = gmn;
-  *mx_out = gmx;
-}
+// the finish emits up to PF_KMAX kept pairs through the spent histogram and stash keys
+constexpr int PF_KMAX = 4096;
+static_assert(NB0 >= PF_KMAX && 2 * PF_STASH >= PF_KMAX &&
+                  offsetof(PfSmem, sidx) == offsetof(PfSmem, skey) + sizeof(uint32_t) * PF_STASH,
+              "finish emission staging");
 
 // Threshold of a row: the key of its r-th largest sample. One wave per row,
 // the row's samples held in registers (RS per lane, lane-strided). Radix
@@ -950,7 +903,9 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint2* 
     if (osel) osel[j] = -INFINITY;
   }
   const uint32_t nc = cnt[row];
-  bool repair = nc < (uint32_t)kk || nc > (uint32_t)capg;  // threshold too high, or too many candidates
+  // threshold too high, or too many candidates (or more kept than the emission stages: the
+  // prefilter's plan never asks for that)
+  bool repair = nc < (uint32_t)kk || nc > (uint32_t)capg || kk > PF_KMAX;
   if (!repair) {
     const u32x2_t* cw = reinterpret_cast<const u32x2_t*>(cpair + row * capg);
     const uint32_t T0 = score_key(Tv[row]);
@@ -968,13 +923,28 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint2* 
     const int words = (n + 31) >> 5;
     uint32_t* bm = dyn;
     uint32_t* pre = dyn + words;
+    // one barrier for the cleared bitmap and histogram and the waves' maxima (every key is >= T0,
+    // so the candidates' range is [T0, max])
     for (int i = t; i < words; i += PF_T) bm[i] = 0u;
+    for (int i = t; i < NB0; i += PF_T) sm.hist[i] = 0u;
     if (t == 0) ps.scnt = 0;
-    uint32_t mn, mx;
-    block_min_max<PF_RC>(key_of, nc, ps, &mn, &mx);
-    (void)mn;
-    int shift;
-    relative_bin<PF_RC>(key_of, nc, T0, mx, (uint32_t)kk, sm, &shift);
+    uint32_t mx = T0;
+#pragma unroll
+    for (int j = 0; j < PF_RC; ++j)
+      if ((uint32_t)(t + PF_T * j) < nc) mx = max(mx, key_of(j));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    if ((t & 63) == 0) ps.red[t >> 6] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PF_NW; ++i) mx = max(mx, ps.red[i]);
+    const uint32_t span = mx - T0;
+    const int shift = span >= 4096u ? (32 - __clz(span)) - 12 : 0;  // span >> shift < 4096
+#pragma unroll
+    for (int j = 0; j < PF_RC; ++j)
+      if ((uint32_t)(t + PF_T * j) < nc) atomicAdd(&sm.hist[(key_of(j) - T0) >> shift], 1u);
+    __syncthreads();
+    find_bin_t<PF_NW>(sm.hist, NB0, (uint32_t)kk, sm);
     const uint32_t bin = sm.res[0], need = (uint32_t)kk - sm.res[1];
     // keys above the critical bin are kept; the bin's elements go to the stash
 #pragma unroll
@@ -1022,6 +992,10 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint2* 
         }
       }
       __syncthreads();
+      // the kept pairs to their slots in LDS (the histogram and the stash are spent: k' <= 4096
+      // entries each), then out with 16-byte stores in slot order
+      uint32_t* lidx = sm.hist;
+      uint32_t* lsel = ps.skey;  // skey and sidx: 2 * PF_STASH contiguous entries
 #pragma unroll
       for (int j = 0; j < PF_RC; ++j) {
         const uint32_t e = t + PF_T * j;
@@ -1031,8 +1005,21 @@ __global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint2* 
         if (!((word >> (p & 31)) & 1u)) continue;
         const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
         if (slot < (uint32_t)kk) {
-          oidx[slot] = p;
-          if (osel) osel[slot] = __uint_as_float(bits[j]);
+          lidx[slot] = (uint32_t)p;
+          lsel[slot] = bits[j];
+        }
+      }
+      __syncthreads();
+      const bool vec = ((reinterpret_cast<uintptr_t>(oidx) | reinterpret_cast<uintptr_t>(osel)) & 15) == 0;
+      for (int i = 4 * t; i < kk; i += 4 * PF_T) {
+        if (vec && i + 3 < kk) {
+          *reinterpret_cast<uint4*>(oidx + i) = *reinterpret_cast<const uint4*>(lidx + i);
+          if (osel) *reinterpret_cast<uint4*>(osel + i) = *reinterpret_cast<const uint4*>(lsel + i);
+        } else {
+          for (int c = i; c < min(i + 4, kk); ++c) {
+            oidx[c] = (int32_t)lidx[c];
+            if (osel) osel[c] = __uint_as_float(lsel[c]);
+          }
         }
       }
     }
