@@ -31,6 +31,9 @@ CASES = {
     "prefilter-g8-m4": (2, 4, 16, 2, 128, 16384, 512),
     "prefilter-g16-m3": (1, 3, 32, 2, 128, 12000, 700),
     "prefilter-g4-m2-d64": (2, 2, 8, 2, 64, 8192, 1024),
+    "prefilter-g8-m3": (1, 3, 16, 2, 128, 16384, 1024),  # 24 rows: the second 16-row block half full
+    "prefilter-g2-m2": (2, 2, 8, 4, 128, 8192, 256),     # 4 rows in one block
+    "prefilter-g8-m2-d256": (1, 2, 16, 2, 256, 8192, 512),
 }
 
 
