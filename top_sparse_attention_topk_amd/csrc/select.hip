@@ -729,9 +729,15 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
 // the exact answer comes from the candidates alone; otherwise the row is
 // flagged and rescored in full.
 // ---------------------------------------------------------------------------
-constexpr int PF_NW = 16;  // waves of the prefilter kernels (1024 threads)
+#ifndef TKA_PF_NW
+#define TKA_PF_NW 16
+#endif
+#ifndef TKA_PF_MINW
+#define TKA_PF_MINW 8
+#endif
+constexpr int PF_NW = TKA_PF_NW;  // waves of the finish kernel (one row per workgroup)
 constexpr int PF_T = 64 * PF_NW;
-constexpr int PF_RC = 12;  // candidates held per thread: capacity <= 12288
+constexpr int PF_RC = 12288 / PF_T;  // candidates held per thread: capacity <= 12288
 
 constexpr int PF_STASH = 2048;  // elements of the critical bin ranked one by one
 
@@ -882,7 +888,7 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
 // first). Kept positions are marked in an LDS bitmap over the row and
 // popcount prefix sums give each its output slot in ascending position
 // order. Dynamic LDS: 2 * ceil(n/32) words (kept bitmap, prefix counts).
-__global__ __launch_bounds__(1024, 8) void prefilter_finish_kernel(const uint2* __restrict__ cpair,
+__global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(const uint2* __restrict__ cpair,
                                                                 const uint32_t* __restrict__ cnt,
                                                                 const float* __restrict__ Tv, int capg, int n,
                                                                 int k, int G, int Hq, int M,
