@@ -355,7 +355,11 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
   while (sc > 128 && 7 * kk * sample_count(L, sc) < 4 * 100 * L) sc >>= 1;
   pf.sample_chunk = (int)sc;
   pf.nsamp = (int)sample_count(L, sc);
-  pf.r = (int)((7 * kk * pf.nsamp + 4 * L - 1) / (4 * L));
+  // r: the samples expected among the k' largest, E = k' nsamp / L, plus 4.5 standard deviations
+  // of that count (and 2): the k'-th largest key is below T only a few times in a million rows
+  const double E = (double)kk * pf.nsamp / (double)L;
+  pf.r = (int)std::ceil(E + 4.5 * std::sqrt(E)) + 2;
+  if (pf.r > pf.nsamp) pf.r = pf.nsamp;
   if (pf.r < 1) pf.r = 1;
   pf.capg = (int)(3 * kk);
   // the threshold and finish kernels hold the samples and the candidates in registers
