@@ -214,10 +214,14 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
   extern __shared__ uint4 smem_raw[];
   uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
   // S (score bits, position) slots per head, then one spare slot per lane that takes the writes
-  // of pairs not kept (a slot per lane: one shared slot would make every such write a conflict)
-  uint2* stg = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB) +
-               (size_t)wave * (G * S + 64);
-  uint2* const spare = stg + G * S + lane;
+  // of pairs not kept (a slot per lane: one shared slot would make every such write a conflict).
+  // A slot is 6 bytes: the score bits, and the position as a 16-bit offset from pbase, the first
+  // position of the stage's first tile (so a stage holds a third more pairs than at 8 bytes)
+  const int NS = G * S + 64;
+  uint32_t* sbits = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB +
+                                                (size_t)wave * NS * 6);
+  uint16_t* soff = reinterpret_cast<uint16_t*>(sbits + NS);
+  int pbase = 0;
 
   const int64_t per = ntiles / gridDim.x, extra = ntiles % gridDim.x;
   const int64_t r0 = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
@@ -249,16 +253,14 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
       if (o.cpair) {  // one 8-byte (bits, position) store per pair
         for (uint32_t e = lane; e < c; e += 64)
           if (bh + e < (uint32_t)o.capg) {  // streaming stores: the lists are read once, by another kernel
-            const uint2 y = stg[h * S + e];
-            u32x2_t x = {y.x, y.y};
+            u32x2_t x = {sbits[h * S + e], (uint32_t)pbase + soff[h * S + e]};
             __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
           }
       } else {
         for (uint32_t e = lane; e < c; e += 64)
           if (bh + e < (uint32_t)o.capg) {
-            const uint2 y = stg[h * S + e];
-            __builtin_nontemporal_store(y.x, o.cbits + r * o.capg + bh + e);
-            __builtin_nontemporal_store((int32_t)y.y, o.cpos + r * o.capg + bh + e);
+            __builtin_nontemporal_store(sbits[h * S + e], o.cbits + r * o.capg + bh + e);
+            __builtin_nontemporal_store(pbase + (int32_t)soff[h * S + e], o.cpos + r * o.capg + bh + e);
           }
       }
     }
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     ct = (int)(t % tpg);
     load(cur, cg, ct);
   }
+  pbase = ct * P;
   bool pend = false;  // wave-uniform: flush the stage before this tile's pairs are staged
   for (; t < r1; t += TL) {
     int ng = cg, nt = ct + TL;  // the wave's next tile
@@ -311,6 +314,7 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     if (pend) {
       copy_out(base);
       pend = false;
+      pbase = ct * P;  // the stage is empty: offsets count from this tile
     }
     if (cg != grp) {  // new KV group (its stage is empty): load the fragments and thresholds
       grp = cg;
@@ -367,20 +371,23 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
     {  // scnt + tot <= S: the stage was flushed when it could not take a whole tile. No branches:
        // a pair not kept (and every pair of a lane without a head) goes to the lane's spare slot
-      uint2* hs = stg + n * S;
+      const uint32_t hs = (uint32_t)(n * S), sp = (uint32_t)(G * S + lane);
       uint32_t slot = scnt + pre;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          *(f[tt][i] ? hs + slot : spare) =
-              make_uint2(__float_as_uint(v[tt][i]), (uint32_t)(pos0 + 16 * tt + 4 * kg + i));
+          const uint32_t e = f[tt][i] ? hs + slot : sp;
+          sbits[e] = __float_as_uint(v[tt][i]);
+          soff[e] = (uint16_t)(pos0 + 16 * tt + 4 * kg + i - pbase);
           slot += f[tt][i] ? 1u : 0u;
         }
       if (hl) scnt += tot;
     }
-    // flush before the next tile if a head could overflow on it or it starts another group
-    pend = more && (ng != cg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
+    // flush before the next tile if a head could overflow on it, it starts another group, or its
+    // positions would not fit 16-bit offsets from the stage's first tile
+    pend = more && (ng != cg || nt * P + (P - 1) - pbase > 65535 ||
+                    ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
     if (more) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
@@ -1001,9 +1008,10 @@ template <int D>
 static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStream_t st) {
   const int tpg = (a.nrows + 31) / 32;
   const int64_t ntiles = (int64_t)a.B * a.Hkv * tpg;
-  // stage slots per head: PS_STAGE_BYTES per wave, less 64 spare slots, over G heads x (bits, position)
-  const int S = (PS_STAGE_BYTES / 8 - 64) / a.G;
-  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * (a.G * S + 64) * 8;
+  // stage slots per head: PS_STAGE_BYTES per wave, less 64 spare slots, over G heads x 6 bytes
+  // (score bits, 16-bit position offset)
+  const int S = ((PS_STAGE_BYTES / 6 - 64) / a.G) & ~1;  // even: each wave's 4-byte bits stay aligned
+  const size_t lds = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * (a.G * S + 64) * 6;
   const int fit = (int)(device_lds_limit() / lds);  // workgroups whose LDS fits one CU
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
