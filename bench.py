@@ -203,7 +203,12 @@ def time_loop(fn, steps: int) -> float:
 def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
     """Fused step and scoring launch of a proxy-score workload (block means or indexer), each timed
     alone on the launch stream; the scoring launch against the HBM roofline (its algorithmic bytes:
-    proxy keys read once, q read, fp32 scores written)."""
+    proxy keys read once, q read, fp32 scores written).
+
+    A step of these workloads touches 70-100 MB, which the 256 MB Infinity Cache (MALL) can hold
+    across back-to-back steps. The reported times therefore rotate over R on-device replicas of
+    every input (copies of the same bytes), R * counted bytes >= 1 GiB, so that each step reads
+    HBM; the same loops on one replica are reported beside them as *_mall_warm (not HBM)."""
     q, K, V = fx.make_attn(w)
     to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     qt, Kt, Vt = to(q), to(K), to(V)
@@ -214,27 +219,44 @@ def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
         means = tka.topk_block_mean_build(p, Kt)
         res["block_size"] = w.block
         res["mean_build_ms"] = round(time_loop(lambda: tka.topk_block_mean_build(p, Kt, means), steps), 4)
-        kw = dict(proxy_keys=means)
-        sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
-        score_call = lambda: tka.topk_attn_score(p, qt, means, scores=sc)
+        ins = dict(q=qt, K=Kt, V=Vt, proxy_keys=means)
         idx = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
     else:
         qI, kI, wt = fx.make_indexer(w)
-        kw = dict(proxy_keys=torch.from_numpy(kI).cuda(), q_idx=torch.from_numpy(qI).cuda(),
-                  idx_w=torch.from_numpy(wt).cuda())
+        ins = dict(q=qt, K=Kt, V=Vt, proxy_keys=torch.from_numpy(kI).cuda(), q_idx=torch.from_numpy(qI).cuda(),
+                   idx_w=torch.from_numpy(wt).cuda())
         res["indexer_heads"], res["indexer_dim"] = w.HI, w.dI
-        sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
-        score_call = lambda: tka.topk_attn_score(p, kw["q_idx"], kw["proxy_keys"], idx_w=kw["idx_w"], scores=sc)
         idx = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    R = -(-(1 << 30) // counted_bytes(w))
+    reps = [ins] + [{n: t.clone() for n, t in ins.items()} for _ in range(R - 1)]
+    sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
     ws = torch.empty(tka.topk_decode_workspace_size(p), dtype=torch.uint8, device="cuda")
-    t_dec = time_loop(lambda: tka.topk_decode(p, qt, Kt, Vt, out=out, idx_out=idx, ws=ws, **kw), steps)
-    t_sc = time_loop(score_call, steps)
+
+    def decode(r):
+        kw = {n: t for n, t in r.items() if n not in ("q", "K", "V")}
+        tka.topk_decode(p, r["q"], r["K"], r["V"], out=out, idx_out=idx, ws=ws, **kw)
+
+    def score(r):
+        if w.mode == fx.MODE_BLOCK:
+            tka.topk_attn_score(p, r["q"], r["proxy_keys"], scores=sc)
+        else:
+            tka.topk_attn_score(p, r["q_idx"], r["proxy_keys"], idx_w=r["idx_w"], scores=sc)
+
+    def rotated(fn):
+        it = iter(range(1 << 62))
+        n = -(-steps // R) * R  # whole passes over the replicas
+        return time_loop(lambda: fn(reps[next(it) % R]), n)
+
+    t_dec, t_sc = rotated(decode), rotated(score)
+    t_dec_w, t_sc_w = time_loop(lambda: decode(ins), steps), time_loop(lambda: score(ins), steps)
     sb = score_kernel_bytes(w)
-    res.update({"decode_ms": round(t_dec, 4), "decode_queries_per_s": round(w.B / (t_dec / 1e3), 1),
+    res.update({"replicas": R, "decode_ms": round(t_dec, 4), "decode_queries_per_s": round(w.B / (t_dec / 1e3), 1),
                 "score_ms": round(t_sc, 4), "score_algorithmic_bytes": sb,
                 "score_gbps": round(sb / (t_sc / 1e3) / 1e9, 1),
-                "score_frac": round(sb / (t_sc / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)})
+                "score_frac": round(sb / (t_sc / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "decode_ms_mall_warm": round(t_dec_w, 4), "score_ms_mall_warm": round(t_sc_w, 4)})
+    del reps, ins
     return res
 
 

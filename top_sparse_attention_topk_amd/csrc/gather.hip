@@ -22,6 +22,16 @@
 #include "device_common.h"
 #include "internal.h"
 
+// launch shape: workgroups the split plan aims for (a task's keys are split until the grid has
+// about this many), and the K or V rows a wave has in flight per round (4 measured best: more
+// rounds over short spans; at d = 128 in bf16 one round is still 16 rows of 256 B per wave)
+#ifndef TKA_G_WANT
+#define TKA_G_WANT 1024
+#endif
+#ifndef TKA_G_UNR
+#define TKA_G_UNR 4
+#endif
+
 namespace tka {
 
 struct GatherK {
@@ -47,7 +57,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   constexpr int EPL = U::N;
   constexpr int LPR = D * ES / 16;
   constexpr int RPW = 64 / LPR;
-  constexpr int UNR = 8;
+  constexpr int UNR = TKA_G_UNR;
   extern __shared__ uint4 smem_raw[];
   float* red = reinterpret_cast<float*>(smem_raw);  // [NH][D]
   float* stat = red + NH * D;                      // M[NH], l[NH], wave maxima [4][NH]
@@ -340,7 +350,7 @@ GatherPlan plan_gather(const GatherArgs& a) {
   const int NH = pl.heads_per_task;
   const int span_max = NH == 1 ? 4096 : 8192 / NH;
   int64_t ns = (pl.expanded + span_max - 1) / span_max;
-  const int64_t want = (512 + pl.tasks - 1) / pl.tasks;
+  const int64_t want = (TKA_G_WANT + pl.tasks - 1) / pl.tasks;
   const int64_t cap64 = (pl.expanded + 63) / 64;
   int64_t ns2 = want < cap64 ? want : cap64;
   if (ns2 > ns) ns = ns2;
