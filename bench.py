@@ -517,6 +517,10 @@ def main():
     if args.copy_calibration:
         log("[bench] copy calibration kernel")
         copy_calibration()
+    # SHA-256 of the seeded input bytes as uploaded (q, K, V in their storage dtype), hashed in place
+    log("[bench] input digests")
+    result["inputs_sha256"] = {n: hashlib.sha256(memoryview(np.ascontiguousarray(a)).cast("B")).hexdigest()
+                               for n, a in (("q", q), ("K", K), ("V", V))}
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, q, K, V, args.cpu_budget)
