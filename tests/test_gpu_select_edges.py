@@ -4,6 +4,8 @@ on the same fp32 array: ties across the threshold (lower index wins), +-0,
 (forces every radix level), sorted rows (candidates all in one wave), huge
 tie runs (streaming emit), k = 1, k = n - 1, k = n, k > n, empty rows, rows
 with a stride, and both launch shapes (one workgroup per row; chunked rows)."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -51,6 +53,10 @@ def _rows(kind, n_rows, n, rng):
     raise ValueError(kind)
 
 
+def _seed(kind, n):  # stable across processes (str hashes are salted per process)
+    return zlib.crc32(f"{kind}/{n}".encode())
+
+
 KINDS = ["normal", "dups", "equal", "zeros", "special", "lowbits", "ascending", "descending", "tierun", "staircase"]
 SHAPES = [(200, 3000), (130, 20000), (3, 70001), (1, 300000)]  # row mode x2, chunked mode x2
 
@@ -59,7 +65,7 @@ SHAPES = [(200, 3000), (130, 20000), (3, 70001), (1, 300000)]  # row mode x2, ch
 @pytest.mark.parametrize("shape", SHAPES)
 def test_select_adversarial(kind, shape):
     n_rows, n = shape
-    rng = np.random.default_rng(hash((kind, n)) % (1 << 32))
+    rng = np.random.default_rng(_seed(kind, n))
     x = _rows(kind, n_rows, n, rng)
     xt = torch.from_numpy(x).cuda()
     m = tka()
@@ -111,3 +117,42 @@ def test_select_empty_rows_pad():
     x = torch.empty((4, 0), dtype=torch.float32, device="cuda")
     idx, sel = m.topk_select(x, 8, row_len=0, row_stride=0)
     assert (idx.cpu() == -1).all() and torch.isneginf(sel.cpu()).all()
+
+
+# short rows with k <= 64 take the one-wave-per-row kernel (n <= 2048); n = 2049 and k = 65 the others
+SHORT_SHAPES = [(128, 2047), (5, 2048), (3, 2049), (70, 64), (3, 63), (2, 1), (9, 1000), (6, 130)]
+
+
+@pytest.mark.parametrize("kind", KINDS + ["skew"])
+@pytest.mark.parametrize("shape", SHORT_SHAPES)
+def test_select_short_rows(kind, shape):
+    n_rows, n = shape
+    rng = np.random.default_rng(_seed(kind, n) + 1)
+    x = _rows(kind, n_rows, n, rng)
+    xt = torch.from_numpy(x).cuda()
+    m = tka()
+    for k in sorted({1, 2, 16, 37, 63, 64, 65, n - 1, n, n + 5} - {0}):
+        if k > 65:
+            continue
+        say(f"[select short] {kind} {shape} k={k}")
+        idx, sel = m.topk_select(xt, k)
+        gi = idx.cpu().numpy()
+        assert np.array_equal(gi, orc.select(x, k)), (kind, shape, k)
+        kk = min(k, n)
+        rows = np.arange(n_rows)[:, None]
+        gs = sel.cpu().numpy()
+        assert np.array_equal(gs[:, :kk].view(np.uint32), x[rows, gi[:, :kk]].view(np.uint32))
+        assert np.all(np.isneginf(gs[:, kk:]))
+
+
+def test_select_short_rows_strided():
+    """Rows of a wider array (row stride > row length), as the block-mean scores are read."""
+    rng = np.random.default_rng(7)
+    full = np.round(rng.standard_normal((64, 2100)), 1).astype(np.float32)
+    n = 2047
+    xt = torch.from_numpy(full).cuda()
+    m = tka()
+    for k in (1, 16, 64):
+        say(f"[select short strided] k={k}")
+        idx, _ = m.topk_select(xt, k, row_len=n, row_stride=2100)
+        assert np.array_equal(idx.cpu().numpy(), orc.select(full[:, :n], k))

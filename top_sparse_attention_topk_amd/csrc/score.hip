@@ -43,11 +43,6 @@ enum { KLOAD_DIRECT = 0, KLOAD_DIRECT_RT = 1, KLOAD_STAGED = 2 };
 #define TKA_SCAN_KLOAD KLOAD_STAGED
 #endif
 
-__device__ __forceinline__ void lds_wave_sync() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-}
-
 template <int D, int MODE, int KL>
 __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ K, int Hq, int Hkv, int G,

@@ -546,6 +546,138 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Short rows (n <= SH_NMAX) with k' <= 64: one wave per row, no workgroup
+// barriers. Lane l holds positions j*64 + l. The k'-th largest of the lane
+// maxima is a lower bound T0 of the row's k'-th largest key (the k' largest
+// lane maxima are k' distinct elements, all >= T0), so every key of the
+// answer, and every key tied with its last one, is >= T0. Those keys go to
+// LDS in position order. With at most 64 of them (the usual case), each
+// lane ranks its candidate against all others (larger key first, then lower
+// position) and the k' best are emitted in position order; otherwise the
+// exact k'-th key T comes from a most-significant-bit-first search whose
+// counts are ballot popcounts, and the keys > T, then the first keys == T,
+// are emitted.
+// ---------------------------------------------------------------------------
+constexpr int SH_PER = 32;             // keys per lane
+constexpr int SH_NMAX = 64 * SH_PER;   // longest row
+constexpr int SH_KMAX = 64;            // largest k
+
+// Rank of this lane's value among the values of lanes 0..cnt-1 (larger first, lower lane first
+// among equals). 64 independent lane reads: no serial chain of reductions.
+__device__ __forceinline__ uint32_t wave_rank(uint32_t v, uint32_t cnt) {
+  const uint32_t lane = (uint32_t)lane_id();
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+    r += ((uint32_t)j < cnt && (o > v || (o == v && (uint32_t)j < lane))) ? 1u : 0u;
+  }
+  return r;
+}
+
+// The k-th largest of the keys get(e), e < cnt, and in *need how many keys equal to it rank among
+// the k largest (k - the count of larger keys).
+template <typename Get>
+__device__ uint32_t wave_kth(Get get, uint32_t cnt, uint32_t k, uint32_t* need) {
+  uint32_t prefix = 0, rem = k;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t hi = ~0u << bit;  // the bits decided so far and this one
+    const uint32_t want = prefix | (1u << bit);
+    uint32_t c = 0;
+    for (uint32_t e0 = 0; e0 < cnt; e0 += 64) {
+      const uint32_t e = e0 + (uint32_t)lane_id();
+      c += (uint32_t)__popcll(ballot(e < cnt && (get(e) & hi) == want));
+    }
+    if (c >= rem) prefix = want;
+    else rem -= c;
+  }
+  *need = rem;
+  return prefix;
+}
+
+__global__ __launch_bounds__(256) void select_short_kernel(const float* __restrict__ S, int64_t n_rows, int n,
+                                                           int64_t stride, int k, int32_t* __restrict__ idx,
+                                                           float* __restrict__ sel) {
+  __shared__ uint32_t cbits[4][SH_NMAX];
+  __shared__ uint16_t cpos[4][SH_NMAX];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= n_rows) return;  // wave-uniform; nothing below waits for other waves
+  const float* s = S + row * stride;
+  int32_t* oidx = idx + row * k;
+  float* osel = sel ? sel + row * k : nullptr;
+  const int kk = min(k, n);
+  for (int j = kk + lane; j < k; j += 64) {
+    oidx[j] = -1;
+    if (osel) osel[j] = -INFINITY;
+  }
+  if (kk <= 0) return;
+  uint32_t bits[SH_PER], key[SH_PER];
+#pragma unroll
+  for (int j = 0; j < SH_PER; ++j) {
+    const int p = j * 64 + lane;
+    bits[j] = p < n ? __float_as_uint(s[p]) : 0u;
+  }
+  uint32_t lm = 0;
+#pragma unroll
+  for (int j = 0; j < SH_PER; ++j) {
+    key[j] = score_key(__uint_as_float(bits[j]));
+    if (j * 64 + lane < n) lm = max(lm, key[j]);
+  }
+  // lanes holding a key: min(64, n) >= kk; T0 = the lane maximum ranked kk - 1
+  const uint32_t nl = (uint32_t)min(64, n);
+  const uint64_t at = ballot((uint32_t)lane < nl && wave_rank(lm, nl) == (uint32_t)kk - 1);
+  const uint32_t T0 = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
+  uint32_t C = 0;
+#pragma unroll
+  for (int j = 0; j < SH_PER; ++j) {
+    const int p = j * 64 + lane;
+    const bool take = p < n && key[j] >= T0;
+    const uint64_t b = ballot(take);
+    if (take) {
+      const uint32_t slot = C + (uint32_t)count_below(b);
+      cbits[w][slot] = bits[j];
+      cpos[w][slot] = (uint16_t)p;
+    }
+    C += (uint32_t)__popcll(b);
+  }
+  lds_wave_sync();
+  if (C <= 64) {  // candidate e on lane e, already in position order
+    const bool ok = lane < (int)C;
+    const uint32_t b = ok ? cbits[w][lane] : 0u;
+    const bool take = ok && wave_rank(score_key(__uint_as_float(b)), C) < (uint32_t)kk;
+    const uint64_t bs = ballot(take);
+    if (take) {
+      const uint32_t slot = (uint32_t)count_below(bs);
+      oidx[slot] = cpos[w][lane];
+      if (osel) osel[slot] = __uint_as_float(b);
+    }
+    return;
+  }
+  uint32_t need;
+  const uint32_t T =
+      wave_kth([&](uint32_t e) { return score_key(__uint_as_float(cbits[w][e])); }, C, (uint32_t)kk, &need);
+  uint32_t run = 0, eqrun = 0;
+  for (uint32_t e0 = 0; e0 < C; e0 += 64) {
+    const uint32_t e = e0 + (uint32_t)lane;
+    const bool ok = e < C;
+    const uint32_t b = ok ? cbits[w][e] : 0u;
+    const uint32_t kv = score_key(__uint_as_float(b));
+    const bool gt = ok && kv > T, eq = ok && kv == T;
+    const uint64_t be = ballot(eq);
+    const bool take = gt || (eq && eqrun + (uint32_t)count_below(be) < need);
+    const uint64_t bs = ballot(take);
+    if (take) {  // exactly kk keys qualify
+      const uint32_t slot = run + (uint32_t)count_below(bs);
+      oidx[slot] = cpos[w][e];
+      if (osel) osel[slot] = __uint_as_float(b);
+    }
+    run += (uint32_t)__popcll(bs);
+    eqrun += (uint32_t)__popcll(be);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Split mode (few long rows)
 // ---------------------------------------------------------------------------
 __global__ void select_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -1680,6 +1812,11 @@ void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* 
 
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   if (a.n_rows <= 0) return;
+  if (a.n <= SH_NMAX && a.k <= SH_KMAX) {
+    hipLaunchKernelGGL(select_short_kernel, dim3((unsigned)((a.n_rows + 3) / 4)), dim3(256), 0, st, a.scores,
+                       a.n_rows, a.n, a.stride, a.k, a.idx, a.sel);
+    return;
+  }
   if (!use_split(a.n_rows, a.n)) {
     size_t lds;
     const int capw = rows_capw(a.n, a.k, &lds);
