@@ -89,7 +89,7 @@ def test_select_long_rows_sampled_threshold(kind):
     """Rows of 131072 with k' <= n/8 take the sampled threshold and one collecting pass; rows
     where it cannot hold (ties, crowding) fall back to the digit search: bit-exact either way."""
     n_rows, n = 128, 131072
-    rng = np.random.default_rng(hash((kind, "long")) % (1 << 32))
+    rng = np.random.default_rng(_seed(kind, "long"))
     x = _rows(kind, n_rows, n, rng)
     xt = torch.from_numpy(x).cuda()
     m = tka()
