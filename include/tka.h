@@ -155,6 +155,9 @@ tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const 
  *   sel_scores_out [n_rows, k] fp32 or NULL: the kept scores aligned with idx_out
  *                 (bit patterns copied), -inf in padded slots.
  * ws/ws_bytes: scratch of at least topk_select_workspace_size bytes.
+ * Fewer than 128 rows longer than 16384 are split over workgroups; such rows
+ * may hold at most about 12 million values (TKA_ERR_UNSUPPORTED beyond; the
+ * same bound applies to the rows that topk_decode and topk_hisa_decode select).
  */
 tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, int32_t k,
                        int32_t* idx_out, float* sel_scores_out, void* ws, size_t ws_bytes, void* stream);

@@ -102,6 +102,10 @@ def test_select_checks():
                    ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
     # many rows: one workgroup per row, no scratch
     assert tka.topk_select_workspace_size(1024, 131072, 4096) == 0
+    # few rows split over workgroups: the finish's table of segment offsets bounds the row length
+    far = 1 << 44
+    assert _select(n_rows=2, row_len=20_000_000, stride=20_000_000, k=2048, idx=far) == tka.TKA_ERR_UNSUPPORTED
+    assert _select(n_rows=2, row_len=12_000_000, stride=12_000_000, k=2048, idx=far) == tka.TKA_ERR_WORKSPACE
 
 
 def _gather(p, q=FAKE, K=FAKE * 2, V=FAKE * 3, idx=FAKE * 4, n_idx=64, unit=0, shared=0, sel=None, out=FAKE * 5,

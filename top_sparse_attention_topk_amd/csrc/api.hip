@@ -499,6 +499,8 @@ tka_status topk_select_workspace_size(int64_t n_rows, int32_t row_len, int32_t k
 tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride, int32_t k,
                        int32_t* idx_out, float* sel_scores_out, void* ws, size_t ws_bytes, void* stream) {
   tka_status s = check_select_args(scores, n_rows, row_len, row_stride, k, idx_out, sel_scores_out);
+  if (!s && !select_len_supported(n_rows, row_len))
+    s = fail(TKA_ERR_UNSUPPORTED, "row_len %d too long for fewer than 128 rows (at most about 12M)", row_len);
   if (s) return s;
   const size_t need = select_workspace_bytes(n_rows, row_len, k);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -625,6 +627,9 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     if (reinterpret_cast<uintptr_t>(idx_w) & 3) return fail(TKA_ERR_ALIGNMENT, "idx_w is not 4-byte aligned");
   }
   const DecodeLayout d = decode_layout(p);
+  if (!select_len_supported(d.rows, d.len))
+    return fail(TKA_ERR_UNSUPPORTED, "seq_len %d too long for %lld selected rows (at most about 12M)", d.len,
+                (long long)d.rows);
   if ((s = check_attn_ptrs(p, q, k_cache, v_cache, out))) return s;
   const Range o = span_of(out, out_bytes(p));
   if (proxy_keys && overlap(o, span_of(proxy_keys, proxy_bytes(p))))
@@ -839,6 +844,8 @@ tka_status check_hisa_problem(const tka_problem* p) {
   if (p->mode != TKA_SCORE_HISA) return fail(TKA_ERR_INVALID_ARG, "topk_hisa_decode needs mode TKA_SCORE_HISA");
   if ((int64_t)p->top_blocks * p->block_size > 0x7fffffff / 4)
     return fail(TKA_ERR_UNSUPPORTED, "top_blocks * block_size too large");
+  if (!select_len_supported(score_rows(p), score_len(p)))
+    return fail(TKA_ERR_UNSUPPORTED, "too many blocks for %lld rows (at most about 12M)", (long long)score_rows(p));
   return check_gather_shape(p, p->top_k, 0, 0, nullptr);
 }
 }  // namespace

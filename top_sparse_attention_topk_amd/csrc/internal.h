@@ -106,6 +106,7 @@ void launch_append_rows(const void* knew, const void* vnew, void* K, void* V, in
 void launch_append_indexer(const float* kI_new, uint8_t* kI, int B, int dI, int Lc, int pos, hipStream_t st);
 
 size_t select_workspace_bytes(int64_t n_rows, int n, int k);
+bool select_len_supported(int64_t n_rows, int n);  // false: rows too long for the split finish
 void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 // one workgroup per row, only rows whose flag is nonzero
 // certified adaptive k per row (a.k = k_max): counts to kout and the kept positions, then

@@ -774,7 +774,9 @@ __global__ __launch_bounds__(256) void select_chunk_collect_kernel(const float* 
   if (lane_id() == 0) ccount[(row * nch + blockIdx.x) * SW + w] = c;
 }
 
-// Dynamic LDS: nseg segment offsets.
+// Dynamic LDS: nseg segment offsets, then room for lcap candidates (bits, positions).
+constexpr int FIN_LDS_CAP = 4096;
+constexpr size_t FIN_DYN_MAX = 65536 - sizeof(SelSmem) - 256;  // dynamic LDS beside the static part
 __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restrict__ S, int n, int64_t stride,
                                                             int k, const uint32_t* __restrict__ ghist,
                                                             const uint32_t* __restrict__ ghist1,
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
                                                             const uint32_t* __restrict__ ccount,
                                                             uint32_t* __restrict__ catb, int32_t* __restrict__ catp,
                                                             int nch, int32_t* __restrict__ idx,
-                                                            float* __restrict__ sel) {
+                                                            float* __restrict__ sel, int lcap) {
   __shared__ SelSmem sm;
   extern __shared__ uint32_t segoff[];
   const int64_t row = blockIdx.x;
@@ -827,30 +829,36 @@ __global__ __launch_bounds__(256) void select_finish_kernel(const float* __restr
     }
   }
   __syncthreads();
-  uint32_t* rb = catb + row * (int64_t)n;
-  int32_t* rp = catp + row * (int64_t)n;
   // concatenate the segments in position order: output e comes from the last segment whose
-  // offset is <= e (binary search over the offsets; independent loads across threads)
-  for (uint32_t e = t; e < total; e += ST) {
-    int lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (segoff[mid] <= e) lo = mid;
-      else hi = mid - 1;
+  // offset is <= e (binary search over the offsets; independent loads across threads), into
+  // LDS after the offsets when they fit (the refinement and the emission then read LDS), else
+  // into the row's global scratch
+  auto tail = [&](uint32_t* rb, int32_t* rp) {
+    for (uint32_t e = t; e < total; e += ST) {
+      int lo = 0, hi = nseg - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (segoff[mid] <= e) lo = mid;
+        else hi = mid - 1;
+      }
+      const int64_t src = row * (int64_t)n + (int64_t)(lo / SW) * CHUNK + (lo % SW) * SUBCH + (e - segoff[lo]);
+      rb[e] = cbits[src];
+      rp[e] = cpos[src];
     }
-    const int64_t src = row * (int64_t)n + (int64_t)(lo / SW) * CHUNK + (lo % SW) * SUBCH + (e - segoff[lo]);
-    rb[e] = cbits[src];
-    rp[e] = cpos[src];
-  }
-  __syncthreads();
-  const uint32_t q = (total + SW - 1) / SW;
-  const uint32_t off = min(total, (uint32_t)w * q);
-  const uint32_t cnt = min(total, off + q) - off;
-  refine_candidates(rb, off, cnt, 1, prefix, (uint32_t)kk - above, sm);
-  const uint32_t T = sm.res[0], need_eq = sm.res[1];
-  __syncthreads();
-  emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = rb[off + e]; pos = rp[off + e]; }, cnt, T,
-                need_eq, sm, oidx, osel, (uint32_t)kk);
+    __syncthreads();
+    const uint32_t q = (total + SW - 1) / SW;
+    const uint32_t off = min(total, (uint32_t)w * q);
+    const uint32_t cnt = min(total, off + q) - off;
+    refine_candidates(rb, off, cnt, 1, prefix, (uint32_t)kk - above, sm);
+    const uint32_t T = sm.res[0], need_eq = sm.res[1];
+    __syncthreads();
+    emit_segments([&](uint32_t e, uint32_t& bits, int32_t& pos) { bits = rb[off + e]; pos = rp[off + e]; }, cnt,
+                  T, need_eq, sm, oidx, osel, (uint32_t)kk);
+  };
+  if (total <= (uint32_t)lcap)  // workgroup-uniform
+    tail(segoff + nseg, reinterpret_cast<int32_t*>(segoff + nseg + lcap));
+  else
+    tail(catb + row * (int64_t)n, catp + row * (int64_t)n);
 }
 
 // ---------------------------------------------------------------------------
@@ -1172,6 +1180,11 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
 // Host side
 // ---------------------------------------------------------------------------
 static bool use_split(int64_t n_rows, int n) { return n_rows < 128 && n > 4 * CHUNK; }
+
+// the split finish keeps one offset per (chunk, wave) segment in LDS
+bool select_len_supported(int64_t n_rows, int n) {
+  return !use_split(n_rows, n) || sizeof(uint32_t) * (((size_t)n + CHUNK - 1) / CHUNK) * SW <= FIN_DYN_MAX;
+}
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1843,9 +1856,11 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
                      a.stride, a.k, ghist, ghist1);
   hipLaunchKernelGGL(select_chunk_collect_kernel, dim3(nch, (unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n,
                      a.stride, a.k, ghist, ghist1, cbits, cpos, ccount, nch);
-  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.n_rows), dim3(ST), sizeof(uint32_t) * nch * SW, st,
+  const size_t seg = sizeof(uint32_t) * (size_t)nch * SW;  // <= FIN_DYN_MAX: select_len_supported
+  const int lcap = (int)std::min<size_t>(FIN_LDS_CAP, (FIN_DYN_MAX - seg) / 8);
+  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.n_rows), dim3(ST), seg + 8 * (size_t)lcap, st,
                      a.scores, a.n, a.stride, a.k, ghist, ghist1, cbits, cpos, ccount, catb, catp, nch, a.idx,
-                     a.sel);
+                     a.sel, lcap);
 }
 
 void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, int r, float* T, uint32_t* cnt,
