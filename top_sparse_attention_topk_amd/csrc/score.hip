@@ -187,6 +187,10 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 constexpr int PS_WPC = TKA_PS_WPC;                  // workgroups per CU
 constexpr int PS_STAGE_BYTES = TKA_PS_STAGE_BYTES;  // candidate stage per wave (G heads x 8 B x slots)
 constexpr int PS_TILE_MAX = 32;                     // most pairs one head can keep from one tile
+#ifndef TKA_PS_GUARD
+#define TKA_PS_GUARD 4
+#endif
+constexpr int PS_GUARD = TKA_PS_GUARD;  // free slots per head below which the next tile is preceded by a flush
 
 template <int D, bool SH>
 __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16_t* __restrict__ q,
@@ -364,7 +368,13 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
     const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
     const uint32_t tot = pair + a2;
     const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
-    {  // scnt + tot <= S: the stage was flushed when it could not take a whole tile. No branches:
+    // a head that cannot take this tile's pairs: flush now (the deferred flush below reserves only
+    // PS_GUARD slots, so this exact test catches the rarer tiles that keep more)
+    if (PS_GUARD < PS_TILE_MAX && ballot(lane < 16 && hl && scnt + tot > (uint32_t)S) != 0) {
+      copy_out(reserve());
+      pbase = ct * P;
+    }
+    {  // scnt + tot <= S: the stage was flushed when it could not take this tile. No branches:
        // a pair not kept (and every pair of a lane without a head) goes to the lane's spare slot
       const uint32_t hs = (uint32_t)(n * S), sp = (uint32_t)(G * S + lane);
       uint32_t slot = scnt + pre;
@@ -379,10 +389,11 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
         }
       if (hl) scnt += tot;
     }
-    // flush before the next tile if a head could overflow on it, it starts another group, or its
-    // positions would not fit 16-bit offsets from the stage's first tile
+    // flush before the next tile if a head is nearly full (a fuller tile is caught by the exact test
+    // before staging), it starts another group, or its positions would not fit 16-bit offsets from
+    // the stage's first tile
     pend = more && (ng != cg || nt * P + (P - 1) - pbase > 65535 ||
-                    ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
+                    ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_GUARD)) != 0);
     if (more) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
