@@ -2,6 +2,8 @@
 exactly the scores of topk_attn_score that rank at or above the row's
 threshold (IEEE order, -0 == +0), bit for bit, and a second call appends the
 same set after the first."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -52,3 +54,37 @@ def test_threshold_scan_keeps_exactly_the_ranked_set(L, k):
         n1 = before[r].item()
         if 2 * n1 <= cap:
             assert np.array_equal(np.sort(cp2[r, n1: 2 * n1]), np.sort(cp_np[r, :n1]))
+
+
+def _check_kept(s_np, thr_np, c_np, cs_np, cp_np):
+    for r in range(s_np.shape[0]):
+        want = np.nonzero(s_np[r] >= thr_np[r])[0]
+        assert c_np[r] == len(want), r
+        order = np.argsort(cp_np[r, : c_np[r]])
+        assert np.array_equal(cp_np[r, : c_np[r]][order], want), r
+        assert np.array_equal(cs_np[r, : c_np[r]][order].view(np.uint32), s_np[r, want].view(np.uint32)), r
+
+
+@pytest.mark.parametrize("G,d", [(2, 128), (4, 64), (16, 128), (8, 256)])
+def test_threshold_scan_head_groupings(G, d):
+    """The per-head stages hold fewer pairs as G and d grow; rows keeping everything overflow a
+    stage on most tiles, rows keeping a third now and then, rows keeping their maximum never.
+    Every row's kept set stays exact."""
+    w = replace(fx.shrink(fx.WORKLOADS["C3"], 20000, B=1, Hq=2 * G, Hkv=2, k=512), d=d)
+    m = tka()
+    q, K, V = fx.make_attn(w)
+    qt, Kt = dev(q), dev(K)
+    p = problem(w)
+    rows, L = w.B * w.Hq, w.L
+    s = m.topk_attn_score(p, qt, Kt).reshape(rows, L)
+    srt = torch.sort(s, dim=1, descending=True).values
+    thr = torch.empty(rows, dtype=torch.float32, device="cuda")
+    for r in range(rows):
+        thr[r] = -torch.inf if r % 3 == 0 else (srt[r, L // 3] if r % 3 == 1 else srt[r, 0])
+    counts = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    cs = torch.empty((rows, L), dtype=torch.float32, device="cuda")
+    cp = torch.empty((rows, L), dtype=torch.int32, device="cuda")
+    say(f"[threshold groupings] G={G} d={d}")
+    m.topk_attn_score_threshold(p, qt, Kt, thr, counts, cs, cp)
+    torch.cuda.synchronize()
+    _check_kept(s.cpu().numpy(), thr.cpu().numpy(), counts.cpu().numpy(), cs.cpu().numpy(), cp.cpu().numpy())
