@@ -417,6 +417,12 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 #ifndef TKA_SHARED_SCAN
 #define TKA_SHARED_SCAN 1
 #endif
+#ifndef TKA_SS_GUARD
+#define TKA_SS_GUARD 8
+#endif
+// free stage slots per row below which a flush is scheduled before the next tile (a tile that
+// would overflow anyway is preceded by an immediate flush)
+constexpr int SS_GUARD = TKA_SS_GUARD;
 
 template <int D, int NTT>
 __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* __restrict__ q,
@@ -578,6 +584,9 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
       const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
       const uint32_t tot = pair + a2;
       const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
+      // a row that cannot take this tile's pairs: flush now (the deferred flush below reserves
+      // only SS_GUARD slots, so this exact test catches the rarer tiles that keep more)
+      if (SS_GUARD < PS_TILE_MAX && ballot(lane < 16 && hl && scnt + tot > (uint32_t)S) != 0) copy_out(reserve());
       {
         uint2* hs = stg + n * S;
         uint32_t slot = scnt + pre;
@@ -591,7 +600,7 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
           }
         if (hl) scnt += tot;
       }
-      pend = more && (ct + 1 == tpg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - PS_TILE_MAX)) != 0);
+      pend = more && (ct + 1 == tpg || ballot(lane < 16 && hl && scnt > (uint32_t)(S - SS_GUARD)) != 0);
     }
     ++u;
     if (++ct == tpg) {
