@@ -107,7 +107,8 @@ typedef struct {
                              Long-Context LLMs", section 6: current length x K). Then q and out are
                              [B,M,Hq,d], scores [B,M,Hq,L] (a position a query cannot see is NaN), index
                              lists [B,M,Hq,n]; built for bf16 with M * Hq/Hkv <= 64 (topk_attn_score,
-                             sparse_attn_gather, topk_decode; TKA_ERR_UNSUPPORTED elsewhere). */
+                             sparse_attn_gather, topk_decode, and topk_attn_score_threshold for M <= 4;
+                             TKA_ERR_UNSUPPORTED elsewhere). */
 } tka_problem;
 
 /*
@@ -140,6 +141,10 @@ tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys
  * and counts[r] is increased by their number; pairs that would land at or
  * beyond capacity are counted but not stored. Needs bf16 caches and
  * 2 <= Hq/Hkv <= 16 (TKA_ERR_UNSUPPORTED otherwise).
+ * Several queries (n_queries = M, 2 <= M <= 4): q is [B,M,Hq,d] and rows are
+ * r = (b*M + t)*Hq + h (thresholds, counts and lists [B*M*Hq, capacity]);
+ * query t keeps only positions 0 .. L-M+t it can see.
+ * A NaN threshold keeps every position the row can see.
  */
 tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const void* k_cache,
                                      const float* thresholds, uint32_t* counts, float* cand_scores, int32_t* cand_pos,
@@ -298,6 +303,21 @@ tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, floa
  */
 tka_status topk_cache_append(const tka_problem* p, const void* k_new, const void* v_new, void* k_cache,
                              void* v_cache, const float* kI_new, void* kI_cache, float* means, void* stream);
+
+/*
+ * One workspace query for the steps of a problem (the per-call queries above
+ * give the same numbers):
+ *   which = TKA_WS_SELECT:  topk_select over the problem's score rows (B*Hq rows
+ *                           of L, or of m-1 blocks; B rows of L for INDEXER), k = top_k;
+ *   which = TKA_WS_GATHER:  sparse_attn_gather with top_k entries per list, in the
+ *                           problem's unit (tokens, or blocks for BLOCK_MEAN) and
+ *                           sharing (one list per sequence for INDEXER);
+ *   which = TKA_WS_DECODE:  topk_decode (topk_hisa_decode for mode HISA);
+ *   which = TKA_WS_DECODE_ADAPTIVE: topk_decode_adaptive.
+ * Any other value of which: TKA_ERR_INVALID_ARG.
+ */
+enum { TKA_WS_SELECT = 0, TKA_WS_GATHER = 1, TKA_WS_DECODE = 2, TKA_WS_DECODE_ADAPTIVE = 3 };
+tka_status topk_workspace_size(const tka_problem* p, int32_t which, size_t* bytes);
 
 const char* tka_status_str(tka_status s);
 /* detail of the last failed argument check in the calling thread ("" if none) */

@@ -59,6 +59,20 @@ def exact_score_bound(w, q, K, rows):
     return np.stack(out) * scale * w.d * 2.0 ** -23 + 1e-30
 
 
+def block_score_bound(w, q, K):
+    """Bound of an fp32 block score <q, mean of the block>: the mean sums up to b terms, the dot d terms;
+    (d + b + 2) * 2^-23 * sum_c |q_c| * mean_i |K_ic|, rows b*Hq + h, the m - 1 competing blocks."""
+    qa = np.abs(as_f64(q, w.dtype))
+    Ka = np.abs(as_f64(K, w.dtype))
+    m = w.m
+    pad = m * w.block - w.L
+    Kp = np.concatenate([Ka, np.zeros(Ka.shape[:2] + (pad, w.d))], 2) if pad else Ka
+    sizes = np.minimum(w.block, w.L - np.arange(m) * w.block)
+    mabs = Kp.reshape(w.B, w.Hkv, m, w.block, w.d).sum(3) / sizes[None, None, :, None]
+    bound = np.stack([mabs[b, h // w.G, : m - 1] @ qa[b, h] for b in range(w.B) for h in range(w.Hq)])
+    return bound * (w.d + w.block + 2) * 2.0 ** -23 + 1e-30
+
+
 def indexer_score_bound(w, qI, kI, wt, b):
     qd = np.abs(orc.decode_values(orc.E4M3, qI[b]))
     kd = np.abs(orc.decode_values(orc.E4M3, kI[b]))

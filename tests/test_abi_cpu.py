@@ -11,7 +11,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tka.h")
 
-tka = pytest.importorskip("top_sparse_attention_topk_amd")
+# no skip: a missing libtka.so (build() not run, or a failed build) fails every test here
+import top_sparse_attention_topk_amd as tka  # noqa: E402
+
 LIB = tka.LIB
 
 FAKE = 1 << 40  # aligned, never dereferenced: every call below fails its checks first
@@ -226,3 +228,37 @@ def test_hisa_checks():
     # topk_decode leaves the two-level mode to topk_hisa_decode
     assert LIB.topk_decode(ctypes.byref(p), FAKE, FAKE * 2, FAKE * 3, FAKE * 6, None, None, FAKE * 5, None, FAKE * 8,
                            1 << 30, None) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_workspace_size_by_kind():
+    """topk_workspace_size(p, which) reports what the per-call queries report."""
+    c3 = tka.problem(tka.EXACT, 16, 64, 8, 128, 131072, 4096)
+    assert tka.topk_workspace_size(c3, tka.WS_DECODE) == tka.topk_decode_workspace_size(c3)
+    assert tka.topk_workspace_size(c3, tka.WS_SELECT) == tka.topk_select_workspace_size(16 * 64, 131072, 4096)
+    assert tka.topk_workspace_size(c3, tka.WS_GATHER) == tka.sparse_attn_gather_workspace_size(c3, 4096)
+    assert tka.topk_workspace_size(c3, tka.WS_DECODE_ADAPTIVE) == tka.topk_decode_adaptive_workspace_size(c3)
+    c5 = tka.problem(tka.INDEXER, 1, 64, 8, 128, 1 << 20, 2048, n_idx_heads=32, idx_dim=64)
+    assert tka.topk_workspace_size(c5, tka.WS_SELECT) == tka.topk_select_workspace_size(1, 1 << 20, 2048) > 0
+    assert tka.topk_workspace_size(c5, tka.WS_GATHER) == tka.sparse_attn_gather_workspace_size(c5, 2048, 0, True)
+    c4 = tka.problem(tka.BLOCK_MEAN, 4, 32, 8, 128, 131072, 16, block_size=64)
+    assert tka.topk_workspace_size(c4, tka.WS_SELECT) == tka.topk_select_workspace_size(128, 2047, 16)
+    assert tka.topk_workspace_size(c4, tka.WS_GATHER) == tka.sparse_attn_gather_workspace_size(c4, 16, 64)
+    assert tka.topk_workspace_size(c4, tka.WS_DECODE) == tka.topk_decode_workspace_size(c4)
+    hs = tka.problem(tka.HISA, 2, 8, 2, 128, 6400, 300, block_size=64, top_blocks=12)
+    assert tka.topk_workspace_size(hs, tka.WS_DECODE) == tka.topk_hisa_decode_workspace_size(hs)
+    n = ctypes.c_size_t(0)
+    assert LIB.topk_workspace_size(ctypes.byref(c3), 7, ctypes.byref(n)) == tka.TKA_ERR_INVALID_ARG
+    assert LIB.topk_workspace_size(ctypes.byref(c3), 0, None) == tka.TKA_ERR_INVALID_ARG
+    bad = tka.problem(tka.EXACT, 0, 64, 8, 128, 131072, 4096)
+    assert LIB.topk_workspace_size(ctypes.byref(bad), 2, ctypes.byref(n)) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_threshold_scan_checks():
+    """The thresholded scan takes up to 4 queries per sequence, bf16, 2 <= G <= 16."""
+    call = lambda p, cap=100: LIB.topk_attn_score_threshold(ctypes.byref(p), FAKE, FAKE * 2, FAKE * 3, FAKE * 4,
+                                                            FAKE * 5, FAKE * 6, cap, None)
+    assert call(_p(n_queries=5)) == tka.TKA_ERR_UNSUPPORTED
+    assert call(_p(dtype=tka.TKA_F32)) == tka.TKA_ERR_UNSUPPORTED
+    assert call(_p(n_q_heads=2, n_kv_heads=2)) == tka.TKA_ERR_UNSUPPORTED
+    assert call(_p(), cap=0) == tka.TKA_ERR_INVALID_ARG
+    assert call(_p(mode=tka.BLOCK_MEAN, block_size=64)) == tka.TKA_ERR_INVALID_ARG

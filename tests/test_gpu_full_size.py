@@ -1,10 +1,12 @@
 """Every workload at its full size, in the launch configuration the bench
-times (one fused topk_decode call), checked on sampled rows the oracle
-computes one by one: scores within the forward-error bound, indices
-bit-exact against the oracle's select on the GPU's score row, outputs within
-tolerance of the oracle's attention over the GPU's index set. Properties that
-hold at any size (k' distinct ascending in-range indices, -1 padding) are
-checked on every row."""
+times (one fused topk_decode call).
+
+On every row: the fused step equals the three calls (score -> select ->
+gather) bitwise, indices and outputs, compared on the GPU; the indices equal
+the oracle's select run on the GPU's whole fp32 score array; k' distinct
+ascending in-range indices and -1 padding. On sampled rows the oracle
+computes one by one: scores within the forward-error bound and outputs within
+tolerance of the oracle's attention over the GPU's index set."""
 import numpy as np
 import pytest
 import torch
@@ -49,7 +51,7 @@ def test_full_size_workload(name):
     _check_index_properties(idx2, w.k, n)
     assert bool(torch.isfinite(out).all())
 
-    say(f"[full size] {name}: scores for sampled rows")
+    say(f"[full size] {name}: the three calls")
     if w.mode == fx.MODE_INDEXER:
         scores = m.topk_attn_score(p, kw["q_idx"], kw["proxy_keys"], idx_w=kw["idx_w"])
         rows = [0]
@@ -61,9 +63,24 @@ def test_full_size_workload(name):
         nr = w.B * w.Hq
         rows = sorted({r for r in (0, nr // 3 + 1, nr // 2 + 7, nr - 1) if r < nr})
     S = scores.reshape(-1, n)
+    exact = w.mode == fx.MODE_EXACT
+    i3, v3 = m.topk_select(S, w.k, want_sel=exact)
+    o3 = m.sparse_attn_gather(p, qt, Kt, Vt, i3, idx_unit=w.block if w.mode == fx.MODE_BLOCK else 0,
+                              shared=w.mode == fx.MODE_INDEXER, sel_scores=v3 if exact else None)
+    torch.cuda.synchronize()
+    assert torch.equal(i3, idx2), "fused and three-call indices differ"
+    assert torch.equal(o3.view(torch.int32), out.view(torch.int32)), "fused and three-call outputs differ"
+    say(f"[full size] {name}: oracle select on all {S.shape[0]} rows of the GPU's scores")
+    s_all = gpu_scores_np(S)
+    gi_all = idx2.cpu().numpy()
+    want_all = orc.select(s_all, w.k)
+    bad = np.nonzero(~np.all(gi_all == want_all, axis=1))[0]
+    assert len(bad) == 0, f"{len(bad)} rows differ, first {bad[:8].tolist()}"
+
+    say(f"[full size] {name}: scores for sampled rows")
     assert all(0 <= r < S.shape[0] for r in rows), rows  # checked on the host before indexing on the GPU
-    gs = gpu_scores_np(S[rows])
-    gi = idx2[rows].cpu().numpy()
+    gs = s_all[rows].astype(np.float64)
+    gi = gi_all[rows]
     if w.mode == fx.MODE_INDEXER:
         ref = orc.score(op, qI=qI, kI=kI, w=wt, rows=rows)
         bound = np.stack([indexer_score_bound(w, qI, kI, wt, b) for b in rows])

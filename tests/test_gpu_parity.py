@@ -15,8 +15,8 @@ import torch
 
 import fixtures as fx
 import oracle as orc
-from tests.gpu_common import (as_f64, dev, exact_score_bound, gpu_scores_np, indexer_score_bound, problem, say,
-                              tka, tol)
+from tests.gpu_common import (block_score_bound, dev, exact_score_bound, gpu_scores_np, indexer_score_bound,
+                              problem, say, tka, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,16 +89,7 @@ def test_scores_within_forward_error_bound(name):
     elif w.mode == fx.MODE_INDEXER:
         bound = np.stack([indexer_score_bound(w, d.qI, d.kI, d.wt, b) for b in range(w.B)])
     else:  # block means (b + d terms) then a d-term dot
-        qa = np.abs(as_f64(d.q, w.dtype))
-        Ka = np.abs(as_f64(d.K, w.dtype))
-        m = w.m
-        pad = m * w.block - w.L
-        Kp = np.concatenate([Ka, np.zeros(Ka.shape[:2] + (pad, w.d))], 2) if pad else Ka
-        sizes = np.minimum(w.block, w.L - np.arange(m) * w.block)
-        mabs = Kp.reshape(w.B, w.Hkv, m, w.block, w.d).sum(3) / sizes[None, None, :, None]
-        G = w.G
-        bound = np.stack([mabs[b, h // G, : m - 1] @ qa[b, h] for b in range(w.B) for h in range(w.Hq)])
-        bound = bound * (w.d + w.block + 2) * 2.0 ** -23 + 1e-30
+        bound = block_score_bound(w, d.q, d.K)
     err = np.abs(s - ref)
     assert np.all(err <= bound), (name, float((err / bound).max()))
 

@@ -88,3 +88,47 @@ def test_threshold_scan_head_groupings(G, d):
     m.topk_attn_score_threshold(p, qt, Kt, thr, counts, cs, cp)
     torch.cuda.synchronize()
     _check_kept(s.cpu().numpy(), thr.cpu().numpy(), counts.cpu().numpy(), cs.cpu().numpy(), cp.cpu().numpy())
+
+
+@pytest.mark.parametrize("M,G,d", [(2, 8, 128), (4, 8, 128), (3, 16, 128), (2, 4, 64), (2, 8, 256)])
+def test_threshold_scan_several_queries(M, G, d):
+    """The several-query scan (one pass over K for the M * G rows of a KV group): rows keeping every
+    visible position overflow their stage on every tile, rows keeping a third now and then, rows
+    keeping their maximum never, and NaN thresholds keep everything a query can see. With at most 32
+    rows per group two waves score each 16-row block (one per tile half); above 32 each wave scores
+    a block on both halves. Every row's kept set is exactly its visible scores at or above the
+    threshold, the scores bit for bit those of topk_attn_score."""
+    B, Hkv, L = 2, 2, 20000 + 11
+    Hq = G * Hkv
+    m = tka()
+    w = fx.Workload("mq-threshold", fx.MODE_EXACT, B, Hq, Hkv, d, L, 512, fx.BF16, 40 + M * G, fx.PLANT_ALIGN,
+                    100, 0.5)
+    _, K, _ = fx.make_attn(w)
+    q = fx.encode(fx.normal(50 + M * G, 0, B * M * Hq * d), fx.BF16).reshape(B, M, Hq, d)
+    qt, Kt = dev(q), dev(K)
+    p = m.problem(m.EXACT, B, Hq, Hkv, d, L, 512, m.TKA_BF16, n_queries=M)
+    rows = B * M * Hq
+    s = m.topk_attn_score(p, qt, Kt).reshape(rows, L)
+    s_np = s.cpu().numpy()
+    thr_np = np.empty(rows, np.float32)
+    for r in range(rows):
+        t = (r // Hq) % M
+        vis = np.sort(s_np[r, : L - M + t + 1])[::-1]
+        thr_np[r] = [-np.inf, vis[len(vis) // 3], vis[0], np.nan][r % 4]
+    thr = torch.from_numpy(thr_np).cuda()
+    counts = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    cs = torch.empty((rows, L), dtype=torch.float32, device="cuda")
+    cp = torch.empty((rows, L), dtype=torch.int32, device="cuda")
+    say(f"[threshold several queries] M={M} G={G} d={d}")
+    m.topk_attn_score_threshold(p, qt, Kt, thr, counts, cs, cp)
+    torch.cuda.synchronize()
+    c_np, cs_np, cp_np = counts.cpu().numpy(), cs.cpu().numpy(), cp.cpu().numpy()
+    for r in range(rows):
+        t = (r // Hq) % M
+        vis = L - M + t + 1
+        assert np.isnan(s_np[r, vis:]).all()
+        want = np.arange(vis) if np.isnan(thr_np[r]) else np.nonzero(s_np[r, :vis] >= thr_np[r])[0]
+        assert c_np[r] == len(want), (r, c_np[r], len(want))
+        order = np.argsort(cp_np[r, : c_np[r]])
+        assert np.array_equal(cp_np[r, : c_np[r]][order], want), r
+        assert np.array_equal(cs_np[r, : c_np[r]][order].view(np.uint32), s_np[r, want].view(np.uint32)), r

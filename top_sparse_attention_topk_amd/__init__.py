@@ -8,7 +8,8 @@ raises ImportError when libtka.so has not been built - there is no fallback.
 The names match the C entry points: topk_attn_score,
 topk_attn_score_threshold, topk_select, topk_select_adaptive,
 sparse_attn_gather, topk_decode, topk_decode_adaptive, topk_hisa_decode,
-topk_cache_append, topk_block_mean_build and the workspace-size queries.
+topk_cache_append, topk_block_mean_build and the workspace-size queries
+(topk_workspace_size and one per call).
 """
 from __future__ import annotations
 
@@ -65,6 +66,7 @@ def _load():
         "topk_select_adaptive_workspace_size": [i64, i32, i32, ctypes.POINTER(sz)],
         "topk_decode_adaptive": [P, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, sz, vp],
         "topk_decode_adaptive_workspace_size": [P, ctypes.POINTER(sz)],
+        "topk_workspace_size": [P, i32, ctypes.POINTER(sz)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -84,7 +86,7 @@ EXPORTS = ["topk_attn_score", "topk_attn_score_threshold", "topk_select", "topk_
            "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
            "topk_block_mean_build", "topk_select_adaptive", "topk_select_adaptive_workspace_size",
            "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "topk_cache_append", "topk_hisa_decode",
-           "topk_hisa_decode_workspace_size", "tka_status_str",
+           "topk_hisa_decode_workspace_size", "topk_workspace_size", "tka_status_str",
            "tka_last_error",
            "tka_abi_version"]
 
@@ -341,6 +343,16 @@ def topk_hisa_decode(p: Problem, q, k_cache, v_cache, means, out=None, idx_out=N
                                 _ptr(idx_out), _ptr(blk), _ptr(bs), _ptr(cs), _ptr(ws), ws.numel(), _stream(stream)),
            "topk_hisa_decode")
     return (out, idx_out, blk, bs, cs) if want_parts else (out, idx_out)
+
+
+WS_SELECT, WS_GATHER, WS_DECODE, WS_DECODE_ADAPTIVE = range(4)
+
+
+def topk_workspace_size(p: Problem, which: int) -> int:
+    """Workspace bytes of one step of p: WS_SELECT, WS_GATHER, WS_DECODE or WS_DECODE_ADAPTIVE."""
+    n = ctypes.c_size_t(0)
+    _check(LIB.topk_workspace_size(ctypes.byref(p), which, ctypes.byref(n)), "topk_workspace_size")
+    return n.value
 
 
 def abi_version() -> int:

@@ -326,13 +326,16 @@ tka_status check_gather_ptrs(const tka_problem* p, const void* q, const void* K,
 
 // ---- fused exact step: candidate prefilter plan ----
 // Used for the bf16 MFMA scan when the kept fraction is small (k' <= L/8) and
-// the row is long. Samples are the first 64 positions of every sample chunk;
-// the threshold is the r-th largest sample with r = 1.75 k' nsamp / L (about
-// 1.75 k' candidates expected), the chunk being chosen so that r >= 100. The
-// fraction of keys at or above the threshold then has a relative spread of
-// about 1/sqrt(r) < 10% for exchangeable scores, so a shortfall below k' is a
-// > 4 sigma event and more than the 3 k' list capacity a > 7 sigma one; both
-// are detected and repaired by a full rescore of the row's group anyway.
+// the row is long. Samples are the first 64 positions of every sample chunk,
+// the chunk halved (down to 128) until E = k' nsamp / L, the samples expected
+// among the k' largest keys, reaches about 57. The threshold is the r-th
+// largest sample with r = ceil(E + 4.5 sqrt(E)) + 2: for exchangeable scores
+// the k'-th largest key falls below it (a shortfall) only a few times in a
+// million rows, and about r L / nsamp keys are expected at or above it (C3:
+// E = 64, r = 102, 1.6 k'). The list capacity covers that count plus four
+// standard deviations of it, L (r + 4 sqrt(r)) / nsamp, and at least 3 k'.
+// A shortfall or an overflow is detected and repaired by a full rescore of
+// the row's group anyway.
 struct PrefilterPlan {
   bool on;
   int sample_chunk, nsamp, r, capg;
@@ -361,7 +364,8 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
   pf.r = (int)std::ceil(E + 4.5 * std::sqrt(E)) + 2;
   if (pf.r > pf.nsamp) pf.r = pf.nsamp;
   if (pf.r < 1) pf.r = 1;
-  pf.capg = (int)(3 * kk);
+  const double expect = ((double)pf.r + 4.0 * std::sqrt((double)pf.r)) * (double)L / (double)pf.nsamp;
+  pf.capg = (int)std::max<double>(3.0 * (double)kk, std::ceil(expect));
   // the threshold and finish kernels hold the samples and the candidates in registers
   if (pf.nsamp > 8192 || pf.capg > 12288) return PrefilterPlan{};
   pf.on = true;
@@ -454,9 +458,9 @@ tka_status topk_attn_score(const tka_problem* p, const void* q, const void* keys
 tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const void* k_cache,
                                      const float* thresholds, uint32_t* counts, float* cand_scores, int32_t* cand_pos,
                                      int32_t capacity, void* stream) {
-  if (p && p->n_queries > 1) return fail(TKA_ERR_UNSUPPORTED, "the thresholded scan takes one query per sequence");
   tka_status s = check_attn_shape(p);
   if (s) return s;
+  if (nqry(p) > 4) return fail(TKA_ERR_UNSUPPORTED, "the thresholded scan takes at most 4 queries per sequence");
   const int G = p->n_q_heads / p->n_kv_heads;
   if (p->mode != TKA_SCORE_EXACT) return fail(TKA_ERR_INVALID_ARG, "mode must be TKA_SCORE_EXACT");
   if (p->qkv_dtype != TKA_BF16 || !score_uses_mfma(1, G))
@@ -469,7 +473,7 @@ tka_status topk_attn_score_threshold(const tka_problem* p, const void* q, const 
   if ((reinterpret_cast<uintptr_t>(thresholds) | reinterpret_cast<uintptr_t>(counts) |
        reinterpret_cast<uintptr_t>(cand_scores) | reinterpret_cast<uintptr_t>(cand_pos)) & 3)
     return fail(TKA_ERR_ALIGNMENT, "thresholds, counts and candidate arrays must be 4-byte aligned");
-  const size_t rows = (size_t)p->batch * p->n_q_heads;
+  const size_t rows = (size_t)p->batch * nqry(p) * p->n_q_heads;
   const Range co = span_of(counts, sizeof(uint32_t) * rows);
   const Range cs = span_of(cand_scores, sizeof(float) * rows * (size_t)capacity);
   const Range cp = span_of(cand_pos, sizeof(int32_t) * rows * (size_t)capacity);
@@ -932,6 +936,29 @@ tka_status topk_hisa_decode(const tka_problem* p, const void* q, const void* k_c
   GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, p->top_k, 0, 0, selv, out);
   launch_gather(ga, d.gp, base + d.gather_ws, st);
   return launched("topk_hisa_decode");
+}
+
+tka_status topk_workspace_size(const tka_problem* p, int32_t which, size_t* bytes) {
+  if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
+  tka_status s = check_attn_shape(p);
+  if (s) return s;
+  switch (which) {
+    case TKA_WS_SELECT: {
+      const int64_t rows = p->mode == TKA_SCORE_HISA ? (int64_t)p->batch * p->n_q_heads : score_rows(p);
+      *bytes = select_workspace_bytes(rows, score_len(p), p->top_k);
+      return ok();
+    }
+    case TKA_WS_GATHER:
+      return sparse_attn_gather_workspace_size(p, p->top_k, p->mode == TKA_SCORE_BLOCK_MEAN ? p->block_size : 0,
+                                               p->mode == TKA_SCORE_INDEXER ? 1 : 0, bytes);
+    case TKA_WS_DECODE:
+      return p->mode == TKA_SCORE_HISA ? topk_hisa_decode_workspace_size(p, bytes)
+                                       : topk_decode_workspace_size(p, bytes);
+    case TKA_WS_DECODE_ADAPTIVE:
+      return topk_decode_adaptive_workspace_size(p, bytes);
+    default:
+      return fail(TKA_ERR_INVALID_ARG, "unknown workspace kind %d", which);
+  }
 }
 
 tka_status topk_block_mean_build(const tka_problem* p, const void* k_cache, float* means, void* stream) {

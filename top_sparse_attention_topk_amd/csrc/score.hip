@@ -185,7 +185,9 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 #define TKA_PS_STAGE_BYTES 11776
 #endif
 constexpr int PS_WPC = TKA_PS_WPC;                  // workgroups per CU
-constexpr int PS_STAGE_BYTES = TKA_PS_STAGE_BYTES;  // candidate stage per wave (G heads x 8 B x slots)
+// candidate stage per wave: G heads x S slots of 6 bytes (4-byte score bits and a 16-bit position
+// offset from the stage's first tile), plus 64 spare slots that take the writes of pairs not kept
+constexpr int PS_STAGE_BYTES = TKA_PS_STAGE_BYTES;
 constexpr int PS_TILE_MAX = 32;                     // most pairs one head can keep from one tile
 #ifndef TKA_PS_GUARD
 #define TKA_PS_GUARD 4
@@ -475,6 +477,7 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
     if (lane < 16 && scnt != 0) base = atomicAdd(&o.cnt[row_of(tl, hh)], scnt);
     return base;
   };
+  const bool packed = o.cpair != nullptr;  // kernel-uniform
   auto copy_out = [&](uint32_t base) {
     for (int h = 0; h < 16; ++h) {
       const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)scnt, h);
@@ -483,10 +486,15 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
       const int rc = cb * 16 + h;
       const int64_t r = row_of(rc / G, rc % G);
       for (uint32_t e = lane; e < c; e += 64)
-        if (bh + e < (uint32_t)o.capg) {  // the fused step's packed lists
+        if (bh + e < (uint32_t)o.capg) {
           const uint2 y = stg[h * S + e];
-          u32x2_t x = {y.x, y.y};
-          __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
+          if (packed) {  // the fused step's packed lists
+            u32x2_t x = {y.x, y.y};
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
+          } else {  // separate score-bit and position lists (the thresholded-scan entry)
+            __builtin_nontemporal_store(y.x, o.cbits + r * o.capg + bh + e);
+            __builtin_nontemporal_store((int32_t)y.y, o.cpos + r * o.capg + bh + e);
+          }
         }
     }
     scnt = 0;
@@ -1031,7 +1039,7 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
   const int M = a.M > 1 ? a.M : 1;  // the caller keeps M <= 4
-  if (M > 1 && TKA_SHARED_SCAN && o.cpair) {
+  if (M > 1 && TKA_SHARED_SCAN) {
     // two tile buffers and four wave stages sized to fit two workgroups per CU
     const size_t tiles = (size_t)2 * 32 * (D * 2 + 16);
     // stages for the scoring waves only, 16 rows each: ceil(M G / 16) blocks, two waves per block
