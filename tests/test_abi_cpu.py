@@ -152,8 +152,13 @@ def test_decode_checks_and_workspace():
 def test_workspace_sizes_scale_with_problem():
     c3 = tka.problem(tka.EXACT, 16, 64, 8, 128, 131072, 4096)
     n = tka.topk_decode_workspace_size(c3)
-    # score array (repair path) + candidate lists (3k per row) + samples + small buffers
-    assert 16 * 64 * 131072 * 4 <= n < 16 * 64 * 131072 * 4 + (192 << 20)
+    # with the prefilter: candidate lists (3k per row, 8-byte pairs) + the repair's score slots
+    # (64 MiB) + indices, kept scores and samples; no [B*Hq, L] score array
+    cand = 16 * 64 * 3 * 4096 * 8
+    assert cand + (64 << 20) <= n < cand + (64 << 20) + (48 << 20)
+    # without it (k' > L/8) the full score array
+    dense = tka.problem(tka.EXACT, 16, 64, 8, 128, 131072, 20000)
+    assert tka.topk_decode_workspace_size(dense) >= 16 * 64 * 131072 * 4
 
 
 def test_adaptive_checks():

@@ -89,3 +89,30 @@ def test_prefilter_repair_crowded_tie_bin():
             K[b, g, pos] = fx.encode(np.tile(d, (len(pos), 1)), fx.BF16)
     say("[prefilter] crowded tie bin")
     _run_both(w, q, K, V)
+
+
+def test_prefilter_repair_more_groups_than_slots():
+    """L = 131072, 16 heads per KV group: a repair slot holds 16 rows x L scores (8 MiB), so the
+    bounded repair runs 8 slots; 12 of the 16 groups are flagged (hot keys at every sampled
+    position: the threshold lands above the k-th score), so some repair workgroups take two groups
+    in turn and others one; the unflagged groups keep their prefilter result."""
+    w = fx.Workload("prefilter-many-repairs", fx.MODE_EXACT, 2, 128, 8, 128, 131072, 4096, fx.BF16, 12,
+                    fx.PLANT_ALIGN, 655, 0.5)
+    q, K, V = fx.make_attn(w)
+    qf = fx.bf16_bits_to_f32(q).astype(np.float64)
+    G = w.Hq // w.Hkv
+    pos = np.arange(w.L)
+    hot = (pos % 4096) < 64  # the runs the sampling pass reads for this shape
+    flagged = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            if (b * w.Hkv + g) % 4 == 3:
+                continue  # left alone
+            d = qf[b, g * G:(g + 1) * G].sum(0)
+            d = d / np.linalg.norm(d)
+            mag = 12.0 + 0.001 * pos[hot]
+            K[b, g, hot] = fx.encode(mag[:, None] * d[None, :], fx.BF16)
+            flagged += 1
+    assert flagged == 12
+    say("[prefilter] 12 of 16 groups flagged, 8 repair slots")
+    _run_both(w, q, K, V)

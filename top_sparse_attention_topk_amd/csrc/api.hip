@@ -391,9 +391,15 @@ DecodeLayout decode_layout(const tka_problem* p) {
   d.k = p->top_k;
   d.unit = p->mode == TKA_SCORE_BLOCK_MEAN ? p->block_size : 0;
   d.shared = p->mode == TKA_SCORE_INDEXER;
+  d.pf = prefilter_plan(p);
   size_t o = 0;
+  // the score array, or with the prefilter the repair kernel's bounded score slots
   d.scores = o;
-  o += al256(sizeof(float) * (size_t)d.rows * (d.len > 0 ? d.len : 1));
+  if (d.pf.on)
+    o += al256(repair_slot_bytes((int64_t)p->batch * p->n_kv_heads, (int)nqry(p) * (p->n_q_heads / p->n_kv_heads),
+                                 p->seq_len));
+  else
+    o += al256(sizeof(float) * (size_t)d.rows * (d.len > 0 ? d.len : 1));
   d.sel_ws = o;
   o += al256(select_workspace_bytes(d.rows, d.len, d.k));
   d.idx = o;
@@ -404,9 +410,8 @@ DecodeLayout decode_layout(const tka_problem* p) {
   d.gp = plan_gather(ga);
   d.gather_ws = o;
   o += al256(d.gp.ws_bytes);
-  d.krow = o;  // several queries: each row's count
-  if (nqry(p) > 1) o += al256(sizeof(int32_t) * (size_t)d.rows);
-  d.pf = prefilter_plan(p);
+  d.krow = o;  // several queries without the prefilter: each row's count
+  if (nqry(p) > 1 && !d.pf.on) o += al256(sizeof(int32_t) * (size_t)d.rows);
   if (d.pf.on) {
     const size_t R = (size_t)d.rows;
     d.samp = o;
@@ -684,13 +689,29 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
     launch_score_mfma_cand(sc, mo, st);
     launch_prefilter_finish(cpair, cnt, T, d.pf.capg, d.rows, d.len, d.k, G, p->n_q_heads, M, idx, selv,
                             row_flag, group_flag, st);
-    launch_score_mfma_guarded(sc, group_flag, st);
-    int32_t* krow = nullptr;  // several queries: query t keeps min(k, L - M + t + 1)
-    if (M > 1) {
-      krow = reinterpret_cast<int32_t*>(base + d.krow);
-      launch_mq_counts(krow, d.rows, M, p->n_q_heads, p->seq_len, d.k, st);
-    }
-    launch_select_rows_flagged(sa, row_flag, krow, st);
+    // flagged rows: their groups' exact scores in bounded slots, then the row select (query t of
+    // several keeps min(k, L - M + t + 1))
+    RepairArgs ra;
+    ra.q = q;
+    ra.K = k_cache;
+    ra.B = p->batch;
+    ra.Hq = p->n_q_heads;
+    ra.Hkv = p->n_kv_heads;
+    ra.G = G;
+    ra.M = M;
+    ra.d = p->head_dim;
+    ra.L = p->seq_len;
+    ra.k = d.k;
+    ra.sb = p->kv_stride_b;
+    ra.sh = p->kv_stride_h;
+    ra.sl = p->kv_stride_l;
+    ra.scale = eff_scale(p);
+    ra.group_flag = group_flag;
+    ra.row_flag = row_flag;
+    ra.slots = scores;
+    ra.idx = idx;
+    ra.sel = selv;
+    launch_prefilter_repair(ra, st);
   } else {
     // 1. score
     if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);

@@ -84,7 +84,6 @@ struct MfmaOut {
   uint2* cpair;                 // candidate mode, packed (when set, instead of cbits/cpos): [B*Hq, capg] (bits, pos)
   int capg;
   int stage;                    // candidate mode: LDS staging entries per head
-  const uint32_t* group_flag;   // guarded mode: [B*Hkv], nonzero = rescore the group
 };
 
 // Largest LDS a workgroup may take on the current device, and a one-time
@@ -96,7 +95,6 @@ bool score_uses_mfma(int dtype_bf16, int G);
 int mfma_scan_chunk(const ScoreArgs& a);
 void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, float* samp, hipStream_t st);
 void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st);
-void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st);
 void launch_score_dense(const ScoreArgs& a, hipStream_t st);
 void launch_score_indexer(const IndexerArgs& a, hipStream_t st);
 void launch_block_mean(const BlockMeanArgs& a, hipStream_t st);
@@ -132,6 +130,23 @@ void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, in
 void launch_prefilter_finish(const uint2* cpair, const uint32_t* cnt, const float* T,
                              int capg, int64_t n_rows, int n, int k, int G, int Hq, int M, int32_t* idx, float* sel,
                              uint32_t* row_flag, uint32_t* group_flag, hipStream_t st);
+
+// repair of the rows the prefilter flagged: exact scores of their groups' 16-row blocks into
+// bounded slots (repair_slot_bytes), then the row select of each flagged row
+struct RepairArgs {
+  const void* q;
+  const void* K;
+  int B, Hq, Hkv, G, M, d, L, k;
+  int64_t sb, sh, sl;
+  float scale;
+  const uint32_t* group_flag;
+  const uint32_t* row_flag;
+  float* slots;
+  int32_t* idx;
+  float* sel;
+};
+size_t repair_slot_bytes(int64_t n_groups, int rows_per_group, int L);
+void launch_prefilter_repair(const RepairArgs& a, hipStream_t st);
 
 // gather planning is shared by the workspace query and the launch
 struct GatherPlan {

@@ -27,9 +27,8 @@ namespace tka {
 //   MFMA_FULL    - write every score, [B*Hq, L].
 //   MFMA_SAMPLE  - only the first 64 positions of every chunk; wave w of
 //                  workgroup x takes chunk 4x+w; scores to [B*Hq, nsamp].
-//   MFMA_GUARDED - MFMA_FULL for the groups whose flag is set, else nothing.
 // ---------------------------------------------------------------------------
-enum { MFMA_FULL = 0, MFMA_SAMPLE = 1, MFMA_GUARDED = 3 };
+enum { MFMA_FULL = 0, MFMA_SAMPLE = 1 };
 // How K reaches the MFMA operand registers:
 //   KLOAD_DIRECT    - each lane loads its own operand slice (16 rows x 64 B per
 //                     load instruction), non-temporal.
@@ -57,7 +56,6 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
   constexpr int RPI = 1024 / RB;         // rows per coalesced load instruction
   constexpr int NI = KL == KLOAD_STAGED ? P / RPI : TILES * KS;  // load instructions per round
   const int task = blockIdx.y;
-  if (MODE == MFMA_GUARDED && o.group_flag[task] == 0) return;
   const int b = task / Hkv, g = task % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
@@ -136,7 +134,7 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = acc[i] * scale;
       if (n < G) {
-        if (MODE == MFMA_FULL || MODE == MFMA_GUARDED) {
+        if (MODE == MFMA_FULL) {
           float* Srow = o.S + row * L;
           if (vec_store && pos + 3 < p1) {
             *reinterpret_cast<float4*>(Srow + pos) = make_float4(v[0], v[1], v[2], v[3]);
@@ -652,17 +650,16 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
 // (b*M + t)*Hq + g*G + hh of [B*M*Hq, L]; positions past the query's own are
 // NaN (they rank below every number). Grid (chunks, B*Hkv), 256 threads.
 // ---------------------------------------------------------------------------
-enum { MQ_FULL = 0, MQ_SAMPLE = 1, MQ_GUARDED = 2 };
+enum { MQ_FULL = 0, MQ_SAMPLE = 1 };
 template <int D, int RT, int MODE>
 __global__ __launch_bounds__(256) void score_mq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
                                                        int Hq, int Hkv, int G, int M, int L, int64_t sb, int64_t sh,
                                                        int64_t sl, float scale, int chunk, float* __restrict__ S,
-                                                       int nsamp, const uint32_t* __restrict__ group_flag) {
+                                                       int nsamp) {
   constexpr int KS = D / 32;
   constexpr int P = 32;
   constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
   const int task = blockIdx.y;
-  if (MODE == MQ_GUARDED && group_flag[task] == 0) return;
   const int b = task / Hkv, g = task % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
@@ -996,11 +993,11 @@ static void launch_mfma(const ScoreArgs& a, int chunk, unsigned gx, const MfmaOu
 int mfma_scan_chunk(const ScoreArgs& a) { return pick_chunk(a.nrows, (int64_t)a.B * a.Hkv, 256, 256, 4096); }
 
 template <int MODE>
-static void launch_mq_mode(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* gf, hipStream_t st);
+static void launch_mq_mode(const ScoreArgs& a, int chunk, float* out, int nsamp, hipStream_t st);
 
 void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, float* samp, hipStream_t st) {
   if (a.M > 1) {
-    launch_mq_mode<MQ_SAMPLE>(a, sample_chunk, samp, nsamp, nullptr, st);
+    launch_mq_mode<MQ_SAMPLE>(a, sample_chunk, samp, nsamp, st);
     return;
   }
   MfmaOut o{};
@@ -1084,39 +1081,38 @@ void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st
   }
 }
 
-// chunk: positions per workgroup (full and guarded modes) or the sample chunk (sample mode,
+// chunk: positions per workgroup (full mode) or the sample chunk (sample mode,
 // which scores the first 64 positions of each, out = [rows, nsamp])
 template <int D, int RT, int MODE>
-static void launch_mq_t(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* group_flag,
-                        hipStream_t st) {
+static void launch_mq_t(const ScoreArgs& a, int chunk, float* out, int nsamp, hipStream_t st) {
   const size_t lds = (size_t)4 * 32 * (D * 2 + 16);
   ensure_dynamic_lds((const void*)score_mq_kernel<D, RT, MODE>, lds);
   dim3 grid((a.nrows + chunk - 1) / chunk, a.B * a.Hkv);
   hipLaunchKernelGGL((score_mq_kernel<D, RT, MODE>), grid, dim3(256), lds, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, a.M, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, out,
-                     nsamp, group_flag);
+                     nsamp);
 }
 
 template <int D, int MODE>
-static void launch_mq_d(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* gf, hipStream_t st) {
+static void launch_mq_d(const ScoreArgs& a, int chunk, float* out, int nsamp, hipStream_t st) {
   const int R = a.M * a.G;
-  if (R <= 16) launch_mq_t<D, 1, MODE>(a, chunk, out, nsamp, gf, st);
-  else if (R <= 32) launch_mq_t<D, 2, MODE>(a, chunk, out, nsamp, gf, st);
-  else launch_mq_t<D, 4, MODE>(a, chunk, out, nsamp, gf, st);
+  if (R <= 16) launch_mq_t<D, 1, MODE>(a, chunk, out, nsamp, st);
+  else if (R <= 32) launch_mq_t<D, 2, MODE>(a, chunk, out, nsamp, st);
+  else launch_mq_t<D, 4, MODE>(a, chunk, out, nsamp, st);
 }
 
 template <int MODE>
-static void launch_mq_mode(const ScoreArgs& a, int chunk, float* out, int nsamp, const uint32_t* gf, hipStream_t st) {
+static void launch_mq_mode(const ScoreArgs& a, int chunk, float* out, int nsamp, hipStream_t st) {
   if (a.nrows <= 0) return;
   switch (a.d) {
-    case 64: launch_mq_d<64, MODE>(a, chunk, out, nsamp, gf, st); break;
-    case 128: launch_mq_d<128, MODE>(a, chunk, out, nsamp, gf, st); break;
-    default: launch_mq_d<256, MODE>(a, chunk, out, nsamp, gf, st); break;
+    case 64: launch_mq_d<64, MODE>(a, chunk, out, nsamp, st); break;
+    case 128: launch_mq_d<128, MODE>(a, chunk, out, nsamp, st); break;
+    default: launch_mq_d<256, MODE>(a, chunk, out, nsamp, st); break;
   }
 }
 
 void launch_score_mq(const ScoreArgs& a, hipStream_t st) {
-  launch_mq_mode<MQ_FULL>(a, mfma_scan_chunk(a), a.scores, 0, nullptr, st);
+  launch_mq_mode<MQ_FULL>(a, mfma_scan_chunk(a), a.scores, 0, st);
 }
 
 void launch_mq_counts(int32_t* krow, int64_t rows, int M, int Hq, int L, int k, hipStream_t st) {
@@ -1124,18 +1120,6 @@ void launch_mq_counts(int32_t* krow, int64_t rows, int M, int Hq, int L, int k, 
   const int64_t blocks = (rows + 255) / 256;
   hipLaunchKernelGGL(mq_counts_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, krow, rows,
                      M, Hq, L, k);
-}
-
-void launch_score_mfma_guarded(const ScoreArgs& a, const uint32_t* group_flag, hipStream_t st) {
-  if (a.M > 1) {
-    launch_mq_mode<MQ_GUARDED>(a, mfma_scan_chunk(a), a.scores, 0, group_flag, st);
-    return;
-  }
-  MfmaOut o{};
-  o.S = a.scores;
-  o.group_flag = group_flag;
-  const int chunk = 8192;
-  launch_mfma<MFMA_GUARDED>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
 }
 
 template <bool BF16, int D, int NH>

@@ -406,24 +406,18 @@ __device__ void emit_segments(Get get, uint32_t cnt, uint32_t T, uint32_t need_e
 }
 
 // ---------------------------------------------------------------------------
-// Row mode: one workgroup per row. Dynamic LDS: SelSmem, then 4*capw
-// candidate bits and 4*capw candidate positions.
+// Row mode: one workgroup per row. Dynamic LDS (smem_raw): SelSmem, then
+// 4*capw candidate bits and 4*capw candidate positions.
+// The k' = kk largest of the row s[0, n) (kk <= k, kk <= n) to oidx[0, k)
+// (ascending, -1 after kk) and their scores to osel (if given). All 256
+// threads of the workgroup call it; they leave it together.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void select_rows_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
-                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                          int capw, const uint32_t* __restrict__ row_flag,
-                                                          const int32_t* __restrict__ krow) {
-  if (row_flag && row_flag[blockIdx.x] == 0) return;  // only the rows flagged for a full select
-  extern __shared__ uint4 smem_raw[];
+__device__ __forceinline__ void select_row_device(const float* __restrict__ s, int n, int64_t stride, int k, int kk,
+                                                  int32_t* __restrict__ oidx, float* __restrict__ osel, int capw,
+                                                  uint4* smem_raw) {
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem_raw);
   uint32_t* cb = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(smem_raw) + ((sizeof(SelSmem) + 15) & ~15));
   int32_t* cp = reinterpret_cast<int32_t*>(cb + 4 * capw);
-
-  const int64_t row = blockIdx.x;
-  const float* s = S + row * stride;
-  int32_t* oidx = idx + row * k;
-  float* osel = sel ? sel + row * k : nullptr;
-  const int kk = min(krow ? min(krow[row], k) : k, n);  // krow: a count per row, at most k (the row stride)
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   for (int j = kk + t; j < k; j += ST) {
     oidx[j] = -1;
@@ -543,6 +537,17 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float* __restric
     }
     ++lv;
   }
+}
+
+__global__ __launch_bounds__(256) void select_rows_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
+                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
+                                                          int capw, const uint32_t* __restrict__ row_flag,
+                                                          const int32_t* __restrict__ krow) {
+  if (row_flag && row_flag[blockIdx.x] == 0) return;  // only the rows flagged for a full select
+  extern __shared__ uint4 smem_raw[];
+  const int64_t row = blockIdx.x;
+  const int kk = min(krow ? min(krow[row], k) : k, n);  // krow: a count per row, at most k (the row stride)
+  select_row_device(S + row * stride, n, stride, k, kk, idx + row * k, sel ? sel + row * k : nullptr, capw, smem_raw);
 }
 
 // ---------------------------------------------------------------------------
@@ -880,6 +885,10 @@ constexpr int PF_T = 64 * PF_NW;
 constexpr int PF_RC = 12288 / PF_T;  // candidates held per thread: capacity <= 12288
 
 constexpr int PF_STASH = 2048;  // elements of the critical bin ranked one by one
+#ifndef TKA_PF_REPAIR_BYTES
+#define TKA_PF_REPAIR_BYTES (64ll << 20)
+#endif
+constexpr long long PF_REPAIR_BYTES = TKA_PF_REPAIR_BYTES;  // score slots of the repair kernel
 
 struct PfSmem {
   uint32_t skey[PF_STASH];
@@ -1173,6 +1182,148 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
   if (repair && t == 0) {
     row_flag[row] = 1u;
     atomicOr(&group_flag[(row / ((int64_t)M * Hq)) * (Hq / G) + (row % Hq) / G], 1u);  // group (b, h / G)
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Repair of the rows the prefilter flagged (the answer is not certainly among
+// a row's candidates): the row's exact scores, then the row select over them.
+// Persistent, nslot workgroups, each with its own slot of min(16, R) score
+// rows (R = M*G rows per group, below): the
+// flagged (b, KV head) groups are taken in order, the i-th by workgroup
+// i % nslot, with no waits between workgroups. A group's R = M*G (query,
+// head) rows are scored in blocks of 16 (skipping blocks with no flagged
+// row) with the scorers' arithmetic: v_mfma_f32_16x16x32_bf16 over the same
+// operand layout and 32-dim step order (A = 16 key rows staged through LDS,
+// B = the block's query rows, one per column), times the scale, positions a
+// query cannot see set to NaN, so the slot holds bitwise what
+// topk_attn_score writes for those rows; each flagged row of the block is
+// then selected from its slot row with k' = min(k, its visible keys).
+// On a step with no flagged group every workgroup reads the group flags and
+// leaves. Dynamic LDS: max(4 waves x 32 staged rows, the row select's).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void prefilter_repair_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ K, int Hq, int Hkv, int G,
+                                                               int M, int L, int64_t sb, int64_t sh, int64_t sl,
+                                                               float scale, int k, int n_groups,
+                                                               const uint32_t* __restrict__ group_flag,
+                                                               const uint32_t* __restrict__ row_flag,
+                                                               float* __restrict__ slots, int32_t* __restrict__ idx,
+                                                               float* __restrict__ sel, int capw) {
+  constexpr int KS = D / 32;
+  constexpr int P = 32;  // positions per wave round (two 16-position MFMA tiles)
+  constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
+  extern __shared__ uint4 smem_raw[];
+  __shared__ int32_t mine[256];  // flagged groups of this workgroup, in order
+  __shared__ uint32_t wcnt[SW];
+  __shared__ int32_t nmine_s;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int nslot = (int)gridDim.x, me = (int)blockIdx.x;
+  const int R = M * G;
+  float* slot = slots + (size_t)me * min(16, R) * (size_t)L;  // min(16, R) score rows per slot
+
+  // this workgroup's flagged groups: ranks among the flagged groups by ballots and a scan over waves
+  if (t == 0) nmine_s = 0;
+  uint32_t rank0 = 0;  // flagged groups before the current window of 256
+  for (int g0 = 0; g0 < n_groups; g0 += 256) {
+    const int gi = g0 + t;
+    const bool f = gi < n_groups && group_flag[gi] != 0u;
+    const uint64_t bl = ballot(f);
+    if (lane == 0) wcnt[wave] = (uint32_t)__popcll(bl);
+    __syncthreads();
+    uint32_t before = rank0 + (uint32_t)count_below(bl), tot = 0;
+    for (int i = 0; i < SW; ++i) {
+      before += i < wave ? wcnt[i] : 0u;
+      tot += wcnt[i];
+    }
+    if (f && (int)(before % (uint32_t)nslot) == me) {
+      const int at = (int)(before / (uint32_t)nslot);
+      if (at < 256) mine[at] = gi;
+      atomicMax(&nmine_s, at + 1);
+    }
+    rank0 += tot;
+    __syncthreads();
+  }
+  const int nmine = min(nmine_s, 256);  // groups beyond 256 per workgroup: the plan keeps n_groups <= 256 * nslot
+  uint8_t* stage = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
+
+  for (int mi = 0; mi < nmine; ++mi) {
+    const int grp = mine[mi];
+    const int b = grp / Hkv, g = grp % Hkv;
+    const uint16_t* Kb = K + (int64_t)b * sb + (int64_t)g * sh;
+    for (int cb = 0; cb * 16 < R; ++cb) {
+      // flagged rows of the block (every wave computes the same mask)
+      const int rl = cb * 16 + (lane & 15);
+      const bool rin = lane < 16 && rl < R;
+      const int64_t rrow = ((int64_t)b * M + (rin ? rl / G : 0)) * Hq + g * G + (rin ? rl % G : 0);
+      const uint64_t fm = ballot(rin && row_flag[rrow] != 0u);
+      if (fm == 0) continue;  // workgroup-uniform
+      // score the block's rows over every position into the slot
+      const int rr = cb * 16 + n;
+      const bool ok = rr < R;
+      const int tq = ok ? rr / G : 0, hh = ok ? rr % G : 0;
+      const int64_t qr = ((int64_t)b * M + tq) * Hq + g * G + hh;
+      const int last = L - M + tq;  // the last position the row's query sees
+      bf16x8_t bq[KS];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok) v = ld16(q + qr * D + 32 * s2 + 8 * kg);
+        bq[s2] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      float* srow = slot + (size_t)n * L;
+      auto load = [&](uint4 (&a)[NI], int at) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int pos = min(at + j * RPI + lane / CPR, L - 1);
+          a[j] = ld16(Kb + (int64_t)pos * sl + (lane % CPR) * 8);
+        }
+      };
+      int base = wave * P;
+      uint4 cur[NI];
+      if (base < L) load(cur, base);
+      for (; base < L; base += 4 * P) {
+        uint4 nxt[NI];
+        const bool more = base + 4 * P < L;
+        if (more) load(nxt, base + 4 * P);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          *reinterpret_cast<uint4*>(stage + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = cur[j];
+        lds_wave_sync();
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < KS; ++s2) {
+            const uint4 a = *reinterpret_cast<const uint4*>(stage + (16 * tt + n) * PADB + (kg + 4 * s2) * 16);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bq[s2], acc, 0, 0, 0);
+          }
+          const int pos = base + 16 * tt + 4 * kg;
+          if (ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (pos + i < L) srow[pos + i] = pos + i <= last ? acc[i] * scale : __int_as_float(0x7fc00000);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();  // reads of this round precede the next writes
+        if (more) {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
+        }
+      }
+      __syncthreads();  // the slot's scores are written (and the staging area is free)
+      for (uint64_t m = fm; m != 0; m &= m - 1) {
+        const int j = (int)__builtin_ctzll(m);
+        const int r2 = cb * 16 + j, t2 = r2 / G;
+        const int64_t row = ((int64_t)b * M + t2) * Hq + g * G + r2 % G;
+        const int kk = min(k, L - M + t2 + 1);
+        select_row_device(slot + (size_t)j * L, L, L, k, kk, idx + row * k, sel ? sel + row * k : nullptr, capw,
+                          smem_raw);
+        __syncthreads();  // the select's LDS and slot reads are done
+      }
+    }
   }
 }
 
@@ -1876,6 +2027,40 @@ void launch_prefilter_threshold(const float* samp, int64_t n_rows, int nsamp, in
   else  // the plan keeps nsamp <= 8192
     hipLaunchKernelGGL(prefilter_threshold_kernel<128>, grid, dim3(256), 0, st, samp, nsamp, r, n_rows, T, cnt,
                        row_flag, group_flag, G, Hq, M);
+}
+
+int repair_slots(int64_t n_groups, int rows_per_group, int L) {
+  // slots of 16 score rows within PF_REPAIR_BYTES (at least one, at most one per group, and enough
+  // that no workgroup holds more than 256 groups)
+  const int64_t per = (int64_t)std::min(16, rows_per_group) * L * (int64_t)sizeof(float);
+  int64_t ns = std::max<int64_t>(1, (int64_t)PF_REPAIR_BYTES / std::max<int64_t>(per, 1));
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, n_groups));
+  ns = std::max<int64_t>(ns, (n_groups + 255) / 256);
+  return (int)ns;
+}
+
+size_t repair_slot_bytes(int64_t n_groups, int rows_per_group, int L) {
+  return (size_t)repair_slots(n_groups, rows_per_group, L) * std::min(16, rows_per_group) * (size_t)L * sizeof(float);
+}
+
+template <int D>
+static void launch_repair_d(const RepairArgs& a, hipStream_t st) {
+  const int nslot = repair_slots((int64_t)a.B * a.Hkv, a.M * a.G, a.L);
+  size_t sel_lds;
+  const int capw = rows_capw(a.L, a.k, &sel_lds);
+  const size_t lds = std::max(sel_lds, (size_t)4 * 32 * (D * 2 + 16));
+  ensure_dynamic_lds((const void*)prefilter_repair_kernel<D>, lds);
+  hipLaunchKernelGGL((prefilter_repair_kernel<D>), dim3((unsigned)nslot), dim3(ST), lds, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.K, a.Hq, a.Hkv, a.G, a.M, a.L, a.sb, a.sh, a.sl, a.scale, a.k,
+                     a.B * a.Hkv, a.group_flag, a.row_flag, a.slots, a.idx, a.sel, capw);
+}
+
+void launch_prefilter_repair(const RepairArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 64: launch_repair_d<64>(a, st); break;
+    case 128: launch_repair_d<128>(a, st); break;
+    default: launch_repair_d<256>(a, st); break;
+  }
 }
 
 static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((n + 31) / 32); }
