@@ -522,6 +522,8 @@ tka_status topk_select(const float* scores, int64_t n_rows, int32_t row_len, int
 }
 
 // ---- certified adaptive k ----
+}  // extern "C"
+
 namespace {
 struct AdaptiveScratch {
   size_t W, M, flag, total;
@@ -550,6 +552,8 @@ tka_status check_adaptive_args(float eps, int32_t k_min, int64_t n_rows, const i
   return TKA_OK;
 }
 }  // namespace
+
+extern "C" {
 
 tka_status topk_select_adaptive_workspace_size(int64_t n_rows, int32_t row_len, int32_t k_max, size_t* bytes) {
   if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
@@ -614,9 +618,13 @@ tka_status topk_decode_workspace_size(const tka_problem* p, size_t* bytes) {
   return ok();
 }
 
-tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
-                       const void* proxy_keys, const void* q_idx, const float* idx_w, float* out, int32_t* idx_out,
-                       void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// every host-side check of a fused step (nothing touches the GPU); d receives the step's layout
+tka_status check_decode_call(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                             const void* proxy_keys, const void* q_idx, const float* idx_w, const float* out,
+                             const int32_t* idx_out, DecodeLayout& d) {
   tka_status s = check_attn_shape(p);
   if (s) return s;
   if (p->mode == TKA_SCORE_HISA) return fail(TKA_ERR_INVALID_ARG, "TKA_SCORE_HISA runs through topk_hisa_decode");
@@ -635,7 +643,7 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
       return s;
     if (reinterpret_cast<uintptr_t>(idx_w) & 3) return fail(TKA_ERR_ALIGNMENT, "idx_w is not 4-byte aligned");
   }
-  const DecodeLayout d = decode_layout(p);
+  d = decode_layout(p);
   if (!select_len_supported(d.rows, d.len))
     return fail(TKA_ERR_UNSUPPORTED, "seq_len %d too long for %lld selected rows (at most about 12M)", d.len,
                 (long long)d.rows);
@@ -654,12 +662,13 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
         (proxy_keys && overlap(io, span_of(proxy_keys, proxy_bytes(p)))))
       return fail(TKA_ERR_INVALID_ARG, "idx_out overlaps another buffer");
   }
-  if (!ws || ws_bytes < d.total)
-    return fail(TKA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", d.total, ws_bytes);
-  if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  return TKA_OK;
+}
 
-  hipStream_t st = as_stream(stream);
-  char* base = static_cast<char*>(ws);
+// the launches of a fused step on stream st, its scratch at base (d.total bytes, 256-byte aligned)
+tka_status run_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                      const void* proxy_keys, const void* q_idx, const float* idx_w, float* out, int32_t* idx_out,
+                      const DecodeLayout& d, char* base, hipStream_t st) {
   float* scores = reinterpret_cast<float*>(base + d.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx);
   float* selv = reinterpret_cast<float*>(base + d.selv);
@@ -731,7 +740,26 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
   return launched("topk_decode");
 }
 
+}  // namespace
+
+extern "C" {
+
+tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                       const void* proxy_keys, const void* q_idx, const float* idx_w, float* out, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  DecodeLayout d;
+  tka_status s = check_decode_call(p, q, k_cache, v_cache, proxy_keys, q_idx, idx_w, out, idx_out, d);
+  if (s) return s;
+  if (!ws || ws_bytes < d.total)
+    return fail(TKA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu)", d.total, ws_bytes);
+  if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  return run_decode(p, q, k_cache, v_cache, proxy_keys, q_idx, idx_w, out, idx_out, d, static_cast<char*>(ws),
+                    as_stream(stream));
+}
+
 // ---- certified adaptive step: full exact scores -> adaptive k -> gather ----
+}  // extern "C"
+
 namespace {
 struct AdaptiveLayout {
   size_t scores, idx, selv, kout, tau, scratch, gather_ws, total;
@@ -770,6 +798,8 @@ tka_status check_adaptive_problem(const tka_problem* p) {
   return check_gather_shape(p, p->top_k, 0, 0, nullptr);
 }
 }  // namespace
+
+extern "C" {
 
 tka_status topk_decode_adaptive_workspace_size(const tka_problem* p, size_t* bytes) {
   if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
@@ -830,6 +860,8 @@ tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void*
 }
 
 // ---- two-level step ----
+}  // extern "C"
+
 namespace {
 struct HisaLayout {
   size_t bscores, blk, sel_ws, cand, krow, idx, selv, gather_ws, total;
@@ -874,6 +906,8 @@ tka_status check_hisa_problem(const tka_problem* p) {
   return check_gather_shape(p, p->top_k, 0, 0, nullptr);
 }
 }  // namespace
+
+extern "C" {
 
 tka_status topk_hisa_decode_workspace_size(const tka_problem* p, size_t* bytes) {
   if (!bytes) return fail(TKA_ERR_INVALID_ARG, "bytes is NULL");
