@@ -236,6 +236,25 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
 tka_status topk_decode_workspace_size(const tka_problem* p, size_t* bytes);
 
 /*
+ * topk_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * same checks, kernels and results (bitwise) as topk_decode, without the
+ * workspace argument: the scratch is a device array inside the library,
+ * TKA_NOALLOC_SCRATCH_BYTES per GPU, set up on the first call on each device
+ * (with that device current) and held until the process ends. Nothing is
+ * allocated or freed by the call itself. A problem whose topk_decode workspace
+ * (topk_decode_workspace_size) exceeds that size returns TKA_ERR_UNSUPPORTED
+ * and launches nothing. Every call on a GPU uses that GPU's one array (its
+ * contents are whatever the last call left; the step needs nothing zeroed in
+ * advance): calls that may overlap in time on one GPU (different streams or
+ * host threads without ordering between them) race and must not be made.
+ */
+#define TKA_NOALLOC_SCRATCH_BYTES (256u << 20)
+tka_status topk_decode_noalloc(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                               const void* proxy_keys, const void* q_idx, const float* idx_w, float* out,
+                               int32_t* idx_out, void* stream);
+
+/*
  * The certified step (TKA_SCORE_EXACT only): full exact scores, the adaptive
  * k of topk_select_adaptive with k_max = p->top_k, then the gather over the
  * kept positions with their scores as logits. Same kernels as

@@ -267,3 +267,18 @@ def test_threshold_scan_checks():
     assert call(_p(n_q_heads=2, n_kv_heads=2)) == tka.TKA_ERR_UNSUPPORTED
     assert call(_p(), cap=0) == tka.TKA_ERR_INVALID_ARG
     assert call(_p(mode=tka.BLOCK_MEAN, block_size=64)) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_steps_beyond_its_scratch():
+    """topk_decode_noalloc runs topk_decode's checks, then refuses a step whose workspace exceeds the
+    library's scratch array, before any GPU call."""
+    call = lambda p, **kw: LIB.topk_decode_noalloc(ctypes.byref(p), kw.get("q", FAKE), FAKE * 2, FAKE * 3, None,
+                                                   None, None, kw.get("out", FAKE * 5), None, None)
+    big = tka.problem(tka.EXACT, 16, 64, 8, 128, 131072, 32768)  # k' > L/8: the full score array (512 MiB)
+    assert tka.topk_decode_workspace_size(big) > tka.NOALLOC_SCRATCH_BYTES
+    assert call(big) == tka.TKA_ERR_UNSUPPORTED
+    assert "topk_decode_noalloc" in LIB.tka_last_error().decode()
+    c3 = tka.problem(tka.EXACT, 16, 64, 8, 128, 131072, 4096)  # the prefilter step fits
+    assert tka.topk_decode_workspace_size(c3) <= tka.NOALLOC_SCRATCH_BYTES
+    assert call(c3, q=None) == tka.TKA_ERR_INVALID_ARG  # the same argument checks as topk_decode
+    assert call(c3, out=FAKE * 2 + 64) == tka.TKA_ERR_INVALID_ARG

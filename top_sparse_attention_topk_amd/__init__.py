@@ -67,6 +67,7 @@ def _load():
         "topk_decode_adaptive": [P, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, sz, vp],
         "topk_decode_adaptive_workspace_size": [P, ctypes.POINTER(sz)],
         "topk_workspace_size": [P, i32, ctypes.POINTER(sz)],
+        "topk_decode_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -86,7 +87,7 @@ EXPORTS = ["topk_attn_score", "topk_attn_score_threshold", "topk_select", "topk_
            "sparse_attn_gather_workspace_size", "topk_decode", "topk_decode_workspace_size",
            "topk_block_mean_build", "topk_select_adaptive", "topk_select_adaptive_workspace_size",
            "topk_decode_adaptive", "topk_decode_adaptive_workspace_size", "topk_cache_append", "topk_hisa_decode",
-           "topk_hisa_decode_workspace_size", "topk_workspace_size", "tka_status_str",
+           "topk_hisa_decode_workspace_size", "topk_workspace_size", "topk_decode_noalloc", "tka_status_str",
            "tka_last_error",
            "tka_abi_version"]
 
@@ -269,6 +270,25 @@ def topk_decode(p: Problem, q, k_cache, v_cache, proxy_keys=None, q_idx=None, id
     _check(LIB.topk_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(proxy_keys), _ptr(q_idx),
                            _ptr(idx_w), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)),
            "topk_decode")
+    return out, idx_out
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def topk_decode_noalloc(p: Problem, q, k_cache, v_cache, proxy_keys=None, q_idx=None, idx_w=None, out=None,
+                        idx_out=None, want_idx: bool = True, stream=None):
+    """topk_decode without a workspace (the library's per-GPU scratch array; see include/tka.h).
+    Returns (out, idx or None); pass out / idx_out to allocate nothing here either."""
+    import torch
+    if out is None:
+        out = _empty(_qrows(p) + (p.head_dim,), torch.float32, q)
+    if idx_out is None and want_idx:
+        shape = (p.batch, p.top_k) if p.mode == INDEXER else _qrows(p) + (p.top_k,)
+        idx_out = _empty(shape, torch.int32, q)
+    _check(LIB.topk_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(proxy_keys),
+                                   _ptr(q_idx), _ptr(idx_w), _ptr(out), _ptr(idx_out), _stream(stream)),
+           "topk_decode_noalloc")
     return out, idx_out
 
 

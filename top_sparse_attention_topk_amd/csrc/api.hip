@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "internal.h"
 #include "tka.h"
@@ -755,6 +756,60 @@ tka_status topk_decode(const tka_problem* p, const void* q, const void* k_cache,
   if (!aligned16(ws)) return fail(TKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
   return run_decode(p, q, k_cache, v_cache, proxy_keys, q_idx, idx_w, out, idx_out, d, static_cast<char*>(ws),
                     as_stream(stream));
+}
+
+// ---- the fused step without a workspace argument ----
+// Scratch of topk_decode_noalloc: a file-scope device array. In host code its
+// name is only a stand-in: its device address, one per GPU, comes from
+// hipGetSymbolAddress on the first call on that device, and only that address
+// is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[TKA_NOALLOC_SCRATCH_BYTES];
+
+}  // extern "C"
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of the scratch array (looked up once per device)
+tka_status scratch_for_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    const hipError_t e = hipGetLastError();
+    return fail(TKA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(TKA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev,
+                                                 kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(TKA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return TKA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+tka_status topk_decode_noalloc(const tka_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                               const void* proxy_keys, const void* q_idx, const float* idx_w, float* out,
+                               int32_t* idx_out, void* stream) {
+  DecodeLayout d;
+  tka_status s = check_decode_call(p, q, k_cache, v_cache, proxy_keys, q_idx, idx_w, out, idx_out, d);
+  if (s) return s;
+  if (d.total > (size_t)TKA_NOALLOC_SCRATCH_BYTES)
+    return fail(TKA_ERR_UNSUPPORTED, "this step needs %zu scratch bytes, more than the %zu of topk_decode_noalloc",
+                d.total, (size_t)TKA_NOALLOC_SCRATCH_BYTES);
+  char* base = nullptr;
+  if ((s = scratch_for_current_device(&base))) return s;
+  return run_decode(p, q, k_cache, v_cache, proxy_keys, q_idx, idx_w, out, idx_out, d, base, as_stream(stream));
 }
 
 // ---- certified adaptive step: full exact scores -> adaptive k -> gather ----
