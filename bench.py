@@ -34,6 +34,10 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "top_sparse_attention_topk_amd", "csrc")
 COPY_BYTES = 1 << 30  # calibration kernel: torch.neg over 1 GiB of fp32 reads and writes this many bytes
 COPY_KERNEL = "torch.neg (copy calibration)"
+STEP_COUNTERS = os.path.join(ROOT, "profiles", "step_counters.json")
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "mfma_counters.json")
+PROBE_LIB = os.path.join(ROOT, "top_sparse_attention_topk_amd", "libtka_probe.so")
+STREAM_BYTES = 4 << 30  # streaming-read probe: bytes read per launch
 
 
 def log(*a):
@@ -75,11 +79,14 @@ def score_kernel_bytes(w) -> int:
 
 
 def source_digest() -> str:
-    """sha256 over every kernel source: counters taken on other sources are stale."""
+    """sha256 over every source of the decode path's kernels (csrc/, without the benchmark's own
+    streaming probe in csrc/probe/): counters taken on other sources are stale."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for path in sorted(glob.glob(os.path.join(CSRC, "**", "*"), recursive=True)):
+        if not os.path.isfile(path) or os.path.relpath(path, CSRC).startswith("probe"):
+            continue
         with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+            h.update(os.path.relpath(path, CSRC).encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -186,6 +193,206 @@ def summarize_counters(fetch_dir: str, write_dir: str, tail: int) -> None:
         f.write("\n")
 
 
+def fresh_record(path: str):
+    """A profiles/*.json record if it was taken on the current kernel sources, else None."""
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        return rec if rec.get("source_sha256") == source_digest() else None
+    except (OSError, ValueError):
+        return None
+
+
+def fused_step_bytes_needed(w) -> int:
+    """Bytes the fused exact step cannot avoid: every K row scanned, q read, the kept V rows of every
+    query head read (the logits come from the kept scores, so no K row is read twice), out written."""
+    es = esize(w)
+    kk = min(w.k, w.L)
+    return (w.B * w.Hkv * w.L * w.d * es + w.B * w.Hq * w.d * es + w.B * w.Hq * kk * w.d * es
+            + 4 * w.B * w.Hq * w.d)
+
+
+def host_record() -> dict:
+    """The host the CPU baseline ran on: CPU model, sockets, physical cores, logical CPUs, the CPUs this
+    process may use and OMP_NUM_THREADS."""
+    model, sockets, cores = None, set(), set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                    sockets.add(v)
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return {"cpu_model": model, "sockets": len(sockets) or None, "physical_cores": len(cores) or None,
+            "logical_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def stream_read_peak(torch, steps: int = 10) -> dict:
+    """Measured HBM read ceiling: the committed streaming-read probe (csrc/probe/stream_read.hip) over
+    4 GiB, read once per launch with 16-byte non-temporal loads, for 1, 2, 4 and 8 persistent
+    workgroups of 256 threads per compute unit; HIP events on the launch stream."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.tka_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    by = {}
+    for wpc in (1, 2, 4, 8):
+        grid = cus * wpc
+
+        def run():
+            if lib.tka_probe_stream_read(buf.data_ptr(), STREAM_BYTES, sink.data_ptr(), grid, st) != 0:
+                raise RuntimeError("stream read probe launch failed")
+        ms = time_loop(run, steps)
+        by[str(wpc)] = round(STREAM_BYTES / (ms / 1e3) / 1e9, 1)
+    del buf, sink
+    best = max(by.values())
+    return {"gbps": best, "frac_of_peak": round(best / PEAK_HBM_GBPS, 4), "bytes_per_launch": STREAM_BYTES,
+            "gbps_by_workgroups_per_cu": by, "kernel": "tka_probe::stream_read_kernel (csrc/probe/stream_read.hip)"}
+
+
+def _counter_rows(dirs):
+    """(kernel short name, dispatch id, counter, value) of every counter_collection.csv under dirs."""
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    name = COPY_KERNEL if "neg_kernel" in r["Kernel_Name"] else short_name(r["Kernel_Name"])
+                    yield name, int(r["Dispatch_Id"]), r["Counter_Name"], float(r["Counter_Value"])
+
+
+def summarize_step_counters(fetch_dir: str, write_dir: str, steps: int) -> None:
+    """HBM bytes per fused step from a --profile-step run under FETCH_SIZE and one under WRITE_SIZE: every
+    dispatch of a libtka kernel summed, divided by the number of steps, each counter scaled by what it
+    reads for the copy calibration kernel over its known size. Writes profiles/step_counters.json."""
+    per = {}  # (kernel, counter) -> {dispatch: value}
+    for name, disp, counter, val in _counter_rows([fetch_dir, write_dir]):
+        if counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = per.setdefault((name, counter), {})
+            d[disp] = d.get(disp, 0.0) + val * 1024.0  # KiB per dispatch
+    cal = {c: sum(per.get((COPY_KERNEL, c), {}).values()) / max(len(per.get((COPY_KERNEL, c), {})), 1) / COPY_BYTES
+           for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    if not all(cal.values()):
+        raise SystemExit("no copy calibration dispatches in the step profile")
+    kern = {}
+    for (name, counter), d in per.items():
+        if not name.startswith("tka::"):
+            continue
+        k = kern.setdefault(name, {"launches_per_step": len(d) / steps})
+        k["fetch_bytes_per_step" if counter == "FETCH_SIZE" else "write_bytes_per_step"] = \
+            round(sum(d.values()) / cal[counter] / steps)
+    fetch = sum(k.get("fetch_bytes_per_step", 0) for k in kern.values())
+    write = sum(k.get("write_bytes_per_step", 0) for k in kern.values())
+    out = {"source_sha256": source_digest(), "workload": fx_workload_name(), "steps": steps,
+           "bytes_per_step": fetch + write, "fetch_bytes_per_step": fetch, "write_bytes_per_step": write,
+           "calibration": {"kernel": COPY_KERNEL, "fetch_factor": round(cal["FETCH_SIZE"], 5),
+                           "write_factor": round(cal["WRITE_SIZE"], 5)},
+           "kernels": kern}
+    print(f"{'kernel':60s} {'launches':>8s} {'fetch_MB':>10s} {'write_MB':>10s}   (per step)")
+    for name, k in sorted(kern.items(), key=lambda kv: -kv[1].get("fetch_bytes_per_step", 0)):
+        print(f"{name[:60]:60s} {k['launches_per_step']:8.2f} {k.get('fetch_bytes_per_step', 0) / 1e6:10.1f} "
+              f"{k.get('write_bytes_per_step', 0) / 1e6:10.1f}")
+    print(f"{'step total':60s} {'':8s} {fetch / 1e6:10.1f} {write / 1e6:10.1f}  = {(fetch + write) / 1e6:.1f} MB")
+    with open(STEP_COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
+def fx_workload_name() -> str:
+    import fixtures as fx
+    return fx.WORKLOADS[os.environ.get("TKA_BENCH_WORKLOAD", "C3")].name
+
+
+# MFMA kernels of the path, their MFMA instruction and the flops one instruction performs
+MFMA_SHAPES = {"bf16_16x16x32": 2 * 16 * 16 * 32, "f8_32x32x64": 2 * 32 * 32 * 64}
+
+
+def summarize_mfma(dirs, tail: int) -> None:
+    """MFMA counters per kernel (mean per dispatch over each kernel's last `tail` dispatches) from
+    --profile-mfma runs: rocprofv3's MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), in %),
+    the raw counters, and the flops the MOPS counters imply (MOPS count operations in units of 512).
+    Writes profiles/mfma_counters.json."""
+    vals = {}
+    for name, disp, counter, val in _counter_rows(dirs):
+        d = vals.setdefault(name, {}).setdefault(counter, {})
+        d[disp] = d.get(disp, 0.0) + val
+    out = {"source_sha256": source_digest(), "kernels": {}}
+    for name in sorted(vals):
+        if not name.startswith("tka::"):
+            continue
+        rec = {}
+        for counter, d in vals[name].items():
+            v = [d[i] for i in sorted(d)][-tail:]
+            rec[counter] = sum(v) / len(v)
+        mops = sum(v for c, v in rec.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
+        if mops:
+            rec["mfma_flops_from_mops"] = mops * 512
+        if "SQ_INSTS_VALU" in rec and rec.get("SQ_BUSY_CYCLES"):
+            rec["valu_insts_per_busy_cycle"] = round(rec["SQ_INSTS_VALU"] / rec["SQ_BUSY_CYCLES"], 4)
+        out["kernels"][name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rec.items()}
+    cols = ["MfmaUtil", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+            "mfma_flops_from_mops", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_BUSY_CYCLES"]
+    print("kernel | " + " | ".join(cols))
+    for name, rec in out["kernels"].items():
+        print(name[:70] + " | " + " | ".join(str(rec.get(c, "-")) for c in cols))
+    with open(MFMA_COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
+def profile_mfma(fx, tka, torch, np, steps: int) -> None:
+    """Launch each MFMA kernel of the path a few times for the MFMA counters: the fused C3 step (sample
+    scores, candidate scan), the full C3 scores, four queries per sequence (its sampled scan and its dense
+    scores), the two-level step's group scores, and the C5 indexer scores."""
+    w = fx.WORKLOADS["C3"]
+    q, K, V = fx.make_attn(w)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    qt, Kt, Vt = to(q), to(K), to(V)
+    del K, V
+    p = tka.problem(tka.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, tka.TKA_BF16)
+    for _ in range(steps):
+        tka.topk_decode(p, qt, Kt, Vt)
+        tka.topk_attn_score(p, qt, Kt)
+    M = 4
+    qm = to(fx.encode(fx.normal(97, 0, w.B * M * w.Hq * w.d), fx.BF16).reshape(w.B, M, w.Hq, w.d))
+    pm = tka.problem(tka.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, tka.TKA_BF16, n_queries=M)
+    for _ in range(steps):
+        tka.topk_decode(pm, qm, Kt, Vt)
+        tka.topk_attn_score(pm, qm, Kt)
+    ph = tka.problem(tka.HISA, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, tka.TKA_BF16, 0.0, 64, top_blocks=128)
+    means = tka.topk_block_mean_build(ph, Kt)
+    for _ in range(steps):
+        tka.topk_hisa_decode(ph, qt, Kt, Vt, means)
+    torch.cuda.synchronize()
+    del Kt, Vt, means
+    torch.cuda.empty_cache()
+    w5 = fx.WORKLOADS["C5"]
+    qI, kI, wt = fx.make_indexer(w5)
+    p5 = tka.problem(tka.INDEXER, w5.B, w5.Hq, w5.Hkv, w5.d, w5.L, w5.k, tka.TKA_BF16, 0.0, 0, w5.HI, w5.dI)
+    qIt, kIt, wtt = torch.from_numpy(qI).cuda(), torch.from_numpy(kI).cuda(), torch.from_numpy(wt).cuda()
+    for _ in range(steps):
+        tka.topk_attn_score(p5, qIt, kIt, idx_w=wtt)
+    torch.cuda.synchronize()
+    log(f"[bench] profile-mfma: {steps} launches of each MFMA kernel done")
+
+
 def time_loop(fn, steps: int) -> float:
     """Average ms per call from HIP events on the current stream (the launch stream)."""
     import torch
@@ -260,11 +467,71 @@ def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
     return res
 
 
-def cpu_baseline(w, q, K, V, budget_s: float):
-    """The fp64 oracle, as it stands, on whole queries (all heads of one
-    sequence) of the same workload until about budget_s seconds have passed."""
-    import oracle as orc
-    p = orc.problem_for(w)
+def exact_variant(fx, tka, torch, np, w, steps: int) -> dict:
+    """The exact variant at another workload's size: the fused step and the three calls (score, select,
+    gather) timed as one step, each on the launch stream. Footprints under 1 GiB rotate over R on-device
+    replicas of q, K and V (R * counted bytes >= 1 GiB) so each step reads HBM rather than the 256 MB
+    Infinity Cache; the single-replica loops are reported beside them as *_mall_warm. A step smaller
+    than 1 MiB (C1) is latency-bound: its time is reported in microseconds, cache-resident."""
+    q, K, V = fx.make_attn(w)
+    if w.dtype == fx.BF16:
+        to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        dt = tka.TKA_BF16
+    else:
+        to = lambda a: torch.from_numpy(a).cuda()
+        dt = tka.TKA_F32
+    ins = dict(q=to(q), K=to(K), V=to(V))
+    del K, V
+    p = tka.problem(tka.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt)
+    cb = counted_bytes(w)
+    latency = cb < (1 << 20)
+    R = 1 if latency else -(-(1 << 30) // cb)
+    reps = [ins] + [{n: t.clone() for n, t in ins.items()} for _ in range(R - 1)]
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(tka.topk_decode_workspace_size(p), dtype=torch.uint8, device="cuda")
+    rows = w.B * w.Hq
+    sc = torch.empty(tka.score_shape(p), dtype=torch.float32, device="cuda")
+    sel_idx = torch.empty((rows, w.k), dtype=torch.int32, device="cuda")
+    sel_val = torch.empty((rows, w.k), dtype=torch.float32, device="cuda")
+    sws = torch.empty(max(tka.topk_select_workspace_size(rows, w.L, w.k), 1), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(max(tka.sparse_attn_gather_workspace_size(p, w.k), 1), dtype=torch.uint8, device="cuda")
+    gout = torch.empty_like(out)
+
+    def fused(r):
+        tka.topk_decode(p, r["q"], r["K"], r["V"], out=out, idx_out=idx, ws=ws)
+
+    def three(r):
+        tka.topk_attn_score(p, r["q"], r["K"], scores=sc)
+        tka.topk_select(sc.reshape(rows, w.L), w.k, idx_out=sel_idx, sel_out=sel_val, ws=sws)
+        tka.sparse_attn_gather(p, r["q"], r["K"], r["V"], sel_idx, sel_scores=sel_val, out=gout, ws=gws)
+
+    def rotated(fn):
+        it = iter(range(1 << 62))
+        n = -(-steps // R) * R
+        return time_loop(lambda: fn(reps[next(it) % R]), n)
+
+    t_f, t_3 = rotated(fused), rotated(three)
+    res = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "seq_len": w.L,
+           "top_k": w.k, "dtype": "bf16" if w.dtype == fx.BF16 else "f32", "replicas": R,
+           "counted_bytes_per_step": cb}
+    if latency:
+        res.update({"bound": "latency (the step's 0.3 MB stay in cache; no HBM roofline)",
+                    "decode_us": round(t_f * 1e3, 2), "three_call_us": round(t_3 * 1e3, 2),
+                    "decode_queries_per_s": round(w.B / (t_f / 1e3), 1)})
+    else:
+        gb = cb / (t_f / 1e3) / 1e9
+        res.update({"decode_ms": round(t_f, 4), "decode_queries_per_s": round(w.B / (t_f / 1e3), 1),
+                    "hbm_gbps_counted": round(gb, 1), "pct_of_hbm_peak": round(100 * gb / PEAK_HBM_GBPS, 2),
+                    "three_call_ms": round(t_3, 4),
+                    "three_call_queries_per_s": round(w.B / (t_3 / 1e3), 1),
+                    "decode_ms_mall_warm": round(time_loop(lambda: fused(ins), steps), 4),
+                    "three_call_ms_mall_warm": round(time_loop(lambda: three(ins), steps), 4)})
+    del reps, ins
+    return res
+
+
+def _oracle_queries(orc, p, w, q, K, V, budget_s: float):
     done = 0
     t0 = time.perf_counter()
     while True:  # sequences in order, wrapping around, until the budget is spent
@@ -273,10 +540,33 @@ def cpu_baseline(w, q, K, V, budget_s: float):
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "queries/s", "cores": orc.threads(), "kind": "oracle",
-            "sample": f"{done} whole queries ({done * w.Hq} query-head rows of L={w.L}) of the timed workload: "
-                      f"fp64 scores, full sort, fp64 attention; {dt:.1f} s"}
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, q, K, V, budget_s: float, single_budget_s: float):
+    """The fp64 oracle, as it stands, on whole queries (all heads of one
+    sequence) of the same workload until about budget_s seconds have passed,
+    on all the threads OpenMP gives it; then the same on one thread."""
+    import ctypes
+
+    import oracle as orc
+    p = orc.problem_for(w)
+    threads = orc.threads()
+    done, dt = _oracle_queries(orc, p, w, q, K, V, budget_s)
+    res = {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} whole queries ({done * w.Hq} query-head rows of L={w.L}) of the timed workload: "
+                     f"fp64 scores, full sort, fp64 attention; {dt:.1f} s on {threads} threads",
+           "host": host_record()}
+    if single_budget_s > 0:
+        gomp = ctypes.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle's parallel loops use
+        gomp.omp_set_num_threads(1)
+        try:
+            d1, t1 = _oracle_queries(orc, p, w, q, K, V, single_budget_s)
+        finally:
+            gomp.omp_set_num_threads(threads)
+        res["single_core"] = {"value": d1 / t1, "unit": "queries/s", "cores": 1,
+                              "sample": f"{d1} whole queries on one thread; {t1:.1f} s"}
+    return res
 
 
 def main():
@@ -286,6 +576,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C3", help="fixtures.WORKLOADS key (C3 is the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-single-budget", type=float, default=6.0,
+                    help="seconds of oracle work on one thread (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the adjacent paths (profiling runs: the roofline launches stay the last ones)")
@@ -295,12 +587,28 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/counters.json from FETCH_SIZE / WRITE_SIZE runs; no GPU")
     ap.add_argument("--tail", type=int, default=3, help="summaries: mean over each kernel's last N dispatches")
+    ap.add_argument("--profile-step", type=int, metavar="N",
+                    help="run N fused steps of the workload and the copy calibration, nothing else (counters)")
+    ap.add_argument("--summarize-step-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "N"),
+                    help="write profiles/step_counters.json from two --profile-step N runs; no GPU")
+    ap.add_argument("--profile-mfma", type=int, metavar="N",
+                    help="launch every MFMA kernel of the path N times (MFMA counters)")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="DIR",
+                    help="write profiles/mfma_counters.json from --profile-mfma counter runs; no GPU")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.tail)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.tail)
+        return
+    if args.summarize_step_counters:
+        f_dir, w_dir, n = args.summarize_step_counters
+        os.environ["TKA_BENCH_WORKLOAD"] = args.workload
+        summarize_step_counters(f_dir, w_dir, int(n))
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.tail)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode.",
@@ -313,6 +621,9 @@ def main():
     import fixtures as fx
     import top_sparse_attention_topk_amd as tka
 
+    if args.profile_mfma:
+        profile_mfma(fx, tka, torch, np, args.profile_mfma)
+        return
     w = fx.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}")
     q, K, V = fx.make_attn(w)
@@ -333,6 +644,13 @@ def main():
                       device="cuda")
     ws = torch.empty(tka.topk_decode_workspace_size(p), dtype=torch.uint8, device="cuda")
     step = lambda: tka.topk_decode(p, qt, Kt, Vt, out=out, idx_out=idx, ws=ws, **kw)
+    if args.profile_step:
+        for _ in range(args.profile_step):
+            step()
+        torch.cuda.synchronize()
+        copy_calibration(launches=1)
+        log(f"[bench] profile-step: {args.profile_step} steps and the copy calibration done")
+        return
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -376,9 +694,20 @@ def main():
     unit = w.block if w.mode == fx.MODE_BLOCK else 0
     shared = w.mode == fx.MODE_INDEXER
     gout = torch.empty_like(out)
-    t_gather = time_loop(lambda: tka.sparse_attn_gather(p, qt, Kt, Vt, sel_idx, idx_unit=unit, shared=shared,
-                                                        sel_scores=sel_val if exact else None, out=gout),
-                         args.steps)
+    gws = torch.empty(max(tka.sparse_attn_gather_workspace_size(p, w.k, unit, shared), 1), dtype=torch.uint8,
+                      device="cuda")
+    gather_call = lambda: tka.sparse_attn_gather(p, qt, Kt, Vt, sel_idx, idx_unit=unit, shared=shared,
+                                                 sel_scores=sel_val if exact else None, out=gout, ws=gws)
+    t_gather = time_loop(gather_call, args.steps)
+    select_call = lambda: tka.topk_select(sc.reshape(rows, -1), w.k, idx_out=sel_idx,
+                                          sel_out=sel_val if exact else None, want_sel=exact, ws=sws)
+
+    def three_call():
+        score_call()
+        select_call()
+        gather_call()
+    log("[bench] the three calls as one step")
+    t_three = time_loop(three_call, args.steps)
     # dominant kernel of the timed step and its algorithmic bytes per launch
     t_thr = None
     if exact and dt == tka.TKA_BF16 and 2 <= w.G <= 16:
@@ -419,6 +748,27 @@ def main():
     if t_thr is not None:
         roofline["kept_pairs"] = kept
 
+    # the bytes the fused step moves: its unavoidable algorithmic bytes, and the HBM bytes its kernels'
+    # counters read (FETCH_SIZE + WRITE_SIZE per step, copy-calibrated; null when taken on other sources)
+    moved = None
+    if exact:
+        need = fused_step_bytes_needed(w)
+        moved = {"bytes_needed": need, "gbps_needed": round(need / (ms / 1e3) / 1e9, 1),
+                 "frac_needed": round(need / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+                 "what": "K scan + kept V rows + q + out (logits from the kept scores: no K row re-read)"}
+        rec = fresh_record(STEP_COUNTERS)
+        if rec and rec.get("workload") == w.name:
+            mb = rec["bytes_per_step"]
+            moved.update({"bytes_measured": mb, "gbps_measured": round(mb / (ms / 1e3) / 1e9, 1),
+                          "frac_measured": round(mb / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)})
+        else:
+            moved.update({"bytes_measured": None, "gbps_measured": None, "frac_measured": None})
+    mrec = fresh_record(MFMA_COUNTERS)
+    if mrec and kname in mrec.get("kernels", {}):
+        roofline["mfma"] = mrec["kernels"][kname]
+    log("[bench] streaming-read probe")
+    read_peak = stream_read_peak(torch)
+
     result = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -427,10 +777,16 @@ def main():
                    "seq_len": w.L, "top_k": w.k, "path": "fused topk_decode",
                    "gather_logits": "selected scores" if exact else "K rows"},
         "hbm_gbps_counted": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
-        "counted_bytes_per_step": cb, "event_ms_per_step": round(ev_ms, 4),
+        "counted_bytes_per_step": cb,
+        "counted_bytes_note": "north-star count: full K scan + k gathered K and V rows per query head"
+                              + (" (this path reads no gathered K row: see step_bytes)" if exact else ""),
+        "step_bytes": moved, "event_ms_per_step": round(ev_ms, 4),
+        "three_call": {"ms_per_step": round(t_three, 4), "queries_per_s": round(w.B / (t_three / 1e3), 1),
+                       "what": "topk_attn_score -> topk_select -> sparse_attn_gather, timed as one step"},
         "kernel_ms": {"score_full": round(t_score, 4), "select": round(t_select, 4), "gather": round(t_gather, 4),
                       "score_threshold": None if t_thr is None else round(t_thr, 4)},
         "roofline": roofline,
+        "measured_read_peak": read_peak,
     }
     # adjacent paths on the same inputs (each timed alone on the launch stream)
     extras = {}
@@ -507,6 +863,12 @@ def main():
     del Kt, Vt, sc, ws
     torch.cuda.empty_cache()
     if exact and not args.no_extras and args.workload == "C3":
+        # the exact variant at the other configurations' sizes: one fp32 query over 1024 keys (C1) and
+        # one sequence of 32 query heads over 8 KV heads at L = 32K, k = 2048 (C2)
+        for wname, key in (("C1", "exact_C1"), ("C2", "exact_C2")):
+            log(f"[bench] {key}")
+            extras[key] = exact_variant(fx, tka, torch, np, fx.WORKLOADS[wname], args.steps)
+            torch.cuda.empty_cache()
         # the proxy-score variants at their own workload sizes: block means (MoBA-style, top 16 blocks
         # of 64 at L = 128K) and the lightning indexer (E4M3 keys, top 2048 of L = 1M)
         for wname, key in (("C4", "block_mean_C4"), ("C5", "indexer_C5")):
@@ -523,7 +885,7 @@ def main():
                                for n, a in (("q", q), ("K", K), ("V", V))}
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, q, K, V, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, q, K, V, args.cpu_budget, args.cpu_single_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -1,0 +1,45 @@
+// Streaming-read probe for the benchmark's measured HBM ceiling (not part of
+// the decode path or of include/tka.h; built into libtka_probe.so).
+//
+// Reads `bytes` (a multiple of 16) once with 16-byte non-temporal loads, the
+// way the decode step's scan streams K: a persistent grid of `wg_per_cu`
+// workgroups of 256 threads per compute unit, each workgroup one contiguous
+// range, UNR loads in flight per lane. Every lane folds what it read into one
+// word and writes it to sink[global thread id] (so the loads cannot be
+// dropped): sink must hold grid * 256 words. Bytes moved per launch: `bytes`
+// read + grid * 1 KiB written.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tka_probe {
+
+constexpr int UNR = 8;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = min(lo + per, n16);
+  uint32_t acc = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256 * UNR) {
+    u32x4_t v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t j = min(i + (int64_t)u * 256, hi - 1);  // past the end: re-read the last chunk, ignored below
+      v[u] = __builtin_nontemporal_load(src + j);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (i + (int64_t)u * 256 < hi) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+}  // namespace tka_probe
+
+extern "C" int tka_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, void* stream) {
+  if (!src || !sink || bytes < 16 || (bytes & 15) || grid < 1) return 1;
+  hipLaunchKernelGGL(tka_probe::stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const tka_probe::u32x4_t*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
