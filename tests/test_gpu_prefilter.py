@@ -116,3 +116,66 @@ def test_prefilter_repair_more_groups_than_slots():
     assert flagged == 12
     say("[prefilter] 12 of 16 groups flagged, 8 repair slots")
     _run_both(w, q, K, V)
+
+
+# ---- the indexer variant on skewed indexer keys (one kept set per sequence) ----
+
+def _run_indexer_both(w, qI, kI, wt, q, K, V):
+    """Fused step vs the three calls (indexer scores -> select -> shared-list gather), bitwise; the
+    indices against the oracle's select on the GPU's indexer scores; outputs against the oracle's
+    attention over them."""
+    m = tka()
+    p = problem(w)
+    qt, Kt, Vt = dev(q), dev(K), dev(V)
+    qIt, kIt, wtt = dev(qI), dev(kI), dev(wt)
+    out_f, idx_f = m.topk_decode(p, qt, Kt, Vt, proxy_keys=kIt, q_idx=qIt, idx_w=wtt)
+    sc = m.topk_attn_score(p, qIt, kIt, idx_w=wtt)
+    idx, _ = m.topk_select(sc.reshape(w.B, w.L), w.k, want_sel=False)
+    out = m.sparse_attn_gather(p, qt, Kt, Vt, idx, shared=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f.reshape(idx.shape), idx)
+    assert torch.equal(out_f.view(torch.int32), out.view(torch.int32))
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, orc.select(sc.reshape(w.B, w.L).cpu().numpy(), w.k))
+    ref = orc.attend(orc.problem_for(w), q, K, V, gi, list_mode=1)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.d) - ref).max() <= tol(w)
+    return gi
+
+
+IDX_BASE = fx.shrink(fx.WORKLOADS["C5"], 50001, B=2)
+
+
+def test_indexer_regular():
+    w = IDX_BASE
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    say("[indexer] two sequences, split select")
+    _run_indexer_both(w, qI, kI, wt, q, K, V)
+
+
+def test_indexer_hot_runs():
+    """Keys aligned with the weighted query heads in runs of 64 every 512 positions of the first
+    sequence: 6272 scores far above the rest, more than k, concentrated in a few histogram bins."""
+    w = IDX_BASE
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    qd = orc.decode_values(orc.E4M3, qI[0])  # [HI, dI]
+    x = (wt[0].astype(np.float64)[:, None] * qd).sum(0)
+    x = 200.0 * x / np.abs(x).max()
+    pos = np.arange(w.L)
+    hot = (pos % 512) < 64
+    kI[0, hot] = fx.encode(np.tile(x, (int(hot.sum()), 1)).astype(np.float32), fx.E4M3)
+    say("[indexer] hot runs in sequence 0")
+    _run_indexer_both(w, qI, kI, wt, q, K, V)
+
+
+def test_indexer_all_keys_equal():
+    """Every indexer key of sequence 1 equal: all its scores tie; the kept set is the first k
+    positions."""
+    w = IDX_BASE
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    kI[1] = kI[1, 0]
+    say("[indexer] all keys equal in sequence 1")
+    gi = _run_indexer_both(w, qI, kI, wt, q, K, V)
+    assert (gi[1] == np.arange(w.k)).all()
