@@ -179,3 +179,52 @@ def test_indexer_all_keys_equal():
     say("[indexer] all keys equal in sequence 1")
     gi = _run_indexer_both(w, qI, kI, wt, q, K, V)
     assert (gi[1] == np.arange(w.k)).all()
+
+
+# ---- the indexer select over per-chunk candidates (long rows, k' <= L / 512) ----
+# Chunks of 2048 positions keep their 16 first positions in the select order; a row whose chunks
+# could hold more kept positions than they kept takes the full row select.
+
+IC_BASE = fx.shrink(fx.WORKLOADS["C5"], 200003, B=2, k=256)  # 98 chunks, the last one of 1347 positions
+
+
+def test_indexer_candidates_regular():
+    w = IC_BASE
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    say("[indexer candidates] two sequences of 200003, k 256")
+    _run_indexer_both(w, qI, kI, wt, q, K, V)
+
+
+def test_indexer_candidates_crowded_chunk():
+    """64 high keys inside one chunk of sequence 0: that chunk holds more kept positions than its
+    16 candidates, so the row takes the full select; sequence 1 keeps the candidate result."""
+    w = IC_BASE
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    qd = orc.decode_values(orc.E4M3, qI[0])
+    x = (wt[0].astype(np.float64)[:, None] * qd).sum(0)
+    x = 200.0 * x / np.abs(x).max()
+    kI[0, 3 * 2048 + 100:3 * 2048 + 164] = fx.encode(np.tile(x, (64, 1)).astype(np.float32), fx.E4M3)
+    say("[indexer candidates] 64 hot keys in chunk 3 of sequence 0")
+    gi = _run_indexer_both(w, qI, kI, wt, q, K, V)
+    assert np.isin(np.arange(3 * 2048 + 100, 3 * 2048 + 164), gi[0]).all()
+
+
+def test_indexer_candidates_all_keys_equal():
+    w = IC_BASE
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    kI[1] = kI[1, 0]
+    say("[indexer candidates] all keys equal in sequence 1")
+    gi = _run_indexer_both(w, qI, kI, wt, q, K, V)
+    assert (gi[1] == np.arange(w.k)).all()
+
+
+def test_indexer_candidates_short_last_chunk():
+    """L = 16 * 2048 + 5: the last chunk's 5 positions are all candidates (261 in all), k 64."""
+    w = fx.shrink(fx.WORKLOADS["C5"], 16 * 2048 + 5, B=3, k=64, seed=21)
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    say("[indexer candidates] L 32773, B 3, k 64")
+    _run_indexer_both(w, qI, kI, wt, q, K, V)

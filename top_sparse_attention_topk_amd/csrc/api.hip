@@ -202,20 +202,24 @@ tka_status check_score_call(const tka_problem* p, const void* q, const void* key
   return TKA_OK;
 }
 
+IndexerArgs indexer_args(const tka_problem* p, const void* q, const void* keys, const float* w, float* scores) {
+  IndexerArgs a;
+  a.qI = static_cast<const uint8_t*>(q);
+  a.kI = static_cast<const uint8_t*>(keys);
+  a.w = w;
+  a.scores = scores;
+  a.B = p->batch;
+  a.HI = p->n_idx_heads;
+  a.dI = p->idx_dim;
+  a.L = p->seq_len;
+  a.Lc = (int)idx_slots(p);
+  return a;
+}
+
 void run_score(const tka_problem* p, const void* q, const void* keys, const float* w, float* scores,
                hipStream_t st) {
   if (p->mode == TKA_SCORE_INDEXER) {
-    IndexerArgs a;
-    a.qI = static_cast<const uint8_t*>(q);
-    a.kI = static_cast<const uint8_t*>(keys);
-    a.w = w;
-    a.scores = scores;
-    a.B = p->batch;
-    a.HI = p->n_idx_heads;
-    a.dI = p->idx_dim;
-    a.L = p->seq_len;
-    a.Lc = (int)idx_slots(p);
-    launch_score_indexer(a, st);
+    launch_score_indexer(indexer_args(p, q, keys, w, scores), st);
   } else {
     launch_score_dense(dense_score_args(p, q, keys, scores), st);
   }
@@ -377,11 +381,13 @@ PrefilterPlan prefilter_plan(const tka_problem* p) {
 struct DecodeLayout {
   size_t scores, sel_ws, idx, selv, gather_ws, krow, total;
   size_t samp, T, cnt, row_flag, group_flag, cpair;
+  size_t icand;  // the indexer select's candidates
   int64_t rows;
   int32_t len;
   int32_t k;
   GatherPlan gp;
   PrefilterPlan pf;
+  IndexerCandPlan ic;
   int unit, shared;
 };
 
@@ -401,8 +407,9 @@ DecodeLayout decode_layout(const tka_problem* p) {
                                  p->seq_len));
   else
     o += al256(sizeof(float) * (size_t)d.rows * (d.len > 0 ? d.len : 1));
+  d.ic = d.shared ? indexer_cand_plan(p->seq_len, d.k) : IndexerCandPlan{};
   d.sel_ws = o;
-  o += al256(select_workspace_bytes(d.rows, d.len, d.k));
+  if (!d.ic.on) o += al256(select_workspace_bytes(d.rows, d.len, d.k));
   d.idx = o;
   o += al256(sizeof(int32_t) * (size_t)d.rows * d.k);
   d.selv = o;
@@ -428,6 +435,8 @@ DecodeLayout decode_layout(const tka_problem* p) {
     d.cpair = o;  // (score bits, position) pairs
     o += al256(sizeof(uint2) * R * d.pf.capg);
   }
+  d.icand = o;
+  o += al256(indexer_cand_bytes(p->batch, d.ic));
   d.total = o;
   return d;
 }
@@ -722,6 +731,10 @@ tka_status run_decode(const tka_problem* p, const void* q, const void* k_cache, 
     ra.idx = idx;
     ra.sel = selv;
     launch_prefilter_repair(ra, st);
+  } else if (d.ic.on) {
+    // 1+2. indexer scores with each chunk's candidates, then the select among the candidates
+    launch_indexer_select(indexer_args(p, q_idx, proxy_keys, idx_w, scores), d.ic, d.k, base + d.icand, idx,
+                          nullptr, st);
   } else {
     // 1. score
     if (p->mode == TKA_SCORE_INDEXER) run_score(p, q_idx, proxy_keys, idx_w, scores, st);

@@ -133,6 +133,20 @@ void launch_prefilter_finish(const uint2* cpair, const uint32_t* cnt, const floa
 
 // repair of the rows the prefilter flagged: exact scores of their groups' 16-row blocks into
 // bounded slots (repair_slot_bytes), then the row select of each flagged row
+// The indexer variant's fused select: each scoring workgroup keeps its chunk's first positions in the
+// select order as candidates; one workgroup per sequence selects among them (or, when a chunk could
+// hold more kept positions than it kept, over the whole score row).
+struct IndexerCandPlan {
+  bool on = false;
+  int nch = 0;    // chunks per sequence
+  int ncand = 0;  // candidates per sequence
+};
+IndexerCandPlan indexer_cand_plan(int L, int k);
+size_t indexer_cand_bytes(int64_t B, const IndexerCandPlan& pl);
+// scores (a.scores, [B, L]) and candidates, then idx [B, k] ascending (-1 padded) and sel (optional)
+void launch_indexer_select(const IndexerArgs& a, const IndexerCandPlan& pl, int k, void* cand_ws, int32_t* idx,
+                           float* sel, hipStream_t st);
+
 struct RepairArgs {
   const void* q;
   const void* K;

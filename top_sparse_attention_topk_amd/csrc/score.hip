@@ -11,6 +11,7 @@
 // used only where several query heads share a key row (a real small-M
 // contraction) and for the fp8 indexer; the rest uses wave dot-reductions.
 #include "device_common.h"
+#include "indexer_core.h"
 #include "internal.h"
 
 namespace tka {
@@ -829,87 +830,32 @@ __global__ __launch_bounds__(256) void score_vec_kernel(const void* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Lightning-indexer scores, E4M3FN inputs, fp32 out:
-//   I[b,i] = sum_j w[b,j] * max(0, <qI[b,j], kI[b,i]>).
-// v_mfma_scale_f32_32x32x64_f8f6f4 (both formats E4M3, unit scales):
-// A = 32 indexer heads x 64 dims (lane l: head l%32, dims 32*(l/32)+[0,32)),
-// B = 64 dims x 32 positions (lane l: position l%32, same dims),
-// C[head][pos]: lane l holds position l%32 for heads 8a + 4*(l/32) + c.
-// ReLU and the weighted head sum stay in registers; lanes l and l^32 hold
-// the two halves of the head sum. Grid (chunks, B), 256 threads.
+// Lightning-indexer scores, E4M3FN inputs, fp32 out (the MFMA core and its
+// operand layout: indexer_core.h). Grid (chunks, B), 256 threads; each wave
+// scores 32 * UNR positions per round.
 // ---------------------------------------------------------------------------
 template <int DI, int NT>
 __global__ __launch_bounds__(256) void score_indexer_kernel(const uint8_t* __restrict__ qI,
                                                             const uint8_t* __restrict__ kI,
                                                             const float* __restrict__ w, float* __restrict__ S,
                                                             int HI, int L, int Lc, int chunk) {
-  constexpr int KS = DI / 64;
   constexpr int UNR = 4;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 31, half = lane >> 5;
-
-  i32x8_t aq[NT][KS];
-  float wt[NT][16];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int head = t * 32 + j;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-      if (head < HI) {
-        const uint8_t* p = qI + ((int64_t)b * HI + head) * DI + 64 * s + 32 * half;
-        lo = ld16(p);
-        hi = ld16(p + 16);
-      }
-      i32x8_t v;
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      aq[t][s] = v;
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int hh = t * 32 + 8 * a + 4 * half + c;
-        wt[t][4 * a + c] = hh < HI ? w[(int64_t)b * HI + hh] : 0.f;
-      }
-  }
+  IndexerQuery<DI, NT> Q;
+  indexer_load_query<DI, NT>(Q, qI, w, b, HI, lane);
   const uint8_t* kb = kI + (int64_t)b * Lc * DI;
   float* Sb = S + (int64_t)b * L;
   const int p0 = blockIdx.x * chunk;
   const int p1 = min(p0 + chunk, L);
   for (int base = p0 + wave * 32 * UNR; base < p1; base += 4 * 32 * UNR) {
-    uint4 raw[UNR][KS][2];
+    float tot[UNR];
+    indexer_round<DI, NT, UNR>(Q, kb, base, L, lane, tot);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int pos = min(base + 32 * u + j, L - 1);
-      const uint8_t* row = kb + (int64_t)pos * DI + 32 * half;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        raw[u][s][0] = ld16_stream(row + 64 * s);
-        raw[u][s][1] = ld16_stream(row + 64 * s + 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      float tot = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x16_t acc = {};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          i32x8_t bk;
-          bk[0] = raw[u][s][0].x; bk[1] = raw[u][s][0].y; bk[2] = raw[u][s][0].z; bk[3] = raw[u][s][0].w;
-          bk[4] = raw[u][s][1].x; bk[5] = raw[u][s][1].y; bk[6] = raw[u][s][1].z; bk[7] = raw[u][s][1].w;
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq[t][s], bk, acc, 0, 0, 0, 127, 0, 127);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tot = fmaf(wt[t][i], fmaxf(acc[i], 0.f), tot);
-      }
-      tot += __shfl_xor(tot, 32, kWave);
       const int pos = base + 32 * u + j;
-      if (half == 0 && pos < p1) Sb[pos] = tot;
+      if (half == 0 && pos < p1) Sb[pos] = tot[u];
     }
   }
 }

@@ -27,6 +27,7 @@
 #include <vector>
 
 #include "device_common.h"
+#include "indexer_core.h"
 #include "internal.h"
 
 namespace tka {
@@ -1328,6 +1329,262 @@ __global__ __launch_bounds__(256) void prefilter_repair_kernel(const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
+// The indexer variant's fused select (few long rows: one kept set per
+// sequence, "Sparse Attention in LLM Inference", "The Role of the Indexer").
+// The scoring pass keeps, for every chunk of IC positions, the chunk's IC_KEEP
+// first positions in the select order as candidates, in position order, at
+// fixed slots (no counters). One workgroup per sequence then selects the k'
+// first candidates. That is the exact answer unless some chunk could hold a
+// kept position beyond its candidates: every candidate of a chunk kept means
+// its worst candidate is kept, so a chunk whose smallest candidate key is at
+// least the k'-th key T (ties included, conservatively) sends the row to the
+// full row select over the score array. The k' first positions overall that
+// are candidates are the k' first candidates; if one position were missing, it
+// would lie in a chunk whose candidates are all ahead of it, and all kept.
+// ---------------------------------------------------------------------------
+constexpr int IC = 2048;           // positions per chunk (one scoring workgroup)
+constexpr int IC_KEEP = 16;        // candidates per chunk
+constexpr int IC_CAND_MAX = 16384;  // candidates per sequence the finish holds in registers
+constexpr uint32_t RK_STASH = 256;  // a critical bin this small is ranked element by element
+
+// The kk-th largest key (1 <= kk <= nvalid) among elements held PER per thread in registers
+// (element e = threadIdx.x * PER + i; e >= nvalid ignored), and how many keys equal to it the
+// select order keeps (the first ones by index). Histograms of NB0 bins over the keys' own range,
+// each level narrowing to the bin that holds the kk-th key, until that bin is one key wide or holds
+// at most RK_STASH keys, which are then ranked one by one. All threads call it.
+template <int PER>
+__device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int nvalid, uint32_t kk, SelSmem& sm, uint32_t* T_out,
+                               uint32_t* need_eq_out) {
+  const int t = threadIdx.x, w = t >> 6, lane = lane_id();
+  const int e0 = t * PER;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (e0 + i < nvalid) {
+      mn = min(mn, key[i]);
+      mx = max(mx, key[i]);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  }
+  if (lane == 0) {
+    sm.gt[w] = mn;
+    sm.eq[w] = mx;
+  }
+  for (int i = t; i < NB0; i += ST) sm.hist[i] = 0;
+  __syncthreads();
+  uint32_t base = sm.gt[0], hi = sm.eq[0];
+#pragma unroll
+  for (int i = 1; i < SW; ++i) {
+    base = min(base, sm.gt[i]);
+    hi = max(hi, sm.eq[i]);
+  }
+  const uint32_t span = hi - base;
+  int sh = span >= (uint32_t)NB0 ? (32 - __clz(span)) - 12 : 0;  // span >> sh < NB0
+  uint32_t width = span;  // keys of the current range: [base, base + width]
+  uint32_t need = kk;
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (e0 + i < nvalid && key[i] >= base && key[i] - base <= width) atomicAdd(&sm.hist[(key[i] - base) >> sh], 1u);
+    __syncthreads();
+    find_bin_t<SW>(sm.hist, NB0, need, sm);
+    const uint32_t bin = sm.res[0], above = sm.res[1], inbin = sm.hist[bin];
+    __syncthreads();  // every thread has read the histogram
+    need -= above;
+    base += bin << sh;
+    if (sh == 0) {  // the bin is one key
+      *T_out = base;
+      *need_eq_out = need;
+      return;
+    }
+    width = (1u << sh) - 1u;
+    if (inbin <= RK_STASH) {
+      if (t == 0) sm.aux = 0u;
+      __syncthreads();
+      uint32_t* stash = sm.hist;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (e0 + i < nvalid && key[i] >= base && key[i] - base <= width) stash[atomicAdd(&sm.aux, 1u)] = key[i];
+      __syncthreads();
+      for (uint32_t j = t; j < inbin; j += ST) {
+        const uint32_t v = stash[j];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t x = 0; x < inbin; ++x) {
+          const uint32_t y = stash[x];
+          gt += y > v;
+          ge += y >= v;
+        }
+        if (gt < need && need <= ge) {  // v is the need-th largest of the bin (all such j agree)
+          sm.res[0] = v;
+          sm.res[1] = need - gt;
+        }
+      }
+      __syncthreads();
+      *T_out = sm.res[0];
+      *need_eq_out = sm.res[1];
+      return;
+    }
+    sh = sh >= 12 ? sh - 12 : 0;  // the next level's NB0 bins cover the bin's 2^sh_old keys
+    for (int i = t; i < NB0; i += ST) sm.hist[i] = 0;
+    __syncthreads();
+  }
+}
+
+// Emit, in index order, the elements with key > T and the first need_eq with key == T: their
+// positions to oidx and score bits to osel (when given). One packed (greater, equal) block scan.
+template <int PER, typename PosOf>
+__device__ __forceinline__ void block_emit_regs(const uint32_t (&key)[PER], const uint32_t (&bits)[PER], PosOf pos_of, int nvalid,
+                                uint32_t T, uint32_t need_eq, SelSmem& sm, int32_t* __restrict__ oidx,
+                                float* __restrict__ osel) {
+  const int e0 = threadIdx.x * PER;
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (e0 + i < nvalid) {
+      ngt += key[i] > T;
+      neq += key[i] == T;
+    }
+  const uint32_t v = (ngt << 16) | neq;  // totals stay below 2^16
+  uint32_t tot;
+  const uint32_t ex = block_incl_scan_t<SW>(v, sm, &tot) - v;
+  const uint32_t eqb = ex & 0xffffu;
+  uint32_t slot = (ex >> 16) + min(eqb, need_eq), eqs = eqb;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (e0 + i >= nvalid) continue;
+    bool take = key[i] > T;
+    if (key[i] == T) take = eqs++ < need_eq;
+    if (take) {
+      oidx[slot] = pos_of(i);
+      if (osel) osel[slot] = __uint_as_float(bits[i]);
+      ++slot;
+    }
+  }
+}
+
+template <int DI, int NT>
+__global__ __launch_bounds__(256) void indexer_cand_kernel(const uint8_t* __restrict__ qI,
+                                                           const uint8_t* __restrict__ kI,
+                                                           const float* __restrict__ w, float* __restrict__ S,
+                                                           int HI, int L, int Lc, uint32_t* __restrict__ cbits,
+                                                           int32_t* __restrict__ cpos, int nch) {
+  constexpr int UNR = 4;
+  constexpr int PER = IC / ST;
+  __shared__ SelSmem sm;
+  __shared__ __align__(16) uint32_t sb[IC];  // the chunk's score bits, position order
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j = lane & 31, half = lane >> 5;
+  IndexerQuery<DI, NT> Q;
+  indexer_load_query<DI, NT>(Q, qI, w, b, HI, lane);
+  const uint8_t* kb = kI + (int64_t)b * Lc * DI;
+  float* Sb = S + (int64_t)b * L;
+  const int p0 = c * IC;
+  const int nv = min(IC, L - p0);
+  for (int base = wave * 32 * UNR; base < nv; base += 4 * 32 * UNR) {
+    float tot[UNR];
+    indexer_round<DI, NT, UNR>(Q, kb, p0 + base, L, lane, tot);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int e = base + 32 * u + j;
+      if (half == 0 && e < nv) {
+        Sb[p0 + e] = tot[u];
+        sb[e] = __float_as_uint(tot[u]);
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t slot0 = ((int64_t)b * nch + c) * IC_KEEP;
+  if (nv <= IC_KEEP) {  // a short last chunk: every position is a candidate
+    for (int e = t; e < nv; e += ST) {
+      cbits[slot0 + e] = sb[e];
+      cpos[slot0 + e] = p0 + e;
+    }
+    return;
+  }
+  uint32_t bits[PER], key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(sb + t * PER + i);
+    bits[i] = x.x; bits[i + 1] = x.y; bits[i + 2] = x.z; bits[i + 3] = x.w;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = score_key(__uint_as_float(bits[i]));
+  uint32_t T, need_eq;
+  block_kth_regs<PER>(key, nv, IC_KEEP, sm, &T, &need_eq);
+  block_emit_regs<PER>(key, bits, [&](int i) { return p0 + t * PER + i; }, nv, T, need_eq, sm, cpos + slot0,
+                       reinterpret_cast<float*>(cbits + slot0));
+}
+
+// One workgroup per sequence, PER candidates per thread in registers (candidate e = t * PER + i,
+// chunk e / IC_KEEP). Dynamic LDS: select_row_device's layout, for the full-select path.
+template <int PER>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void indexer_finish_kernel(
+    const float* __restrict__ S, int L, int k, const uint32_t* __restrict__ cbits, const int32_t* __restrict__ cpos,
+    int nch, int ncand, int32_t* __restrict__ idx, float* __restrict__ sel, int capw) {
+  static_assert(PER % IC_KEEP == 0 && PER % 4 == 0, "a thread holds whole chunks");
+  extern __shared__ uint4 smem_raw[];
+  SelSmem& sm = *reinterpret_cast<SelSmem*>(smem_raw);
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int kk = min(k, L);
+  int32_t* oidx = idx + (int64_t)b * k;
+  float* osel = sel ? sel + (int64_t)b * k : nullptr;
+  bool full = ncand < kk;  // workgroup-uniform
+  if (!full) {
+    const uint32_t* gb = cbits + (int64_t)b * nch * IC_KEEP;
+    const int32_t* gp = cpos + (int64_t)b * nch * IC_KEEP;
+    const int e0 = t * PER;
+    uint32_t bits[PER], key[PER];
+    int32_t pos[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      if (e0 + i + 3 < ncand) {
+        const uint4 x = ld16(gb + e0 + i), y = ld16(gp + e0 + i);
+        bits[i] = x.x; bits[i + 1] = x.y; bits[i + 2] = x.z; bits[i + 3] = x.w;
+        pos[i] = (int32_t)y.x; pos[i + 1] = (int32_t)y.y; pos[i + 2] = (int32_t)y.z; pos[i + 3] = (int32_t)y.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = e0 + i + u < ncand;
+          bits[i + u] = in ? gb[e0 + i + u] : 0u;
+          pos[i + u] = in ? gp[e0 + i + u] : -1;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = score_key(__uint_as_float(bits[i]));
+    uint32_t T, need_eq;
+    block_kth_regs<PER>(key, ncand, (uint32_t)kk, sm, &T, &need_eq);
+    // a chunk with more positions than candidates whose smallest candidate key is >= T could hold
+    // a kept position that is not a candidate
+    bool risk = false;
+#pragma unroll
+    for (int cc = 0; cc < PER / IC_KEEP; ++cc) {
+      const int c = (e0 + cc * IC_KEEP) / IC_KEEP;
+      if (c < nch && min(IC, L - c * IC) > IC_KEEP) {
+        uint32_t m = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < IC_KEEP; ++i) m = min(m, key[cc * IC_KEEP + i]);
+        risk |= m >= T;
+      }
+    }
+    full = __syncthreads_or(risk) != 0;
+    if (!full) {
+      for (int jj = kk + t; jj < k; jj += ST) {
+        oidx[jj] = -1;
+        if (osel) osel[jj] = -INFINITY;
+      }
+      block_emit_regs<PER>(key, bits, [&](int i) { return pos[i]; }, ncand, T, need_eq, sm, oidx, osel);
+      return;
+    }
+  }
+  select_row_device(S + (int64_t)b * L, L, L, k, kk, oidx, osel, capw, smem_raw);
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static bool use_split(int64_t n_rows, int n) { return n_rows < 128 && n > 4 * CHUNK; }
@@ -2071,6 +2328,70 @@ void launch_prefilter_finish(const uint2* cpair, const uint32_t* cnt, const floa
   (void)max_lds_bytes();
   hipLaunchKernelGGL(prefilter_finish_kernel, dim3((unsigned)n_rows), dim3(PF_T), prefilter_finish_lds(n), st, cpair,
                      cnt, T, capg, n, k, G, Hq, M, idx, sel, row_flag, group_flag);
+}
+
+
+IndexerCandPlan indexer_cand_plan(int L, int k) {
+  IndexerCandPlan pl;
+  pl.nch = (L + IC - 1) / IC;
+  pl.ncand = pl.nch > 0 ? (pl.nch - 1) * IC_KEEP + std::min(IC_KEEP, L - (pl.nch - 1) * IC) : 0;
+  // long rows only, at most four kept positions expected per chunk (k * IC <= 4 L: a chunk with more
+  // than IC_KEEP of them is then far in the tail), and the candidates within the finish's LDS
+  const int kk = std::min(k, L);
+  pl.on = L >= 8 * IC && kk >= 1 && (int64_t)kk * IC <= 4 * (int64_t)L && pl.ncand <= IC_CAND_MAX && pl.ncand >= kk;
+  return pl;
+}
+
+size_t indexer_cand_bytes(int64_t B, const IndexerCandPlan& pl) {
+  return pl.on ? 2 * al256(sizeof(uint32_t) * (size_t)B * pl.nch * IC_KEEP) : 0;
+}
+
+template <int DI, int NT>
+static void launch_icand_t(const IndexerArgs& a, const IndexerCandPlan& pl, uint32_t* cbits, int32_t* cpos,
+                           hipStream_t st) {
+  hipLaunchKernelGGL((indexer_cand_kernel<DI, NT>), dim3((unsigned)pl.nch, (unsigned)a.B), dim3(ST), 0, st, a.qI,
+                     a.kI, a.w, a.scores, a.HI, a.L, a.Lc > 0 ? a.Lc : a.L, cbits, cpos, pl.nch);
+}
+
+template <int DI>
+static void launch_icand_d(const IndexerArgs& a, const IndexerCandPlan& pl, uint32_t* cbits, int32_t* cpos,
+                           hipStream_t st) {
+  if (a.HI <= 32) launch_icand_t<DI, 1>(a, pl, cbits, cpos, st);
+  else if (a.HI <= 64) launch_icand_t<DI, 2>(a, pl, cbits, cpos, st);
+  else launch_icand_t<DI, 4>(a, pl, cbits, cpos, st);
+}
+
+void launch_indexer_select(const IndexerArgs& a, const IndexerCandPlan& pl, int k, void* cand_ws, int32_t* idx,
+                           float* sel, hipStream_t st) {
+  if (a.B <= 0) return;
+  uint32_t* cbits = static_cast<uint32_t*>(cand_ws);
+  int32_t* cpos = reinterpret_cast<int32_t*>(static_cast<char*>(cand_ws) +
+                                             al256(sizeof(uint32_t) * (size_t)a.B * pl.nch * IC_KEEP));
+  if (a.dI == 64) launch_icand_d<64>(a, pl, cbits, cpos, st);
+  else launch_icand_d<128>(a, pl, cbits, cpos, st);
+  size_t lds;
+  const int capw = rows_capw(a.L, k, &lds);
+  const size_t own = sizeof(SelSmem);
+  if (lds < own) lds = own;
+  auto go = [&](const void* kern, auto f) {
+    ensure_dynamic_lds(kern, lds);
+    f();
+  };
+  if (pl.ncand <= 16 * ST)
+    go((const void*)indexer_finish_kernel<16>, [&] {
+      hipLaunchKernelGGL((indexer_finish_kernel<16>), dim3((unsigned)a.B), dim3(ST), lds, st, a.scores, a.L, k,
+                         cbits, cpos, pl.nch, pl.ncand, idx, sel, capw);
+    });
+  else if (pl.ncand <= 32 * ST)
+    go((const void*)indexer_finish_kernel<32>, [&] {
+      hipLaunchKernelGGL((indexer_finish_kernel<32>), dim3((unsigned)a.B), dim3(ST), lds, st, a.scores, a.L, k,
+                         cbits, cpos, pl.nch, pl.ncand, idx, sel, capw);
+    });
+  else  // the plan keeps ncand <= IC_CAND_MAX = 64 * ST
+    go((const void*)indexer_finish_kernel<64>, [&] {
+      hipLaunchKernelGGL((indexer_finish_kernel<64>), dim3((unsigned)a.B), dim3(ST), lds, st, a.scores, a.L, k,
+                         cbits, cpos, pl.nch, pl.ncand, idx, sel, capw);
+    });
 }
 
 }  // namespace tka
