@@ -8,15 +8,16 @@
 // A task is one (b, query head) with its own kept list, or one (b, KV head)
 // with the G query heads that share a kept list (indexer variant: one set per
 // sequence). A task's expanded token list (block ids expand to their keys,
-// plus the current block) is cut into splits; each workgroup:
-//   1. resolves its tokens into LDS,
-//   2. computes the logits z = scale <q, K_t> (16-byte row gathers, lane
-//      groups reduce with xor shuffles) - or takes them from the selected
-//      scores when the caller passes them, skipping the K rows,
-//   3. the maximum logit per head,
-//   4. gathers the V rows and accumulates p V and p, p = exp(z - max), in fp32
-//      (K and V rows are read once: non-temporal loads; sums in a fixed order),
-//   5. writes o (one split) or (M, l, acc) partials merged in split order.
+// plus the current block) is cut into splits, one workgroup each, which writes
+// o (one split) or an (M, l, acc) partial; partials are merged in split order.
+// Two kernels:
+//   - gather_kernel: the logits are the selected scores (the exact variant):
+//     tokens and logits into LDS, the maximum logit per head, then the V rows
+//     streamed with p = exp(z - max) accumulated in fp32;
+//   - gather_kv_kernel: the logits come from the K rows (the proxy-scored
+//     variants): K and V slices of a row loaded together, a running softmax
+//     per lane, lane groups and waves merged in a fixed order.
+// Rows are read once (non-temporal 16-byte loads); every sum has a fixed order.
 #include <math.h>
 
 #include "device_common.h"
@@ -52,6 +53,7 @@ struct GatherK {
 
 template <bool BF16, int D, int NH, bool SEL>
 __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
+  static_assert(SEL, "K-row logits take gather_kv_kernel");
   using U = Unpack<BF16>;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPL = U::N;
@@ -130,55 +132,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   }
   __syncthreads();
 
-  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.K) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.V) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
 
-  // 2. logits from the K rows
-  if (!SEL) {
-    float qf[NH][EPL];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const uint8_t* qp =
-          reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(b * a.Hq + h0 + h) * D + sub * EPL) * ES;
-      U::run(ld16(qp), qf[h]);
-    }
-    for (int ib = w * RPW * UNR; ib < ne; ib += 4 * RPW * UNR) {
-      uint4 raw[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int i = ib + u * RPW + grp;
-        const int tk = i < ne ? tok[i] : -1;
-        raw[u] = tk >= 0 ? ld16_stream(Kb + ((int64_t)tk * a.sl + sub * EPL) * ES) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        float kf[EPL];
-        U::run(raw[u], kf);
-        float part[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          float x = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) x = fmaf(qf[h][e], kf[e], x);
-          part[h] = x;
-        }
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1)
-#pragma unroll
-          for (int h = 0; h < NH; ++h) part[h] += __shfl_xor(part[h], o, kWave);
-        const int i = ib + u * RPW + grp;
-        if (i < ne) {
-          const bool ok = tok[i] >= 0;
-#pragma unroll
-          for (int h = 0; h < NH; ++h)
-            if (h % LPR == sub) lg[h * a.span + i] = ok ? part[h] * a.scale : -INFINITY;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // 3. the maximum logit per head (every thread takes a strided share; waves combine through LDS)
+  // 2. the maximum logit per head (every thread takes a strided share; waves combine through LDS)
   float* wmax = stat + 2 * NH;  // [4][NH]
   {
     float mloc[NH];
@@ -199,7 +155,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   for (int h = 0; h < NH; ++h)
     mx[h] = fmaxf(fmaxf(wmax[h], wmax[NH + h]), fmaxf(wmax[2 * NH + h], wmax[3 * NH + h]));
 
-  // 4. V gather and weighted accumulation; the weights p = exp(z - max) are formed here, and each
+  // 3. V gather and weighted accumulation; the weights p = exp(z - max) are formed here, and each
   //    lane group sums the weights of its own rows (the sums are combined in a fixed order below)
   float acc[NH][EPL], psum[NH];
 #pragma unroll
@@ -259,7 +215,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   if (t < NH) stat[t] = mx[t];
   __syncthreads();
 
-  // 5. output or partials
+  // 4. output or partials
   if (a.nsplit == 1) {
     for (int i = t; i < NH * D; i += 256) {
       const int h = i / D, c = i % D;
@@ -270,6 +226,251 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
     float* p = a.part + ((int64_t)task * a.nsplit + split) * (NH * (D + 2));
     for (int i = t; i < NH * D; i += 256) p[i] = red[i];
     if (t < 2 * NH) p[NH * D + t] = stat[t];
+  }
+}
+
+// Logits from the K rows (the proxy-scored variants): one pass that loads each
+// row's K and V slices together. Every lane resolves the tokens of its own rows
+// (no token staging), its lane group (LPR lanes per row) reduces the dot
+// products with xor shuffles, and each lane keeps a running softmax over its
+// rows in base 2 (logits y = z log2(e), weights 2^(y - m) on v_exp_f32): per
+// round of UNR rows the maximum m, the mass l and acc = sum p V, rescaled by
+// 2^(m_old - m) when the maximum grows. The lane groups of a wave, then the
+// four waves, merge in a fixed order: the maxima first, then the rescaled
+// sums. The result is the split's partial (its maximum back in natural-log
+// units, as the merge expects) or, unsplit, the output.
+__device__ __forceinline__ float pow2(float y) { return __builtin_amdgcn_exp2f(y); }
+
+template <bool BF16, int D, int NH>
+__global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
+  using U = Unpack<BF16>;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPL = U::N;
+  constexpr int LPR = D * ES / 16;
+  constexpr int RPW = 64 / LPR;
+  constexpr int UNR = 4;
+  constexpr int PS = NH * (D + 2);  // floats of one (m, l, acc) partial
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  extern __shared__ uint4 smem_raw[];
+  float* wpart = reinterpret_cast<float*>(smem_raw);  // [4 waves][PS]: acc [NH][D], m [NH], l [NH]
+  float* wfac = wpart + 4 * PS;                        // [4 waves][NH] rescale factors
+
+  const unsigned lid = xcd_logical_id(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int task = (int)(lid / gridDim.x), split = (int)(lid % gridDim.x);
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int sub = lane % LPR, grp = lane / LPR;
+  int b, h0, g;
+  const int32_t* list;
+  if (a.shared) {
+    b = task / a.Hkv;
+    g = task % a.Hkv;
+    h0 = g * a.G;
+    list = a.idx + (int64_t)b * a.n_idx;
+  } else {
+    b = task / a.Hq;
+    h0 = task % a.Hq;
+    g = h0 / a.G;
+    list = a.idx + (int64_t)task * a.n_idx;
+  }
+  const int bkv = b / a.M;
+  const int lim = a.L - a.M + 1 + b % a.M;
+  const int64_t e0 = (int64_t)split * a.span;
+  const int ne = (int)max((int64_t)0, min(a.E, e0 + a.span) - e0);
+  const int64_t nb = (int64_t)a.n_idx * (a.unit > 0 ? a.unit : 1);
+  auto token = [&](int i) {  // the token of expanded entry e0 + i (-1: none)
+    const int64_t e = e0 + i;
+    if (a.unit == 0) {
+      const int v = list[e];
+      return (v >= 0 && v < lim) ? v : -1;
+    }
+    if (e < nb) {
+      const int j = list[e / a.unit];
+      if (j < 0 || j >= a.m - 1) return -1;
+      const int64_t x = (int64_t)j * a.unit + e % a.unit;
+      return x < a.L ? (int)x : -1;
+    }
+    const int64_t x = (int64_t)(a.m - 1) * a.unit + (e - nb);
+    return x < a.L ? (int)x : -1;
+  };
+
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.K) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
+  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.V) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
+  const float yscale = a.scale * kLog2e;
+  float qf[NH][EPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(b * a.Hq + h0 + h) * D + sub * EPL) * ES;
+    U::run(ld16(qp), qf[h]);
+  }
+  // the span's tokens into LDS (one list read), then rounds of UNR rows per lane; with NH <= 4
+  // the next round's K and V slices are in flight while the current round is reduced
+  int32_t* tokl = reinterpret_cast<int32_t*>(wfac + 6 * NH);  // [span]
+#pragma unroll 4
+  for (int i = t; i < ne; i += 256) tokl[i] = token(i);
+  __syncthreads();
+  float m[NH], l[NH], acc[NH][EPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  auto issue = [&](int ib, int (&tk)[UNR], uint4 (&kr)[UNR], uint4 (&vr)[UNR]) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = ib + u * RPW + grp;
+      tk[u] = i < ne ? tokl[i] : -1;
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+      if (tk[u] >= 0) {
+        const int64_t off = ((int64_t)tk[u] * a.sl + sub * EPL) * ES;
+        kr[u] = ld16_stream(Kb + off);
+        vr[u] = ld16_stream(Vb + off);
+      }
+    }
+  };
+  auto consume = [&](const int (&tk)[UNR], const uint4 (&kr)[UNR], const uint4 (&vr)[UNR]) {
+    float y[UNR][NH];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float kf[EPL];
+      U::run(kr[u], kf);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x = fmaf(qf[h][e], kf[e], x);
+        y[u][h] = x;
+      }
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) y[u][h] += __shfl_xor(y[u][h], o, kWave);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) y[u][h] = tk[u] >= 0 ? y[u][h] * yscale : -INFINITY;
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float mn = m[h];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) mn = fmaxf(mn, y[u][h]);
+      if (mn == -INFINITY) continue;  // nothing seen yet
+      const float sc = pow2(m[h] - mn);  // m = -inf: 0 (l and acc are still 0)
+      l[h] *= sc;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= sc;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float pu = pow2(y[u][h] - mn);  // y = -inf: 0
+        float vf[EPL];
+        U::run(vr[u], vf);
+        l[h] += pu;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pu, vf[e], acc[h][e]);
+      }
+      m[h] = mn;
+    }
+  };
+  constexpr int STRIDE = 4 * RPW * UNR;
+  if constexpr (NH <= 4) {
+    int tkc[UNR];
+    uint4 krc[UNR], vrc[UNR];
+    int ib = w * RPW * UNR;
+    if (ib < ne) issue(ib, tkc, krc, vrc);
+    for (; ib < ne; ib += STRIDE) {
+      int tkn[UNR];
+      uint4 krn[UNR], vrn[UNR];
+      const bool more = ib + STRIDE < ne;
+      if (more) issue(ib + STRIDE, tkn, krn, vrn);
+      consume(tkc, krc, vrc);
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          tkc[u] = tkn[u];
+          krc[u] = krn[u];
+          vrc[u] = vrn[u];
+        }
+      }
+    }
+  } else {
+    for (int ib = w * RPW * UNR; ib < ne; ib += STRIDE) {
+      int tk[UNR];
+      uint4 kr[UNR], vr[UNR];
+      issue(ib, tk, kr, vr);
+      consume(tk, kr, vr);
+    }
+  }
+  // the wave's lane groups (lanes sub, sub + LPR, ...): the maximum over the groups, each group's
+  // state rescaled to it, then the sums over the groups (xor butterflies over the group index)
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float M = m[h];
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    const float f = M == -INFINITY ? 0.f : pow2(m[h] - M);
+    m[h] = M;
+    l[h] *= f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+      l[h] += __shfl_xor(l[h], o, kWave);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, kWave);
+    }
+  }
+  if (grp == 0) {
+    float* wp = wpart + w * PS;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) wp[h * D + sub * EPL + e] = acc[h][e];
+      if (sub == 0) {
+        wp[NH * D + h] = m[h];
+        wp[NH * D + NH + h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  // the four waves: their factors 2^(m_w - M) per head, then the sums in wave order
+  if (t < 4 * NH) {
+    const int ww = t / NH, h = t % NH;
+    float M = wpart[NH * D + h];
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, wpart[i * PS + NH * D + h]);
+    const float mw = wpart[ww * PS + NH * D + h];
+    wfac[t] = M == -INFINITY ? 0.f : pow2(mw - M);
+    if (ww == 0) wfac[4 * NH + h] = M;
+  }
+  __syncthreads();
+  for (int i = t; i < NH * D; i += 256) {
+    const int h = i / D;
+    float aa = 0.f, ll = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = wfac[ww * NH + h];
+      aa = fmaf(f, wpart[ww * PS + i], aa);
+      if (i % D == 0) ll = fmaf(f, wpart[ww * PS + NH * D + NH + h], ll);
+    }
+    if (a.nsplit == 1) {
+      if (i % D == 0) wfac[5 * NH + h] = ll;
+    } else {
+      float* p = a.part + ((int64_t)task * a.nsplit + split) * PS;
+      p[i] = aa;
+      if (i % D == 0) {
+        const float M = wfac[4 * NH + h];
+        p[NH * D + h] = M == -INFINITY ? -INFINITY : M * kLn2;  // natural-log units for the merge
+        p[NH * D + NH + h] = ll;
+      }
+    }
+    if (a.nsplit == 1) wpart[i] = aa;  // wave 0's slot: this thread's own element, read no more
+  }
+  if (a.nsplit == 1) {
+    __syncthreads();
+    for (int i = t; i < NH * D; i += 256) {
+      const float ll = wfac[5 * NH + i / D];
+      a.out[((int64_t)b * a.Hq + h0 + i / D) * D + i % D] = ll > 0.f ? wpart[i] / ll : 0.f;
+    }
   }
 }
 
@@ -368,8 +569,14 @@ GatherPlan plan_gather(const GatherArgs& a) {
 
 template <bool BF16, int D, int NH, bool SEL>
 static void launch_g(const GatherK& k, const GatherPlan& pl, hipStream_t st) {
-  const size_t lds = sizeof(float) * (NH * D + 6 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
-  hipLaunchKernelGGL((gather_kernel<BF16, D, NH, SEL>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
+  if constexpr (SEL) {
+    const size_t lds = sizeof(float) * (NH * D + 6 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
+    hipLaunchKernelGGL((gather_kernel<BF16, D, NH, true>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
+  } else {
+    const size_t lds = sizeof(float) * (4 * NH * (D + 2) + 6 * NH) + sizeof(int32_t) * pl.span;
+    ensure_dynamic_lds((const void*)gather_kv_kernel<BF16, D, NH>, lds);
+    hipLaunchKernelGGL((gather_kv_kernel<BF16, D, NH>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
+  }
   if (pl.nsplit > 1)
     hipLaunchKernelGGL((gather_merge_kernel<D, NH>), dim3(pl.tasks, NH), dim3(D < 256 ? D : 256),
                        pl.nsplit <= kMergeLdsSplits ? sizeof(float) * pl.nsplit : 0, st, k.part, k.out, pl.nsplit,
