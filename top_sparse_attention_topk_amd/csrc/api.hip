@@ -151,6 +151,7 @@ ScoreArgs dense_score_args(const tka_problem* p, const void* q, const void* keys
     a.sl = p->head_dim;
     a.scale = 1.0f;
     a.bf16 = 0;
+    a.block = 1;
   } else {
     a.nrows = p->seq_len;
     a.sb = p->kv_stride_b;

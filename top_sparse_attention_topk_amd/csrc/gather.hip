@@ -51,6 +51,42 @@ struct GatherK {
   int M;  // queries per sequence (causal): task's K/V sequence is b / M, its last visible key L - M + b % M
 };
 
+// The merge of a task's split partials (PS = NH (D + 2) floats each, p at the first): for head h,
+// with M the maximum of the splits' M_s and weights f_s = e^(M_s - M) (0 for an empty split),
+// o = sum_s f_s acc_s / sum_s f_s l_s, accumulated in split order. wt(s) gives f_s.
+template <int D, int NH, typename Wt>
+__device__ __forceinline__ float merge_column(const float* __restrict__ p, int nsplit, int h, int c, Wt wt) {
+  constexpr int PS = NH * (D + 2);
+  float num = 0.f, den = 0.f;
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    float a[8], l[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = p[(s + u) * PS + h * D + c];
+      l[u] = p[(s + u) * PS + NH * D + NH + h];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = wt(s + u);
+      if (f == 0.f) continue;
+      num = fmaf(f, a[u], num);
+      den = fmaf(f, l[u], den);
+    }
+  }
+  for (; s < nsplit; ++s) {
+    const float f = wt(s);
+    if (f == 0.f) continue;
+    num = fmaf(f, p[s * PS + h * D + c], num);
+    den = fmaf(f, p[s * PS + NH * D + NH + h], den);
+  }
+  return den > 0.f ? num / den : 0.f;
+}
+
+__device__ __forceinline__ float split_weight(float ms, float M) {
+  return (M == -INFINITY || ms == -INFINITY) ? 0.f : expf(ms - M);
+}
+
 template <bool BF16, int D, int NH, bool SEL>
 __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
   static_assert(SEL, "K-row logits take gather_kv_kernel");
@@ -241,6 +277,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
 // units, as the merge expects) or, unsplit, the output.
 __device__ __forceinline__ float pow2(float y) { return __builtin_amdgcn_exp2f(y); }
 
+// byte offset of gather_kv_kernel's token array in its dynamic LDS (after the wave partials)
+__host__ __device__ constexpr size_t kv_tok_offset(int NH, int D) {
+  return (sizeof(float) * (4 * (size_t)NH * (D + 2) + 6 * (size_t)NH) + 15) & ~(size_t)15;
+}
+
 template <bool BF16, int D, int NH>
 __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
   using U = Unpack<BF16>;
@@ -253,7 +294,9 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   extern __shared__ uint4 smem_raw[];
   float* wpart = reinterpret_cast<float*>(smem_raw);  // [4 waves][PS]: acc [NH][D], m [NH], l [NH]
-  float* wfac = wpart + 4 * PS;                        // [4 waves][NH] rescale factors
+  float* wfac = wpart + 4 * PS;                        // [4 waves][NH] rescale factors, M, l
+  // then, 16-byte aligned: the span's tokens
+  int32_t* tokl = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_raw) + kv_tok_offset(NH, D));
 
   const unsigned lid = xcd_logical_id(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int task = (int)(lid / gridDim.x), split = (int)(lid % gridDim.x);
@@ -272,6 +315,11 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
     g = h0 / a.G;
     list = a.idx + (int64_t)task * a.n_idx;
   }
+  // the query slices first: their loads overlap the token staging below
+  uint4 qraw[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+    qraw[h] = ld16(reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(b * a.Hq + h0 + h) * D + sub * EPL) * ES);
   const int bkv = b / a.M;
   const int lim = a.L - a.M + 1 + b % a.M;
   const int64_t e0 = (int64_t)split * a.span;
@@ -296,18 +344,14 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.K) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.V) + ((int64_t)bkv * a.sb + (int64_t)g * a.sh) * ES;
   const float yscale = a.scale * kLog2e;
-  float qf[NH][EPL];
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(b * a.Hq + h0 + h) * D + sub * EPL) * ES;
-    U::run(ld16(qp), qf[h]);
-  }
   // the span's tokens into LDS (one list read), then rounds of UNR rows per lane; with NH <= 4
   // the next round's K and V slices are in flight while the current round is reduced
-  int32_t* tokl = reinterpret_cast<int32_t*>(wfac + 6 * NH);  // [span]
 #pragma unroll 4
   for (int i = t; i < ne; i += 256) tokl[i] = token(i);
   __syncthreads();
+  float qf[NH][EPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) U::run(qraw[h], qf[h]);
   float m[NH], l[NH], acc[NH][EPL];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -456,10 +500,11 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
       if (i % D == 0) wfac[5 * NH + h] = ll;
     } else {
       float* p = a.part + ((int64_t)task * a.nsplit + split) * PS;
+      const float M = wfac[4 * NH + h];
+      const float Mn = M == -INFINITY ? -INFINITY : M * kLn2;  // natural-log units for the merge
       p[i] = aa;
       if (i % D == 0) {
-        const float M = wfac[4 * NH + h];
-        p[NH * D + h] = M == -INFINITY ? -INFINITY : M * kLn2;  // natural-log units for the merge
+        p[NH * D + h] = Mn;
         p[NH * D + NH + h] = ll;
       }
     }
@@ -474,9 +519,8 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
   }
 }
 
-// o = sum_s e^(M_s - M) acc_s / sum_s e^(M_s - M) l_s, splits in order. A workgroup per
-// (task, head): the split weights e^(M_s - M) first (to LDS), then thread c accumulates output
-// column c over the splits with independent loads.
+// The merge as its own launch. A workgroup per (task, head): the split weights first (to LDS), then
+// thread c accumulates output column c over the splits.
 constexpr int kMergeLdsSplits = 8192;
 template <int D, int NH>
 __global__ __launch_bounds__(256) void gather_merge_kernel(const float* __restrict__ part, float* __restrict__ out,
@@ -503,41 +547,15 @@ __global__ __launch_bounds__(256) void gather_merge_kernel(const float* __restri
   float M = -INFINITY;
   for (int i = 0; i < (int)(blockDim.x + 63) / 64; ++i) M = fmaxf(M, red[i]);
   const bool in_lds = nsplit <= kMergeLdsSplits;
-  auto weight = [&](int s) {
-    const float ms = p[s * PS + NH * D + h];
-    return (M == -INFINITY || ms == -INFINITY) ? 0.f : expf(ms - M);
-  };
   if (in_lds)
-    for (int s = t; s < nsplit; s += blockDim.x) fw[s] = weight(s);
+    for (int s = t; s < nsplit; s += blockDim.x) fw[s] = split_weight(p[s * PS + NH * D + h], M);
   __syncthreads();
-  for (int c = t; c < D; c += 256) {
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      int s = 0;
-      for (; s + 8 <= nsplit; s += 8) {
-        float a[8], l[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          a[u] = p[(s + u) * PS + h * D + c];
-          l[u] = p[(s + u) * PS + NH * D + NH + h];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float f = in_lds ? fw[s + u] : weight(s + u);
-          if (f == 0.f) continue;
-          num = fmaf(f, a[u], num);
-          den = fmaf(f, l[u], den);
-        }
-      }
-      for (; s < nsplit; ++s) {
-        const float f = in_lds ? fw[s] : weight(s);
-        if (f == 0.f) continue;
-        num = fmaf(f, p[s * PS + h * D + c], num);
-        den = fmaf(f, p[s * PS + NH * D + NH + h], den);
-      }
-    }
-    out[((int64_t)b * Hq + h0 + h) * D + c] = den > 0.f ? num / den : 0.f;
-  }
+  for (int c = t; c < D; c += 256)
+    out[((int64_t)b * Hq + h0 + h) * D + c] =
+        M == -INFINITY ? 0.f
+                       : merge_column<D, NH>(p, nsplit, h, c, [&](int s) {
+                           return in_lds ? fw[s] : split_weight(p[s * PS + NH * D + h], M);
+                         });
 }
 
 // ---------------------------------------------------------------------------
@@ -573,7 +591,7 @@ static void launch_g(const GatherK& k, const GatherPlan& pl, hipStream_t st) {
     const size_t lds = sizeof(float) * (NH * D + 6 * NH) + sizeof(int32_t) * pl.span + sizeof(float) * NH * pl.span;
     hipLaunchKernelGGL((gather_kernel<BF16, D, NH, true>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
   } else {
-    const size_t lds = sizeof(float) * (4 * NH * (D + 2) + 6 * NH) + sizeof(int32_t) * pl.span;
+    const size_t lds = kv_tok_offset(NH, D) + sizeof(int32_t) * pl.span;
     ensure_dynamic_lds((const void*)gather_kv_kernel<BF16, D, NH>, lds);
     hipLaunchKernelGGL((gather_kv_kernel<BF16, D, NH>), dim3(pl.nsplit, pl.tasks), dim3(256), lds, st, k);
   }

@@ -16,6 +16,7 @@ struct ScoreArgs {
   int bf16;    // rows: 1 bf16, 0 fp32
   int q_bf16;  // query: 1 bf16, 0 fp32
   int M = 1;   // queries per sequence (q [B,M,Hq,d], scores [B,M,Hq,nrows], causal)
+  int block = 0;  // rows are fp32 block means (one query per sequence)
 };
 
 struct IndexerArgs {

@@ -752,6 +752,103 @@ __global__ void mq_counts_kernel(int32_t* __restrict__ krow, int64_t rows, int M
 }
 
 // ---------------------------------------------------------------------------
+// Block-mean scores s[b,h,j] = <q[b,h], mean[b,g,j]> ("Sparse Attention
+// Landscape", "Block Sparse Attention": the block score from the mean-pooled
+// keys), fp32 means, the query bf16 or fp32. A row of D floats is read by a
+// group of 8 lanes, lane c taking the 16-byte pieces c, c + 8, ... (a load
+// instruction covers 128 contiguous bytes of each of 8 rows); each lane keeps
+// the matching slices of the NH query heads, and the partial dots are reduced
+// over the 8 lanes with three xor shuffles. A wave takes RND consecutive
+// rounds of 8 rows with all their loads issued before the first use.
+// Grid (chunks, B*Hkv*htiles), 256 threads.
+// ---------------------------------------------------------------------------
+#ifndef TKA_BLK_LOADS
+#define TKA_BLK_LOADS 8
+#endif
+template <int D, int NH>
+struct BlockScoreShape {
+  static constexpr int LPR = 8;                            // lanes per row
+  static constexpr int NL = D / 32;                        // 16-byte pieces per lane
+  static constexpr int LD = NH > 4 ? TKA_BLK_LOADS / 2 : TKA_BLK_LOADS;  // 16-byte loads in flight per lane
+  static constexpr int RND = LD / NL > 0 ? LD / NL : 1;    // rounds of 8 rows in flight per wave
+  static constexpr int ROWS = 4 * 8 * RND;                 // rows per workgroup pass
+};
+
+template <int D, int NH>
+__global__ __launch_bounds__(256) void score_block_kernel(const void* __restrict__ qv, const float* __restrict__ means,
+                                                          float* __restrict__ S, int Hq, int Hkv, int G, int nrows,
+                                                          int64_t sb, int64_t sh, int64_t sl, float scale, int chunk,
+                                                          int htiles, int q_bf16) {
+  using SH = BlockScoreShape<D, NH>;
+  constexpr int NL = SH::NL, RND = SH::RND;
+  const int task = blockIdx.y;
+  const int ht = task % htiles, bg = task / htiles;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % SH::LPR, grp = lane / SH::LPR;
+  const int h0 = g * G + ht * NH;
+  const int nh = min(NH, g * G + G - h0);
+  float qf[NH][NL][4];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int64_t at = (int64_t)(b * Hq + h0 + h) * D + 4 * (sub + 8 * j);
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (h < nh) {
+        if (q_bf16) {
+          const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(qv) + at);
+          v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x); v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
+        } else {
+          const uint4 x = ld16(reinterpret_cast<const float*>(qv) + at);
+          v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y);
+          v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[h][j][e] = v[e];
+    }
+  const float* kb = means + (int64_t)b * sb + (int64_t)g * sh;
+  const int p0 = blockIdx.x * chunk, p1 = min(p0 + chunk, nrows);
+  for (int base = p0 + wave * 8 * RND; base < p1; base += SH::ROWS) {
+    uint4 raw[RND][NL];
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+      const int row = base + 8 * r + grp;
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        raw[r][j] = row < p1 ? ld16_stream(kb + (int64_t)row * sl + 4 * (sub + 8 * j)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+      float part[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float x = 0.f;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          x = fmaf(qf[h][j][0], __uint_as_float(raw[r][j].x), x);
+          x = fmaf(qf[h][j][1], __uint_as_float(raw[r][j].y), x);
+          x = fmaf(qf[h][j][2], __uint_as_float(raw[r][j].z), x);
+          x = fmaf(qf[h][j][3], __uint_as_float(raw[r][j].w), x);
+        }
+        part[h] = x;
+      }
+#pragma unroll
+      for (int o = 1; o < SH::LPR; o <<= 1)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) part[h] += __shfl_xor(part[h], o, kWave);
+      const int row = base + 8 * r + grp;
+      if (row < p1) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          if (h == sub && h < nh) S[(int64_t)(b * Hq + h0 + h) * nrows + row] = part[h] * scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Wave dot-reduction scores for fp32 or bf16 rows, NH query heads per task.
 // A row of D elements is 16*LPR bytes: LPR lanes load 16 B each, RPW = 64/LPR
 // rows per wave load. Each lane keeps its 16-byte slice of q for every head,
@@ -1097,12 +1194,44 @@ static void launch_vec(const ScoreArgs& a, hipStream_t st) {
   }
 }
 
+template <int D, int NH>
+static void launch_block_nh(const ScoreArgs& a, hipStream_t st) {
+  using SH = BlockScoreShape<D, NH>;
+  const int htiles = (a.G + NH - 1) / NH;
+  const int64_t tasks = (int64_t)a.B * a.Hkv * htiles;
+  int chunk = SH::ROWS;  // one pass per workgroup, unless that makes far more workgroups than the chip holds
+  while (tasks * ((a.nrows + chunk - 1) / chunk) > 2048) chunk *= 2;
+  dim3 grid((a.nrows + chunk - 1) / chunk, (unsigned)tasks);
+  hipLaunchKernelGGL((score_block_kernel<D, NH>), grid, dim3(256), 0, st, a.q, (const float*)a.keys, a.scores, a.Hq,
+                     a.Hkv, a.G, a.nrows, a.sb, a.sh, a.sl, a.scale, chunk, htiles, a.q_bf16);
+}
+
+template <int D>
+static void launch_block_d(const ScoreArgs& a, hipStream_t st) {
+  if (a.G > 4) launch_block_nh<D, 8>(a, st);
+  else if (a.G > 2) launch_block_nh<D, 4>(a, st);
+  else if (a.G > 1) launch_block_nh<D, 2>(a, st);
+  else launch_block_nh<D, 1>(a, st);
+}
+
+static void launch_block(const ScoreArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 64: launch_block_d<64>(a, st); break;
+    case 128: launch_block_d<128>(a, st); break;
+    default: launch_block_d<256>(a, st); break;
+  }
+}
+
 bool score_uses_mfma(int dtype_bf16, int G) { return dtype_bf16 && G >= 2 && G <= 16; }
 
 void launch_score_dense(const ScoreArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return;
   if (a.M > 1) {
     launch_score_mq(a, st);
+    return;
+  }
+  if (a.block) {
+    launch_block(a, st);
     return;
   }
   if (score_uses_mfma(a.bf16, a.G)) {
