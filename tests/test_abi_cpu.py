@@ -102,8 +102,13 @@ def test_select_checks():
     assert _select(n_rows=2, row_len=1 << 20, stride=1 << 20, k=2048, idx=FAKE * 4) == tka.TKA_ERR_WORKSPACE
     assert _select(n_rows=2, row_len=1 << 20, stride=1 << 20, k=2048, idx=FAKE * 4, ws=FAKE * 8,
                    ws_bytes=need - 1) == tka.TKA_ERR_WORKSPACE
-    # many rows: one workgroup per row, no scratch
-    assert tka.topk_select_workspace_size(1024, 131072, 4096) == 0
+    # many long rows: samples, thresholds, flags and candidate lists (3 k' pairs a row at most 12288)
+    need = tka.topk_select_workspace_size(1024, 131072, 4096)
+    assert 1024 * 12288 * 8 <= need < 1024 * 12288 * 8 + (16 << 20)
+    assert _select(n_rows=1024, row_len=131072, stride=131072, k=4096, idx=FAKE * 64) == tka.TKA_ERR_WORKSPACE
+    # short rows: one workgroup (or wave) per row, no scratch
+    assert tka.topk_select_workspace_size(1024, 8192, 256) == 0
+    assert tka.topk_select_workspace_size(1024, 131072, 32768) == 0  # k' > n/8: the row kernel
     # few rows split over workgroups: the finish's table of segment offsets bounds the row length
     far = 1 << 44
     assert _select(n_rows=2, row_len=20_000_000, stride=20_000_000, k=2048, idx=far) == tka.TKA_ERR_UNSUPPORTED

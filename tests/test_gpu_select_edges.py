@@ -156,3 +156,35 @@ def test_select_short_rows_strided():
         say(f"[select short strided] k={k}")
         idx, _ = m.topk_select(xt, k, row_len=n, row_stride=2100)
         assert np.array_equal(idx.cpu().numpy(), orc.select(full[:, :n], k))
+
+
+def test_select_many_long_rows_hot_samples_and_strides():
+    """Many long rows take the candidate select (samples -> per-row threshold -> one collecting
+    pass over all rows -> select among the candidates). Scores planted high exactly on the sampled
+    runs (32 runs of 64 starting at j n / 32) put the threshold above the k'-th score, so those rows
+    have too few candidates and take the full row select; a padded stride, rows starting off 16-byte
+    alignment (the row kernel instead) and exactly 64 rows are covered too. Bit-exact throughout."""
+    m = tka()
+    rng = np.random.default_rng(41)
+    n_rows, n, k = 96, 32768, 2048
+    x = rng.standard_normal((n_rows, n)).astype(np.float32)
+    for r in range(0, n_rows, 3):  # every third row: the sampled runs hold the largest values
+        for j in range(32):
+            at = j * n // 32
+            x[r, at:at + 64] = 50.0 + rng.random(64).astype(np.float32)
+    say("[select many rows] hot samples")
+    idx, sel = m.topk_select(torch.from_numpy(x).cuda(), k)
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, orc.select(x, k))
+    rows = np.arange(n_rows)[:, None]
+    assert np.array_equal(sel.cpu().numpy().view(np.uint32), x[rows, gi].view(np.uint32))
+
+    flat = torch.from_numpy(rng.standard_normal(64 * (n + 8) + 8).astype(np.float32)).cuda()
+    base = flat[:64 * (n + 8)].reshape(64, n + 8)
+    say("[select many rows] stride n + 8, 64 rows")
+    idx, _ = m.topk_select(base, 1000, row_len=n, row_stride=n + 8)
+    assert np.array_equal(idx.cpu().numpy(), orc.select(base.cpu().numpy()[:, :n].copy(), 1000))
+    say("[select many rows] rows 4 bytes off alignment")
+    view = flat[1:1 + 64 * (n + 8)].reshape(64, n + 8)
+    idx, _ = m.topk_select(view, 1000, row_len=n, row_stride=n + 8)
+    assert np.array_equal(idx.cpu().numpy(), orc.select(view.cpu().numpy()[:, :n].copy(), 1000))

@@ -410,7 +410,7 @@ DecodeLayout decode_layout(const tka_problem* p) {
     o += al256(sizeof(float) * (size_t)d.rows * (d.len > 0 ? d.len : 1));
   d.ic = d.shared ? indexer_cand_plan(p->seq_len, d.k) : IndexerCandPlan{};
   d.sel_ws = o;
-  if (!d.ic.on) o += al256(select_workspace_bytes(d.rows, d.len, d.k));
+  if (!d.ic.on && !d.pf.on) o += al256(select_workspace_bytes(d.rows, d.len, d.k));  // the row select's scratch
   d.idx = o;
   o += al256(sizeof(int32_t) * (size_t)d.rows * d.k);
   d.selv = o;

@@ -1410,6 +1410,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// Many long rows of a score array: the fused exact step's candidate select
+// run over stored scores. 32 runs of 64 consecutive scores per row give each
+// row a threshold T a few standard deviations below its k'-th score
+// (prefilter_threshold_kernel, which also clears the row's count and flags);
+// one pass over every row on the whole chip keeps the (score bits, position)
+// pairs with key >= key(T) (rows_collect_kernel); prefilter_finish_kernel
+// selects the k' first among them and flags the rows whose candidates cannot
+// hold the answer (fewer than k', more than the capacity, a crowded tie bin),
+// which select_rows_kernel then selects over the whole row.
+// ---------------------------------------------------------------------------
+constexpr int RC_RUNS = 32, RC_NSAMP = RC_RUNS * 64;
+constexpr int RC_CHUNK = 16384;  // positions per collect workgroup: 16 float4 loads per thread
+
+__global__ __launch_bounds__(256) void rows_sample_kernel(const float* __restrict__ S, int n, int64_t stride,
+                                                          float* __restrict__ samp) {
+  const int64_t row = blockIdx.x;
+  const float* s = S + row * stride;
+  float v[RC_NSAMP / 256];
+#pragma unroll
+  for (int u = 0; u < RC_NSAMP / 256; ++u) {
+    const int i = u * 256 + threadIdx.x, run = i >> 6;
+    v[u] = s[(int64_t)run * n / RC_RUNS + (i & 63)];
+  }
+#pragma unroll
+  for (int u = 0; u < RC_NSAMP / 256; ++u) samp[row * RC_NSAMP + u * 256 + threadIdx.x] = v[u];
+}
+
+constexpr int RC_STAGE = 1024;  // pairs a wave compacts in LDS before writing them out
+
+__global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restrict__ S, int n, int64_t stride,
+                                                           const float* __restrict__ Tv, uint2* __restrict__ cpair,
+                                                           uint32_t* __restrict__ cnt, int capg) {
+  constexpr int U = RC_CHUNK / (256 * 4);
+  __shared__ uint2 stage_all[SW][RC_STAGE];
+  const int64_t row = blockIdx.y;
+  const float* s = S + row * stride;
+  const uint32_t T = score_key(Tv[row]);
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int p0 = blockIdx.x * RC_CHUNK;
+  float4 x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;  // n is a multiple of 4: e < n covers all four
+    uint4 r4 = make_uint4(0, 0, 0, 0);
+    if (e < n) r4 = ld16_stream(s + e);
+    x[u] = make_float4(__uint_as_float(r4.x), __uint_as_float(r4.y), __uint_as_float(r4.z), __uint_as_float(r4.w));
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
+    const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c += (e < n && score_key(v[j]) >= T) ? 1u : 0u;
+  }
+  // the wave's pairs go to one reserved run of the row's list
+  const uint32_t incl = wave_incl_scan(c);
+  const uint32_t tot = (uint32_t)__shfl((int)incl, 63, kWave);
+  if (tot == 0) return;  // wave-uniform
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(&cnt[row], tot);
+  base = (uint32_t)__shfl((int)base, 0, kWave);
+  uint2* out = cpair + row * (int64_t)capg;
+  const bool staged = tot <= (uint32_t)RC_STAGE;  // wave-uniform
+  uint2* stage = stage_all[w];
+  uint32_t slot = incl - c;  // this lane's first pair within the wave's run
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
+    const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e < n && score_key(v[j]) >= T) {
+        const uint2 pr = make_uint2(__float_as_uint(v[j]), (uint32_t)(e + j));
+        if (staged) stage[slot] = pr;
+        else if (base + slot < (uint32_t)capg) out[base + slot] = pr;  // a crowded wave: direct stores
+        ++slot;
+      }
+  }
+  if (!staged) return;
+  lds_wave_sync();
+  for (uint32_t i = lane; i < tot && base + i < (uint32_t)capg; i += 64) out[base + i] = stage[i];
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static bool use_split(int64_t n_rows, int n) { return n_rows < 128 && n > 4 * CHUNK; }
@@ -1424,6 +1509,45 @@ static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct SplitLayout {
   size_t ghist, cbits, cpos, ccount, catb, catp, total;
 };
+
+struct RowCandPlan {
+  bool on = false;
+  int r = 0, capg = 0;
+};
+
+// Rows the candidate select takes: many (the split mode takes few), long, k' <= n/8 and within the
+// finish's limits, n a multiple of 4 (float4 loads; the row stride and base are checked at launch)
+static RowCandPlan row_cand_plan(int64_t n_rows, int n, int k) {
+  RowCandPlan pl;
+  const int kk = std::min(k, n);
+  if (use_split(n_rows, n) || n_rows < 64 || n < 16384 || n > 262144 || (n & 3) || kk < 1 || (int64_t)kk * 8 > n ||
+      kk > PF_KMAX)
+    return pl;
+  const double E = (double)kk * RC_NSAMP / n;
+  pl.r = std::min(RC_NSAMP, (int)std::ceil(E + 4.5 * std::sqrt(E)) + 2);
+  const double expect = (double)n * (pl.r + 4.0 * std::sqrt((double)pl.r)) / RC_NSAMP;
+  pl.capg = (int)std::max(3.0 * kk, std::ceil(expect));
+  if (pl.capg > 12288) return RowCandPlan{};
+  pl.on = true;
+  return pl;
+}
+
+struct RowCandLayout {
+  size_t samp, T, cnt, flag, gflag, cpair, total;
+};
+
+static RowCandLayout row_cand_layout(int64_t n_rows, const RowCandPlan& pl) {
+  RowCandLayout L;
+  size_t o = 0;
+  L.samp = o; o += al256(sizeof(float) * (size_t)n_rows * RC_NSAMP);
+  L.T = o; o += al256(sizeof(float) * (size_t)n_rows);
+  L.cnt = o; o += al256(sizeof(uint32_t) * (size_t)n_rows);
+  L.flag = o; o += al256(sizeof(uint32_t) * (size_t)n_rows);
+  L.gflag = o; o += al256(sizeof(uint32_t) * (size_t)n_rows);
+  L.cpair = o; o += al256(sizeof(uint2) * (size_t)n_rows * pl.capg);
+  L.total = o;
+  return L;
+}
 
 static SplitLayout split_layout(int64_t n_rows, int n) {
   const int64_t nch = (n + CHUNK - 1) / CHUNK;
@@ -1959,9 +2083,9 @@ __global__ __launch_bounds__(256) void adaptive_tau_kernel(const float* __restri
 }
 
 size_t select_workspace_bytes(int64_t n_rows, int n, int k) {
-  (void)k;
-  if (!use_split(n_rows, n)) return 0;
-  return split_layout(n_rows, n).total;
+  if (use_split(n_rows, n)) return split_layout(n_rows, n).total;
+  const RowCandPlan pc = row_cand_plan(n_rows, n, k);
+  return pc.on ? row_cand_layout(n_rows, pc).total : 0;
 }
 
 // Let a kernel take dynamic LDS up to the device limit minus its own static
@@ -2064,6 +2188,25 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
     return;
   }
   if (!use_split(a.n_rows, a.n)) {
+    const RowCandPlan pc = row_cand_plan(a.n_rows, a.n, a.k);
+    if (pc.on && ws && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && (a.stride & 3) == 0) {
+      const RowCandLayout L = row_cand_layout(a.n_rows, pc);
+      char* base = static_cast<char*>(ws);
+      float* samp = reinterpret_cast<float*>(base + L.samp);
+      float* T = reinterpret_cast<float*>(base + L.T);
+      uint32_t* cnt = reinterpret_cast<uint32_t*>(base + L.cnt);
+      uint32_t* flag = reinterpret_cast<uint32_t*>(base + L.flag);
+      uint32_t* gflag = reinterpret_cast<uint32_t*>(base + L.gflag);
+      uint2* cpair = reinterpret_cast<uint2*>(base + L.cpair);
+      hipLaunchKernelGGL(rows_sample_kernel, dim3((unsigned)a.n_rows), dim3(256), 0, st, a.scores, a.n, a.stride,
+                         samp);
+      launch_prefilter_threshold(samp, a.n_rows, RC_NSAMP, pc.r, T, cnt, flag, gflag, 1, 1, 1, st);
+      hipLaunchKernelGGL(rows_collect_kernel, dim3((unsigned)((a.n + RC_CHUNK - 1) / RC_CHUNK), (unsigned)a.n_rows),
+                         dim3(256), 0, st, a.scores, a.n, a.stride, (const float*)T, cpair, cnt, pc.capg);
+      launch_prefilter_finish(cpair, cnt, T, pc.capg, a.n_rows, a.n, a.k, 1, 1, 1, a.idx, a.sel, flag, gflag, st);
+      launch_select_rows_flagged(a, flag, nullptr, st);  // rows whose candidates cannot hold the answer
+      return;
+    }
     size_t lds;
     const int capw = rows_capw(a.n, a.k, &lds);
     hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride,
