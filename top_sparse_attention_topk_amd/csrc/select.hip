@@ -1421,7 +1421,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // which select_rows_kernel then selects over the whole row.
 // ---------------------------------------------------------------------------
 constexpr int RC_RUNS = 32, RC_NSAMP = RC_RUNS * 64;
-constexpr int RC_CHUNK = 16384;  // positions per collect workgroup: 16 float4 loads per thread
+#ifndef TKA_RC_CHUNK
+#define TKA_RC_CHUNK 16384
+#endif
+constexpr int RC_CHUNK = TKA_RC_CHUNK;  // positions per collect workgroup
+constexpr int RC_ROUND = 16384;        // positions per round of it: 16 float4 loads per thread
+static_assert(RC_CHUNK % RC_ROUND == 0, "whole rounds per chunk");
 
 __global__ __launch_bounds__(256) void rows_sample_kernel(const float* __restrict__ S, int n, int64_t stride,
                                                           float* __restrict__ samp) {
@@ -1442,56 +1447,59 @@ constexpr int RC_STAGE = 1024;  // pairs a wave compacts in LDS before writing t
 __global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restrict__ S, int n, int64_t stride,
                                                            const float* __restrict__ Tv, uint2* __restrict__ cpair,
                                                            uint32_t* __restrict__ cnt, int capg) {
-  constexpr int U = RC_CHUNK / (256 * 4);
+  constexpr int U = RC_ROUND / (256 * 4);
   __shared__ uint2 stage_all[SW][RC_STAGE];
   const int64_t row = blockIdx.y;
   const float* s = S + row * stride;
   const uint32_t T = score_key(Tv[row]);
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  const int p0 = blockIdx.x * RC_CHUNK;
-  float4 x[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;  // n is a multiple of 4: e < n covers all four
-    uint4 r4 = make_uint4(0, 0, 0, 0);
-    if (e < n) r4 = ld16_stream(s + e);
-    x[u] = make_float4(__uint_as_float(r4.x), __uint_as_float(r4.y), __uint_as_float(r4.z), __uint_as_float(r4.w));
-  }
-  uint32_t c = 0;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
-    const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c += (e < n && score_key(v[j]) >= T) ? 1u : 0u;
-  }
-  // the wave's pairs go to one reserved run of the row's list
-  const uint32_t incl = wave_incl_scan(c);
-  const uint32_t tot = (uint32_t)__shfl((int)incl, 63, kWave);
-  if (tot == 0) return;  // wave-uniform
-  uint32_t base = 0;
-  if (lane == 0) base = atomicAdd(&cnt[row], tot);
-  base = (uint32_t)__shfl((int)base, 0, kWave);
   uint2* out = cpair + row * (int64_t)capg;
-  const bool staged = tot <= (uint32_t)RC_STAGE;  // wave-uniform
   uint2* stage = stage_all[w];
-  uint32_t slot = incl - c;  // this lane's first pair within the wave's run
+  const int c0 = blockIdx.x * RC_CHUNK, c1 = min(n, c0 + RC_CHUNK);
+  for (int p0 = c0; p0 < c1; p0 += RC_ROUND) {
+    float4 x[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
-    const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    for (int u = 0; u < U; ++u) {
+      const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;  // n is a multiple of 4: e < n covers all four
+      uint4 r4 = make_uint4(0, 0, 0, 0);
+      if (e < c1) r4 = ld16_stream(s + e);
+      x[u] = make_float4(__uint_as_float(r4.x), __uint_as_float(r4.y), __uint_as_float(r4.z), __uint_as_float(r4.w));
+    }
+    uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (e < n && score_key(v[j]) >= T) {
-        const uint2 pr = make_uint2(__float_as_uint(v[j]), (uint32_t)(e + j));
-        if (staged) stage[slot] = pr;
-        else if (base + slot < (uint32_t)capg) out[base + slot] = pr;  // a crowded wave: direct stores
-        ++slot;
-      }
+    for (int u = 0; u < U; ++u) {
+      const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
+      const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c += (e < c1 && score_key(v[j]) >= T) ? 1u : 0u;
+    }
+    // the wave's pairs of the round go to one reserved run of the row's list
+    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t tot = (uint32_t)__shfl((int)incl, 63, kWave);
+    if (tot == 0) continue;  // wave-uniform
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&cnt[row], tot);
+    base = (uint32_t)__shfl((int)base, 0, kWave);
+    const bool staged = tot <= (uint32_t)RC_STAGE;  // wave-uniform
+    uint32_t slot = incl - c;  // this lane's first pair within the wave's run
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
+      const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e < c1 && score_key(v[j]) >= T) {
+          const uint2 pr = make_uint2(__float_as_uint(v[j]), (uint32_t)(e + j));
+          if (staged) stage[slot] = pr;
+          else if (base + slot < (uint32_t)capg) out[base + slot] = pr;  // a crowded wave: direct stores
+          ++slot;
+        }
+    }
+    if (!staged) continue;
+    lds_wave_sync();
+    for (uint32_t i = lane; i < tot && base + i < (uint32_t)capg; i += 64) out[base + i] = stage[i];
+    lds_wave_sync();  // the stage's reads are done before the next round writes it
   }
-  if (!staged) return;
-  lds_wave_sync();
-  for (uint32_t i = lane; i < tot && base + i < (uint32_t)capg; i += 64) out[base + i] = stage[i];
 }
 
 // ---------------------------------------------------------------------------
