@@ -15,11 +15,13 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 // Order-preserving key of an fp32 score: larger key <=> ranks higher.
 // -0 and +0 share one key; every NaN maps to key 0, below -inf (0x007fffff).
+// Integer selects only (no branch): negative scores flip every bit, the rest
+// set the sign bit.
 __device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f != f) return 0u;
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t z = u == 0x80000000u ? 0u : u;
+  const uint32_t key = z ^ ((uint32_t)((int32_t)z >> 31) | 0x80000000u);
+  return (u & 0x7fffffffu) > 0x7f800000u ? 0u : key;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -81,15 +83,29 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Inclusive prefix sum across the 64 lanes.
+// Inclusive prefix sum across the 64 lanes, on DPP lane moves (no LDS crossbar): Kogge-Stone
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes (lanes shifted in from outside the row add
+// 0), then row 15's total is broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
   return v;
+}
+
+// Maximum across the 64 lanes (wave-uniform result): DPP swaps inside quads, half rows and rows
+// leave each row's maximum in all its lanes; the four rows are then read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Workgroups are dispatched to the 8 XCDs (each with its own L2) in turn by

@@ -424,6 +424,10 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 // free stage slots per row below which a flush is scheduled before the next tile (a tile that
 // would overflow anyway is preceded by an immediate flush)
 constexpr int SS_GUARD = TKA_SS_GUARD;
+#ifndef TKA_SS_WPC
+#define TKA_SS_WPC 2
+#endif
+constexpr int SS_WPC = TKA_SS_WPC;  // workgroups per CU
 
 template <int D, int NTT>
 __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* __restrict__ q,
@@ -1080,15 +1084,15 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
   const int M = a.M > 1 ? a.M : 1;  // the caller keeps M <= 4
   if (M > 1 && TKA_SHARED_SCAN) {
-    // two tile buffers and four wave stages sized to fit two workgroups per CU
+    // two tile buffers and four wave stages sized to fit SS_WPC workgroups per CU
     const size_t tiles = (size_t)2 * 32 * (D * 2 + 16);
     // stages for the scoring waves only, 16 rows each: ceil(M G / 16) blocks, two waves per block
     // (one per tile half) when there are at most two blocks
     const int ncb = (M * a.G + 15) / 16;
     const int nst = ncb <= 2 ? 2 * ncb : ncb;
-    const int S2 = (int)((((size_t)device_lds_limit() / 2 - tiles - 256) / (8 * (size_t)nst) - 64) / 16);
+    const int S2 = (int)((((size_t)device_lds_limit() / SS_WPC - tiles - 256) / (8 * (size_t)nst) - 64) / 16);
     const size_t lds2 = tiles + (size_t)nst * (16 * S2 + 64) * 8;
-    int64_t g2 = (int64_t)device_cus() * 2;
+    int64_t g2 = (int64_t)device_cus() * SS_WPC;
     if (g2 > ntiles) g2 = ntiles;
     if (ncb <= 2) {
       ensure_dynamic_lds((const void*)score_cand_shared_kernel<D, 1>, lds2);

@@ -842,7 +842,6 @@ struct PfSmem {
   int32_t spos[PF_STASH];
   uint32_t scnt;
   uint32_t red[PF_NW];
-  uint32_t tval;
 };
 // the finish emits up to PF_KMAX kept pairs through the spent histogram and stash keys
 constexpr int PF_KMAX = 4096;
@@ -977,12 +976,26 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
   if (lane == 0) T[row] = key_value(result);
 }
 
+// An empty asm that takes v in a VGPR and may change it: the value is materialised here, and
+// nothing computed from it before is reused after (so its register is the only one kept live).
+template <typename T>
+__device__ __forceinline__ void pin_vgpr(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Exact top-k of a row from its (unordered) candidates, whose keys are all
 // >= T[row]. One relative-digit histogram finds the bin holding the k'-th
 // key; its few elements are ranked one by one (key, then lower position
 // first). Kept positions are marked in an LDS bitmap over the row and
 // popcount prefix sums give each its output slot in ascending position
 // order. Dynamic LDS: 2 * ceil(n/32) words (kept bitmap, prefix counts).
+// Thread t holds candidates t + PF_T j, j < PF_RC, with their keys computed
+// once. The valid elements of a wave are a prefix of j (only the last can be
+// valid on part of the wave), so each per-element pass stops at the wave's
+// count and takes the partial element without a branch: a lane's invalid
+// element adds to a dummy bin of its own and ORs zero into the bitmap. (With
+// 16 waves per row and two rows per CU, the exec-mask branches of a plain
+// per-element loop made these passes scalar-issue bound.)
 __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(const uint2* __restrict__ cpair,
                                                                 const uint32_t* __restrict__ cnt,
                                                                 const float* __restrict__ Tv, int capg, int n,
@@ -993,9 +1006,10 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
                                                                 uint32_t* __restrict__ group_flag) {
   __shared__ SelSmem sm;
   __shared__ PfSmem ps;
-  extern __shared__ uint32_t dyn[];
+  extern __shared__ uint4 dyn4[];  // 16-byte aligned
+  uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn4);
   const int64_t row = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
   const int kk = min(k, n);
   int32_t* oidx = idx + row * k;
   float* osel = sel ? sel + row * k : nullptr;
@@ -1011,31 +1025,37 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
     const u32x2_t* cw = reinterpret_cast<const u32x2_t*>(cpair + row * capg);
     const uint32_t T0 = score_key(Tv[row]);
     // the thread's candidates, every load of the batch in flight together (indices past the
-    // count re-read the last candidate and are masked below)
-    uint32_t bits[PF_RC];
+    // count re-read the last candidate and are marked invalid: position -1, key T0)
+    u32x2_t x[PF_RC];
+#pragma unroll
+    for (int j = 0; j < PF_RC; ++j) x[j] = cw[min((uint32_t)(t + PF_T * j), nc - 1u)];  // (score bits, position)
+    // the scores are kept as their keys, whose inverse gives back every score's bits except a
+    // NaN's payload and the sign of -0 (keys 0 and 0x80000000: those are re-read at emission)
+    uint32_t key[PF_RC];
     int32_t pos[PF_RC];
 #pragma unroll
     for (int j = 0; j < PF_RC; ++j) {
-      const u32x2_t x = cw[min((uint32_t)(t + PF_T * j), nc - 1u)];  // (score bits, position)
-      bits[j] = x[0];
-      pos[j] = (int32_t)x[1];
+      const bool ok = (uint32_t)(t + PF_T * j) < nc;
+      const uint32_t kv = score_key(__uint_as_float(x[j][0]));  // computed for every lane: a select, no branch
+      pos[j] = ok ? (int32_t)x[j][1] : -1;
+      key[j] = ok ? kv : T0;
+      pin_vgpr(pos[j]);
+      pin_vgpr(key[j]);
     }
-    auto key_of = [&](int j) { return score_key(__uint_as_float(bits[j])); };
     const int words = (n + 31) >> 5;
     uint32_t* bm = dyn;
     uint32_t* pre = dyn + words;
     // one barrier for the cleared bitmap and histogram and the waves' maxima (every key is >= T0,
     // so the candidates' range is [T0, max])
-    for (int i = t; i < words; i += PF_T) bm[i] = 0u;
-    for (int i = t; i < NB0; i += PF_T) sm.hist[i] = 0u;
+    // 16-byte stores (the dynamic area holds whole quads: up to three words of pre are cleared too)
+    for (int i = t; i < (words + 3) / 4; i += PF_T) dyn4[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = t; i < NB0 / 4; i += PF_T) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (t == 0) ps.scnt = 0;
     uint32_t mx = T0;
 #pragma unroll
-    for (int j = 0; j < PF_RC; ++j)
-      if ((uint32_t)(t + PF_T * j) < nc) mx = max(mx, key_of(j));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    if ((t & 63) == 0) ps.red[t >> 6] = mx;
+    for (int j = 0; j < PF_RC; ++j) mx = max(mx, key[j]);
+    mx = wave_max_u32(mx);
+    if (lane == 0) ps.red[t >> 6] = mx;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PF_NW; ++i) mx = max(mx, ps.red[i]);
@@ -1043,24 +1063,30 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
     const int shift = span >= 4096u ? (32 - __clz(span)) - 12 : 0;  // span >> shift < 4096
 #pragma unroll
     for (int j = 0; j < PF_RC; ++j)
-      if ((uint32_t)(t + PF_T * j) < nc) atomicAdd(&sm.hist[(key_of(j) - T0) >> shift], 1u);
+      if (pos[j] >= 0) atomicAdd(&sm.hist[(key[j] - T0) >> shift], 1u);
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PF_RC; ++j) pin_vgpr(key[j]);  // digits recomputed below, not held
     find_bin_t<PF_NW>(sm.hist, NB0, (uint32_t)kk, sm);
-    const uint32_t bin = sm.res[0], need = (uint32_t)kk - sm.res[1];
+    // (bin and rank in SGPRs: no LDS wait inside the passes below)
+    const uint32_t bin = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.res[0]);
+    const uint32_t need = (uint32_t)kk - (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.res[1]);
     // keys above the critical bin are kept; the bin's elements go to the stash
 #pragma unroll
     for (int j = 0; j < PF_RC; ++j) {
-      const uint32_t e = t + PF_T * j;
-      if (e >= nc) continue;
-      const uint32_t d = (key_of(j) - T0) >> shift;
-      if (d < bin) continue;
       const int32_t p = pos[j];
-      if (d > bin) {
-        atomicOr(&bm[p >> 5], 1u << (p & 31));
-      } else {
-        const uint32_t slot = atomicAdd(&ps.scnt, 1u);
-        if (slot < PF_STASH) {
-          ps.skey[slot] = key_of(j);
+      const uint32_t d = (key[j] - T0) >> shift;
+      if (p >= 0 && d > bin) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      const bool eq = p >= 0 && d == bin;
+      const uint64_t me = ballot(eq);
+      if (__builtin_expect(me != 0, 0)) {  // wave-uniform: one reservation for the wave's stash entries
+        const int first = (int)__builtin_ctzll(me);
+        uint32_t base = 0;
+        if (lane == first) base = atomicAdd(&ps.scnt, (uint32_t)__builtin_popcountll(me));
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+        const uint32_t slot = base + (uint32_t)count_below(me);
+        if (eq && slot < PF_STASH) {
+          ps.skey[slot] = key[j];
           ps.spos[slot] = p;
         }
       }
@@ -1081,10 +1107,10 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
       uint32_t loc = 0;
       for (int i = 0; i < per; ++i) {
         const int wd = t * per + i;
-        if (wd < words) loc += __popc(bm[wd]);
+        loc += wd < words ? __popc(bm[min(wd, words - 1)]) : 0u;
       }
       uint32_t total;
-      uint32_t run = block_incl_scan_t<PF_NW>(loc, sm, &total) - loc;
+      uint32_t run = block_incl_scan_t<PF_NW, SelSmem, false>(loc, sm, &total) - loc;  // closed by the barrier below
       for (int i = 0; i < per; ++i) {
         const int wd = t * per + i;
         if (wd < words) {
@@ -1094,20 +1120,23 @@ __global__ __launch_bounds__(PF_T, TKA_PF_MINW) void prefilter_finish_kernel(con
       }
       __syncthreads();
       // the kept pairs to their slots in LDS (the histogram and the stash are spent: k' <= 4096
-      // entries each), then out with 16-byte stores in slot order
+      // entries each), then out with 16-byte stores in slot order; a candidate is kept exactly
+      // when its bit is set (each position is a candidate once)
       uint32_t* lidx = sm.hist;
       uint32_t* lsel = ps.skey;  // skey and sidx: 2 * PF_STASH contiguous entries
 #pragma unroll
       for (int j = 0; j < PF_RC; ++j) {
-        const uint32_t e = t + PF_T * j;
-        if (e >= nc || ((key_of(j) - T0) >> shift) < bin) continue;
         const int32_t p = pos[j];
-        const uint32_t word = bm[p >> 5];
-        if (!((word >> (p & 31)) & 1u)) continue;
-        const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u));
+        const uint32_t kj = key[j];
+        if (p < 0 || ((kj - T0) >> shift) < bin) continue;
+        const uint32_t word = bm[p >> 5], bit = (uint32_t)p & 31u;
+        if (!((word >> bit) & 1u)) continue;
+        const uint32_t slot = pre[p >> 5] + __popc(word & ((1u << bit) - 1u));
         if (slot < (uint32_t)kk) {
+          uint32_t sb = (kj & 0x80000000u) ? (kj & 0x7fffffffu) : ~kj;  // the key's inverse
+          if ((kj & 0x7fffffffu) == 0u) sb = cw[t + PF_T * j][0];          // a NaN or a zero: its own bits
           lidx[slot] = (uint32_t)p;
-          lsel[slot] = bits[j];
+          lsel[slot] = sb;
         }
       }
       __syncthreads();
@@ -2296,7 +2325,8 @@ void launch_prefilter_repair(const RepairArgs& a, hipStream_t st) {
   }
 }
 
-static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((n + 31) / 32); }
+// kept bitmap and prefix counts, ceil(n/32) words each, rounded up to whole 16-byte quads
+static size_t prefilter_finish_lds(int n) { return sizeof(uint32_t) * 2 * (size_t)((((n + 31) / 32) + 3) & ~3); }
 
 void launch_prefilter_finish(const uint2* cpair, const uint32_t* cnt, const float* T,
                              int capg, int64_t n_rows, int n, int k, int G, int Hq, int M, int32_t* idx, float* sel,

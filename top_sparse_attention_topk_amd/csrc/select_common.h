@@ -13,7 +13,7 @@ constexpr int SW = 4;    // waves per workgroup
 constexpr int NB0 = 4096;
 
 template <int NB>
-struct SelSmemT {
+struct alignas(16) SelSmemT {
   static constexpr int kBins = NB;
   uint32_t hist[NB];
   uint32_t scan[16];
@@ -25,7 +25,9 @@ struct SelSmemT {
 };
 using SelSmem = SelSmemT<NB0>;
 
-template <int NW, typename SM>
+// Inclusive scan over the workgroup (NW waves). TRAIL = false leaves out the closing barrier
+// that lets sm.scan be written again: for callers that pass another barrier first.
+template <int NW, typename SM, bool TRAIL = true>
 __device__ uint32_t block_incl_scan_t(uint32_t v, SM& sm, uint32_t* total) {
   const int w = threadIdx.x >> 6, l = lane_id();
   uint32_t x = wave_incl_scan(v);
@@ -37,7 +39,7 @@ __device__ uint32_t block_incl_scan_t(uint32_t v, SM& sm, uint32_t* total) {
     off += (i < w) ? sm.scan[i] : 0u;
     tot += sm.scan[i];
   }
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   *total = tot;
   return x + off;
 }
@@ -51,7 +53,7 @@ __device__ void find_bin_t(const uint32_t* hist, int nb, uint32_t need, SM& sm) 
   uint32_t s = 0;
   for (int i = 0; i < per; ++i) s += hist[t * per + i];
   uint32_t tot;
-  const uint32_t incl = block_incl_scan_t<NW>(s, sm, &tot);
+  const uint32_t incl = block_incl_scan_t<NW, SM, false>(s, sm, &tot);  // the barrier below closes it
   const uint32_t above = tot - incl;
   if (above < need && need <= above + s) {
     uint32_t acc = above;
