@@ -96,6 +96,42 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// gfx950 lane swaps between 16-lane rows (v_permlane16_swap: x[0] holds rows 0,0,2,2 and x[1]
+// rows 1,1,3,3 of v) and between wave halves (v_permlane32_swap: x[0] holds the low half twice,
+// x[1] the high half). Plain VALU moves, no LDS crossbar.
+__device__ __forceinline__ void rows_swap16(uint32_t v, uint32_t& even, uint32_t& odd) {
+  const auto x = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  even = x[0];
+  odd = x[1];
+}
+__device__ __forceinline__ void halves_swap32(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto x = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = x[0];
+  hi = x[1];
+}
+// v + v of lane l ^ 16 and v + v of lane l ^ 32 (the same bits: the two terms commute)
+__device__ __forceinline__ float sum_xor16(float v) {
+  uint32_t e, o;
+  rows_swap16(__float_as_uint(v), e, o);
+  return __uint_as_float(e) + __uint_as_float(o);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  uint32_t lo, hi;
+  halves_swap32(__float_as_uint(v), lo, hi);
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
+// Minimum across the 64 lanes, as wave_max_u32 below.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+
 // Maximum across the 64 lanes (wave-uniform result): DPP swaps inside quads, half rows and rows
 // leave each row's maximum in all its lanes; the four rows are then read from lanes 0, 16, 32, 48.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -8,7 +8,8 @@
 // 32*(l/32)+[0,32)), B = 64 dims x 32 positions (lane l: position l%32, same
 // dims), C[head][pos]: lane l holds position l%32 for heads 8a + 4*(l/32) + c.
 // ReLU and the weighted head sum stay in registers; lanes l and l^32 add
-// their halves of the head sum, so both hold the position's score.
+// their halves of the head sum (a lane swap between the wave halves), so
+// both hold the position's score.
 #pragma once
 
 #include "device_common.h"
@@ -88,8 +89,7 @@ __device__ __forceinline__ void indexer_round(const IndexerQuery<DI, NT>& Q, con
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc_tot = fmaf(Q.wt[t][i], fmaxf(acc[i], 0.f), acc_tot);
     }
-    acc_tot += __shfl_xor(acc_tot, 32, kWave);
-    tot[u] = acc_tot;
+    tot[u] = sum_xor32(acc_tot);
   }
 }
 

@@ -363,12 +363,14 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 #pragma unroll
       for (int i = 0; i < 4; ++i) c += f[tt][i] ? 1u : 0u;
     __builtin_amdgcn_wave_barrier();  // operand reads of this tile precede the next tile's writes
-    // per head: total over the four lanes holding it, and this lane's offset among them (kg order)
-    const uint32_t a1 = (uint32_t)__shfl_xor((int)c, 16, kWave);
-    const uint32_t pair = c + a1;
-    const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
-    const uint32_t tot = pair + a2;
-    const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
+    // per head: total over the four lanes holding it (rows kg = 0..3 of the wave), and this lane's
+    // offset among them (kg order): row swaps give each row pair's counts, then each half's
+    uint32_t c0, c1, p0, p1;
+    rows_swap16(c, c0, c1);
+    const uint32_t pair = c0 + c1;
+    halves_swap32(pair, p0, p1);
+    const uint32_t tot = p0 + p1;
+    const uint32_t pre = ((kg & 1) ? c0 : 0u) + ((kg & 2) ? p0 : 0u);
     // a head that cannot take this tile's pairs: flush now (the deferred flush below reserves only
     // PS_GUARD slots, so this exact test catches the rarer tiles that keep more)
     if (PS_GUARD < PS_TILE_MAX && ballot(lane < 16 && hl && scnt + tot > (uint32_t)S) != 0) {
@@ -590,11 +592,12 @@ __global__ __launch_bounds__(256) void score_cand_shared_kernel(const uint16_t* 
       for (int j = 0; j < NTT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) c += f[j][i] ? 1u : 0u;
-      const uint32_t a1 = (uint32_t)__shfl_xor((int)c, 16, kWave);
-      const uint32_t pair = c + a1;
-      const uint32_t a2 = (uint32_t)__shfl_xor((int)pair, 32, kWave);
-      const uint32_t tot = pair + a2;
-      const uint32_t pre = ((kg & 1) ? a1 : 0u) + ((kg & 2) ? a2 : 0u);
+      uint32_t c0, c1, p0, p1;  // row and half swaps, as in the one-query scan
+      rows_swap16(c, c0, c1);
+      const uint32_t pair = c0 + c1;
+      halves_swap32(pair, p0, p1);
+      const uint32_t tot = p0 + p1;
+      const uint32_t pre = ((kg & 1) ? c0 : 0u) + ((kg & 2) ? p0 : 0u);
       // a row that cannot take this tile's pairs: flush now (the deferred flush below reserves
       // only SS_GUARD slots, so this exact test catches the rarer tiles that keep more)
       if (SS_GUARD < PS_TILE_MAX && ballot(lane < 16 && hl && scnt + tot > (uint32_t)S) != 0) copy_out(reserve());

@@ -249,8 +249,7 @@ __device__ bool relative_kth(const uint32_t* cb, uint32_t off, uint32_t cnt, uin
   const int t = threadIdx.x, w = t >> 6, lane = lane_id();
   uint32_t mx = lo;
   for (uint32_t e = lane; e < cnt; e += 64) mx = max(mx, score_key(__uint_as_float(cb[off + e])));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  mx = wave_max_u32(mx);
   if (lane == 0) sm.gt[w] = mx;
   for (int i = t; i < NB0; i += ST) sm.hist[i] = 0;
   __syncthreads();
@@ -893,11 +892,8 @@ __global__ __launch_bounds__(256) void prefilter_threshold_kernel(const float* _
     mn = ok ? min(mn, key[j]) : mn;
     mx = ok ? max(mx, key[j]) : mx;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   uint32_t lo = mn, span = mx - mn, need = (uint32_t)r, result = mn;
   for (;;) {
     const int shift = span >= 1024u ? (32 - __clz(span)) - 10 : 0;  // span >> shift < 1024
@@ -1504,11 +1500,11 @@ __global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restri
     }
     // the wave's pairs of the round go to one reserved run of the row's list
     const uint32_t incl = wave_incl_scan(c);
-    const uint32_t tot = (uint32_t)__shfl((int)incl, 63, kWave);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     if (tot == 0) continue;  // wave-uniform
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(&cnt[row], tot);
-    base = (uint32_t)__shfl((int)base, 0, kWave);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
     const bool staged = tot <= (uint32_t)RC_STAGE;  // wave-uniform
     uint32_t slot = incl - c;  // this lane's first pair within the wave's run
 #pragma unroll
@@ -1792,8 +1788,7 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
         if (base + u * 256 + 4 * lane < r1)
           mk = max(max(max(mk, score_key(x[u].x)), score_key(x[u].y)), max(score_key(x[u].z), score_key(x[u].w)));
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, kWave));
+    mk = wave_max_u32(mk);
     if (lane == 0) fr.wk[w] = mk;
     __syncthreads();
     mk = 0;
@@ -1956,8 +1951,7 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
       for (int j = 0; j < 4; ++j)
         if (base + u * 256 + 4 * lane + j < r1) mk = max(mk, score_key(v[u][j]));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, kWave));
+  mk = wave_max_u32(mk);
   if (lane == 0) sm.wk[w] = mk;
   __syncthreads();
   mk = 0;

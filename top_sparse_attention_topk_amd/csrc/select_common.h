@@ -92,11 +92,8 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
       mn = min(mn, key[i]);
       mx = max(mx, key[i]);
     }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   if (lane == 0) {
     sm.gt[w] = mn;
     sm.eq[w] = mx;
