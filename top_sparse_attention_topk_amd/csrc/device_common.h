@@ -70,32 +70,6 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-// Inclusive prefix sum across the 64 lanes, on DPP lane moves (no LDS crossbar): Kogge-Stone
-// shifts by 1, 2, 4 and 8 inside each row of 16 lanes (lanes shifted in from outside the row add
-// 0), then row 15's total is broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
-  return v;
-}
-
 // gfx950 lane swaps between 16-lane rows (v_permlane16_swap: x[0] holds rows 0,0,2,2 and x[1]
 // rows 1,1,3,3 of v) and between wave halves (v_permlane32_swap: x[0] holds the low half twice,
 // x[1] the high half). Plain VALU moves, no LDS crossbar.
@@ -119,6 +93,85 @@ __device__ __forceinline__ float sum_xor32(float v) {
   uint32_t lo, hi;
   halves_swap32(__float_as_uint(v), lo, hi);
   return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// v of another lane through a DPP pattern (every lane active; patterns within a 16-lane row)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of W lanes (W = 2 .. 64, a power of two), the total in every lane of
+// the group. Each step adds a lane that holds the same partial as the xor-butterfly partner (xor
+// 1 and 2 by quad permutes, then the half-row and row mirrors, then row and half swaps), so the
+// result has the bits of the xor butterfly: a + b == b + a.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: a power of two up to 64");
+  if constexpr (W >= 2) v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (W >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  if constexpr (W >= 32) v = sum_xor16(v);
+  if constexpr (W >= 64) v = sum_xor32(v);
+  return v;
+}
+
+// Sums (and maxima) over the lanes l ^ O, l ^ 2O, ..., l ^ 32 (groups of O lanes merged
+// position by position, O = 8, 16 or 32): exact xor partners, by row rotation for 8 and by the
+// row and half swaps for 16 and 32; the bits of the xor butterfly.
+template <int O>
+__device__ __forceinline__ float cross_sum(float v) {
+  static_assert(O == 8 || O == 16 || O == 32 || O == 64, "O: 8, 16, 32 (64: nothing to merge)");
+  if constexpr (O <= 8) v += dpp_mov<0x128>(v);  // row_ror:8 = lane ^ 8 within the row
+  if constexpr (O <= 16) v = sum_xor16(v);
+  if constexpr (O <= 32) v = sum_xor32(v);
+  return v;
+}
+template <int O>
+__device__ __forceinline__ float cross_max(float v) {
+  static_assert(O == 8 || O == 16 || O == 32 || O == 64, "O: 8, 16, 32 (64: nothing to merge)");
+  if constexpr (O <= 8) v = fmaxf(v, dpp_mov<0x128>(v));
+  if constexpr (O <= 16) {
+    uint32_t e, o;
+    rows_swap16(__float_as_uint(v), e, o);
+    v = fmaxf(__uint_as_float(e), __uint_as_float(o));
+  }
+  if constexpr (O <= 32) {
+    uint32_t lo, hi;
+    halves_swap32(__float_as_uint(v), lo, hi);
+    v = fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+  }
+  return v;
+}
+
+// maximum across the 64 lanes (every lane active)
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xb1>(v));
+  v = fmaxf(v, dpp_mov<0x4e>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return cross_max<16>(v);
+}
+
+// Inclusive prefix sum across the 64 lanes, on DPP lane moves (no LDS crossbar): Kogge-Stone
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes (lanes shifted in from outside the row add
+// 0), then row 15's total is broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return v;
 }
 
 // Minimum across the 64 lanes, as wave_max_u32 below.

@@ -226,13 +226,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherK a) {
     }
   }
 #pragma unroll
-  for (int o = LPR; o < 64; o <<= 1)
+  for (int h = 0; h < NH; ++h) {  // the wave's lane groups, merged position by position
+    psum[h] = cross_sum<LPR>(psum[h]);
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      psum[h] += __shfl_xor(psum[h], o, kWave);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, kWave);
-    }
+    for (int e = 0; e < EPL; ++e) acc[h][e] = cross_sum<LPR>(acc[h][e]);
+  }
   // waves add their sums in a fixed order
   for (int ww = 0; ww < 4; ++ww) {
     if (w == ww && grp == 0) {
@@ -388,9 +386,7 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
         y[u][h] = x;
       }
 #pragma unroll
-      for (int o = 1; o < LPR; o <<= 1)
-#pragma unroll
-        for (int h = 0; h < NH; ++h) y[u][h] += __shfl_xor(y[u][h], o, kWave);
+      for (int h = 0; h < NH; ++h) y[u][h] = group_sum<LPR>(y[u][h]);  // the row's dot product
 #pragma unroll
       for (int h = 0; h < NH; ++h) y[u][h] = tk[u] >= 0 ? y[u][h] * yscale : -INFINITY;
     }
@@ -449,20 +445,15 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherK a) {
   // state rescaled to it, then the sums over the groups (xor butterflies over the group index)
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    const float M = cross_max<LPR>(m[h]);
     const float f = M == -INFINITY ? 0.f : pow2(m[h] - M);
     m[h] = M;
     l[h] *= f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+    l[h] = cross_sum<LPR>(l[h]);
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
-      l[h] += __shfl_xor(l[h], o, kWave);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, kWave);
-    }
+    for (int e = 0; e < EPL; ++e) acc[h][e] = cross_sum<LPR>(acc[h][e]);
   }
   if (grp == 0) {
     float* wp = wpart + w * PS;

@@ -75,8 +75,7 @@ __global__ __launch_bounds__(256) void hisa_token_score_kernel(const void* __res
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
-#pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) a += __shfl_xor(a, o, kWave);
+      a = group_sum<LPR>(a);
       const int64_t t = base + u * RPW + grp;
       if (t < t1 && sub == 0) crow[t] = pos[u] >= 0 ? a * scale : __int_as_float(0x7fc00000);
     }

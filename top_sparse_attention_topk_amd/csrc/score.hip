@@ -842,9 +842,7 @@ __global__ __launch_bounds__(256) void score_block_kernel(const void* __restrict
         part[h] = x;
       }
 #pragma unroll
-      for (int o = 1; o < SH::LPR; o <<= 1)
-#pragma unroll
-        for (int h = 0; h < NH; ++h) part[h] += __shfl_xor(part[h], o, kWave);
+      for (int h = 0; h < NH; ++h) part[h] = group_sum<SH::LPR>(part[h]);
       const int row = base + 8 * r + grp;
       if (row < p1) {
 #pragma unroll
@@ -920,9 +918,7 @@ __global__ __launch_bounds__(256) void score_vec_kernel(const void* __restrict__
         part[h] = a;
       }
 #pragma unroll
-      for (int o = 1; o < LPR; o <<= 1)
-#pragma unroll
-        for (int h = 0; h < NH; ++h) part[h] += __shfl_xor(part[h], o, kWave);
+      for (int h = 0; h < NH; ++h) part[h] = group_sum<LPR>(part[h]);
       const int pos = base + u * RPW + grp;
       if (pos < p1) {
 #pragma unroll
@@ -996,9 +992,7 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const void* __restrict_
     for (int e = 0; e < EPL; ++e) acc[e] += kf[e];
   }
 #pragma unroll
-  for (int o = LPR; o < 64; o <<= 1)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  for (int e = 0; e < EPL; ++e) acc[e] = cross_sum<LPR>(acc[e]);
   if (grp == 0) {
     const float inv = 1.0f / (float)(i1 - i0);
     float* dst = means + (((int64_t)b * Hkv + g) * m + j) * D + sub * EPL;
