@@ -244,11 +244,15 @@ def host_record() -> dict:
 def stream_read_peak(torch, steps: int = 10) -> dict:
     """Measured HBM read ceiling: the committed streaming-read probe (csrc/probe/stream_read.hip) over
     4 GiB, read once per launch with 16-byte non-temporal loads, for 1, 2, 4 and 8 persistent
-    workgroups of 256 threads per compute unit; HIP events on the launch stream."""
+    workgroups of 256 threads per compute unit; HIP events on the launch stream. Beside it, the same
+    stream with one byte written per 8 read (contiguous 1 KiB per 8 KiB tile: the ratio of a scan
+    that writes an fp32 score per head for 8 heads of bf16 d = 128 rows), 1 and 2 workgroups per CU."""
     import ctypes
     lib = ctypes.CDLL(PROBE_LIB)
     lib.tka_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                           ctypes.c_void_p]
+    lib.tka_probe_stream_read_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int, ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
     sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda")
@@ -262,10 +266,26 @@ def stream_read_peak(torch, steps: int = 10) -> dict:
                 raise RuntimeError("stream read probe launch failed")
         ms = time_loop(run, steps)
         by[str(wpc)] = round(STREAM_BYTES / (ms / 1e3) / 1e9, 1)
-    del buf, sink
+    dst = torch.empty(STREAM_BYTES // 8, dtype=torch.uint8, device="cuda")
+    rw = {}
+    for wpc in (1, 2):
+        grid = cus * wpc
+
+        def run_rw():
+            if lib.tka_probe_stream_read_write(buf.data_ptr(), STREAM_BYTES, dst.data_ptr(), sink.data_ptr(), grid,
+                                               st) != 0:
+                raise RuntimeError("read-write probe launch failed")
+        ms = time_loop(run_rw, steps)
+        rw[str(wpc)] = {"ms": round(ms, 4), "gbps_read": round(STREAM_BYTES / (ms / 1e3) / 1e9, 1),
+                        "gbps_read_plus_write": round(STREAM_BYTES * 9 / 8 / (ms / 1e3) / 1e9, 1)}
+    del buf, sink, dst
     best = max(by.values())
+    best_rw = max(v["gbps_read_plus_write"] for v in rw.values())
     return {"gbps": best, "frac_of_peak": round(best / PEAK_HBM_GBPS, 4), "bytes_per_launch": STREAM_BYTES,
-            "gbps_by_workgroups_per_cu": by, "kernel": "tka_probe::stream_read_kernel (csrc/probe/stream_read.hip)"}
+            "gbps_by_workgroups_per_cu": by, "kernel": "tka_probe::stream_read_kernel (csrc/probe/stream_read.hip)",
+            "with_writes": {"bytes_written_per_byte_read": 0.125, "gbps_read_plus_write": best_rw,
+                            "frac_of_peak": round(best_rw / PEAK_HBM_GBPS, 4), "by_workgroups_per_cu": rw,
+                            "kernel": "tka_probe::stream_read_write_kernel (csrc/probe/stream_read.hip)"}}
 
 
 def _counter_rows(dirs):

@@ -287,3 +287,15 @@ def test_noalloc_refuses_steps_beyond_its_scratch():
     assert tka.topk_decode_workspace_size(c3) <= tka.NOALLOC_SCRATCH_BYTES
     assert call(c3, q=None) == tka.TKA_ERR_INVALID_ARG  # the same argument checks as topk_decode
     assert call(c3, out=FAKE * 2 + 64) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_bench_probe_library_checks():
+    """The benchmark's probe library (not part of the decode ABI) loads, exports its two
+    streaming probes, and rejects bad arguments before any launch."""
+    probe = ctypes.CDLL(os.path.join(ROOT, "top_sparse_attention_topk_amd", "libtka_probe.so"))
+    rd, rw = probe.tka_probe_stream_read, probe.tka_probe_stream_read_write
+    rd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    rw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert rd(None, 4096, FAKE, 1, None) == 1 and rd(FAKE, 4100, FAKE, 1, None) == 1 and rd(FAKE, 4096, FAKE, 0, None) == 1
+    assert rw(FAKE, 8192 * 3 + 16, FAKE, FAKE, 1, None) == 1  # not whole 8 KiB tiles
+    assert rw(FAKE, 8192, None, FAKE, 1, None) == 1 and rw(FAKE, 8192, FAKE, FAKE, 0, None) == 1
