@@ -521,6 +521,13 @@ def exact_variant(fx, tka, torch, np, w, steps: int) -> dict:
     def fused(r):
         tka.topk_decode(p, r["q"], r["K"], r["V"], out=out, idx_out=idx, ws=ws)
 
+    # the candidate prefilter forced where the automatic choice takes the dense composition
+    pp = tka.problem(tka.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, decode_path=tka.TKA_PATH_PREFILTER)
+    ws_p = torch.empty(tka.topk_decode_workspace_size(pp), dtype=torch.uint8, device="cuda")
+
+    def fused_prefilter(r):
+        tka.topk_decode(pp, r["q"], r["K"], r["V"], out=out, idx_out=idx, ws=ws_p)
+
     def three(r):
         tka.topk_attn_score(p, r["q"], r["K"], scores=sc)
         tka.topk_select(sc.reshape(rows, w.L), w.k, idx_out=sel_idx, sel_out=sel_val, ws=sws)
@@ -545,6 +552,7 @@ def exact_variant(fx, tka, torch, np, w, steps: int) -> dict:
                     "hbm_gbps_counted": round(gb, 1), "pct_of_hbm_peak": round(100 * gb / PEAK_HBM_GBPS, 2),
                     "three_call_ms": round(t_3, 4),
                     "three_call_queries_per_s": round(w.B / (t_3 / 1e3), 1),
+                    "decode_prefilter_forced_ms": round(rotated(fused_prefilter), 4),
                     "decode_ms_mall_warm": round(time_loop(lambda: fused(ins), steps), 4),
                     "three_call_ms_mall_warm": round(time_loop(lambda: three(ins), steps), 4)})
     del reps, ins

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TKA_ABI_VERSION 2
+#define TKA_ABI_VERSION 3
 
 typedef enum {
   TKA_OK = 0,
@@ -109,7 +109,12 @@ typedef struct {
                              lists [B,M,Hq,n]; built for bf16 with M * Hq/Hkv <= 64 (topk_attn_score,
                              sparse_attn_gather, topk_decode, and topk_attn_score_threshold for M <= 4;
                              TKA_ERR_UNSUPPORTED elsewhere). */
+  int32_t decode_path;    /* topk_decode in EXACT mode: TKA_PATH_AUTO (0), TKA_PATH_PREFILTER or
+                             TKA_PATH_DENSE; see topk_decode. The results are the same bits on every path. */
 } tka_problem;
+
+/* tka_problem.decode_path */
+enum { TKA_PATH_AUTO = 0, TKA_PATH_PREFILTER = 1, TKA_PATH_DENSE = 2 };
 
 /*
  * Scoring pass (one of the three variants above), writes fp32 scores.
@@ -220,8 +225,16 @@ tka_status sparse_attn_gather_workspace_size(const tka_problem* p, int32_t n_idx
 
 /*
  * The whole step in one call, on one stream: score -> select -> gather, with
- * the same kernels and launch shapes as the three calls above (bitwise equal
- * results).
+ * results bitwise equal to the three calls above.
+ *   EXACT bf16 with 2 <= Hq/Hkv <= 16, 8192 <= L <= 262144, k' <= L/8 and
+ *   n_queries <= 4 can run the candidate prefilter instead of writing the score
+ *   array: sampled thresholds, one thresholded scan, an exact select over the
+ *   candidates, a full rescore of any row whose candidates cannot hold the answer
+ *   ("Sparse Attention in LLM Inference", "The Overhead of the Indexer": filter
+ *   coarsely, then sort finely among the survivors). decode_path TKA_PATH_AUTO
+ *   takes it when B * n_queries * Hq * L >= 2^22 scores (below that its six
+ *   launches cost more than the score array saves), TKA_PATH_PREFILTER whenever
+ *   it applies, TKA_PATH_DENSE never; any other value is TKA_ERR_INVALID_ARG.
  *   EXACT:      proxy_keys, q_idx, idx_w NULL; the gather uses the selected scores.
  *   BLOCK_MEAN: proxy_keys = block means [B,Hkv,mc,d] fp32; idx_out (if given)
  *               [B,Hq,k] block ids without the current block.

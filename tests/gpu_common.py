@@ -30,10 +30,14 @@ def dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a).to("cuda")
 
 
-def problem(w: fx.Workload, scale: float = 0.0):
+def problem(w: fx.Workload, scale: float = 0.0, decode_path=None):
+    """The workload's tka_problem. topk_decode takes the candidate prefilter wherever it applies
+    (TKA_PATH_PREFILTER) unless decode_path says otherwise, so that the reduced test sizes exercise
+    the path the full sizes take."""
     m = tka()
     dt = m.TKA_BF16 if w.dtype == fx.BF16 else m.TKA_F32
-    return m.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, scale, w.block, w.HI, w.dI)
+    path = m.TKA_PATH_PREFILTER if decode_path is None else decode_path
+    return m.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, scale, w.block, w.HI, w.dI, decode_path=path)
 
 
 def tol(w: fx.Workload) -> float:

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     missing = [n for n in names if n not in exported]
     assert not missing, missing
-    assert LIB.tka_abi_version() == 2
+    assert LIB.tka_abi_version() == 3
 
 
 def _status(code):
@@ -152,6 +152,25 @@ def test_decode_checks_and_workspace():
     assert LIB.topk_decode(ctypes.byref(pb), FAKE, FAKE * 2, FAKE * 3, None, None, None, FAKE * 5, None, FAKE * 8,
                            1 << 30, None) == tka.TKA_ERR_INVALID_ARG  # block means missing
     assert LIB.topk_block_mean_build(ctypes.byref(p), FAKE, FAKE * 2, None) == tka.TKA_ERR_INVALID_ARG
+
+
+def test_decode_path_values():
+    """decode_path takes auto, prefilter or dense; anything else fails before any launch. The
+    automatic choice keeps the score array below 2^22 scores (it is in the workspace) and drops it
+    above; forced paths size the workspace for their own path."""
+    ok = tka.problem(tka.EXACT, 2, 8, 2, 128, 32768, 2048)
+    for bad in (-1, 3):
+        p = tka.problem(tka.EXACT, 2, 8, 2, 128, 32768, 2048, decode_path=bad)
+        assert LIB.topk_attn_score(ctypes.byref(p), FAKE, FAKE * 2, None, FAKE * 3, None) == tka.TKA_ERR_INVALID_ARG
+    scores = 2 * 8 * 32768 * 4
+    assert tka.topk_decode_workspace_size(ok) >= scores  # 2^19 scores: dense
+    pre = tka.problem(tka.EXACT, 2, 8, 2, 128, 32768, 2048, decode_path=tka.TKA_PATH_PREFILTER)
+    assert tka.topk_decode_workspace_size(pre) != tka.topk_decode_workspace_size(ok)
+    big = tka.problem(tka.EXACT, 16, 8, 2, 128, 32768, 2048)  # 2^22 scores: prefilter
+    dense = tka.problem(tka.EXACT, 16, 8, 2, 128, 32768, 2048, decode_path=tka.TKA_PATH_DENSE)
+    assert tka.topk_decode_workspace_size(dense) >= 16 * 8 * 32768 * 4
+    assert tka.topk_decode_workspace_size(big) == tka.topk_decode_workspace_size(
+        tka.problem(tka.EXACT, 16, 8, 2, 128, 32768, 2048, decode_path=tka.TKA_PATH_PREFILTER))
 
 
 def test_workspace_sizes_scale_with_problem():

@@ -70,7 +70,7 @@ def test_prefilter_repair_several_queries():
 
 def check_several_queries(name, w, M, q, K, V):
     m = tka()
-    p = m.problem(m.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, m.TKA_BF16, n_queries=M)
+    p = m.problem(m.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, m.TKA_BF16, n_queries=M, decode_path=m.TKA_PATH_PREFILTER)
     qt, Kt, Vt = dev(q), dev(K), dev(V)
     out, idx = m.topk_decode(p, qt, Kt, Vt)
     out2, idx2 = m.topk_decode(p, qt, Kt, Vt)

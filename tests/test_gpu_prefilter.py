@@ -228,3 +228,27 @@ def test_indexer_candidates_short_last_chunk():
     q, K, V = fx.make_attn(w)
     say("[indexer candidates] L 32773, B 3, k 64")
     _run_indexer_both(w, qI, kI, wt, q, K, V)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_decode_paths_agree(B):
+    """topk_decode's three decode_path values on the C2 shape (32 query heads over 8 KV heads,
+    L = 32768, k = 2048): with B = 1 (2^20 scores) the automatic choice takes the dense composition,
+    with B = 4 (2^22) the candidate prefilter; outputs and indices are the same bits on every path."""
+    m = tka()
+    w = fx.shrink(fx.WORKLOADS["C2"], fx.WORKLOADS["C2"].L, B=B)
+    q, K, V = fx.make_attn(w)
+    qt, Kt, Vt = dev(q), dev(K), dev(V)
+    got = {}
+    for path in (m.TKA_PATH_AUTO, m.TKA_PATH_PREFILTER, m.TKA_PATH_DENSE):
+        say(f"[decode paths] B={B} decode_path={path}")
+        got[path] = m.topk_decode(problem(w, decode_path=path), qt, Kt, Vt)
+    torch.cuda.synchronize()
+    ref_out, ref_idx = got[m.TKA_PATH_DENSE]
+    for path, (out, idx) in got.items():
+        assert torch.equal(idx, ref_idx), path
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), path
+    auto_ws = m.topk_decode_workspace_size(problem(w, decode_path=m.TKA_PATH_AUTO))
+    pre_ws = m.topk_decode_workspace_size(problem(w, decode_path=m.TKA_PATH_PREFILTER))
+    dense_ws = m.topk_decode_workspace_size(problem(w, decode_path=m.TKA_PATH_DENSE))
+    assert auto_ws == (dense_ws if B == 1 else pre_ws)

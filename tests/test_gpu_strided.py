@@ -44,6 +44,7 @@ def strides_of(Xs: np.ndarray):
 def gpu_problem(w, strides, **kw):
     m = tka()
     dt = m.TKA_BF16 if w.dtype == fx.BF16 else m.TKA_F32
+    kw.setdefault("decode_path", m.TKA_PATH_PREFILTER)  # the prefilter wherever it applies, as at full size
     return m.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt, 0.0, w.block, w.HI, w.dI, strides=strides, **kw)
 
 

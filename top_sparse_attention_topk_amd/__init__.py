@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG, "libtka.so")
 TKA_OK, TKA_ERR_INVALID_ARG, TKA_ERR_UNSUPPORTED, TKA_ERR_WORKSPACE, TKA_ERR_ALIGNMENT, TKA_ERR_HIP = range(6)
 TKA_F32, TKA_BF16, TKA_FP8_E4M3 = 0, 1, 2
 EXACT, BLOCK_MEAN, INDEXER, HISA = 0, 1, 2, 3
+TKA_PATH_AUTO, TKA_PATH_PREFILTER, TKA_PATH_DENSE = 0, 1, 2  # tka_problem.decode_path
 
 
 class TkaError(RuntimeError):
@@ -37,7 +38,7 @@ class Problem(ctypes.Structure):
                 ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("mode", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
                 ("idx_dtype", ctypes.c_int32), ("block_capacity", ctypes.c_int32), ("idx_capacity", ctypes.c_int32),
-                ("top_blocks", ctypes.c_int32), ("n_queries", ctypes.c_int32)]
+                ("top_blocks", ctypes.c_int32), ("n_queries", ctypes.c_int32), ("decode_path", ctypes.c_int32)]
 
 
 def _load():
@@ -115,12 +116,12 @@ def _stream(stream):
 def problem(mode: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int, top_k: int,
             dtype: int = TKA_BF16, scale: float = 0.0, block_size: int = 0, n_idx_heads: int = 0, idx_dim: int = 0,
             strides=None, block_capacity: int = 0, idx_capacity: int = 0, top_blocks: int = 0,
-            n_queries: int = 0) -> Problem:
+            n_queries: int = 0, decode_path: int = 0) -> Problem:
     """tka_problem; strides default to a contiguous [B, Hkv, L, d] cache."""
     sb, sh, sl = strides if strides is not None else (n_kv_heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     return Problem(batch, n_q_heads, n_kv_heads, head_dim, seq_len, top_k, sb, sh, sl, dtype, scale, mode,
                    block_size, n_idx_heads, idx_dim, TKA_FP8_E4M3, block_capacity, idx_capacity, top_blocks,
-                   n_queries)
+                   n_queries, decode_path)
 
 
 def score_shape(p: Problem):
