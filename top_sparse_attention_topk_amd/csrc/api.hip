@@ -837,8 +837,9 @@ tka_status topk_decode_noalloc(const tka_problem* p, const void* q, const void* 
 
 namespace {
 struct AdaptiveLayout {
-  size_t scores, idx, selv, kout, tau, scratch, gather_ws, total;
+  size_t scores, idx, selv, kout, tau, scratch, gather_ws, rmax, total;
   int64_t rows;
+  int rslots;  // partial row maxima written by the scoring pass (0: none)
   GatherPlan gp;
 };
 AdaptiveLayout adaptive_layout(const tka_problem* p) {
@@ -862,6 +863,9 @@ AdaptiveLayout adaptive_layout(const tka_problem* p) {
   GatherArgs ga = gather_args(p, nullptr, nullptr, nullptr, nullptr, p->top_k, 0, 0, nullptr, nullptr);
   d.gp = plan_gather(ga);
   o += al256(d.gp.ws_bytes);
+  d.rmax = o;
+  d.rslots = score_rmax_slots(dense_score_args(p, nullptr, nullptr, nullptr));
+  o += al256(sizeof(uint32_t) * (size_t)d.rows * (size_t)d.rslots);
   d.total = o;
   return d;
 }
@@ -924,11 +928,15 @@ tka_status topk_decode_adaptive(const tka_problem* p, const void* q, const void*
   float* tau = tau_out ? tau_out : reinterpret_cast<float*>(base + d.tau);
   const AdaptiveScratch sc = adaptive_scratch(d.rows);
   const int32_t len = score_len(p);
-  run_score(p, q, k_cache, nullptr, scores, st);
+  // the scores, with each row's partial maxima beside them where the scoring kernel writes them
+  uint32_t* rmax = d.rslots > 0 ? reinterpret_cast<uint32_t*>(base + d.rmax) : nullptr;
+  ScoreArgs sa_score = dense_score_args(p, q, k_cache, scores);
+  sa_score.rmax = rmax;
+  launch_score_dense(sa_score, st);
   SelectArgs sa{scores, d.rows, len, (int64_t)len, p->top_k, idx, selv};
   launch_select_adaptive(sa, eps, k_min, kk, reinterpret_cast<uint64_t*>(base + d.scratch + sc.W),
                          reinterpret_cast<float*>(base + d.scratch + sc.M),
-                         reinterpret_cast<uint32_t*>(base + d.scratch + sc.flag), tau, st);
+                         reinterpret_cast<uint32_t*>(base + d.scratch + sc.flag), tau, st, rmax, d.rslots);
   GatherArgs ga = gather_args(p, q, k_cache, v_cache, idx, p->top_k, 0, 0, selv, out);
   launch_gather(ga, d.gp, base + d.gather_ws, st);
   return launched("topk_decode_adaptive");

@@ -17,6 +17,7 @@ struct ScoreArgs {
   int q_bf16;  // query: 1 bf16, 0 fp32
   int M = 1;   // queries per sequence (q [B,M,Hq,d], scores [B,M,Hq,nrows], causal)
   int block = 0;  // rows are fp32 block means (one query per sequence)
+  uint32_t* rmax = nullptr;  // optional: partial row maxima (score keys), score_rmax_slots per row
 };
 
 struct IndexerArgs {
@@ -85,6 +86,8 @@ struct MfmaOut {
   uint2* cpair;                 // candidate mode, packed (when set, instead of cbits/cpos): [B*Hq, capg] (bits, pos)
   int capg;
   int stage;                    // candidate mode: LDS staging entries per head
+  uint32_t* rmax;               // full mode, optional: [B*Hq, rmax_slots] maxima of score keys, one per
+  int rmax_slots;               //   (workgroup chunk, wave) of the row
 };
 
 // Largest LDS a workgroup may take on the current device, and a one-time
@@ -97,6 +100,9 @@ int mfma_scan_chunk(const ScoreArgs& a);
 void launch_score_mfma_sample(const ScoreArgs& a, int sample_chunk, int nsamp, float* samp, hipStream_t st);
 void launch_score_mfma_cand(const ScoreArgs& a, const MfmaOut& o, hipStream_t st);
 void launch_score_dense(const ScoreArgs& a, hipStream_t st);
+// Partial row maxima the dense scores can write beside the scores (ScoreArgs.rmax): the number
+// per row, 0 where the launch writes none (then rmax is ignored).
+int score_rmax_slots(const ScoreArgs& a);
 void launch_score_indexer(const IndexerArgs& a, hipStream_t st);
 void launch_block_mean(const BlockMeanArgs& a, hipStream_t st);
 // append one position of every (b, KV head) row (16-byte rows) and/or encode indexer keys
@@ -110,8 +116,11 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 // one workgroup per row, only rows whose flag is nonzero
 // certified adaptive k per row (a.k = k_max): counts to kout and the kept positions, then
 // tau; W, M and row_flag [n_rows] are scratch
+// rmax (optional, rslots per row): partial maxima of each row's score keys that the scoring pass
+// wrote (ScoreArgs.rmax); the long-row path then skips its pass for the row maximum.
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
-                            uint32_t* row_flag, float* tau, hipStream_t st);
+                            uint32_t* row_flag, float* tau, hipStream_t st, const uint32_t* rmax = nullptr,
+                            int rslots = 0);
 // several causal queries per sequence: exact scores (bf16, M*G <= 64 rows per KV head; a
 // position a query cannot see is NaN) and each row's count min(k, L - M + t + 1)
 void launch_score_mq(const ScoreArgs& a, hipStream_t st);

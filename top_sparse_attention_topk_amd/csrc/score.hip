@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
   };
 
   uint4 cur[NI];
+  uint32_t kmax = 0;  // full mode: the largest score key this lane wrote (head n)
   if (base < p1) load(cur, base);
   for (; base < p1; base += step) {
     uint4 nxt[NI];
@@ -134,6 +135,10 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = acc[i] * scale;
+      if (MODE == MFMA_FULL && o.rmax) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kmax = pos + i < p1 ? max(kmax, score_key(v[i])) : kmax;
+      }
       if (n < G) {
         if (MODE == MFMA_FULL) {
           float* Srow = o.S + row * L;
@@ -157,6 +162,14 @@ __global__ __launch_bounds__(256) void score_exact_mfma_kernel(const uint16_t* _
 #pragma unroll
       for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
     }
+  }
+  if (MODE == MFMA_FULL && o.rmax) {  // the four lanes of head n (rows kg = 0..3 of the wave) combine
+    uint32_t e, od;
+    rows_swap16(kmax, e, od);
+    kmax = max(e, od);
+    halves_swap32(kmax, e, od);
+    kmax = max(e, od);
+    if (lane < G) o.rmax[row * o.rmax_slots + blockIdx.x * 4 + wave] = kmax;
   }
 }
 
@@ -1225,6 +1238,14 @@ static void launch_block(const ScoreArgs& a, hipStream_t st) {
 
 bool score_uses_mfma(int dtype_bf16, int G) { return dtype_bf16 && G >= 2 && G <= 16; }
 
+// the full-score MFMA kernel (one query per sequence, not block means) writes a maximum per
+// (chunk workgroup, wave) of each row
+int score_rmax_slots(const ScoreArgs& a) {
+  if (a.nrows <= 0 || a.M > 1 || a.block || !score_uses_mfma(a.bf16, a.G)) return 0;
+  const int chunk = mfma_scan_chunk(a);
+  return 4 * ((a.nrows + chunk - 1) / chunk);
+}
+
 void launch_score_dense(const ScoreArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return;
   if (a.M > 1) {
@@ -1239,6 +1260,8 @@ void launch_score_dense(const ScoreArgs& a, hipStream_t st) {
     MfmaOut o{};
     o.S = a.scores;
     const int chunk = mfma_scan_chunk(a);
+    o.rmax = a.rmax;
+    o.rmax_slots = score_rmax_slots(a);
     launch_mfma<MFMA_FULL>(a, chunk, (unsigned)((a.nrows + chunk - 1) / chunk), o, st);
   } else if (a.bf16) {
     launch_vec<true>(a, st);

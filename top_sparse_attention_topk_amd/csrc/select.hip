@@ -1741,6 +1741,9 @@ __device__ void ak_find_bin(Sm& sm, const uint64_t* mass, const uint32_t* cnt, i
 
 // One workgroup per row; wave w streams its own segment [r0, r1) of the row
 // (UNR float4 loads in flight per lane), as the count-based row select does.
+// Given rmax (rslots partial maxima per row, written beside the scores by the
+// scoring pass), the long-row path takes the row maximum from them instead of
+// a pass over the row.
 // Rows whose k is the unclamped budget answer emit their kept set here (every
 // key above T, then the first `ties` keys equal to T in position order);
 // rows held by k_min or k_max, or without mass, are flagged for the
@@ -1749,7 +1752,8 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
                                                          int k_min, int k_max, int32_t* __restrict__ kout,
                                                          uint64_t* __restrict__ Wout, float* __restrict__ Mout,
                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                         uint32_t* __restrict__ row_flag) {
+                                                         uint32_t* __restrict__ row_flag,
+                                                         const uint32_t* __restrict__ rmax, int rslots) {
   __shared__ AkShared shm;
   __shared__ AkRed fr;
   AkSmem& sm = shm.ak;
@@ -1776,17 +1780,22 @@ __global__ __launch_bounds__(256) void adaptive_k_kernel(const float* __restrict
                     0, 0u, rs, f.sel);
     const uint32_t T0 = f.sel.res[0];
     __syncthreads();  // the samples are spent
-    // the row maximum (every load one float4 with no branch around it)
+    // the row maximum: from the partial maxima the scoring pass wrote beside the scores, else a
+    // pass over the row (every load one float4 with no branch around it)
     uint32_t mk = 0;
-    for (int base = r0; base < r1; base += 256 * AK_UNR) {
-      float4 x[AK_UNR];
+    if (rmax) {
+      for (int i = t; i < rslots; i += ST) mk = max(mk, rmax[row * rslots + i]);
+    } else {
+      for (int base = r0; base < r1; base += 256 * AK_UNR) {
+        float4 x[AK_UNR];
 #pragma unroll
-      for (int u = 0; u < AK_UNR; ++u)
-        x[u] = *reinterpret_cast<const float4*>(s + min(base + u * 256 + 4 * lane, r1 - 4));
+        for (int u = 0; u < AK_UNR; ++u)
+          x[u] = *reinterpret_cast<const float4*>(s + min(base + u * 256 + 4 * lane, r1 - 4));
 #pragma unroll
-      for (int u = 0; u < AK_UNR; ++u)
-        if (base + u * 256 + 4 * lane < r1)
-          mk = max(max(max(mk, score_key(x[u].x)), score_key(x[u].y)), max(score_key(x[u].z), score_key(x[u].w)));
+        for (int u = 0; u < AK_UNR; ++u)
+          if (base + u * 256 + 4 * lane < r1)
+            mk = max(max(max(mk, score_key(x[u].x)), score_key(x[u].y)), max(score_key(x[u].z), score_key(x[u].w)));
+      }
     }
     mk = wave_max_u32(mk);
     if (lane == 0) fr.wk[w] = mk;
@@ -2197,11 +2206,11 @@ void launch_select_rows_flagged(const SelectArgs& a, const uint32_t* row_flag, c
 }
 
 void launch_select_adaptive(const SelectArgs& a, float eps, int k_min, int32_t* kout, uint64_t* W, float* M,
-                            uint32_t* row_flag, float* tau, hipStream_t st) {
+                            uint32_t* row_flag, float* tau, hipStream_t st, const uint32_t* rmax, int rslots) {
   if (a.n_rows <= 0) return;
   const unsigned rows = (unsigned)a.n_rows;
   hipLaunchKernelGGL(adaptive_k_kernel, dim3(rows), dim3(ST), 0, st, a.scores, a.n, a.stride, eps, k_min, a.k, kout,
-                     W, M, a.idx, a.sel, row_flag);
+                     W, M, a.idx, a.sel, row_flag, rslots > 0 ? rmax : nullptr, rslots);
   // rows whose k is held by k_min / k_max or that have no mass: the count-based row select
   size_t lds;
   const int capw = rows_capw(a.n, a.k, &lds);
