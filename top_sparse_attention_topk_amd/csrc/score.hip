@@ -775,11 +775,12 @@ __global__ void mq_counts_kernel(int32_t* __restrict__ krow, int64_t rows, int M
 // Block-mean scores s[b,h,j] = <q[b,h], mean[b,g,j]> ("Sparse Attention
 // Landscape", "Block Sparse Attention": the block score from the mean-pooled
 // keys), fp32 means, the query bf16 or fp32. A row of D floats is read by a
-// group of 8 lanes, lane c taking the 16-byte pieces c, c + 8, ... (a load
-// instruction covers 128 contiguous bytes of each of 8 rows); each lane keeps
-// the matching slices of the NH query heads, and the partial dots are reduced
-// over the 8 lanes with three xor shuffles. A wave takes RND consecutive
-// rounds of 8 rows with all their loads issued before the first use.
+// group of LPR lanes (8, or 16 for more than 4 heads), lane c taking the
+// 16-byte pieces c, c + LPR, ... (a load instruction covers 16·LPR contiguous
+// bytes of each of 64/LPR rows); each lane keeps the matching slices of the NH
+// query heads, and the partial dots are summed over the row's lanes (DPP). A
+// wave takes RND consecutive rounds of rows with all their loads issued before
+// the first use.
 // Grid (chunks, B*Hkv*htiles), 256 threads.
 // ---------------------------------------------------------------------------
 #ifndef TKA_BLK_LOADS
@@ -787,11 +788,14 @@ __global__ void mq_counts_kernel(int32_t* __restrict__ krow, int64_t rows, int M
 #endif
 template <int D, int NH>
 struct BlockScoreShape {
-  static constexpr int LPR = 8;                            // lanes per row
-  static constexpr int NL = D / 32;                        // 16-byte pieces per lane
-  static constexpr int LD = NH > 4 ? TKA_BLK_LOADS / 2 : TKA_BLK_LOADS;  // 16-byte loads in flight per lane
-  static constexpr int RND = LD / NL > 0 ? LD / NL : 1;    // rounds of 8 rows in flight per wave
-  static constexpr int ROWS = 4 * 8 * RND;                 // rows per workgroup pass
+  // lanes per row: 8, or 16 for more than 4 heads, so that the query slices a lane keeps (NH x its
+  // pieces) stay at 64 registers
+  static constexpr int LPR = NH > 4 ? 16 : 8;
+  static constexpr int RPW = 64 / LPR;                     // rows per load instruction (per wave)
+  static constexpr int NL = D / (4 * LPR) > 0 ? D / (4 * LPR) : 1;  // 16-byte pieces per lane
+  static constexpr int LD = TKA_BLK_LOADS;                 // 16-byte loads in flight per lane
+  static constexpr int RND = LD / NL > 0 ? LD / NL : 1;    // rounds of RPW rows in flight per wave
+  static constexpr int ROWS = 4 * RPW * RND;               // rows per workgroup pass
 };
 
 template <int D, int NH>
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(256) void score_block_kernel(const void* __restrict
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int64_t at = (int64_t)(b * Hq + h0 + h) * D + 4 * (sub + 8 * j);
+      const int64_t at = (int64_t)(b * Hq + h0 + h) * D + 4 * (sub + SH::LPR * j);
       float v[4] = {0.f, 0.f, 0.f, 0.f};
       if (h < nh) {
         if (q_bf16) {
@@ -830,14 +834,14 @@ __global__ __launch_bounds__(256) void score_block_kernel(const void* __restrict
     }
   const float* kb = means + (int64_t)b * sb + (int64_t)g * sh;
   const int p0 = blockIdx.x * chunk, p1 = min(p0 + chunk, nrows);
-  for (int base = p0 + wave * 8 * RND; base < p1; base += SH::ROWS) {
+  for (int base = p0 + wave * SH::RPW * RND; base < p1; base += SH::ROWS) {
     uint4 raw[RND][NL];
 #pragma unroll
     for (int r = 0; r < RND; ++r) {
-      const int row = base + 8 * r + grp;
+      const int row = base + SH::RPW * r + grp;
 #pragma unroll
       for (int j = 0; j < NL; ++j)
-        raw[r][j] = row < p1 ? ld16_stream(kb + (int64_t)row * sl + 4 * (sub + 8 * j)) : make_uint4(0, 0, 0, 0);
+        raw[r][j] = row < p1 ? ld16_stream(kb + (int64_t)row * sl + 4 * (sub + SH::LPR * j)) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < RND; ++r) {
@@ -856,7 +860,7 @@ __global__ __launch_bounds__(256) void score_block_kernel(const void* __restrict
       }
 #pragma unroll
       for (int h = 0; h < NH; ++h) part[h] = group_sum<SH::LPR>(part[h]);
-      const int row = base + 8 * r + grp;
+      const int row = base + SH::RPW * r + grp;
       if (row < p1) {
 #pragma unroll
         for (int h = 0; h < NH; ++h)
