@@ -1469,6 +1469,9 @@ __global__ __launch_bounds__(256) void rows_sample_kernel(const float* __restric
 
 constexpr int RC_STAGE = 1024;  // pairs a wave compacts in LDS before writing them out
 
+// Kept: key(s) >= key(T), which for a number T is the float test s >= T (NaN scores fail it, -0
+// equals +0), and everything when T is NaN. Each round is counted, reserved with one atomic per
+// wave, and its kept pairs staged in LDS, which the wave copies out with full-width stores.
 __global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restrict__ S, int n, int64_t stride,
                                                            const float* __restrict__ Tv, uint2* __restrict__ cpair,
                                                            uint32_t* __restrict__ cnt, int capg) {
@@ -1476,7 +1479,8 @@ __global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restri
   __shared__ uint2 stage_all[SW][RC_STAGE];
   const int64_t row = blockIdx.y;
   const float* s = S + row * stride;
-  const uint32_t T = score_key(Tv[row]);
+  const float Tf = Tv[row];
+  const bool tnan = Tf != Tf;
   const int lane = lane_id(), w = threadIdx.x >> 6;
   uint2* out = cpair + row * (int64_t)capg;
   uint2* stage = stage_all[w];
@@ -1490,13 +1494,20 @@ __global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restri
       if (e < c1) r4 = ld16_stream(s + e);
       x[u] = make_float4(__uint_as_float(r4.x), __uint_as_float(r4.y), __uint_as_float(r4.z), __uint_as_float(r4.w));
     }
+    auto kept = [&](int u, float v) {
+      return p0 + (u * 256 + (int)threadIdx.x) * 4 < c1 && (tnan || v >= Tf);
+    };
     uint32_t c = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
-      const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    for (int u = 0; u < U; ++u)
+      c += (kept(u, x[u].x) ? 1u : 0u) + (kept(u, x[u].y) ? 1u : 0u) + (kept(u, x[u].z) ? 1u : 0u) +
+           (kept(u, x[u].w) ? 1u : 0u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c += (e < c1 && score_key(v[j]) >= T) ? 1u : 0u;
+    for (int u = 0; u < U; ++u) {  // the tests are made again below, not held in scalar masks
+      pin_vgpr(x[u].x);
+      pin_vgpr(x[u].y);
+      pin_vgpr(x[u].z);
+      pin_vgpr(x[u].w);
     }
     // the wave's pairs of the round go to one reserved run of the row's list
     const uint32_t incl = wave_incl_scan(c);
@@ -1505,25 +1516,32 @@ __global__ __launch_bounds__(256) void rows_collect_kernel(const float* __restri
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(&cnt[row], tot);
     base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
-    const bool staged = tot <= (uint32_t)RC_STAGE;  // wave-uniform
     uint32_t slot = incl - c;  // this lane's first pair within the wave's run
+    if (tot <= (uint32_t)RC_STAGE) {  // wave-uniform
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
-      const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      for (int u = 0; u < U; ++u) {
+        const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
+        const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e < c1 && score_key(v[j]) >= T) {
-          const uint2 pr = make_uint2(__float_as_uint(v[j]), (uint32_t)(e + j));
-          if (staged) stage[slot] = pr;
-          else if (base + slot < (uint32_t)capg) out[base + slot] = pr;  // a crowded wave: direct stores
-          ++slot;
-        }
+        for (int j = 0; j < 4; ++j)
+          if (kept(u, v[j])) stage[slot++] = make_uint2(__float_as_uint(v[j]), (uint32_t)(e + j));
+      }
+      lds_wave_sync();
+      for (uint32_t i = lane; i < tot && base + i < (uint32_t)capg; i += 64) out[base + i] = stage[i];
+      lds_wave_sync();  // the stage's reads are done before the next round writes it
+    } else {  // a crowded wave: direct stores
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = p0 + (u * 256 + (int)threadIdx.x) * 4;
+        const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (kept(u, v[j])) {
+            if (base + slot < (uint32_t)capg) out[base + slot] = make_uint2(__float_as_uint(v[j]), (uint32_t)(e + j));
+            ++slot;
+          }
+      }
     }
-    if (!staged) continue;
-    lds_wave_sync();
-    for (uint32_t i = lane; i < tot && base + i < (uint32_t)capg; i += 64) out[base + i] = stage[i];
-    lds_wave_sync();  // the stage's reads are done before the next round writes it
   }
 }
 
