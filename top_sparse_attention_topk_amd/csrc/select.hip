@@ -1447,9 +1447,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 constexpr int RC_RUNS = 32, RC_NSAMP = RC_RUNS * 64;
 #ifndef TKA_RC_CHUNK
-#define TKA_RC_CHUNK 16384
+#define TKA_RC_CHUNK 32768
 #endif
-constexpr int RC_CHUNK = TKA_RC_CHUNK;  // positions per collect workgroup
+constexpr int RC_CHUNK = TKA_RC_CHUNK;  // positions per collect workgroup (two rounds)
 constexpr int RC_ROUND = 16384;        // positions per round of it: 16 float4 loads per thread
 static_assert(RC_CHUNK % RC_ROUND == 0, "whole rounds per chunk");
 
