@@ -1434,6 +1434,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   select_row_device(S + (int64_t)b * L, L, L, k, kk, oidx, osel, capw, smem_raw);
 }
 
+// Rows of at most 256 * PER elements, held in registers (thread t the elements t*PER ..): one
+// load of the row, then the k' largest keys by relative-range histograms and the critical bin's
+// few keys ranked one by one (block_kth_regs), and the kept elements emitted in position order
+// with one block scan (block_emit_regs). The same selection as select_row_device: the k' largest
+// keys, the lower position first among equal keys, positions ascending; -1 and -inf past k'.
+template <int PER>
+__global__ __launch_bounds__(256) void select_regs_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
+                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
+                                                          const int32_t* __restrict__ krow) {
+  static_assert(PER % 4 == 0, "16-byte loads of a thread's run");
+  __shared__ SelSmem sm;
+  const int64_t row = blockIdx.x;
+  const float* s = S + row * stride;
+  const int kk = max(0, min(krow ? min(krow[row], k) : k, n));  // krow: a count per row, at most k
+  int32_t* oidx = idx + row * k;
+  float* osel = sel ? sel + row * k : nullptr;
+  const int t = threadIdx.x;
+  for (int j = kk + t; j < k; j += ST) {
+    oidx[j] = -1;
+    if (osel) osel[j] = -INFINITY;
+  }
+  if (kk == 0) return;  // workgroup-uniform
+  const int e0 = t * PER;
+  const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+  uint32_t bits[PER], key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    if (vec && e0 + i + 3 < n) {
+      const uint4 x = ld16(s + e0 + i);
+      bits[i] = x.x; bits[i + 1] = x.y; bits[i + 2] = x.z; bits[i + 3] = x.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bits[i + u] = e0 + i + u < n ? __float_as_uint(s[e0 + i + u]) : 0u;
+    }
+  }
+  // elements past n take key 0 (a NaN's): they rank below every element and after every NaN of
+  // the row (higher positions), and k' <= n never reaches them, so all 256 * PER count as valid
+  // and no per-element bound test is kept live
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = e0 + i < n ? score_key(__uint_as_float(bits[i])) : 0u;
+  uint32_t T, need_eq;
+  block_kth_regs<PER>(key, ST * PER, (uint32_t)kk, sm, &T, &need_eq);
+  block_emit_regs<PER>(key, bits, [&](int i) { return e0 + i; }, ST * PER, T, need_eq, sm, oidx, osel);
+}
+
+// a select of n <= REGS_NMAX elements per row goes through select_regs_kernel. Measured on the
+// two-level step's selects (1024 rows): 2048 -> 128 blocks in 9.3 us against about 15 for
+// select_rows_kernel; 8192 -> 4096 candidates (32 per thread, 156 VGPRs) in 64 us against 60,
+// so longer rows stay with select_rows_kernel
+constexpr int REGS_NMAX = 256 * 8;
+
+static void launch_select_regs(const SelectArgs& a, const int32_t* krow, hipStream_t st) {
+  hipLaunchKernelGGL(select_regs_kernel<8>, dim3((unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n, a.stride, a.k,
+                     a.idx, a.sel, krow);
+}
+
 // ---------------------------------------------------------------------------
 // Many long rows of a score array: the fused exact step's candidate select
 // run over stored scores. 32 runs of 64 consecutive scores per row give each
@@ -2209,6 +2265,10 @@ static int rows_capw(int n, int k, size_t* lds) {
 
 void launch_select_rows_counts(const SelectArgs& a, const int32_t* krow, hipStream_t st) {
   if (a.n_rows <= 0) return;
+  if (a.n <= REGS_NMAX) {  // the whole row in registers
+    launch_select_regs(a, krow, st);
+    return;
+  }
   size_t lds;
   const int capw = rows_capw(a.n, a.k, &lds);
   hipLaunchKernelGGL(select_rows_kernel, dim3((unsigned)a.n_rows), dim3(ST), lds, st, a.scores, a.n, a.stride, a.k,
@@ -2263,6 +2323,10 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
                          dim3(256), 0, st, a.scores, a.n, a.stride, (const float*)T, cpair, cnt, pc.capg);
       launch_prefilter_finish(cpair, cnt, T, pc.capg, a.n_rows, a.n, a.k, 1, 1, 1, a.idx, a.sel, flag, gflag, st);
       launch_select_rows_flagged(a, flag, nullptr, st);  // rows whose candidates cannot hold the answer
+      return;
+    }
+    if (a.n <= REGS_NMAX) {  // the whole row in registers
+      launch_select_regs(a, nullptr, st);
       return;
     }
     size_t lds;
