@@ -163,7 +163,38 @@ __global__ __launch_bounds__(256) void hisa_group_score_kernel(const uint16_t* _
     }
   }
   const uint32_t r0 = blockIdx.x * HG_CB;
-  if (r0 >= U) return;  // workgroup-uniform; no barrier follows
+  if (r0 >= U) return;  // workgroup-uniform
+  // this workgroup's union blocks (ranks r0 .. r0 + HG_CB - 1) and each head's slot of them, found
+  // once here, in parallel (a search per block and per (block, head)), rather than by every wave
+  // in a dependent chain ahead of each block's loads
+  __shared__ int32_t ublk[HG_CB];
+  __shared__ int32_t uslot[HG_CB][16];
+  if (tid < HG_CB && r0 + tid < U) {  // union rank r -> block u: the word holding it, then the bit
+    const uint32_t r = r0 + tid;
+    int lo = 0, hi = W - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    uint32_t x = bm[lo];
+    for (uint32_t c = r - pre[lo]; c > 0; --c) x &= x - 1u;
+    ublk[tid] = lo * 32 + __builtin_ctz(x);
+  }
+  __syncthreads();
+  if (tid < HG_CB * G && r0 + tid / G < U) {  // head h's slot of block u (-1: not kept by head h)
+    const int rr = tid / G, h = tid % G, u = ublk[rr];
+    const int32_t* lh = lists + h * KB;
+    int a = 0, z = KB - 1;
+    while (a < z) {  // first entry >= u (-1 entries sit at the end and count as above every block)
+      const int mid = (a + z) >> 1;
+      const int v = lh[mid];
+      if (v >= 0 && v < u) a = mid + 1;
+      else z = mid;
+    }
+    uslot[rr][h] = lh[a] == u ? a : -1;
+  }
+  __syncthreads();
   // the G heads' query fragments (column n = head n)
   bf16x8_t bq[KS];
   {
@@ -175,30 +206,9 @@ __global__ __launch_bounds__(256) void hisa_group_score_kernel(const uint16_t* _
     }
   }
   const uint16_t* Kb = K + (int64_t)b * sb + (int64_t)g * sh;
-  const int32_t* lh = lists + (n < G ? n : 0) * KB;
   for (uint32_t r = r0 + wave; r < min(U, r0 + HG_CB); r += 4) {
-    // union rank r -> block u: the word holding it, then the bit
-    int lo = 0, hi = W - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= r) lo = mid;
-      else hi = mid - 1;
-    }
-    uint32_t x = bm[lo];
-    for (uint32_t c = r - pre[lo]; c > 0; --c) x &= x - 1u;
-    const int u = lo * 32 + __builtin_ctz(x);
-    // head n's slot of block u (-1: not kept by head n)
-    int j = -1;
-    if (n < G) {
-      int a = 0, z = KB - 1;
-      while (a < z) {  // first entry >= u (-1 entries sit at the end and count as above every block)
-        const int mid = (a + z) >> 1;
-        const int v = lh[mid];
-        if (v >= 0 && v < u) a = mid + 1;
-        else z = mid;
-      }
-      if (lh[a] == u) j = a;
-    }
+    const int u = ublk[r - r0];
+    const int j = n < G ? uslot[r - r0][n] : -1;  // head n's slot of block u
     const int p0 = u * bsz, pe = min(p0 + bsz, L);
     float* crow = j >= 0 ? cand + (row0 + n) * ncand + (int64_t)j * bsz : nullptr;
     for (int t0 = 0; t0 < bsz; t0 += 64) {  // up to four 16-key tiles at a time
