@@ -1434,6 +1434,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   select_row_device(S + (int64_t)b * L, L, L, k, kk, oidx, osel, capw, smem_raw);
 }
 
+constexpr int REGS_STAGE = 4096;  // most kept pairs the register select stages in LDS (32 KiB)
+
 // Rows of at most 256 * PER elements, held in registers (thread t the elements t*PER ..): one
 // load of the row, then the k' largest keys by relative-range histograms and the critical bin's
 // few keys ranked one by one (block_kth_regs), and the kept elements emitted in position order
@@ -1444,7 +1446,9 @@ __global__ __launch_bounds__(256) void select_regs_kernel(const float* __restric
                                                           int32_t* __restrict__ idx, float* __restrict__ sel,
                                                           const int32_t* __restrict__ krow) {
   static_assert(PER % 4 == 0, "16-byte loads of a thread's run");
+  constexpr int STG = ST * PER < REGS_STAGE ? ST * PER : REGS_STAGE;  // kept pairs staged in LDS
   __shared__ SelSmem sm;
+  __shared__ uint32_t stg[2 * STG];  // kept positions, then their score bits
   const int64_t row = blockIdx.x;
   const float* s = S + row * stride;
   const int kk = max(0, min(krow ? min(krow[row], k) : k, n));  // krow: a count per row, at most k
@@ -1476,18 +1480,31 @@ __global__ __launch_bounds__(256) void select_regs_kernel(const float* __restric
   for (int i = 0; i < PER; ++i) key[i] = e0 + i < n ? score_key(__uint_as_float(bits[i])) : 0u;
   uint32_t T, need_eq;
   block_kth_regs<PER>(key, ST * PER, (uint32_t)kk, sm, &T, &need_eq);
-  block_emit_regs<PER>(key, bits, [&](int i) { return e0 + i; }, ST * PER, T, need_eq, sm, oidx, osel);
+  if (kk <= STG) {  // the kept pairs staged in LDS and written out in whole lines
+    block_emit_regs_staged<PER>(key, bits, [&](int i) { return e0 + i; }, ST * PER, T, need_eq, kk, sm, stg,
+                                stg + STG, oidx, osel);
+  } else {
+    block_emit_regs<PER>(key, bits, [&](int i) { return e0 + i; }, ST * PER, T, need_eq, sm, oidx, osel);
+  }
 }
 
 // a select of n <= REGS_NMAX elements per row goes through select_regs_kernel. Measured on the
-// two-level step's selects (1024 rows): 2048 -> 128 blocks in 9.3 us against about 15 for
-// select_rows_kernel; 8192 -> 4096 candidates (32 per thread, 156 VGPRs) in 64 us against 60,
-// so longer rows stay with select_rows_kernel
-constexpr int REGS_NMAX = 256 * 8;
+// two-level step's selects (1024 rows): 2048 -> 128 blocks in 9.4 us against about 15 for
+// select_rows_kernel; 8192 -> 4096 candidates (32 per thread) in 35 us against 60 (64 when the
+// kept pairs were written straight from registers, one scattered word per lane)
+#ifndef TKA_REGS_NMAX
+#define TKA_REGS_NMAX 8192
+#endif
+constexpr int REGS_NMAX = TKA_REGS_NMAX;
 
 static void launch_select_regs(const SelectArgs& a, const int32_t* krow, hipStream_t st) {
-  hipLaunchKernelGGL(select_regs_kernel<8>, dim3((unsigned)a.n_rows), dim3(ST), 0, st, a.scores, a.n, a.stride, a.k,
-                     a.idx, a.sel, krow);
+  const dim3 grid((unsigned)a.n_rows), blk(ST);
+  if (a.n <= 256 * 8)
+    hipLaunchKernelGGL(select_regs_kernel<8>, grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
+  else if (a.n <= 256 * 16)
+    hipLaunchKernelGGL(select_regs_kernel<16>, grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
+  else
+    hipLaunchKernelGGL(select_regs_kernel<32>, grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
 }
 
 // ---------------------------------------------------------------------------

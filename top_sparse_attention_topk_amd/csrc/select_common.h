@@ -158,6 +158,53 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
   }
 }
 
+// As block_emit_regs below, but the kept (position, score bits) go to their slots in LDS first
+// (lidx, lsel: at least kk entries each) and out with 16-byte stores in slot order, so that the
+// global writes are whole lines rather than one scattered word per lane. kk: the number kept.
+template <int PER, typename PosOf, typename SM>
+__device__ __forceinline__ void block_emit_regs_staged(const uint32_t (&key)[PER], const uint32_t (&bits)[PER],
+                                                       PosOf pos_of, int nvalid, uint32_t T, uint32_t need_eq,
+                                                       int kk, SM& sm, uint32_t* lidx, uint32_t* lsel,
+                                                       int32_t* __restrict__ oidx, float* __restrict__ osel) {
+  const int e0 = threadIdx.x * PER;
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (e0 + i < nvalid) {
+      ngt += key[i] > T;
+      neq += key[i] == T;
+    }
+  const uint32_t v = (ngt << 16) | neq;  // totals stay below 2^16
+  uint32_t tot;
+  const uint32_t ex = block_incl_scan_t<SW>(v, sm, &tot) - v;
+  const uint32_t eqb = ex & 0xffffu;
+  uint32_t slot = (ex >> 16) + min(eqb, need_eq), eqs = eqb;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (e0 + i >= nvalid) continue;
+    bool take = key[i] > T;
+    if (key[i] == T) take = eqs++ < need_eq;
+    if (take) {
+      lidx[slot] = (uint32_t)pos_of(i);
+      lsel[slot] = bits[i];
+      ++slot;
+    }
+  }
+  __syncthreads();
+  const bool vec = ((reinterpret_cast<uintptr_t>(oidx) | reinterpret_cast<uintptr_t>(osel)) & 15) == 0;
+  for (int i = 4 * (int)threadIdx.x; i < kk; i += 4 * ST) {
+    if (vec && i + 3 < kk) {
+      *reinterpret_cast<uint4*>(oidx + i) = *reinterpret_cast<const uint4*>(lidx + i);
+      if (osel) *reinterpret_cast<uint4*>(osel + i) = *reinterpret_cast<const uint4*>(lsel + i);
+    } else {
+      for (int c = i; c < min(i + 4, kk); ++c) {
+        oidx[c] = (int32_t)lidx[c];
+        if (osel) osel[c] = __uint_as_float(lsel[c]);
+      }
+    }
+  }
+}
+
 // Emit, in index order, the elements with key > T and the first need_eq with key == T: their
 // positions to oidx and score bits to osel (when given). One packed (greater, equal) block scan.
 template <int PER, typename PosOf, typename SM>
