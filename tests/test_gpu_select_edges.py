@@ -3,7 +3,7 @@ on the same fp32 array: ties across the threshold (lower index wins), +-0,
 +-inf, NaN (below -inf), all-equal rows, values sharing their top 20 bits
 (forces every radix level), sorted rows (candidates all in one wave), huge
 tie runs (streaming emit), k = 1, k = n - 1, k = n, k > n, empty rows, rows
-with a stride, and both launch shapes (one workgroup per row; chunked rows)."""
+with a stride, and every launch shape (one workgroup per row, 256 or 1024 threads; chunked rows)."""
 import zlib
 
 import numpy as np
@@ -58,7 +58,8 @@ def _seed(kind, n):  # stable across processes (str hashes are salted per proces
 
 
 KINDS = ["normal", "dups", "equal", "zeros", "special", "lowbits", "ascending", "descending", "tierun", "staircase"]
-SHAPES = [(200, 3000), (130, 20000), (3, 70001), (1, 300000)]  # row mode x2, chunked mode x2
+# row mode x2, one 1024-thread workgroup per row (a few rows of 8193..32768) x3, chunked mode x2
+SHAPES = [(200, 3000), (130, 20000), (7, 9001), (100, 20000), (5, 32768), (3, 70001), (1, 300000)]
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -110,6 +111,18 @@ def test_select_strided_and_unaligned_rows():
     idx, _ = m.topk_select(view, 100, row_len=4000, row_stride=5003)
     want = orc.select(base.cpu().numpy()[:, 1:4001].copy(), 100)
     assert np.array_equal(idx.cpu().numpy(), want)
+    # a few long rows (one 1024-thread workgroup per row), off alignment, with NaN and -0 kept
+    x = rng.standard_normal((8, 20003)).astype(np.float32)
+    x[:, ::97] = np.nan
+    x[:, 5::89] = -0.0
+    x[:, 7::101] = 0.0
+    wide = torch.from_numpy(x).cuda()
+    for k in (3000, 20000):
+        idx, sel = m.topk_select(wide[:, 1:20002], k, row_len=20001, row_stride=20003)
+        xs = x[:, 1:20002].copy()
+        gi = idx.cpu().numpy()
+        assert np.array_equal(gi, orc.select(xs, k)), k
+        assert np.array_equal(sel.cpu().numpy().view(np.uint32), xs[np.arange(8)[:, None], gi].view(np.uint32))
 
 
 def test_select_empty_rows_pad():

@@ -1365,7 +1365,7 @@ __global__ __launch_bounds__(256) void indexer_cand_kernel(const uint8_t* __rest
   for (int i = 0; i < PER; ++i) key[i] = score_key(__uint_as_float(bits[i]));
   uint32_t T, need_eq;
   block_kth_regs<PER>(key, nv, IC_KEEP, sm, &T, &need_eq);
-  block_emit_regs<PER>(key, bits, [&](int i) { return p0 + t * PER + i; }, nv, T, need_eq, sm, cpos + slot0,
+  block_emit_regs<PER>(key, [&](int i) { return bits[i]; }, [&](int i) { return p0 + t * PER + i; }, nv, T, need_eq, sm, cpos + slot0,
                        reinterpret_cast<float*>(cbits + slot0));
 }
 
@@ -1427,7 +1427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         oidx[jj] = -1;
         if (osel) osel[jj] = -INFINITY;
       }
-      block_emit_regs<PER>(key, bits, [&](int i) { return pos[i]; }, ncand, T, need_eq, sm, oidx, osel);
+      block_emit_regs<PER>(key, [&](int i) { return bits[i]; }, [&](int i) { return pos[i]; }, ncand, T, need_eq, sm, oidx, osel);
       return;
     }
   }
@@ -1436,18 +1436,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 constexpr int REGS_STAGE = 4096;  // most kept pairs the register select stages in LDS (32 KiB)
 
-// Rows of at most 256 * PER elements, held in registers (thread t the elements t*PER ..): one
-// load of the row, then the k' largest keys by relative-range histograms and the critical bin's
-// few keys ranked one by one (block_kth_regs), and the kept elements emitted in position order
-// with one block scan (block_emit_regs). The same selection as select_row_device: the k' largest
-// keys, the lower position first among equal keys, positions ascending; -1 and -inf past k'.
-template <int PER>
-__global__ __launch_bounds__(256) void select_regs_kernel(const float* __restrict__ S, int n, int64_t stride, int k,
-                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                          const int32_t* __restrict__ krow) {
+// Rows of at most 64 * NW * PER elements, held in registers by a workgroup of NW waves (thread t
+// the elements t*PER ..): one load of the row, then the k' largest keys by relative-range
+// histograms and the critical bin's few keys ranked one by one (block_kth_regs), and the kept
+// elements emitted in position order with one block scan (block_emit_regs). The same selection as
+// select_row_device: the k' largest keys, the lower position first among equal keys, positions
+// ascending; -1 and -inf past k'.
+template <int PER, int NW>
+__global__ __launch_bounds__(64 * NW) void select_regs_kernel(const float* __restrict__ S, int n, int64_t stride,
+                                                              int k, int32_t* __restrict__ idx,
+                                                              float* __restrict__ sel,
+                                                              const int32_t* __restrict__ krow) {
   static_assert(PER % 4 == 0, "16-byte loads of a thread's run");
-  constexpr int STG = ST * PER < REGS_STAGE ? ST * PER : REGS_STAGE;  // kept pairs staged in LDS
-  __shared__ SelSmem sm;
+  constexpr int NT = 64 * NW;
+  constexpr int STG = NT * PER < REGS_STAGE ? NT * PER : REGS_STAGE;  // kept pairs staged in LDS
+  __shared__ SelSmemT<NB0, NW> sm;
   __shared__ uint32_t stg[2 * STG];  // kept positions, then their score bits
   const int64_t row = blockIdx.x;
   const float* s = S + row * stride;
@@ -1455,56 +1458,86 @@ __global__ __launch_bounds__(256) void select_regs_kernel(const float* __restric
   int32_t* oidx = idx + row * k;
   float* osel = sel ? sel + row * k : nullptr;
   const int t = threadIdx.x;
-  for (int j = kk + t; j < k; j += ST) {
+  for (int j = kk + t; j < k; j += NT) {
     oidx[j] = -1;
     if (osel) osel[j] = -INFINITY;
   }
   if (kk == 0) return;  // workgroup-uniform
   const int e0 = t * PER;
   const bool vec = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
-  uint32_t bits[PER], key[PER];
+  // only the keys stay in registers; a kept element's score bits come back from its key, except
+  // for the keys that lose them (+-0, NaN), which are read again
+  uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; i += 4) {
+    uint32_t b[4];
     if (vec && e0 + i + 3 < n) {
       const uint4 x = ld16(s + e0 + i);
-      bits[i] = x.x; bits[i + 1] = x.y; bits[i + 2] = x.z; bits[i + 3] = x.w;
+      b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) bits[i + u] = e0 + i + u < n ? __float_as_uint(s[e0 + i + u]) : 0u;
+      for (int u = 0; u < 4; ++u) b[u] = e0 + i + u < n ? __float_as_uint(s[e0 + i + u]) : 0u;
     }
-  }
-  // elements past n take key 0 (a NaN's): they rank below every element and after every NaN of
-  // the row (higher positions), and k' <= n never reaches them, so all 256 * PER count as valid
-  // and no per-element bound test is kept live
+    // elements past n take key 0 (a NaN's): they rank below every element and after every NaN of
+    // the row (higher positions), and k' <= n never reaches them, so all NT * PER count as valid
+    // and no per-element bound test is kept live
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = e0 + i < n ? score_key(__uint_as_float(bits[i])) : 0u;
+    for (int u = 0; u < 4; ++u) key[i + u] = e0 + i + u < n ? score_key(__uint_as_float(b[u])) : 0u;
+  }
+  auto bits_of = [&](int i) -> uint32_t {
+    const uint32_t kx = key[i];
+    if (kx == 0u || kx == 0x80000000u) return __float_as_uint(s[e0 + i]);
+    return (kx & 0x80000000u) ? kx ^ 0x80000000u : ~kx;
+  };
   uint32_t T, need_eq;
-  block_kth_regs<PER>(key, ST * PER, (uint32_t)kk, sm, &T, &need_eq);
+  block_kth_regs<PER>(key, NT * PER, (uint32_t)kk, sm, &T, &need_eq);
   if (kk <= STG) {  // the kept pairs staged in LDS and written out in whole lines
-    block_emit_regs_staged<PER>(key, bits, [&](int i) { return e0 + i; }, ST * PER, T, need_eq, kk, sm, stg,
+    block_emit_regs_staged<PER>(key, bits_of, [&](int i) { return e0 + i; }, NT * PER, T, need_eq, kk, sm, stg,
                                 stg + STG, oidx, osel);
   } else {
-    block_emit_regs<PER>(key, bits, [&](int i) { return e0 + i; }, ST * PER, T, need_eq, sm, oidx, osel);
+    block_emit_regs<PER>(key, bits_of, [&](int i) { return e0 + i; }, NT * PER, T, need_eq, sm, oidx, osel);
   }
 }
 
-// a select of n <= REGS_NMAX elements per row goes through select_regs_kernel. Measured on the
-// two-level step's selects (1024 rows): 2048 -> 128 blocks in 9.4 us against about 15 for
-// select_rows_kernel; 8192 -> 4096 candidates (32 per thread) in 35 us against 60 (64 when the
-// kept pairs were written straight from registers, one scattered word per lane)
+// A select of n <= REGS_NMAX elements per row goes through select_regs_kernel with one 256-thread
+// workgroup per row. Measured on the two-level step's selects (1024 rows): 2048 -> 128 blocks in
+// 9.4 us against about 15 for select_rows_kernel; 8192 -> 4096 candidates (32 per thread) in 35 us
+// against 60 (64 when the kept pairs were written straight from registers, one scattered word per
+// lane). A few rows (fewer than WIDE_ROWS) of up to WIDE_NMAX elements take 1024-thread
+// workgroups instead: a row then needs no split over several workgroups and launches.
 #ifndef TKA_REGS_NMAX
 #define TKA_REGS_NMAX 8192
 #endif
 constexpr int REGS_NMAX = TKA_REGS_NMAX;
+#ifndef TKA_WIDE_ROWS
+#define TKA_WIDE_ROWS 128
+#endif
+#ifndef TKA_WIDE_NW
+#define TKA_WIDE_NW 16
+#endif
+constexpr int WIDE_NMAX = 32768, WIDE_ROWS = TKA_WIDE_ROWS;
+// waves of a wide workgroup: 16 (32 elements per thread) or 8 (64). Measured: 32 rows x 32768,
+// k' = 2048 in 21.4 us with 16 waves (44 bytes per lane spilled at the 128-register cap) against
+// 26.4 with 8 and 38.6 for the split select of several launches; the C2 step 0.0649 -> 0.048 ms
+constexpr int WIDE_NW = TKA_WIDE_NW;
 
 static void launch_select_regs(const SelectArgs& a, const int32_t* krow, hipStream_t st) {
   const dim3 grid((unsigned)a.n_rows), blk(ST);
   if (a.n <= 256 * 8)
-    hipLaunchKernelGGL(select_regs_kernel<8>, grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
+    hipLaunchKernelGGL((select_regs_kernel<8, SW>), grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel,
+                       krow);
   else if (a.n <= 256 * 16)
-    hipLaunchKernelGGL(select_regs_kernel<16>, grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
-  else
-    hipLaunchKernelGGL(select_regs_kernel<32>, grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
+    hipLaunchKernelGGL((select_regs_kernel<16, SW>), grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel,
+                       krow);
+  else if (a.n <= REGS_NMAX)
+    hipLaunchKernelGGL((select_regs_kernel<32, SW>), grid, blk, 0, st, a.scores, a.n, a.stride, a.k, a.idx, a.sel,
+                       krow);
+  else if (a.n <= 1024 * 16)
+    hipLaunchKernelGGL((select_regs_kernel<16, 16>), grid, dim3(1024), 0, st, a.scores, a.n, a.stride, a.k, a.idx,
+                       a.sel, krow);
+  else  // n <= WIDE_NMAX
+    hipLaunchKernelGGL((select_regs_kernel<WIDE_NMAX / (64 * WIDE_NW), WIDE_NW>), grid, dim3(64 * WIDE_NW), 0, st,
+                       a.scores, a.n, a.stride, a.k, a.idx, a.sel, krow);
 }
 
 // ---------------------------------------------------------------------------
@@ -2282,7 +2315,7 @@ static int rows_capw(int n, int k, size_t* lds) {
 
 void launch_select_rows_counts(const SelectArgs& a, const int32_t* krow, hipStream_t st) {
   if (a.n_rows <= 0) return;
-  if (a.n <= REGS_NMAX) {  // the whole row in registers
+  if (a.n <= REGS_NMAX || (a.n_rows < WIDE_ROWS && a.n <= WIDE_NMAX)) {  // the whole row in registers
     launch_select_regs(a, krow, st);
     return;
   }
@@ -2320,6 +2353,10 @@ void launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   if (a.n <= SH_NMAX && a.k <= SH_KMAX) {
     hipLaunchKernelGGL(select_short_kernel, dim3((unsigned)((a.n_rows + 3) / 4)), dim3(256), 0, st, a.scores,
                        a.n_rows, a.n, a.stride, a.k, a.idx, a.sel);
+    return;
+  }
+  if (a.n_rows < WIDE_ROWS && a.n > REGS_NMAX && a.n <= WIDE_NMAX) {  // a few rows, each in one workgroup
+    launch_select_regs(a, nullptr, st);
     return;
   }
   if (!use_split(a.n_rows, a.n)) {

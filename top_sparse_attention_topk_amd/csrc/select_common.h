@@ -12,16 +12,19 @@ constexpr int ST = 256;  // threads per workgroup
 constexpr int SW = 4;    // waves per workgroup
 constexpr int NB0 = 4096;
 
-template <int NB>
+// LDS of a select workgroup of NW waves (at most 16: one scan slot per wave)
+template <int NB, int NW = SW>
 struct alignas(16) SelSmemT {
+  static_assert(NW >= 1 && NW <= 16, "at most 16 waves");
   static constexpr int kBins = NB;
+  static constexpr int kWaves = NW;
   uint32_t hist[NB];
   uint32_t scan[16];
   uint32_t res[2];
   uint32_t aux;
-  uint32_t cnt[SW];
-  uint32_t gt[SW], eq[SW];
-  uint32_t obase[SW], eqbase[SW];
+  uint32_t cnt[NW];
+  uint32_t gt[NW], eq[NW];
+  uint32_t obase[NW], eqbase[NW];
 };
 using SelSmem = SelSmemT<NB0>;
 
@@ -83,8 +86,9 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
   const int t = threadIdx.x, w = t >> 6, lane = lane_id();
   const int e0 = t * PER;
   constexpr int NB = SM::kBins;
+  constexpr int NW = SM::kWaves, NT = 64 * NW;  // the workgroup: NW waves
   constexpr int LB = NB == 4096 ? 12 : (NB == 2048 ? 11 : (NB == 1024 ? 10 : 8));  // bits per level
-  static_assert(NB == (1 << LB) && NB % (64 * SW) == 0, "bins: 256, 1024, 2048 or 4096");
+  static_assert(NB == (1 << LB) && NB % NT == 0, "bins: 256, 1024, 2048 or 4096, a multiple of the threads");
   uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < PER; ++i)
@@ -98,11 +102,11 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
     sm.gt[w] = mn;
     sm.eq[w] = mx;
   }
-  for (int i = t; i < NB; i += ST) sm.hist[i] = 0;
+  for (int i = t; i < NB; i += NT) sm.hist[i] = 0;
   __syncthreads();
   uint32_t base = sm.gt[0], hi = sm.eq[0];
 #pragma unroll
-  for (int i = 1; i < SW; ++i) {
+  for (int i = 1; i < NW; ++i) {
     base = min(base, sm.gt[i]);
     hi = max(hi, sm.eq[i]);
   }
@@ -115,7 +119,7 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
     for (int i = 0; i < PER; ++i)
       if (e0 + i < nvalid && key[i] >= base && key[i] - base <= width) atomicAdd(&sm.hist[(key[i] - base) >> sh], 1u);
     __syncthreads();
-    find_bin_t<SW>(sm.hist, NB, need, sm);
+    find_bin_t<NW>(sm.hist, NB, need, sm);
     const uint32_t bin = sm.res[0], above = sm.res[1], inbin = sm.hist[bin];
     __syncthreads();  // every thread has read the histogram
     need -= above;
@@ -134,7 +138,7 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
       for (int i = 0; i < PER; ++i)
         if (e0 + i < nvalid && key[i] >= base && key[i] - base <= width) stash[atomicAdd(&sm.aux, 1u)] = key[i];
       __syncthreads();
-      for (uint32_t j = t; j < inbin; j += ST) {
+      for (uint32_t j = t; j < inbin; j += NT) {
         const uint32_t v = stash[j];
         uint32_t gt = 0, ge = 0;
         for (uint32_t x = 0; x < inbin; ++x) {
@@ -153,7 +157,7 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
       return;
     }
     sh = sh >= LB ? sh - LB : 0;  // the next level's NB bins cover the bin's 2^sh_old keys
-    for (int i = t; i < NB; i += ST) sm.hist[i] = 0;
+    for (int i = t; i < NB; i += NT) sm.hist[i] = 0;
     __syncthreads();
   }
 }
@@ -161,8 +165,8 @@ __device__ __forceinline__ void block_kth_regs(const uint32_t (&key)[PER], int n
 // As block_emit_regs below, but the kept (position, score bits) go to their slots in LDS first
 // (lidx, lsel: at least kk entries each) and out with 16-byte stores in slot order, so that the
 // global writes are whole lines rather than one scattered word per lane. kk: the number kept.
-template <int PER, typename PosOf, typename SM>
-__device__ __forceinline__ void block_emit_regs_staged(const uint32_t (&key)[PER], const uint32_t (&bits)[PER],
+template <int PER, typename BitsOf, typename PosOf, typename SM>
+__device__ __forceinline__ void block_emit_regs_staged(const uint32_t (&key)[PER], BitsOf bits_of,
                                                        PosOf pos_of, int nvalid, uint32_t T, uint32_t need_eq,
                                                        int kk, SM& sm, uint32_t* lidx, uint32_t* lsel,
                                                        int32_t* __restrict__ oidx, float* __restrict__ osel) {
@@ -176,7 +180,7 @@ __device__ __forceinline__ void block_emit_regs_staged(const uint32_t (&key)[PER
     }
   const uint32_t v = (ngt << 16) | neq;  // totals stay below 2^16
   uint32_t tot;
-  const uint32_t ex = block_incl_scan_t<SW>(v, sm, &tot) - v;
+  const uint32_t ex = block_incl_scan_t<SM::kWaves>(v, sm, &tot) - v;
   const uint32_t eqb = ex & 0xffffu;
   uint32_t slot = (ex >> 16) + min(eqb, need_eq), eqs = eqb;
 #pragma unroll
@@ -186,13 +190,13 @@ __device__ __forceinline__ void block_emit_regs_staged(const uint32_t (&key)[PER
     if (key[i] == T) take = eqs++ < need_eq;
     if (take) {
       lidx[slot] = (uint32_t)pos_of(i);
-      lsel[slot] = bits[i];
+      lsel[slot] = bits_of(i);
       ++slot;
     }
   }
   __syncthreads();
   const bool vec = ((reinterpret_cast<uintptr_t>(oidx) | reinterpret_cast<uintptr_t>(osel)) & 15) == 0;
-  for (int i = 4 * (int)threadIdx.x; i < kk; i += 4 * ST) {
+  for (int i = 4 * (int)threadIdx.x; i < kk; i += 4 * 64 * SM::kWaves) {
     if (vec && i + 3 < kk) {
       *reinterpret_cast<uint4*>(oidx + i) = *reinterpret_cast<const uint4*>(lidx + i);
       if (osel) *reinterpret_cast<uint4*>(osel + i) = *reinterpret_cast<const uint4*>(lsel + i);
@@ -206,9 +210,10 @@ __device__ __forceinline__ void block_emit_regs_staged(const uint32_t (&key)[PER
 }
 
 // Emit, in index order, the elements with key > T and the first need_eq with key == T: their
-// positions to oidx and score bits to osel (when given). One packed (greater, equal) block scan.
-template <int PER, typename PosOf, typename SM>
-__device__ __forceinline__ void block_emit_regs(const uint32_t (&key)[PER], const uint32_t (&bits)[PER], PosOf pos_of, int nvalid,
+// positions to oidx and score bits (bits_of(i) of the thread's element i) to osel (when given).
+// One packed (greater, equal) block scan.
+template <int PER, typename BitsOf, typename PosOf, typename SM>
+__device__ __forceinline__ void block_emit_regs(const uint32_t (&key)[PER], BitsOf bits_of, PosOf pos_of, int nvalid,
                                 uint32_t T, uint32_t need_eq, SM& sm, int32_t* __restrict__ oidx,
                                 float* __restrict__ osel) {
   const int e0 = threadIdx.x * PER;
@@ -221,7 +226,7 @@ __device__ __forceinline__ void block_emit_regs(const uint32_t (&key)[PER], cons
     }
   const uint32_t v = (ngt << 16) | neq;  // totals stay below 2^16
   uint32_t tot;
-  const uint32_t ex = block_incl_scan_t<SW>(v, sm, &tot) - v;
+  const uint32_t ex = block_incl_scan_t<SM::kWaves>(v, sm, &tot) - v;
   const uint32_t eqb = ex & 0xffffu;
   uint32_t slot = (ex >> 16) + min(eqb, need_eq), eqs = eqb;
 #pragma unroll
@@ -231,7 +236,7 @@ __device__ __forceinline__ void block_emit_regs(const uint32_t (&key)[PER], cons
     if (key[i] == T) take = eqs++ < need_eq;
     if (take) {
       oidx[slot] = pos_of(i);
-      if (osel) osel[slot] = __uint_as_float(bits[i]);
+      if (osel) osel[slot] = __uint_as_float(bits_of(i));
       ++slot;
     }
   }
