@@ -221,6 +221,21 @@ def test_indexer_candidates_all_keys_equal():
     assert (gi[1] == np.arange(w.k)).all()
 
 
+def test_indexer_candidates_many_chunks():
+    """601 chunks (9616 candidates: 32 a thread in the finish) over L = 601 * 2048 - 100, with 64 hot
+    keys in one chunk of sequence 0 (its full row select) and sequence 1 on its candidates."""
+    w = fx.shrink(fx.WORKLOADS["C5"], 601 * 2048 - 100, B=2, Hq=8, Hkv=1, k=2048, seed=23)
+    qI, kI, wt = fx.make_indexer(w)
+    q, K, V = fx.make_attn(w)
+    qd = orc.decode_values(orc.E4M3, qI[0])
+    x = (wt[0].astype(np.float64)[:, None] * qd).sum(0)
+    x = 200.0 * x / np.abs(x).max()
+    kI[0, 7 * 2048 + 10:7 * 2048 + 74] = fx.encode(np.tile(x, (64, 1)).astype(np.float32), fx.E4M3)
+    say("[indexer candidates] L 1230748, B 2, k 2048, 64 hot keys in chunk 7 of sequence 0")
+    gi = _run_indexer_both(w, qI, kI, wt, q, K, V)
+    assert np.isin(np.arange(7 * 2048 + 10, 7 * 2048 + 74), gi[0]).all()
+
+
 def test_indexer_candidates_short_last_chunk():
     """L = 16 * 2048 + 5: the last chunk's 5 positions are all candidates (261 in all), k 64."""
     w = fx.shrink(fx.WORKLOADS["C5"], 16 * 2048 + 5, B=3, k=64, seed=21)
