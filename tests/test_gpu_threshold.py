@@ -95,9 +95,10 @@ def test_threshold_scan_several_queries(M, G, d):
     """The several-query scan (one pass over K for the M * G rows of a KV group): rows keeping every
     visible position overflow their stage on every tile, rows keeping a third now and then, rows
     keeping their maximum never, and NaN thresholds keep everything a query can see. With at most 32
-    rows per group two waves score each 16-row block (one per tile half); above 32 each wave scores
-    a block on both halves. Every row's kept set is exactly its visible scores at or above the
-    threshold, the scores bit for bit those of topk_attn_score."""
+    rows per group each wave scores all of them (one or two 16-row blocks) on its own tiles; above
+    32 the workgroup shares each tile and each wave scores a block on both halves. Every row's kept
+    set is exactly its visible scores at or above the threshold, the scores bit for bit those of
+    topk_attn_score."""
     B, Hkv, L = 2, 2, 20000 + 11
     Hq = G * Hkv
     m = tka()

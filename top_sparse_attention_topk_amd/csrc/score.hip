@@ -421,7 +421,268 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Candidate scan for several queries per sequence (2 <= M <= 4), persistent.
+// Candidate scan for several queries per sequence with R = M * G <= 16 * NBLK
+// (query, head) rows per KV group, persistent like the one-query scan: each
+// wave streams its own tiles (every fourth of the workgroup's range) through
+// its padded LDS rows, with no workgroup barrier, and scores all R rows of the
+// group on each tile: the rows fill the 16 columns of NBLK MFMA blocks (column
+// n of block cb is row cb * 16 + n: query (cb * 16 + n) / G, head
+// (cb * 16 + n) % G), so K is read once for every query and no column is
+// padding when R is a multiple of 16. Each lane keeps its rows' fragments,
+// thresholds and causal limits (L - M + t + 1); staging, flushes and the list
+// reservation work per row as in the one-query scan, over R rows.
+// ---------------------------------------------------------------------------
+template <int D, int NBLK>
+__global__ __launch_bounds__(256) void score_cand_rows_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ K, int Hq, int Hkv,
+                                                              int G, int M, int L, int64_t sb, int64_t sh,
+                                                              int64_t sl, float scale, int64_t ntiles, int tpg,
+                                                              int S, MfmaOut o) {
+  constexpr int KS = D / 32;
+  constexpr int P = 32;
+  constexpr int RB = D * 2, PADB = RB + 16, CPR = RB / 16, RPI = 1024 / RB, NI = P / RPI;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, kg = lane >> 4;
+  const int R = M * G;
+  bool hl[NBLK];
+  int tq[NBLK], hh[NBLK], lim[NBLK];
+#pragma unroll
+  for (int cb = 0; cb < NBLK; ++cb) {
+    const int rr = cb * 16 + n;
+    hl[cb] = rr < R;
+    tq[cb] = hl[cb] ? rr / G : 0;
+    hh[cb] = hl[cb] ? rr % G : 0;
+    lim[cb] = L - M + tq[cb] + 1;  // positions this row's query may see
+  }
+  const int lim_all = L - M + 1;  // ... that every query may see
+  extern __shared__ uint4 smem_raw[];
+  uint8_t* rows = reinterpret_cast<uint8_t*>(smem_raw) + (size_t)wave * P * PADB;
+  // S slots per row (R rows), then one spare slot per lane; 6-byte slots as in the one-query scan
+  const int NS = R * S + 64;
+  uint32_t* sbits = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(smem_raw) + (size_t)4 * P * PADB +
+                                                (size_t)wave * NS * 6);
+  uint16_t* soff = reinterpret_cast<uint16_t*>(sbits + NS);
+  int pbase = 0;
+
+  const int64_t per = ntiles / gridDim.x, extra = ntiles % gridDim.x;
+  const int64_t r0 = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
+  const int64_t r1 = r0 + per + ((int64_t)blockIdx.x < extra ? 1 : 0);
+
+  int grp = -1;
+  bf16x8_t bq[NBLK][KS];
+  float Tf[NBLK];
+  bool tnan[NBLK];
+  uint32_t scnt[NBLK];  // staged pairs of row cb * 16 + n (every lane of column n holds it)
+#pragma unroll
+  for (int cb = 0; cb < NBLK; ++cb) {
+    Tf[cb] = 0.f;
+    tnan[cb] = false;
+    scnt[cb] = 0;
+  }
+  auto row_of = [&](int cb) -> int64_t {
+    const int b = grp / Hkv, g = grp % Hkv;
+    return ((int64_t)b * M + tq[cb]) * Hq + g * G + hh[cb];
+  };
+  // list space for every row's staged pairs: lane n < 16 reserves for row cb * 16 + n
+  auto reserve = [&](uint32_t (&base)[NBLK]) {
+#pragma unroll
+    for (int cb = 0; cb < NBLK; ++cb) {
+      base[cb] = 0;
+      if (lane < 16 && hl[cb] && scnt[cb] != 0) base[cb] = atomicAdd(&o.cnt[row_of(cb)], scnt[cb]);
+    }
+  };
+  auto copy_out = [&](const uint32_t (&base)[NBLK]) {
+    const int b = grp / Hkv, g = grp % Hkv;
+#pragma unroll
+    for (int cb = 0; cb < NBLK; ++cb) {
+      for (int h = 0; h < 16; ++h) {
+        const int rr = cb * 16 + h;
+        const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)scnt[cb], h);
+        if (rr >= R || c == 0) continue;  // wave-uniform
+        const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)base[cb], h);
+        const int64_t r = ((int64_t)b * M + rr / G) * Hq + g * G + rr % G;
+        if (o.cpair) {
+          for (uint32_t e = lane; e < c; e += 64)
+            if (bh + e < (uint32_t)o.capg) {
+              u32x2_t x = {sbits[rr * S + e], (uint32_t)pbase + soff[rr * S + e]};
+              __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(o.cpair + r * o.capg + bh + e));
+            }
+        } else {
+          for (uint32_t e = lane; e < c; e += 64)
+            if (bh + e < (uint32_t)o.capg) {
+              __builtin_nontemporal_store(sbits[rr * S + e], o.cbits + r * o.capg + bh + e);
+              __builtin_nontemporal_store(pbase + (int32_t)soff[rr * S + e], o.cpos + r * o.capg + bh + e);
+            }
+        }
+      }
+      scnt[cb] = 0;
+    }
+  };
+  auto flush = [&]() {
+    uint32_t base[NBLK];
+    reserve(base);
+    copy_out(base);
+  };
+  const int64_t jstep = (int64_t)RPI * sl;
+  int lg = -1;
+  const uint16_t* lK = K;
+  auto load = [&](uint4 (&a)[NI], int g, int tin) {
+    if (g != lg) {
+      lg = g;
+      lK = K + (int64_t)(g / Hkv) * sb + (int64_t)(g % Hkv) * sh + (lane % CPR) * 8;
+    }
+    const int at = tin * P;
+    if (at + P <= L) {
+      const uint16_t* p = lK + (int64_t)(at + lane / CPR) * sl;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) a[j] = ld16_stream(p + j * jstep);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int pos = min(at + j * RPI + lane / CPR, L - 1);
+        a[j] = ld16_stream(lK + (int64_t)pos * sl);
+      }
+    }
+  };
+
+  int64_t t = r0 + wave;  // this wave takes every fourth tile of [r0, r1)
+  int cg = 0, ct = 0;
+  uint4 cur[NI];
+  if (t < r1) {
+    cg = (int)(t / tpg);
+    ct = (int)(t % tpg);
+    load(cur, cg, ct);
+  }
+  pbase = ct * P;
+  bool pend = false;  // wave-uniform: flush the stage before this tile's pairs are staged
+  for (; t < r1; t += 4) {
+    int ng = cg, nt = ct + 4;
+    while (nt >= tpg) {
+      nt -= tpg;
+      ++ng;
+    }
+    uint32_t base[NBLK];
+    if (pend) reserve(base);
+    uint4 nxt[NI];
+    const bool more = t + 4 < r1;
+    if (more) load(nxt, ng, nt);
+    if (pend) {
+      copy_out(base);
+      pend = false;
+      pbase = ct * P;
+    }
+    if (cg != grp) {  // new KV group (its stage is empty): the rows' fragments and thresholds
+      grp = cg;
+#pragma unroll
+      for (int cb = 0; cb < NBLK; ++cb) {
+        const int64_t qr = row_of(cb);
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (hl[cb]) v = ld16(q + qr * D + 32 * s2 + 8 * kg);
+          bq[cb][s2] = __builtin_bit_cast(bf16x8_t, v);
+        }
+        const float tv = hl[cb] ? o.T[qr] : 0.f;
+        Tf[cb] = tv;
+        tnan[cb] = tv != tv;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      *reinterpret_cast<uint4*>(rows + (j * RPI + lane / CPR) * PADB + (lane % CPR) * 16) = cur[j];
+    lds_wave_sync();
+    const int pos0 = ct * P;
+    const bool whole = pos0 + P <= lim_all;
+    bool f[NBLK][2][4];
+    float v[NBLK][2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4_t acc[NBLK];
+#pragma unroll
+      for (int cb = 0; cb < NBLK; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const uint4 a = *reinterpret_cast<const uint4*>(rows + (16 * tt + n) * PADB + (kg + 4 * s2) * 16);
+#pragma unroll
+        for (int cb = 0; cb < NBLK; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bq[cb][s2], acc[cb], 0,
+                                                            0, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NBLK; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[cb][tt][i] = acc[cb][i] * scale;
+          f[cb][tt][i] = hl[cb] & (tnan[cb] | (v[cb][tt][i] >= Tf[cb]));
+        }
+    }
+    if (!whole) {  // the last tiles: positions past a row's query limit (or past L) are never kept
+#pragma unroll
+      for (int cb = 0; cb < NBLK; ++cb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[cb][tt][i] = f[cb][tt][i] & (pos0 + 16 * tt + 4 * kg + i < lim[cb]);
+    }
+    __builtin_amdgcn_wave_barrier();  // operand reads of this tile precede the next tile's writes
+    uint32_t tot[NBLK], pre[NBLK];
+    bool over = false;
+#pragma unroll
+    for (int cb = 0; cb < NBLK; ++cb) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c += f[cb][tt][i] ? 1u : 0u;
+      uint32_t c0, c1, p0, p1;  // a row's total over its four lanes and this lane's offset (kg order)
+      rows_swap16(c, c0, c1);
+      const uint32_t pair = c0 + c1;
+      halves_swap32(pair, p0, p1);
+      tot[cb] = p0 + p1;
+      pre[cb] = ((kg & 1) ? c0 : 0u) + ((kg & 2) ? p0 : 0u);
+      over = over || (hl[cb] && scnt[cb] + tot[cb] > (uint32_t)S);
+    }
+    // a row that cannot take this tile's pairs: flush now
+    if (ballot(lane < 16 && over) != 0) {
+      flush();
+      pbase = ct * P;
+    }
+    {  // no branches: a pair not kept goes to the lane's spare slot
+      const uint32_t sp = (uint32_t)(R * S + lane);
+#pragma unroll
+      for (int cb = 0; cb < NBLK; ++cb) {
+        const uint32_t hs = (uint32_t)((cb * 16 + n) * S);
+        uint32_t slot = scnt[cb] + pre[cb];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t e = f[cb][tt][i] ? hs + slot : sp;
+            sbits[e] = __float_as_uint(v[cb][tt][i]);
+            soff[e] = (uint16_t)(pos0 + 16 * tt + 4 * kg + i - pbase);
+            slot += f[cb][tt][i] ? 1u : 0u;
+          }
+        if (hl[cb]) scnt[cb] += tot[cb];
+      }
+    }
+    bool near = false;
+#pragma unroll
+    for (int cb = 0; cb < NBLK; ++cb) near = near || (hl[cb] && scnt[cb] > (uint32_t)(S - PS_GUARD));
+    pend = more && (ng != cg || nt * P + (P - 1) - pbase > 65535 || ballot(lane < 16 && near) != 0);
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) cur[j] = nxt[j];
+    }
+    cg = ng;
+    ct = nt;
+  }
+  if (grp >= 0) flush();
+}
+
+// ---------------------------------------------------------------------------
+// Candidate scan for several queries per sequence (2 <= M <= 4) with more
+// than 32 (query, head) rows per KV group, persistent.
 // Workgroup i owns a contiguous range of 32-position tiles of the flattened
 // (batch * KV head, position) space, as above, but its four waves take every
 // tile together: the workgroup loads a tile once (each thread 16-byte chunks
@@ -432,6 +693,9 @@ __global__ __launch_bounds__(256) void score_cand_persistent_kernel(const uint16
 // ---------------------------------------------------------------------------
 #ifndef TKA_SHARED_SCAN
 #define TKA_SHARED_SCAN 1
+#endif
+#ifndef TKA_ROWS_SCAN
+#define TKA_ROWS_SCAN 1
 #endif
 #ifndef TKA_SS_GUARD
 #define TKA_SS_GUARD 8
@@ -1097,6 +1361,28 @@ static void launch_cand_persistent(const ScoreArgs& a, const MfmaOut& o, hipStre
   int64_t grid = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit));
   if (grid > (ntiles + 3) / 4) grid = (ntiles + 3) / 4;
   const int M = a.M > 1 ? a.M : 1;  // the caller keeps M <= 4
+  if (M > 1 && TKA_ROWS_SCAN && M * a.G <= 32) {
+    // every (query, head) row of a group on one wave's tiles: the one-query scan's LDS layout with
+    // R = M G rows sharing the stage
+    const int R = M * a.G;
+    const int S3 = ((PS_STAGE_BYTES / 6 - 64) / R) & ~1;
+    const size_t lds3 = (size_t)4 * 32 * (D * 2 + 16) + (size_t)4 * (R * S3 + 64) * 6;
+    const int fit3 = (int)(device_lds_limit() / lds3);
+    int64_t g3 = (int64_t)device_cus() * std::max(1, std::min(PS_WPC, fit3));
+    if (g3 > (ntiles + 3) / 4) g3 = (ntiles + 3) / 4;
+    if (R <= 16) {
+      ensure_dynamic_lds((const void*)score_cand_rows_kernel<D, 1>, lds3);
+      hipLaunchKernelGGL((score_cand_rows_kernel<D, 1>), dim3((unsigned)g3), dim3(256), lds3, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh,
+                         a.sl, a.scale, ntiles, tpg, S3, o);
+    } else {
+      ensure_dynamic_lds((const void*)score_cand_rows_kernel<D, 2>, lds3);
+      hipLaunchKernelGGL((score_cand_rows_kernel<D, 2>), dim3((unsigned)g3), dim3(256), lds3, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.keys, a.Hq, a.Hkv, a.G, M, a.nrows, a.sb, a.sh,
+                         a.sl, a.scale, ntiles, tpg, S3, o);
+    }
+    return;
+  }
   if (M > 1 && TKA_SHARED_SCAN) {
     // two tile buffers and four wave stages sized to fit SS_WPC workgroups per CU
     const size_t tiles = (size_t)2 * 32 * (D * 2 + 16);
