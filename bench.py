@@ -806,7 +806,7 @@ def main():
                    "gather_logits": "selected scores" if exact else "K rows"},
         "hbm_gbps_counted": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
         "counted_bytes_per_step": cb,
-        "counted_bytes_note": "north-star count: full K scan + k gathered K and V rows per query head"
+        "counted_bytes_note": "headline byte count: full K scan + k gathered K and V rows per query head"
                               + (" (this path reads no gathered K row: see step_bytes)" if exact else ""),
         "step_bytes": moved, "event_ms_per_step": round(ev_ms, 4),
         "three_call": {"ms_per_step": round(t_three, 4), "queries_per_s": round(w.B / (t_three / 1e3), 1),
