@@ -90,7 +90,7 @@ def test_threshold_scan_head_groupings(G, d):
     _check_kept(s.cpu().numpy(), thr.cpu().numpy(), counts.cpu().numpy(), cs.cpu().numpy(), cp.cpu().numpy())
 
 
-@pytest.mark.parametrize("M,G,d", [(2, 8, 128), (4, 8, 128), (3, 16, 128), (2, 4, 64), (2, 8, 256)])
+@pytest.mark.parametrize("M,G,d", [(2, 8, 128), (4, 8, 128), (3, 16, 128), (2, 4, 64), (2, 8, 256), (4, 8, 64), (2, 16, 256)])
 def test_threshold_scan_several_queries(M, G, d):
     """The several-query scan (one pass over K for the M * G rows of a KV group): rows keeping every
     visible position overflow their stage on every tile, rows keeping a third now and then, rows
