@@ -34,6 +34,8 @@ CASES = {
     "prefilter-g8-m3": (1, 3, 16, 2, 128, 16384, 1024),  # 24 rows: the second 16-row block half full
     "prefilter-g2-m2": (2, 2, 8, 4, 128, 8192, 256),     # 4 rows in one block
     "prefilter-g8-m2-d256": (1, 2, 16, 2, 256, 8192, 512),
+    "prefilter-g16-m2": (1, 2, 32, 2, 128, 12000, 700),  # 32 rows: two full blocks, 16 heads a query
+    "prefilter-g8-m4-d64": (1, 4, 16, 2, 64, 9000, 512),
 }
 
 
