@@ -429,7 +429,23 @@ def time_loop(fn, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
+def cpu_oracle_step(w, q, K, V, qI=None, kI=None, wt=None, repeats: int = 3) -> dict:
+    """The fp64 oracle, as it stands, on one whole step of this workload (every row: score, full
+    sort, attention) on all host threads, `repeats` times; the median with queries/s and GB/s over
+    the same counted bytes as the GPU figures. An unoptimised reference, not a tuned CPU library."""
+    import oracle as orc
+    p = orc.problem_for(w)
+    ts = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        orc.decode(p, q, K, V, qI=qI, kI=kI, w=wt)
+        ts.append(time.perf_counter() - t0)
+    t = statistics.median(ts)
+    return {"kind": "oracle", "threads": orc.threads(), "repeats": repeats, "t_step_ms": round(t * 1e3, 3),
+            "queries_per_s": round(w.B / t, 2), "gbps_counted": round(counted_bytes(w) / t / 1e9, 3)}
+
+
+def proxy_variant(fx, tka, torch, np, w, steps: int, cpu: bool = False) -> dict:
     """Fused step and scoring launch of a proxy-score workload (block means or indexer), each timed
     alone on the launch stream; the scoring launch against the HBM roofline (its algorithmic bytes:
     proxy keys read once, q read, fp32 scores written).
@@ -441,9 +457,13 @@ def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
     q, K, V = fx.make_attn(w)
     to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     qt, Kt, Vt = to(q), to(K), to(V)
+    res = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.L, "top_k": w.k}
+    if cpu:  # the oracle on the same host bytes (one step of L = 1M takes seconds: one repeat there)
+        oi = fx.make_indexer(w) if w.mode == fx.MODE_INDEXER else (None, None, None)
+        res["cpu_oracle"] = cpu_oracle_step(w, q, K, V, *oi, repeats=1 if w.mode == fx.MODE_INDEXER else 3)
+        del oi
     del K, V
     p = tka.problem(w.mode, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, tka.TKA_BF16, 0.0, w.block, w.HI, w.dI)
-    res = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.L, "top_k": w.k}
     if w.mode == fx.MODE_BLOCK:
         means = tka.topk_block_mean_build(p, Kt)
         res["block_size"] = w.block
@@ -489,7 +509,7 @@ def proxy_variant(fx, tka, torch, np, w, steps: int) -> dict:
     return res
 
 
-def exact_variant(fx, tka, torch, np, w, steps: int) -> dict:
+def exact_variant(fx, tka, torch, np, w, steps: int, cpu: bool = False) -> dict:
     """The exact variant at another workload's size: the fused step and the three calls (score, select,
     gather) timed as one step, each on the launch stream. Footprints under 1 GiB rotate over R on-device
     replicas of q, K and V (R * counted bytes >= 1 GiB) so each step reads HBM rather than the 256 MB
@@ -503,6 +523,7 @@ def exact_variant(fx, tka, torch, np, w, steps: int) -> dict:
         to = lambda a: torch.from_numpy(a).cuda()
         dt = tka.TKA_F32
     ins = dict(q=to(q), K=to(K), V=to(V))
+    cpu_rec = cpu_oracle_step(w, q, K, V) if cpu else None
     del K, V
     p = tka.problem(tka.EXACT, w.B, w.Hq, w.Hkv, w.d, w.L, w.k, dt)
     cb = counted_bytes(w)
@@ -557,6 +578,8 @@ def exact_variant(fx, tka, torch, np, w, steps: int) -> dict:
                     "decode_prefilter_forced_ms": round(rotated(fused_prefilter), 4),
                     "decode_ms_mall_warm": round(time_loop(lambda: fused(ins), steps), 4),
                     "three_call_ms_mall_warm": round(time_loop(lambda: three(ins), steps), 4)})
+    if cpu_rec is not None:
+        res["cpu_oracle"] = cpu_rec
     del reps, ins
     return res
 
@@ -907,13 +930,15 @@ def main():
         # one sequence of 32 query heads over 8 KV heads at L = 32K, k = 2048 (C2)
         for wname, key in (("C1", "exact_C1"), ("C2", "exact_C2")):
             log(f"[bench] {key}")
-            extras[key] = exact_variant(fx, tka, torch, np, fx.WORKLOADS[wname], args.steps)
+            extras[key] = exact_variant(fx, tka, torch, np, fx.WORKLOADS[wname], args.steps,
+                                        cpu=not args.no_cpu_baseline)
             torch.cuda.empty_cache()
         # the proxy-score variants at their own workload sizes: block means (MoBA-style, top 16 blocks
         # of 64 at L = 128K) and the lightning indexer (E4M3 keys, top 2048 of L = 1M)
         for wname, key in (("C4", "block_mean_C4"), ("C5", "indexer_C5")):
             log(f"[bench] {key}")
-            extras[key] = proxy_variant(fx, tka, torch, np, fx.WORKLOADS[wname], args.steps)
+            extras[key] = proxy_variant(fx, tka, torch, np, fx.WORKLOADS[wname], args.steps,
+                                        cpu=not args.no_cpu_baseline)
             torch.cuda.empty_cache()
     result["extras"] = extras
     if args.copy_calibration:
