@@ -415,6 +415,15 @@ def profile_mfma(fx, tka, torch, np, steps: int) -> None:
     log(f"[bench] profile-mfma: {steps} launches of each MFMA kernel done")
 
 
+def time_windows(fn, steps: int, multiple: int = 1) -> float:
+    """Median ms per call over five event-timed windows of back-to-back calls, each window at least
+    100 ms (and `steps` calls), its length a whole multiple of `multiple` (replica passes)."""
+    est = time_loop(fn, steps)
+    n = max(steps, int(math.ceil(100.0 / max(est, 1e-4))))
+    n = -(-n // multiple) * multiple
+    return statistics.median([time_loop(fn, n) for _ in range(5)])
+
+
 def time_loop(fn, steps: int) -> float:
     """Average ms per call from HIP events on the current stream (the launch stream)."""
     import torch
@@ -492,10 +501,9 @@ def proxy_variant(fx, tka, torch, np, w, steps: int, cpu: bool = False) -> dict:
         else:
             tka.topk_attn_score(p, r["q_idx"], r["proxy_keys"], idx_w=r["idx_w"], scores=sc)
 
-    def rotated(fn):
+    def rotated(fn):  # whole passes over the replicas; the median of five windows of >= 100 ms
         it = iter(range(1 << 62))
-        n = -(-steps // R) * R  # whole passes over the replicas
-        return time_loop(lambda: fn(reps[next(it) % R]), n)
+        return time_windows(lambda: fn(reps[next(it) % R]), -(-steps // R) * R, R)
 
     t_dec, t_sc = rotated(decode), rotated(score)
     t_dec_w, t_sc_w = time_loop(lambda: decode(ins), steps), time_loop(lambda: score(ins), steps)
@@ -556,10 +564,9 @@ def exact_variant(fx, tka, torch, np, w, steps: int, cpu: bool = False) -> dict:
         tka.topk_select(sc.reshape(rows, w.L), w.k, idx_out=sel_idx, sel_out=sel_val, ws=sws)
         tka.sparse_attn_gather(p, r["q"], r["K"], r["V"], sel_idx, sel_scores=sel_val, out=gout, ws=gws)
 
-    def rotated(fn):
+    def rotated(fn):  # whole passes over the replicas; the median of five windows of >= 100 ms
         it = iter(range(1 << 62))
-        n = -(-steps // R) * R
-        return time_loop(lambda: fn(reps[next(it) % R]), n)
+        return time_windows(lambda: fn(reps[next(it) % R]), -(-steps // R) * R, R)
 
     t_f, t_3 = rotated(fused), rotated(three)
     res = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "seq_len": w.L,
